@@ -1,0 +1,119 @@
+"""Seeded synthetic inputs shared by the tests, the smoke check and the
+benchmark.
+
+This module holds none of the method's arithmetic: it only draws random
+numbers and stores them as 16-bit patterns, using numpy's float64->float16
+conversion and torch's float32->bfloat16 conversion (both round to nearest
+even).  Both the HIP path and the CPU oracle receive what it returns.
+
+Input recipe (the pages fix shapes and distributions, not the generator):
+  * one ``numpy.random.default_rng(seed)`` (PCG64) per workload;
+  * operands are drawn in argument order -- A then B for the GEMM, W then X
+    for the GEMV -- each filled in its own flat storage order (column-major
+    index for GEMM operands, row-major for GEMV operands);
+  * FP16: float64 draw -> nearest-even binary16.  BF16: float64 draw ->
+    nearest-even float32 -> nearest-even bfloat16;
+  * "N(0, s)" means standard deviation s.
+"""
+import numpy as np
+
+F16 = "f16"
+BF16 = "bf16"
+
+# The five workloads of the pages (shapes from the S4000 GEMM write-up's
+# contest size and the DCU decode page's gate/up projection).
+WORKLOADS = {
+    "gemm_512_f16": dict(kind="gemm", M=512, N=512, K=512, fmt=F16,
+                         dist=("uniform", 1.0, 1.0), seed=0),
+    "gemm_8192x8192x16384_f16": dict(kind="gemm", M=8192, N=8192, K=16384, fmt=F16,
+                                     dist=("uniform", 1.0, 1.0), seed=1),
+    "gemm_5000x3000x4100_bf16": dict(kind="gemm", M=5000, N=3000, K=4100, fmt=BF16,
+                                     dist=("normal", 1.0, 1.0), seed=2),
+    "gemv_34816x5120_bf16": dict(kind="gemv", M=34816, K=5120, fmt=BF16,
+                                 n_values=(1, 4, 16), seed=3),
+    "prefill_4096x34816x5120_bf16": dict(kind="gemm", M=4096, N=34816, K=5120, fmt=BF16,
+                                         dist=("normal", 1.0, 0.02), seed=4),
+}
+
+
+def to_bits(values, fmt) -> np.ndarray:
+    """Store float64 values as 16-bit patterns (uint16), nearest-even."""
+    v = np.asarray(values, dtype=np.float64)
+    if fmt == F16:
+        return v.astype(np.float16).view(np.uint16)
+    if fmt == BF16:
+        import torch
+        t = torch.from_numpy(np.ascontiguousarray(v.astype(np.float32)))
+        return t.to(torch.bfloat16).view(torch.int16).numpy().view(np.uint16)
+    raise ValueError(fmt)
+
+
+def from_bits(bits, fmt) -> np.ndarray:
+    """float32 view of 16-bit patterns (for quick looks; exact for both)."""
+    b = np.asarray(bits, np.uint16)
+    if fmt == F16:
+        return b.view(np.float16).astype(np.float32)
+    if fmt == BF16:
+        return (b.astype(np.uint32) << 16).view(np.float32)
+    raise ValueError(fmt)
+
+
+def _draw(rng, size, kind, scale):
+    if kind == "uniform":
+        return rng.uniform(-scale, scale, size)
+    if kind == "normal":
+        return rng.normal(0.0, scale, size)
+    raise ValueError(kind)
+
+
+def gemm_operands(M, N, K, fmt, dist=("uniform", 1.0, 1.0), seed=0):
+    """A (M x K) and B (K x N), column-major, as flat uint16 arrays.
+    dist = (kind, scale_A, scale_B): uniform[-s, s] or normal(0, s)."""
+    kind, sa, sb = dist
+    rng = np.random.default_rng(seed)
+    A = to_bits(_draw(rng, M * K, kind, sa), fmt)
+    B = to_bits(_draw(rng, K * N, kind, sb), fmt)
+    return A, B
+
+
+def gemv_operands(M, K, n, seed=3, sigma_w=0.02, sigma_x=1.0, fmt=BF16):
+    """W row-major [M, K] ~ N(0, sigma_w), X row-major [n, K] ~ N(0, sigma_x)."""
+    rng = np.random.default_rng(seed)
+    W = to_bits(rng.normal(0.0, sigma_w, M * K), fmt)
+    X = to_bits(rng.normal(0.0, sigma_x, n * K), fmt)
+    return W, X
+
+
+def workload_operands(name, n=None):
+    w = WORKLOADS[name]
+    if w["kind"] == "gemm":
+        return gemm_operands(w["M"], w["N"], w["K"], w["fmt"], w["dist"], w["seed"])
+    return gemv_operands(w["M"], w["K"], n, seed=w["seed"], fmt=w["fmt"])
+
+
+def sample_indices(M, N, seed, count=4096):
+    """``count`` distinct flat output indices (m + n*M) drawn with
+    default_rng(1000 + seed), plus the four corners, sorted."""
+    total = M * N
+    rng = np.random.default_rng(1000 + seed)
+    idx = rng.choice(total, size=min(count, total), replace=False)
+    corners = np.array([0, M - 1, (N - 1) * M, total - 1], np.int64)
+    return np.unique(np.concatenate([idx.astype(np.int64), corners]))
+
+
+def small_ints(rng, size, lo, hi):
+    """Integers in [lo, hi] as float64 (exact in every 16-bit format here)."""
+    return rng.integers(lo, hi + 1, size).astype(np.float64)
+
+
+def identity_colmajor(n):
+    """n x n identity, column-major flat float64."""
+    return np.eye(n, dtype=np.float64).ravel(order="F")
+
+
+def cyclic_shift_colmajor(n, s=1):
+    """Permutation matrix P (n x n) with P(i, (i + s) mod n) = 1, column-major
+    flat float64 -- not symmetric for n > 2 and s != 0, n/2."""
+    P = np.zeros((n, n))
+    P[np.arange(n), (np.arange(n) + s) % n] = 1.0
+    return P.ravel(order="F")
