@@ -1,0 +1,220 @@
+"""Benchmark of the hot path on one MI355X.
+
+One step = the dense column-major GEMM at 8192 x 8192 x 16384 (FP16 in, FP32
+accumulation, FP16 out) followed by the decode GEMV y[1,34816] = x[1,5120] W^T
+(BF16), both through the C ABI on one dedicated stream, inputs resident in
+HBM.  The GEMV rotates over 4 copies of W (4 x 356.5 MB) so that W cannot sit
+in the 256 MB last-level cache between steps.
+
+Printed: one JSON line.  `value` is the GEMM's TFLOP/s (2*M*N*K per launch over
+the average launch time measured with HIP events on the launch stream); the
+GEMV's HBM GB/s is reported beside it with its own roofline, against both the
+8 TB/s nominal peak and the read bandwidth measured here by the streaming-read
+probe.  `cpu_baseline` times the CPU oracle on a bounded sample of the same
+GEMM (sampled output entries), scaled to TFLOP/s.
+
+Usage: python bench.py [--gpus 1] [--steps 20] [--warmup 5] [--no-cpu-baseline]
+"""
+import argparse
+import json
+import os
+import sys
+import time
+
+ROOT = os.path.dirname(os.path.abspath(__file__))
+sys.path.insert(0, ROOT)
+
+METRIC = "GEMM TFLOP/s at 8192x8192x16384 (% MFMA peak); decode GEMV HBM GB/s (% peak)"
+GEMM_CFG = "gemm_8192x8192x16384_f16"
+GEMV_CFG = "gemv_34816x5120_bf16"
+W_COPIES = 4
+
+
+def parse():
+    p = argparse.ArgumentParser()
+    p.add_argument("--gpus", type=int, default=1)
+    p.add_argument("--steps", type=int, default=20)
+    p.add_argument("--warmup", type=int, default=5)
+    p.add_argument("--tile", type=int, default=0, help="GEMM tile (0 = automatic)")
+    p.add_argument("--group-m", type=int, default=0)
+    p.add_argument("--xcd-remap", type=int, default=1)
+    p.add_argument("--rows-per-block", type=int, default=0)
+    p.add_argument("--gemv-n", type=int, default=1)
+    p.add_argument("--no-cpu-baseline", action="store_true")
+    p.add_argument("--cpu-seconds", type=float, default=12.0,
+                   help="target CPU time of the oracle sample")
+    return p.parse_args()
+
+
+def dev(bits):
+    import numpy as np
+    import torch
+    return torch.from_numpy(np.ascontiguousarray(bits).view(np.int16)).cuda()
+
+
+def hbm_probe(binding, torch, stream, nbytes=4 << 30, reps=20):
+    """Median achievable read bandwidth (GB/s) of the streaming-read probe."""
+    buf = torch.empty(nbytes // 4, dtype=torch.int32, device="cuda")
+    buf.fill_(7)
+    sink = torch.zeros(binding.hbm_read_sink_words(), dtype=torch.int32, device="cuda")
+    ts = []
+    with torch.cuda.stream(stream):
+        for i in range(reps + 3):
+            e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+            e0.record(stream)
+            code = binding.lib().migemm_hbm_read(buf.data_ptr(), nbytes, sink.data_ptr(),
+                                                 stream.cuda_stream)
+            e1.record(stream)
+            assert code == 0, code
+            stream.synchronize()
+            if i >= 3:
+                ts.append(e0.elapsed_time(e1) / 1e3)
+    ts.sort()
+    del buf
+    return nbytes / ts[len(ts) // 2] / 1e9
+
+
+def cpu_baseline(A, B, M, N, K, target_s):
+    """Oracle GFLOP rate on sampled entries of the GEMM, ~target_s seconds."""
+    import numpy as np
+    import oracle
+    import synth
+    cores = int(os.environ.get("OMP_NUM_THREADS", len(os.sched_getaffinity(0))))
+    idx_all = synth.sample_indices(M, N, 1, count=65536)
+    n = 64
+    t0 = time.perf_counter()
+    oracle.gemm_sampled(A, B, M, N, K, idx_all[:n], "f16")
+    dt = time.perf_counter() - t0
+    n = int(min(idx_all.size, max(64, n * target_s / max(dt, 1e-3))))
+    t0 = time.perf_counter()
+    r = oracle.gemm_sampled(A, B, M, N, K, idx_all[:n], "f16")
+    dt = time.perf_counter() - t0
+    assert r.macs == n * K
+    return {"value": round(2.0 * n * K / dt / 1e12, 9), "unit": "TFLOP/s", "cores": cores,
+            "kind": "oracle", "seconds": round(dt, 3),
+            "sample": "%d sampled output entries of the 8192x8192x16384 FP16 GEMM "
+                      "(K = 16384 multiply-adds each, FP64 accumulation)" % n}
+
+
+def main():
+    args = parse()
+    if args.gpus != 1:
+        print("bench.py measures one GPU: the path runs on a single MI355X and has no "
+              "multi-GPU mode (--gpus %d requested)" % args.gpus, file=sys.stderr)
+        sys.exit(2)
+    import numpy as np
+    import torch
+
+    import synth
+    from bf16_gemm_decode_amd import binding, roofline as rf
+
+    torch.cuda.set_device(0)
+    stream = torch.cuda.Stream()
+    props = torch.cuda.get_device_properties(0)
+
+    wg = synth.WORKLOADS[GEMM_CFG]
+    M, N, K = wg["M"], wg["N"], wg["K"]
+    A, B = synth.workload_operands(GEMM_CFG)
+    dA, dB = dev(A), dev(B)
+    dC = torch.empty(M * N, dtype=torch.int16, device="cuda")
+
+    wv = synth.WORKLOADS[GEMV_CFG]
+    GM, GK, gn = wv["M"], wv["K"], args.gemv_n
+    W, X = synth.gemv_operands(GM, GK, gn, seed=wv["seed"])
+    dW = [dev(W)]
+    for _ in range(W_COPIES - 1):
+        dW.append(dW[0].clone())
+    dX = dev(X)
+    dY = torch.empty(gn * GM, dtype=torch.int16, device="cuda")
+    torch.cuda.synchronize()
+
+    probe_GBps = hbm_probe(binding, torch, stream)
+
+    L = binding.lib()
+    h = stream.cuda_stream
+
+    def gemm():
+        return L.gemm_ex(binding.F16, dA.data_ptr(), dB.data_ptr(), dC.data_ptr(), M, N, K,
+                         args.tile, args.group_m, args.xcd_remap, h)
+
+    def gemv(i):
+        return L.gemv_bf16_ex(dW[i % W_COPIES].data_ptr(), dX.data_ptr(), dY.data_ptr(),
+                              GM, GK, gn, args.rows_per_block, h)
+
+    for i in range(args.warmup):
+        assert gemm() == 0 and gemv(i) == 0
+    stream.synchronize()
+
+    ev = [[torch.cuda.Event(enable_timing=True) for _ in range(4)] for _ in range(args.steps)]
+    torch.cuda.synchronize()
+    t0 = time.perf_counter()
+    for i in range(args.steps):
+        e = ev[i]
+        e[0].record(stream)
+        rc1 = gemm()
+        e[1].record(stream)
+        e[2].record(stream)
+        rc2 = gemv(i)
+        e[3].record(stream)
+        assert rc1 == 0 and rc2 == 0, (rc1, rc2)
+    stream.synchronize()
+    torch.cuda.synchronize()
+    wall = time.perf_counter() - t0
+
+    gemm_s = [e[0].elapsed_time(e[1]) / 1e3 for e in ev]
+    gemv_s = [e[2].elapsed_time(e[3]) / 1e3 for e in ev]
+    gemm_avg, gemv_avg = sum(gemm_s) / len(gemm_s), sum(gemv_s) / len(gemv_s)
+    tflops = rf.gemm_flop(M, N, K) / gemm_avg / 1e12
+    gemv_bytes = rf.gemv_bytes(GM, GK, gn)
+    gemv_GBps = gemv_bytes / gemv_avg / 1e9
+    peak = rf.MI355X["mfma_f16_tflops"]
+    hbm = rf.MI355X["hbm_GBps"]
+
+    # parity spot check of what was timed (the full checks live in the tests)
+    import oracle
+    idx = synth.sample_indices(M, N, wg["seed"], count=256)
+    got = dC.cpu().numpy().view(np.uint16)[idx]
+    ok_g, _ = oracle.check(got, oracle.gemm_sampled(A, B, M, N, K, idx, "f16"), "f16")
+    ok_v, _ = oracle.check(dY.cpu().numpy().view(np.uint16), oracle.gemv(W, X, GM, GK, gn), "bf16")
+
+    out = {
+        "metric": METRIC,
+        "value": round(tflops, 2),
+        "unit": "TFLOP/s",
+        "n_gpus": 1,
+        "steps": args.steps,
+        "warmup": args.warmup,
+        "ms_per_step": round(wall / args.steps * 1e3, 4),
+        "higher_is_better": True,
+        "scaling": "weak",
+        "vs_baseline": None,
+        "dtype": "f16",
+        "data": "synthetic",
+        "config": {"workload": "%s + %s (n=%d)" % (GEMM_CFG, GEMV_CFG, gn),
+                   "gemm": {"M": M, "N": N, "K": K, "dtype": "f16", "layout": "column-major",
+                            "tile": args.tile, "group_m": args.group_m,
+                            "xcd_remap": args.xcd_remap},
+                   "gemv": {"M": GM, "K": GK, "n": gn, "dtype": "bf16",
+                            "rows_per_block": args.rows_per_block or 8,
+                            "w_copies_rotated": W_COPIES}},
+        "roofline": {"bound": "mfma", "achieved": round(tflops, 2), "peak": peak,
+                     "unit": "TFLOP/s", "frac": round(tflops / peak, 4), "traffic": None,
+                     "kernel": "gemm_kernel (2*M*N*K FLOP per launch)",
+                     "avg_launch_ms": round(gemm_avg * 1e3, 4)},
+        "gemv": {"GBps": round(gemv_GBps, 1), "avg_launch_us": round(gemv_avg * 1e6, 2),
+                 "roofline": {"bound": "hbm", "achieved": round(gemv_GBps, 1), "peak": hbm,
+                              "unit": "GB/s", "frac": round(gemv_GBps / hbm, 4),
+                              "traffic": None,
+                              "algorithmic_bytes": int(gemv_bytes)},
+                 "probe_read_GBps": round(probe_GBps, 1),
+                 "frac_of_probe": round(gemv_GBps / probe_GBps, 4)},
+        "parity_spot_check": {"gemm_256_samples": bool(ok_g), "gemv_all": bool(ok_v)},
+        "device": {"name": props.name, "cus": props.multi_processor_count},
+    }
+    if not args.no_cpu_baseline:
+        out["cpu_baseline"] = cpu_baseline(A, B, M, N, K, args.cpu_seconds)
+    print(json.dumps(out), flush=True)
+
+
+if __name__ == "__main__":
+    main()

@@ -1,0 +1,223 @@
+// api.hip -- the C ABI declared in include/migemm.h: argument checks,
+// configuration choice and launch.  Every argument error is detected here,
+// on the host, before any HIP call.
+#include <stdint.h>
+#include <string.h>
+
+#include "common.hpp"
+#include "kernels.hpp"
+#include "migemm.h"
+#include "tile_map.hpp"
+
+namespace migemm {
+int gemv_rows_per_wave(int n_tokens, int rows_per_block);
+}
+
+using namespace migemm;
+
+namespace {
+
+bool overlaps(const void *a, size_t abytes, const void *b, size_t bbytes)
+{
+    if (abytes == 0 || bbytes == 0) return false;
+    uintptr_t a0 = (uintptr_t)a, b0 = (uintptr_t)b;
+    return a0 < b0 + bbytes && b0 < a0 + abytes;
+}
+
+int vec_width(const void *p, int64_t stride_elems)
+{
+    uintptr_t a = (uintptr_t)p;
+    if (stride_elems % 8 == 0 && a % 16 == 0) return 8;
+    if (stride_elems % 2 == 0 && a % 4 == 0) return 2;
+    return 1;
+}
+
+int64_t cdiv(int64_t a, int64_t b) { return (a + b - 1) / b; }
+
+// Shared by gemm_ex and migemm_gemm_plan_for.  Returns 0 and fills L (and
+// *launch = true) when a kernel must run, 0 with *launch = false for an empty
+// output, or a negative MIGEMM_ERR_* code.
+int plan_gemm(int dtype, const uint16_t *A, const uint16_t *B, const uint16_t *C, int M, int N,
+              int K, int tile, int group_m, int xcd_remap, GemmLaunch &L, bool &launch)
+{
+    launch = false;
+    if (dtype != DT_F16 && dtype != DT_BF16) return MIGEMM_ERR_CONFIG;
+    if (tile < TILE_AUTO || tile > TILE_128x128 || group_m < 0 || xcd_remap < 0 || xcd_remap > 1)
+        return MIGEMM_ERR_CONFIG;
+    if (M < 0 || N < 0 || K < 0) return MIGEMM_ERR_DIM;
+    if (M > MIGEMM_MAX_MN || N > MIGEMM_MAX_MN || K > MIGEMM_MAX_K) return MIGEMM_ERR_SIZE;
+    const size_t abytes = (size_t)M * K * 2, bbytes = (size_t)K * N * 2, cbytes = (size_t)M * N * 2;
+    if ((abytes && !A) || (bbytes && !B) || (cbytes && !C)) return MIGEMM_ERR_NULL;
+    if (((uintptr_t)A | (uintptr_t)B | (uintptr_t)C) & 1) return MIGEMM_ERR_ALIGN;
+    if (overlaps(C, cbytes, A, abytes) || overlaps(C, cbytes, B, bbytes)) return MIGEMM_ERR_OVERLAP;
+
+    L = GemmLaunch{};
+    L.dtype = dtype;
+    L.A = A;
+    L.B = B;
+    L.C = const_cast<uint16_t *>(C);
+    L.M = M;
+    L.N = N;
+    L.K = K;
+    L.vec_a = vec_width(A, M);
+    L.vec_b = vec_width(B, K);
+    L.c_vec = (M % 4 == 0 && (uintptr_t)C % 8 == 0) ? 1 : 0;
+    const bool wide = (L.vec_a == 8 && L.vec_b == 8);
+    if (tile == TILE_AUTO) {
+        if (wide && cdiv(M, 256) * cdiv(N, 256) >= 512)
+            tile = TILE_256x256;
+        else if (wide && cdiv(M, 256) * cdiv(N, 128) >= 512)
+            tile = TILE_256x128;
+        else
+            tile = TILE_128x128;
+    } else if (tile != TILE_128x128 && !wide) {
+        return MIGEMM_ERR_CONFIG;   // the 256-row tiles load only 16-byte vectors
+    }
+    L.tile = tile;
+    const int bm = (tile == TILE_128x128) ? 128 : 256;
+    const int bn = (tile == TILE_256x256) ? 256 : 128;
+    const int64_t pm = cdiv(M, bm), pn = cdiv(N, bn);
+    if (pm * pn > 0x7fffffff) return MIGEMM_ERR_SIZE;
+    L.num_pid_m = (int)(pm ? pm : 1);
+    L.num_pid_n = (int)(pn ? pn : 1);
+    int gm = group_m ? group_m : 8;
+    if (gm > L.num_pid_m) gm = L.num_pid_m;
+    L.group_m = gm;
+    L.num_xcd = xcd_remap ? 8 : 1;
+    L.grid = pm * pn;
+    launch = (M > 0 && N > 0);
+    return MIGEMM_OK;
+}
+
+int finish(hipError_t e, void *stream)
+{
+    if (e != hipSuccess) return (int)e;
+    if (stream == nullptr) {
+        e = hipStreamSynchronize(nullptr);
+        if (e != hipSuccess) return (int)e;
+    }
+    return MIGEMM_OK;
+}
+
+}  // namespace
+
+extern "C" {
+
+int gemm_ex(int dtype, const uint16_t *A, const uint16_t *B, uint16_t *C, int M, int N, int K,
+            int tile, int group_m, int xcd_remap, void *stream)
+{
+    GemmLaunch L;
+    bool launch;
+    int rc = plan_gemm(dtype, A, B, C, M, N, K, tile, group_m, xcd_remap, L, launch);
+    if (rc != MIGEMM_OK || !launch) return rc;
+    return finish(gemm_launch(L, (hipStream_t)stream), stream);
+}
+
+int gemm_f16(const uint16_t *A, const uint16_t *B, uint16_t *C, int M, int N, int K, void *stream)
+{
+    return gemm_ex(DT_F16, A, B, C, M, N, K, TILE_AUTO, 0, 1, stream);
+}
+
+int gemm_bf16(const uint16_t *A, const uint16_t *B, uint16_t *C, int M, int N, int K, void *stream)
+{
+    return gemm_ex(DT_BF16, A, B, C, M, N, K, TILE_AUTO, 0, 1, stream);
+}
+
+int migemm_gemm_plan_for(int dtype, const uint16_t *A, const uint16_t *B, const uint16_t *C,
+                         int M, int N, int K, int tile, int group_m, int xcd_remap,
+                         migemm_gemm_plan *plan)
+{
+    GemmLaunch L;
+    bool launch;
+    int rc = plan_gemm(dtype, A, B, C, M, N, K, tile, group_m, xcd_remap, L, launch);
+    if (rc != MIGEMM_OK || !plan) return rc;
+    memset(plan, 0, sizeof(*plan));
+    plan->tile_m = (L.tile == TILE_128x128) ? 128 : 256;
+    plan->tile_n = (L.tile == TILE_256x256) ? 256 : 128;
+    plan->tile_k = 64;
+    plan->waves = 4;
+    plan->group_m = L.group_m;
+    plan->xcd_remap = L.num_xcd > 1;
+    plan->vec_a = L.vec_a;
+    plan->vec_b = L.vec_b;
+    plan->grid = launch ? L.grid : 0;
+    plan->lds_bytes = 2 * 64 * (plan->tile_m + plan->tile_n) * 2;
+    return rc;
+}
+
+int gemv_bf16_ex(const uint16_t *W, const uint16_t *X, uint16_t *Y, int M, int K, int n,
+                 int rows_per_block, void *stream)
+{
+    if (!(rows_per_block == 0 || rows_per_block == 2 || rows_per_block == 4 ||
+          rows_per_block == 8 || rows_per_block == 16 || rows_per_block == 32))
+        return MIGEMM_ERR_CONFIG;
+    if (M < 0 || K < 0 || n < 0) return MIGEMM_ERR_DIM;
+    const size_t wbytes = (size_t)M * K * 2, xbytes = (size_t)n * K * 2, ybytes = (size_t)n * M * 2;
+    if ((wbytes && !W) || (xbytes && !X) || (ybytes && !Y)) return MIGEMM_ERR_NULL;
+    if (((uintptr_t)W | (uintptr_t)X | (uintptr_t)Y) & 1) return MIGEMM_ERR_ALIGN;
+    if (overlaps(Y, ybytes, W, wbytes) || overlaps(Y, ybytes, X, xbytes)) return MIGEMM_ERR_OVERLAP;
+    if (M == 0 || n == 0) return MIGEMM_OK;
+
+    GemvLaunch L{};
+    L.W = W;
+    L.M = M;
+    L.K = K;
+    L.rows_per_block = rows_per_block ? rows_per_block : 8;
+    L.vec = (K % 8 == 0 && (uintptr_t)W % 16 == 0 && (uintptr_t)X % 16 == 0) ? 8 : 1;
+    L.grid = cdiv(M, L.rows_per_block);
+    // Token blocks of 16, 8, 4, 2, 1: each launch streams W once.
+    int done = 0;
+    hipError_t e = hipSuccess;
+    while (done < n && e == hipSuccess) {
+        int left = n - done;
+        int nt = left >= 16 ? 16 : left >= 8 ? 8 : left >= 4 ? 4 : left >= 2 ? 2 : 1;
+        L.n = nt;
+        L.X = X + (size_t)done * K;
+        L.Y = Y + (size_t)done * M;
+        e = gemv_launch(L, (hipStream_t)stream);
+        done += nt;
+    }
+    return finish(e, stream);
+}
+
+int gemv_bf16(const uint16_t *W, const uint16_t *X, uint16_t *Y, int M, int K, int n, void *stream)
+{
+    return gemv_bf16_ex(W, X, Y, M, K, n, 0, stream);
+}
+
+int migemm_tile_coord(int64_t wg, int64_t num_pid_m, int64_t num_pid_n, int64_t group_m,
+                      int64_t num_xcd, int64_t *pid_m, int64_t *pid_n)
+{
+    if (num_pid_m <= 0 || num_pid_n <= 0 || group_m <= 0 || num_xcd <= 0 || wg < 0 ||
+        wg >= num_pid_m * num_pid_n || !pid_m || !pid_n)
+        return MIGEMM_ERR_DIM;
+    tile_coord<int64_t>(wg, num_pid_m, num_pid_n, group_m, num_xcd, *pid_m, *pid_n);
+    return MIGEMM_OK;
+}
+
+const char *migemm_strerror(int code)
+{
+    switch (code) {
+    case MIGEMM_OK: return "ok";
+    case MIGEMM_ERR_DIM: return "negative dimension";
+    case MIGEMM_ERR_NULL: return "null pointer with a non-zero extent";
+    case MIGEMM_ERR_OVERLAP: return "output overlaps an input";
+    case MIGEMM_ERR_ALIGN: return "pointer not 2-byte aligned";
+    case MIGEMM_ERR_CONFIG: return "configuration not offered";
+    case MIGEMM_ERR_SIZE: return "dimension beyond the supported range";
+    }
+    return code > 0 ? "HIP runtime error (code is a hipError_t)" : "unknown error";
+}
+
+int migemm_abi_version(void) { return 1; }
+
+int migemm_hbm_read(const void *buf, size_t bytes, uint32_t *sink, void *stream)
+{
+    if ((bytes && !buf) || !sink) return MIGEMM_ERR_NULL;
+    if ((uintptr_t)buf % 16 || bytes % 16) return MIGEMM_ERR_ALIGN;
+    return finish(hbm_read_launch(buf, bytes, sink, (hipStream_t)stream), stream);
+}
+
+int migemm_hbm_read_sink_words(void) { return hbm_read_sink_words(); }
+
+}  // extern "C"

@@ -1,0 +1,40 @@
+// kernels.hpp -- launch descriptors shared by the C-ABI layer and the kernels.
+#pragma once
+
+#include <hip/hip_runtime.h>
+#include <stdint.h>
+
+namespace migemm {
+
+enum GemmTile { TILE_AUTO = 0, TILE_256x256 = 1, TILE_256x128 = 2, TILE_128x128 = 3 };
+
+struct GemmLaunch {
+    int dtype;                    // DT_F16 or DT_BF16
+    int tile;                     // GemmTile (never TILE_AUTO here)
+    const uint16_t *A, *B;
+    uint16_t *C;
+    int M, N, K;
+    int num_pid_m, num_pid_n;
+    int group_m, num_xcd;
+    int vec_a, vec_b;             // elements per global->LDS load (8, 2 or 1)
+    int c_vec;                    // 1: 8-byte stores of 4 rows are aligned
+    int64_t grid;
+};
+
+hipError_t gemm_launch(const GemmLaunch &L, hipStream_t stream);
+
+struct GemvLaunch {
+    const uint16_t *W, *X;
+    uint16_t *Y;
+    int M, K, n;                  // n: tokens in this launch (1, 2, 4, 8 or 16)
+    int rows_per_block;           // 2, 4, 8, 16 or 32
+    int vec;                      // 8: 16-byte loads; 1: element loads
+    int64_t grid;
+};
+
+hipError_t gemv_launch(const GemvLaunch &L, hipStream_t stream);
+
+hipError_t hbm_read_launch(const void *buf, size_t bytes, uint32_t *sink, hipStream_t stream);
+int hbm_read_sink_words();
+
+}  // namespace migemm

@@ -1,0 +1,167 @@
+/*
+ * migemm.h -- C ABI of the MI355X (gfx950) dense GEMM and decode GEMV.
+ *
+ * Element types.  Every matrix element is a raw 16-bit pattern (uint16_t):
+ * IEEE binary16 for the *_f16 calls, bfloat16 for the *_bf16 calls.  The
+ * library reinterprets the bits; it never converts the caller's data.
+ *
+ * Arithmetic (MTT S4000 GEMM write-up, blog.mthreads.com GEMM03, section 1,
+ * rules table): 16-bit inputs, FP32 accumulation, 16-bit output rounded to
+ * nearest-even.  The k-summation order is unspecified (any FP32 order).
+ *
+ * Pointers are DEVICE pointers (hipMalloc / torch CUDA tensors) unless noted.
+ * The caller owns every buffer.  The library allocates no device memory,
+ * creates no streams and keeps no mutable state, so calls on different
+ * streams may run concurrently.
+ *
+ * stream: a hipStream_t passed as void*.  NULL means the null stream AND that
+ * the call waits for its work to finish before returning (the "complete before
+ * return" rule of the write-up's rules table).  A non-NULL stream makes the call
+ * stream-ordered: it returns after enqueueing.
+ *
+ * Return codes: 0 on success; a negative MIGEMM_ERR_* code for argument
+ * errors, detected on the host BEFORE any HIP call (nothing is launched or
+ * written); a positive hipError_t if a launch or the synchronisation fails.
+ * No exceptions cross the ABI and nothing is printed.
+ */
+#ifndef MIGEMM_H
+#define MIGEMM_H
+
+#include <stddef.h>
+#include <stdint.h>
+
+#ifdef __cplusplus
+extern "C" {
+#endif
+
+#define MIGEMM_OK            0
+#define MIGEMM_ERR_DIM      (-1)  /* a dimension is negative                     */
+#define MIGEMM_ERR_NULL     (-2)  /* NULL pointer where the extent is non-zero   */
+#define MIGEMM_ERR_OVERLAP  (-3)  /* the output overlaps an input's byte range   */
+#define MIGEMM_ERR_ALIGN    (-4)  /* a pointer is not 2-byte aligned             */
+#define MIGEMM_ERR_CONFIG   (-5)  /* an explicit configuration is not offered    */
+#define MIGEMM_ERR_SIZE     (-6)  /* a dimension exceeds the supported range     */
+
+/* Largest supported dimensions (element offsets inside one tile must fit the
+ * 31-bit range of a buffer descriptor): M and N up to 2^23, K up to 2^21. */
+#define MIGEMM_MAX_MN  (1 << 23)
+#define MIGEMM_MAX_K   (1 << 21)
+
+/*
+ * gemm_f16 / gemm_bf16 -- C = A x B, column-major.
+ *
+ * Defined by the write-up's section 2 (GEMM basics): the triple loop
+ * C(m,n) = sum_k A(m,k) * B(k,n) and the column-major addressing
+ *     A(m,k) = A[m + k*M]   (M x K, m fastest)
+ *     B(k,n) = B[k + n*K]   (K x N, k fastest)
+ *     C(m,n) = C[m + n*M]   (M x N, m fastest)
+ * with the argument order (A, B, C, M, N, K) of the write-up's host entry
+ * point (section 3.1); `stream` is appended.
+ *
+ * A and B are read only, never written.  C is written only at its M*N
+ * elements.  Any shape is accepted: M == 0 or N == 0 returns 0 without a
+ * launch; K == 0 writes +0.0 to every element of C (the empty sum).
+ * Errors: MIGEMM_ERR_DIM, _NULL, _ALIGN, _OVERLAP (C's bytes intersect A's
+ * or B's), _SIZE; see above.
+ */
+int gemm_f16(const uint16_t *A, const uint16_t *B, uint16_t *C,
+             int M, int N, int K, void *stream);
+int gemm_bf16(const uint16_t *A, const uint16_t *B, uint16_t *C,
+              int M, int N, int K, void *stream);
+
+/*
+ * gemv_bf16 -- decode GEMV Y = X W^T (bfloat16).
+ *
+ * Defined by the DCU decode page (forum.sourcefind.cn db785961), section 6.1:
+ * the linear layer Y = X W^T with X:[n,k] (tokens x input features),
+ * W:[m,k] (output x input features) and Y:[n,m], all row-major here:
+ *     Y[i*M + j] = sum_k X[i*K + k] * W[j*K + k],   i < n, j < M.
+ * Section 6.2: every Y[i*M + j] is an independent full-K dot product; the
+ * kernel splits W's output rows across workgroups.  No bias.
+ *
+ * W and X are read only.  n == 0 or M == 0 returns 0 without a launch;
+ * K == 0 writes +0.0 to Y.  Errors as for the GEMM (Y must not overlap W, X).
+ * n may be any positive value; the kernel is built for n <= 16 tokens per
+ * pass and loops over larger n.
+ */
+int gemv_bf16(const uint16_t *W, const uint16_t *X, uint16_t *Y,
+              int M, int K, int n, void *stream);
+
+/* ---- explicit-configuration variants (tuning sweeps) --------------------- */
+
+/*
+ * Same contract as gemm_f16 / gemm_bf16 with the tile configuration named by
+ * the caller instead of chosen by the library:
+ *   tile:    0 = automatic, 1 = 256x256x64 (4 waves), 2 = 256x128x64 (4 waves),
+ *            3 = 128x128x64 (4 waves);
+ *   group_m: width of the grouped tile ordering (FlagGems "Hygon 优化" page,
+ *            section "分组调度"), >= 1, or 0 for automatic;
+ *   xcd_remap: 1 to place consecutive tiles of the ordering on one XCD's L2,
+ *            0 to use the hardware's round-robin dispatch order unchanged.
+ * dtype: 0 = binary16, 1 = bfloat16.  MIGEMM_ERR_CONFIG for values out of range.
+ */
+int gemm_ex(int dtype, const uint16_t *A, const uint16_t *B, uint16_t *C,
+            int M, int N, int K, int tile, int group_m, int xcd_remap,
+            void *stream);
+
+/*
+ * Same contract as gemv_bf16 with rows_per_block (output rows of W per
+ * workgroup: 2, 4, 8, 16 or 32; 0 = automatic), the knob swept on the DCU
+ * decode page, section 6.2.
+ */
+int gemv_bf16_ex(const uint16_t *W, const uint16_t *X, uint16_t *Y,
+                 int M, int K, int n, int rows_per_block, void *stream);
+
+/* ---- host-only helpers (no GPU work; callable without a GPU) ------------ */
+
+/*
+ * The tile scheduler used by the GEMM kernel, evaluated on the host: maps
+ * workgroup id `wg` of a grid of num_pid_m x num_pid_n tiles to its tile
+ * (*pid_m, *pid_n).  num_xcd > 1 first renumbers ids so that the ids the
+ * hardware sends to one XCD form a contiguous range, then applies the grouped
+ * ordering with width group_m.  Returns 0, or MIGEMM_ERR_DIM for bad input.
+ */
+int migemm_tile_coord(int64_t wg, int64_t num_pid_m, int64_t num_pid_n,
+                      int64_t group_m, int64_t num_xcd,
+                      int64_t *pid_m, int64_t *pid_n);
+
+/* What the library would launch for a GEMM call (for tests and reports). */
+typedef struct {
+    int tile_m, tile_n, tile_k;   /* workgroup tile                       */
+    int waves;                    /* waves per workgroup                  */
+    int group_m;                  /* grouped-ordering width               */
+    int xcd_remap;                /* 1 if the XCD renumbering is applied  */
+    int vec_a, vec_b;             /* elements per global->LDS load of A, B */
+    int64_t grid;                 /* workgroups launched                  */
+    int lds_bytes;                /* LDS per workgroup                    */
+} migemm_gemm_plan;
+
+/* Fill *plan for gemm_ex's arguments (pointers are inspected for alignment
+ * only, never dereferenced).  Returns the code gemm_ex would return for the
+ * argument checks (0 if a launch would happen). */
+int migemm_gemm_plan_for(int dtype, const uint16_t *A, const uint16_t *B,
+                         const uint16_t *C, int M, int N, int K, int tile,
+                         int group_m, int xcd_remap, migemm_gemm_plan *plan);
+
+/* Human-readable text for a return code (static storage). */
+const char *migemm_strerror(int code);
+
+/* Library ABI version (bumped when a signature changes). */
+int migemm_abi_version(void);
+
+/* ---- measurement --------------------------------------------------------- */
+
+/*
+ * Streaming-read bandwidth probe: reads `bytes` bytes from device buffer
+ * `buf` once with 16-byte loads and writes one 32-bit checksum per workgroup
+ * to `sink` (device, at least migemm_hbm_read_sink_words() words).  `bytes`
+ * must be a multiple of 16 and `buf` 16-byte aligned.  Used to measure the
+ * achievable HBM read bandwidth that the GEMV is compared with.
+ */
+int migemm_hbm_read(const void *buf, size_t bytes, uint32_t *sink, void *stream);
+int migemm_hbm_read_sink_words(void);
+
+#ifdef __cplusplus
+}
+#endif
+#endif /* MIGEMM_H */

@@ -1,0 +1,74 @@
+"""Shared helpers for the GPU parity tests: device buffers with guard bands,
+calls through the C ABI, and checks against the oracle."""
+import numpy as np
+
+import oracle
+import synth
+
+SENTINEL = 0xFFFF
+GUARD = 4096
+
+
+def dev(bits):
+    """uint16 numpy array -> int16 CUDA tensor holding the same bits."""
+    import torch
+    return torch.from_numpy(np.ascontiguousarray(bits).view(np.int16)).cuda()
+
+
+def host(t):
+    return t.cpu().numpy().view(np.uint16)
+
+
+class Guarded:
+    """An output buffer of `count` uint16 with GUARD sentinel words on both
+    sides; `ptr` is the address of the first output element."""
+
+    def __init__(self, count, guard=GUARD):
+        import torch
+        self.count, self.guard = count, guard
+        self.buf = torch.full((count + 2 * guard,), -1, dtype=torch.int16, device="cuda")
+        self.ptr = self.buf.data_ptr() + 2 * guard
+
+    def out(self):
+        return host(self.buf[self.guard:self.guard + self.count])
+
+    def guards_intact(self):
+        h = host(self.buf)
+        return bool(np.all(h[:self.guard] == SENTINEL) and np.all(h[self.guard + self.count:] == SENTINEL))
+
+
+def gemm_gpu(A_bits, B_bits, M, N, K, fmt, tile=0, group_m=0, xcd_remap=1, stream=0):
+    """Run the library GEMM through the C ABI; returns (C bits, guards ok,
+    inputs unchanged)."""
+    import torch
+    from bf16_gemm_decode_amd import binding
+    dA, dB = dev(A_bits), dev(B_bits)
+    cA, cB = dA.clone(), dB.clone()
+    C = Guarded(M * N)
+    code = binding.gemm_ex_ptr(binding.F16 if fmt == "f16" else binding.BF16,
+                               dA.data_ptr(), dB.data_ptr(), C.ptr, M, N, K,
+                               tile, group_m, xcd_remap, stream)
+    assert code == 0, "gemm_ex returned %d" % code
+    torch.cuda.synchronize()
+    unchanged = bool(torch.equal(dA, cA) and torch.equal(dB, cB))
+    return C.out(), C.guards_intact(), unchanged
+
+
+def gemv_gpu(W_bits, X_bits, M, K, n, rows_per_block=0, stream=0):
+    import torch
+    from bf16_gemm_decode_amd import binding
+    dW, dX = dev(W_bits), dev(X_bits)
+    cW, cX = dW.clone(), dX.clone()
+    Y = Guarded(n * M)
+    code = binding.gemv_bf16_ex_ptr(dW.data_ptr(), dX.data_ptr(), Y.ptr, M, K, n,
+                                    rows_per_block, stream)
+    assert code == 0, "gemv_bf16_ex returned %d" % code
+    torch.cuda.synchronize()
+    unchanged = bool(torch.equal(dW, cW) and torch.equal(dX, cX))
+    return Y.out(), Y.guards_intact(), unchanged
+
+
+def assert_parity(got, ref, fmt, what):
+    ok, rep = oracle.check(got, ref, fmt)
+    assert ok, "%s: %s" % (what, rep)
+    return rep

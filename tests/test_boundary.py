@@ -1,0 +1,138 @@
+"""The C-ABI library on the CPU: it loads, exports every function the header
+declares, rejects bad arguments before touching the GPU, and its tile
+scheduler is a bijection that reduces to the grouped ordering of the
+FlagGems Hygon page when the XCD renumbering is off."""
+import ctypes
+import os
+import re
+
+import pytest
+
+import oracle
+from bf16_gemm_decode_amd import binding
+
+ROOT = os.path.dirname(os.path.dirname(os.path.abspath(__file__)))
+
+
+def header_functions():
+    src = open(os.path.join(ROOT, "include", "migemm.h")).read()
+    src = re.sub(r"/\*.*?\*/", "", src, flags=re.S)
+    return set(re.findall(r"^\s*(?:const\s+)?\w+\s*\*?\s*(\w+)\s*\(", src, flags=re.M))
+
+
+def test_library_exports_every_declared_function():
+    L = binding.lib()
+    names = header_functions()
+    assert {"gemm_f16", "gemm_bf16", "gemv_bf16"} <= names
+    for n in names:
+        assert hasattr(L, n), n
+    assert names == set(binding.SIGNATURES), names ^ set(binding.SIGNATURES)
+    assert L.migemm_abi_version() == 1
+
+
+P = 0x10000        # a fake, aligned device address: never dereferenced on error paths
+
+
+@pytest.mark.parametrize("fn", ["gemm_f16", "gemm_bf16"])
+def test_gemm_argument_errors(fn):
+    f = getattr(binding.lib(), fn)
+    assert f(P, P + 0x100000, P + 0x200000, -1, 4, 4, None) == -1
+    assert f(P, P + 0x100000, P + 0x200000, 4, 4, -2, None) == -1
+    assert f(None, P + 0x100000, P + 0x200000, 4, 4, 4, None) == -2
+    assert f(P, None, P + 0x200000, 4, 4, 4, None) == -2
+    assert f(P, P + 0x100000, None, 4, 4, 4, None) == -2
+    assert f(P + 1, P + 0x100000, P + 0x200000, 4, 4, 4, None) == -4
+    assert f(P, P + 0x100000, P + 0x200001, 4, 4, 4, None) == -4
+    # C overlaps A (A spans 4*4*2 = 32 bytes from P)
+    assert f(P, P + 0x100000, P + 16, 4, 4, 4, None) == -3
+    # C overlaps B
+    assert f(P, P + 0x100000, P + 0x100000 - 8, 4, 4, 4, None) == -3
+    # just touching is not overlapping: C starts where A ends (checked via plan, no launch)
+    code, _ = binding.gemm_plan(0, P, P + 0x100000, P + 32, 4, 4, 4)
+    assert code == 0
+    assert f(P, P + 0x100000, P + 0x200000, 1 << 24, 4, 4, None) == -6
+    assert f(P, P + 0x100000, P + 0x200000, 4, 4, 1 << 22, None) == -6
+
+
+def test_gemm_empty_output_is_a_noop_without_gpu():
+    L = binding.lib()
+    # M == 0 or N == 0: nothing to write, returns before any HIP call
+    assert L.gemm_f16(None, P + 0x100000, None, 0, 4, 4, None) == 0
+    assert L.gemm_bf16(P, None, None, 4, 0, 4, None) == 0
+
+
+def test_gemm_ex_config_errors():
+    L = binding.lib()
+    args = (P, P + 0x100000, P + 0x200000, 64, 64, 64)
+    assert L.gemm_ex(2, *args, 0, 0, 1, None) == -5
+    assert L.gemm_ex(0, *args, 4, 0, 1, None) == -5
+    assert L.gemm_ex(0, *args, 0, -1, 1, None) == -5
+    assert L.gemm_ex(0, *args, 0, 0, 2, None) == -5
+    # 256-row tiles need 16-byte loads: M = 5000 has them, K = 4100 does not
+    assert L.gemm_ex(1, P, P + 0x10000000, P + 0x20000000, 5000, 3000, 4100, 1, 0, 1, None) == -5
+
+
+def test_gemv_argument_errors():
+    L = binding.lib()
+    assert L.gemv_bf16(P, P + 0x100000, P + 0x200000, -1, 8, 1, None) == -1
+    assert L.gemv_bf16(None, P + 0x100000, P + 0x200000, 8, 8, 1, None) == -2
+    assert L.gemv_bf16(P, P + 0x100000, P + 0x200001, 8, 8, 1, None) == -4
+    assert L.gemv_bf16(P, P + 0x100000, P + 8, 8, 8, 1, None) == -3       # Y inside W
+    assert L.gemv_bf16(P, P + 0x100000, P + 0x100000, 8, 8, 1, None) == -3  # Y on X
+    assert L.gemv_bf16_ex(P, P + 0x100000, P + 0x200000, 8, 8, 1, 3, None) == -5
+    assert L.gemv_bf16(P, P + 0x100000, P + 0x200000, 8, 8, 0, None) == 0    # n == 0
+    assert L.gemv_bf16(None, P, None, 0, 8, 4, None) == 0                    # M == 0
+    assert L.gemv_bf16(None, None, None, 0, 8, 4, None) == -2                # X has 32 elements
+
+
+def test_plan_choices():
+    # headline square shape: 256x256 tiles, 16-byte loads, 32 x 32 tiles
+    code, p = binding.gemm_plan(0, P, P + 2 ** 30, P + 2 ** 31, 8192, 8192, 16384)
+    assert code == 0 and (p["tile_m"], p["tile_n"], p["vec_a"], p["vec_b"], p["grid"]) == \
+        (256, 256, 8, 8, 1024)
+    assert p["lds_bytes"] <= 160 * 1024
+    # ragged: M = 5000 keeps 16-byte A loads, K = 4100 drops B to 4-byte loads
+    code, p = binding.gemm_plan(1, P, P + 2 ** 30, P + 2 ** 31, 5000, 3000, 4100)
+    assert code == 0 and (p["tile_m"], p["vec_a"], p["vec_b"]) == (128, 8, 2)
+    assert p["grid"] == 40 * 24
+    # odd everything: element loads
+    code, p = binding.gemm_plan(1, P + 2, P + 2 ** 30 + 2, P + 2 ** 31, 33, 17, 65)
+    assert code == 0 and (p["vec_a"], p["vec_b"]) == (1, 1)
+    # explicit grouped width is clamped to the tile rows
+    code, p = binding.gemm_plan(0, P, P + 2 ** 30, P + 2 ** 31, 1024, 1024, 64, 3, 16, 0)
+    assert code == 0 and p["group_m"] == 8 and p["xcd_remap"] == 0
+
+
+@pytest.mark.parametrize("group_m", [1, 2, 3, 4, 8, 16])
+@pytest.mark.parametrize("num_xcd", [1, 8])
+def test_tile_scheduler_bijection(group_m, num_xcd):
+    for npm in (1, 2, 5, 8, 13, 32):
+        for npn in (1, 3, 7, 16, 33):
+            seen = {binding.tile_coord(w, npm, npn, group_m, num_xcd) for w in range(npm * npn)}
+            assert len(seen) == npm * npn
+            assert all(0 <= a < npm and 0 <= b < npn for a, b in seen)
+
+
+def test_tile_scheduler_without_remap_is_the_grouped_ordering():
+    for npm, npn, gm in ((5, 3, 2), (16, 136, 8), (7, 9, 4), (32, 32, 16)):
+        for w in range(npm * npn):
+            assert binding.tile_coord(w, npm, npn, gm, 1) == oracle.grouped_tile(w, npm, npn, gm)
+
+
+def test_tile_scheduler_xcd_locality():
+    # With the renumbering, the ids one XCD receives (x, x+8, x+16, ...) are a
+    # contiguous range of the grouped ordering.
+    npm, npn, gm = 32, 32, 8
+    for x in range(8):
+        ids = list(range(x, npm * npn, 8))
+        coords = [binding.tile_coord(w, npm, npn, gm, 8) for w in ids]
+        logical = [i for i in range(npm * npn)
+                   if oracle.grouped_tile(i, npm, npn, gm) in set(coords)]
+        assert logical == list(range(logical[0], logical[0] + len(ids)))
+
+
+def test_tile_coord_rejects_bad_input():
+    with pytest.raises(binding.MigemmError):
+        binding.tile_coord(15, 5, 3, 2, 1)
+    with pytest.raises(binding.MigemmError):
+        binding.tile_coord(0, 5, 3, 0, 1)
