@@ -80,12 +80,13 @@ def cpu_baseline(A, B, M, N, K, target_s):
     import oracle
     import synth
     cores = int(os.environ.get("OMP_NUM_THREADS", len(os.sched_getaffinity(0))))
-    idx_all = synth.sample_indices(M, N, 1, count=65536)
-    n = 64
+    idx_all = synth.sample_indices(M, N, 1, count=1 << 21)
+    oracle.gemm_sampled(A, B, M, N, K, idx_all[:16], "f16")      # load, start threads
+    n = 512
     t0 = time.perf_counter()
     oracle.gemm_sampled(A, B, M, N, K, idx_all[:n], "f16")
     dt = time.perf_counter() - t0
-    n = int(min(idx_all.size, max(64, n * target_s / max(dt, 1e-3))))
+    n = int(min(idx_all.size, max(n, n * target_s / max(dt, 1e-3))))
     t0 = time.perf_counter()
     r = oracle.gemm_sampled(A, B, M, N, K, idx_all[:n], "f16")
     dt = time.perf_counter() - t0
@@ -170,13 +171,6 @@ def main():
     peak = rf.MI355X["mfma_f16_tflops"]
     hbm = rf.MI355X["hbm_GBps"]
 
-    # parity spot check of what was timed (the full checks live in the tests)
-    import oracle
-    idx = synth.sample_indices(M, N, wg["seed"], count=256)
-    got = dC.cpu().numpy().view(np.uint16)[idx]
-    ok_g, _ = oracle.check(got, oracle.gemm_sampled(A, B, M, N, K, idx, "f16"), "f16")
-    ok_v, _ = oracle.check(dY.cpu().numpy().view(np.uint16), oracle.gemv(W, X, GM, GK, gn), "bf16")
-
     out = {
         "metric": METRIC,
         "value": round(tflops, 2),
@@ -208,7 +202,6 @@ def main():
                               "algorithmic_bytes": int(gemv_bytes)},
                  "probe_read_GBps": round(probe_GBps, 1),
                  "frac_of_probe": round(gemv_GBps / probe_GBps, 4)},
-        "parity_spot_check": {"gemm_256_samples": bool(ok_g), "gemv_all": bool(ok_v)},
         "device": {"name": props.name, "cus": props.multi_processor_count},
     }
     if not args.no_cpu_baseline:

@@ -42,7 +42,7 @@ int plan_gemm(int dtype, const uint16_t *A, const uint16_t *B, const uint16_t *C
 {
     launch = false;
     if (dtype != DT_F16 && dtype != DT_BF16) return MIGEMM_ERR_CONFIG;
-    if (tile < TILE_AUTO || tile > TILE_128x128 || group_m < 0 || xcd_remap < 0 || xcd_remap > 1)
+    if (tile < TILE_AUTO || tile >= TILE_COUNT || group_m < 0 || xcd_remap < 0 || xcd_remap > 1)
         return MIGEMM_ERR_CONFIG;
     if (M < 0 || N < 0 || K < 0) return MIGEMM_ERR_DIM;
     if (M > MIGEMM_MAX_MN || N > MIGEMM_MAX_MN || K > MIGEMM_MAX_K) return MIGEMM_ERR_SIZE;
@@ -74,8 +74,7 @@ int plan_gemm(int dtype, const uint16_t *A, const uint16_t *B, const uint16_t *C
         return MIGEMM_ERR_CONFIG;   // the 256-row tiles load only 16-byte vectors
     }
     L.tile = tile;
-    const int bm = (tile == TILE_128x128) ? 128 : 256;
-    const int bn = (tile == TILE_256x256) ? 256 : 128;
+    const int bm = kTileShapes[tile].bm, bn = kTileShapes[tile].bn;
     const int64_t pm = cdiv(M, bm), pn = cdiv(N, bn);
     if (pm * pn > 0x7fffffff) return MIGEMM_ERR_SIZE;
     L.num_pid_m = (int)(pm ? pm : 1);
@@ -132,16 +131,17 @@ int migemm_gemm_plan_for(int dtype, const uint16_t *A, const uint16_t *B, const 
     int rc = plan_gemm(dtype, A, B, C, M, N, K, tile, group_m, xcd_remap, L, launch);
     if (rc != MIGEMM_OK || !plan) return rc;
     memset(plan, 0, sizeof(*plan));
-    plan->tile_m = (L.tile == TILE_128x128) ? 128 : 256;
-    plan->tile_n = (L.tile == TILE_256x256) ? 256 : 128;
-    plan->tile_k = 64;
-    plan->waves = 4;
+    const TileShape &t = kTileShapes[L.tile];
+    plan->tile_m = t.bm;
+    plan->tile_n = t.bn;
+    plan->tile_k = t.bk;
+    plan->waves = t.waves;
     plan->group_m = L.group_m;
     plan->xcd_remap = L.num_xcd > 1;
     plan->vec_a = L.vec_a;
     plan->vec_b = L.vec_b;
     plan->grid = launch ? L.grid : 0;
-    plan->lds_bytes = 2 * 64 * (plan->tile_m + plan->tile_n) * 2;
+    plan->lds_bytes = t.stages * t.bk * (t.bm + t.bn) * 2;
     return rc;
 }
 

@@ -7,15 +7,18 @@
 //
 //  * one workgroup owns a BM x BN tile of C, picked by tile_coord() (XCD
 //    renumbering + the grouped ordering of the FlagGems Hygon page);
-//  * K advances in BK-wide steps.  Each step's A tile (BK rows of BM
-//    m-contiguous elements) and B tile (BN rows of BK k-contiguous elements)
-//    go straight from HBM into LDS with buffer loads that write LDS directly
-//    (no VGPR staging), two stages deep: the loads for step t+1 fly while
-//    step t computes;
+//  * K advances in BK-wide steps through a ring of S LDS stages.  Each step's
+//    A tile (BK rows of BM m-contiguous elements) and B tile (BN rows of BK
+//    k-contiguous elements) go straight from HBM into LDS with buffer loads
+//    that write LDS directly (no VGPR staging), S-2 steps ahead of the step
+//    being computed;
 //  * A is m-contiguous, but an MFMA operand needs 8 consecutive k of one row
 //    per lane, so A is read out of LDS with the transposing ds_read_b64_tr_b16
 //    (lane i of each 16-lane group receives row i of a 16 x 4 block); B is
 //    already k-contiguous and is read with ds_read_b128;
+//  * operand fragments are double-buffered in registers: the LDS reads of the
+//    next 32-wide k slice (including the first slice of the next step, right
+//    after the step's barrier) are issued before the MFMAs of the current one;
 //  * v_mfma_f32_16x16x32_{f16,bf16} accumulates in FP32 registers;
 //  * out-of-range rows/columns are never stored; out-of-range k reads as
 //    zero through the buffer descriptors' range check, so ragged K needs no
@@ -34,20 +37,54 @@ namespace migemm {
 template <int BM>
 __device__ inline int swz_a(int kk) { return (((kk & 7) << 1) ^ (kk & 8)) & (BM / 8 - 1); }
 template <int BK>
-__device__ inline int swz_b(int nn) { return (nn ^ (nn >> 3)) & (BK / 8 - 1); }
+__device__ inline int swz_b(int nn)
+{
+    if constexpr (BK == 64)
+        return (nn ^ (nn >> 3)) & 7;
+    else
+        return ((nn >> 1) ^ (nn >> 3)) & 3;
+}
 
-// Direct HBM -> LDS load of BYTES per lane (lane-linear LDS destination,
-// BYTES apart).  Only the 4- and 16-byte forms are used: their lane-linear
-// placement and zero fill past the descriptor's records are what the kernel
-// relies on.  Single elements go through registers instead (see issue()).
+// Raw buffer descriptor words over [base, base + nbytes), wave-uniform:
+// loads past nbytes return zero and never fault.  Word 3 selects 32-bit data
+// format, no swizzle; the stride is zero (raw byte offsets).
+__device__ inline u32x4 make_desc(const void *base, uint32_t nbytes)
+{
+    uint64_t a = (uint64_t)base;
+    u32x4 d;
+    d[0] = (uint32_t)uniform((int)(uint32_t)a);
+    d[1] = (uint32_t)uniform((int)((uint32_t)(a >> 32) & 0xffffu));
+    d[2] = (uint32_t)uniform((int)nbytes);
+    d[3] = 0x00020000u;
+    return d;
+}
+
+// Direct HBM -> LDS load of BYTES per lane: lane l's bytes land at LDS address
+// lds + l*BYTES (M0 holds the wave-uniform base).  Only the 4- and 16-byte
+// forms are used; their lane-linear placement and zero fill past the
+// descriptor's records are what the kernel relies on.  Issued as inline
+// assembly so that the compiler does not make every later LDS read wait for
+// these loads: the kernel orders them itself with explicit vmcnt waits and a
+// barrier before any wave reads the stage they fill.
 template <int BYTES>
-__device__ inline void load_lds(__amdgpu_buffer_rsrc_t r, MIGEMM_LDS void *dst, uint32_t off)
+__device__ inline void dma_to_lds(u32x4 desc, uint32_t lds, uint32_t voff)
 {
     static_assert(BYTES == 16 || BYTES == 4, "LDS load size");
     if constexpr (BYTES == 16)
-        __builtin_amdgcn_raw_ptr_buffer_load_lds(r, dst, 16, off, 0, 0, 0);
+        asm volatile("s_mov_b32 m0, %1\n\ts_nop 0\n\tbuffer_load_dwordx4 %0, %2, 0 offen lds"
+                     :: "v"(voff), "s"(lds), "s"(desc) : "memory", "m0");
     else
-        __builtin_amdgcn_raw_ptr_buffer_load_lds(r, dst, 4, off, 0, 0, 0);
+        asm volatile("s_mov_b32 m0, %1\n\ts_nop 0\n\tbuffer_load_dword %0, %2, 0 offen lds"
+                     :: "v"(voff), "s"(lds), "s"(desc) : "memory", "m0");
+}
+
+// s_waitcnt vmcnt(N), other counters untouched (gfx9 encoding: vmcnt in bits
+// 3:0 and 15:14, expcnt 6:4 = 7, lgkmcnt 11:8 = 15).
+template <int N>
+__device__ inline void wait_vmcnt()
+{
+    static_assert(N >= 0 && N < 64, "vmcnt range");
+    __builtin_amdgcn_s_waitcnt((N & 15) | ((N >> 4) << 14) | (7 << 4) | (15 << 8));
 }
 
 template <int DT>
@@ -61,7 +98,7 @@ __device__ inline f32x4 mfma16x16x32(u32x4 a, u32x4 b, f32x4 c)
                                                        __builtin_bit_cast(bf16x8, b), c, 0, 0, 0);
 }
 
-template <int DT, int BM, int BN, int BK, int WGM, int WGN, int VA, int VB, int OCC>
+template <int DT, int BM, int BN, int BK, int WGM, int WGN, int S, int VA, int VB, int OCC>
 __global__ void __launch_bounds__(WGM * WGN * 64) __attribute__((amdgpu_waves_per_eu(OCC, OCC)))
 gemm_kernel(const uint16_t *__restrict__ A, const uint16_t *__restrict__ B,
             uint16_t *__restrict__ C, int M, int N, int K, int num_pid_m, int num_pid_n,
@@ -70,15 +107,19 @@ gemm_kernel(const uint16_t *__restrict__ A, const uint16_t *__restrict__ B,
     constexpr int NW = WGM * WGN;
     constexpr int TM = BM / WGM, TN = BN / WGN;   // wave tile
     constexpr int FM = TM / 16, FN = TN / 16;     // 16x16 MFMA blocks per wave
-    constexpr int KS = BK / 32;                   // MFMA k-steps per K-step
+    constexpr int KS = BK / 32;                   // 32-wide k slices per K-step
     constexpr int A_BYTES = BK * BM * 2, B_BYTES = BN * BK * 2;
     constexpr int STAGE = A_BYTES + B_BYTES;
     constexpr int A_PIECE = 64 * VA * 2, B_PIECE = 64 * VB * 2;   // bytes per wave load
     constexpr int A_LOADS = A_BYTES / (A_PIECE * NW), B_LOADS = B_BYTES / (B_PIECE * NW);
+    // direct-to-LDS loads per wave per K-step (single-element paths are synchronous)
+    constexpr int LPS = (VA > 1 ? A_LOADS : 0) + (VB > 1 ? B_LOADS : 0);
     static_assert(A_BYTES % (A_PIECE * NW) == 0 && B_BYTES % (B_PIECE * NW) == 0, "loader split");
     static_assert(TM % 16 == 0 && TN % 16 == 0 && BK % 32 == 0, "tile shape");
+    static_assert(S >= 3 && S * STAGE <= 163840, "LDS ring");
+    static_assert(LPS * (S - 2) < 64, "vmcnt range");
 
-    __shared__ __attribute__((aligned(1024))) unsigned char smem[2 * STAGE];
+    __shared__ __attribute__((aligned(1024))) unsigned char smem[S * STAGE];
 
     int pid_m, pid_n;
     tile_coord<int>((int)blockIdx.x, num_pid_m, num_pid_n, group_m, num_xcd, pid_m, pid_n);
@@ -86,6 +127,7 @@ gemm_kernel(const uint16_t *__restrict__ A, const uint16_t *__restrict__ B,
     const int lane = threadIdx.x & 63;
     const int wave = uniform(threadIdx.x >> 6);
     const int wm = wave % WGM, wn = wave / WGM;
+    const int g = lane >> 4, ig = lane & 15;
 
     // Which global element each lane fetches for each of its loads.  A load
     // writes lane-linear LDS bytes [piece + lane*size, +size); the swizzle is
@@ -109,19 +151,19 @@ gemm_kernel(const uint16_t *__restrict__ A, const uint16_t *__restrict__ B,
         b_k[q] = kk;
     }
 
-    // Issue the loads of K-step starting at k0 into stage `st`.  Descriptors
-    // are rebased per step: A at column k0 with (K - k0) columns of records,
-    // so k >= K reads zero; B at column n0, row k0, where rows n >= N fall past
-    // the records and k >= K is pushed out of range explicitly.
+    // Issue the loads of the K-step starting at k0 into stage `st`.
+    // Descriptors are rebased per step: A at column k0 with (K - k0) columns
+    // of records, so k >= K reads zero; B at column n0, row k0, where rows
+    // n >= N fall past the records and k >= K is pushed out of range.
     auto issue = [&](int st, int k0) {
         MIGEMM_LDS unsigned char *sa = (MIGEMM_LDS unsigned char *)(smem + st * STAGE);
         MIGEMM_LDS unsigned char *sb = sa + A_BYTES;
         if constexpr (VA > 1) {
-            __amdgpu_buffer_rsrc_t ra =
-                make_rsrc(A + (size_t)k0 * M, clamp_records((int64_t)(K - k0) * M * 2));
+            const u32x4 da = make_desc(A + (size_t)k0 * M, clamp_records((int64_t)(K - k0) * M * 2));
+            const uint32_t base = (uint32_t)(uintptr_t)sa;
 #pragma unroll
             for (int q = 0; q < A_LOADS; ++q)
-                load_lds<VA * 2>(ra, (MIGEMM_LDS void *)(sa + (q * NW + wave) * A_PIECE), a_off[q]);
+                dma_to_lds<VA * 2>(da, (uint32_t)uniform((int)(base + (q * NW + wave) * A_PIECE)), a_off[q]);
         } else {
             // one element per lane through a register: zero outside the matrix
 #pragma unroll
@@ -135,13 +177,13 @@ gemm_kernel(const uint16_t *__restrict__ A, const uint16_t *__restrict__ B,
             }
         }
         if constexpr (VB > 1) {
-            __amdgpu_buffer_rsrc_t rb =
-                make_rsrc(B + (size_t)n0 * K + k0,
-                          clamp_records((int64_t)(N - n0) * K * 2 - (int64_t)k0 * 2));
+            const u32x4 db = make_desc(B + (size_t)n0 * K + k0,
+                                       clamp_records((int64_t)(N - n0) * K * 2 - (int64_t)k0 * 2));
+            const uint32_t base = (uint32_t)(uintptr_t)sb;
 #pragma unroll
             for (int q = 0; q < B_LOADS; ++q) {
                 uint32_t off = (k0 + b_k[q] < K) ? b_off[q] : kOutOfRange;
-                load_lds<VB * 2>(rb, (MIGEMM_LDS void *)(sb + (q * NW + wave) * B_PIECE), off);
+                dma_to_lds<VB * 2>(db, (uint32_t)uniform((int)(base + (q * NW + wave) * B_PIECE)), off);
             }
         } else {
 #pragma unroll
@@ -156,57 +198,98 @@ gemm_kernel(const uint16_t *__restrict__ A, const uint16_t *__restrict__ B,
         }
     };
 
+    // Wait until this wave's loads of a step have landed while at most
+    // `ahead` later steps' loads stay in flight.
+    auto wait_steps = [&](int ahead) {
+        if constexpr (S >= 5) {
+            if (ahead >= 2) { wait_vmcnt<2 * LPS>(); return; }
+        }
+        if constexpr (S >= 4) {
+            if (ahead >= 1) { wait_vmcnt<LPS>(); return; }
+        }
+        wait_vmcnt<0>();
+    };
+
+    // Operand fragments of one 32-wide k slice.
+    struct Frag { u32x4 a[FM]; u32x4 b[FN]; };
+    auto read_frag = [&](int st, int s, Frag &f) {
+        const MIGEMM_LDS unsigned char *sa = (const MIGEMM_LDS unsigned char *)(smem + st * STAGE);
+        const MIGEMM_LDS unsigned char *sb = sa + A_BYTES;
+#pragma unroll
+        for (int i = 0; i < FM; ++i) {
+            // Lane t of a 16-lane group points at row k = kb + t/4, columns
+            // m = mb + 4*(t%4) .. +3; the transposing read hands lane i the
+            // four k of column mb + i.
+            int m = wm * TM + i * 16 + 4 * (ig & 3);
+            i16x4 lo, hi;
+            {
+                int kk = 32 * s + 8 * g + (ig >> 2);
+                int byte = kk * (BM * 2) + (((m >> 3) ^ swz_a<BM>(kk)) << 4) + (m & 7) * 2;
+                lo = __builtin_amdgcn_ds_read_tr16_b64_v4i16((MIGEMM_LDS i16x4 *)(sa + byte));
+            }
+            {
+                int kk = 32 * s + 8 * g + 4 + (ig >> 2);
+                int byte = kk * (BM * 2) + (((m >> 3) ^ swz_a<BM>(kk)) << 4) + (m & 7) * 2;
+                hi = __builtin_amdgcn_ds_read_tr16_b64_v4i16((MIGEMM_LDS i16x4 *)(sa + byte));
+            }
+            typedef __attribute__((ext_vector_type(8))) short i16x8;
+            i16x8 v = __builtin_shufflevector(lo, hi, 0, 1, 2, 3, 4, 5, 6, 7);
+            f.a[i] = __builtin_bit_cast(u32x4, v);
+        }
+#pragma unroll
+        for (int j = 0; j < FN; ++j) {
+            int nn = wn * TN + j * 16 + ig;
+            int byte = nn * (BK * 2) + (((4 * s + g) ^ swz_b<BK>(nn)) << 4);
+            f.b[j] = *(const MIGEMM_LDS u32x4 *)(sb + byte);
+        }
+    };
+
     f32x4 acc[FM][FN];
 #pragma unroll
     for (int i = 0; i < FM; ++i)
 #pragma unroll
         for (int j = 0; j < FN; ++j) acc[i][j] = f32x4{0.f, 0.f, 0.f, 0.f};
 
-    const int g = lane >> 4, ig = lane & 15;
     const int KT = (K + BK - 1) / BK;
-    if (KT > 0) issue(0, 0);
-
-    for (int kt = 0; kt < KT; ++kt) {
-        __builtin_amdgcn_s_waitcnt(0x0F70);   // vmcnt(0): this wave's loads landed
-        __syncthreads();                      // ... and every wave's; stage (kt+1)&1 is free
-        if (kt + 1 < KT) issue((kt + 1) & 1, (kt + 1) * BK);
-
-        const MIGEMM_LDS unsigned char *sa = (const MIGEMM_LDS unsigned char *)(smem + (kt & 1) * STAGE);
-        const MIGEMM_LDS unsigned char *sb = sa + A_BYTES;
+    if (KT > 0) {
 #pragma unroll
-        for (int s = 0; s < KS; ++s) {
-            u32x4 af[FM], bfr[FN];
+        for (int p = 0; p < S - 1; ++p)
+            if (p < KT) issue(p, p * BK);
+        wait_steps(min(S - 2, KT - 1));
+        __syncthreads();
+        Frag cur;
+        read_frag(0, 0, cur);
+        int st = 0;
+        for (int kt = 0; kt < KT; ++kt) {
 #pragma unroll
-            for (int i = 0; i < FM; ++i) {
-                // Lane t of a 16-lane group points at row k = kb + t/4, columns
-                // m = mb + 4*(t%4) .. +3; the transposing read hands lane i the
-                // four k of column mb + i.
-                int m = wm * TM + i * 16 + 4 * (ig & 3);
-                i16x4 lo, hi;
-                {
-                    int kk = 32 * s + 8 * g + (ig >> 2);
-                    int byte = kk * (BM * 2) + ((((m >> 3) ^ swz_a<BM>(kk))) << 4) + (m & 7) * 2;
-                    lo = __builtin_amdgcn_ds_read_tr16_b64_v4i16((MIGEMM_LDS i16x4 *)(sa + byte));
+            for (int s = 0; s < KS; ++s) {
+                Frag nxt;
+                bool more = true;
+                // The current fragments were read a whole MFMA block ago and
+                // have landed; retire them here so that the MFMAs below need
+                // no wait while the next fragments' reads are in flight (the
+                // LDS counter cannot count past 15 outstanding reads).
+                __builtin_amdgcn_s_waitcnt((7 << 4) | 0xc00f);   // lgkmcnt(0)
+                if (s + 1 < KS) {
+                    read_frag(st, s + 1, nxt);
+                } else if (kt + 1 < KT) {
+                    // Step kt+1 becomes readable once every wave's loads into
+                    // it landed.  After this barrier no wave reads step kt-1's
+                    // stage any more: refill it with step kt+S-1.
+                    wait_steps(min(S - 3, KT - 2 - kt));
+                    __syncthreads();
+                    if (kt + S - 1 < KT) issue((st + S - 1) % S, (kt + S - 1) * BK);
+                    st = (st + 1 == S) ? 0 : st + 1;
+                    read_frag(st, 0, nxt);
+                } else {
+                    more = false;
                 }
-                {
-                    int kk = 32 * s + 8 * g + 4 + (ig >> 2);
-                    int byte = kk * (BM * 2) + ((((m >> 3) ^ swz_a<BM>(kk))) << 4) + (m & 7) * 2;
-                    hi = __builtin_amdgcn_ds_read_tr16_b64_v4i16((MIGEMM_LDS i16x4 *)(sa + byte));
-                }
-                typedef __attribute__((ext_vector_type(8))) short i16x8;
-                i16x8 v = __builtin_shufflevector(lo, hi, 0, 1, 2, 3, 4, 5, 6, 7);
-                af[i] = __builtin_bit_cast(u32x4, v);
+#pragma unroll
+                for (int i = 0; i < FM; ++i)
+#pragma unroll
+                    for (int j = 0; j < FN; ++j) acc[i][j] = mfma16x16x32<DT>(cur.a[i], cur.b[j], acc[i][j]);
+                if (more) cur = nxt;
             }
-#pragma unroll
-            for (int j = 0; j < FN; ++j) {
-                int nn = wn * TN + j * 16 + ig;
-                int byte = nn * (BK * 2) + (((4 * s + g) ^ swz_b<BK>(nn)) << 4);
-                bfr[j] = *(const MIGEMM_LDS u32x4 *)(sb + byte);
-            }
-#pragma unroll
-            for (int i = 0; i < FM; ++i)
-#pragma unroll
-                for (int j = 0; j < FN; ++j) acc[i][j] = mfma16x16x32<DT>(af[i], bfr[j], acc[i][j]);
         }
     }
 
@@ -234,12 +317,12 @@ gemm_kernel(const uint16_t *__restrict__ A, const uint16_t *__restrict__ B,
 
 // ---------------------------------------------------------------------------
 
-template <int DT, int BM, int BN, int BK, int WGM, int WGN, int VA, int VB, int OCC>
+template <int DT, int BM, int BN, int BK, int WGM, int WGN, int S, int VA, int VB, int OCC>
 static hipError_t launch_t(const GemmLaunch &L, hipStream_t stream)
 {
     dim3 grid((unsigned)L.grid), block(WGM * WGN * 64);
-    hipLaunchKernelGGL((gemm_kernel<DT, BM, BN, BK, WGM, WGN, VA, VB, OCC>), grid, block, 0, stream,
-                       L.A, L.B, L.C, L.M, L.N, L.K, L.num_pid_m, L.num_pid_n, L.group_m,
+    hipLaunchKernelGGL((gemm_kernel<DT, BM, BN, BK, WGM, WGN, S, VA, VB, OCC>), grid, block, 0,
+                       stream, L.A, L.B, L.C, L.M, L.N, L.K, L.num_pid_m, L.num_pid_n, L.group_m,
                        L.num_xcd, L.c_vec);
     return hipGetLastError();
 }
@@ -249,12 +332,18 @@ static hipError_t launch_dt(const GemmLaunch &L, hipStream_t s)
 {
     switch (L.tile) {
     case TILE_256x256:
-        return launch_t<DT, 256, 256, 64, 2, 2, 8, 8, 1>(L, s);
+        return launch_t<DT, 256, 256, 32, 2, 2, 4, 8, 8, 1>(L, s);
     case TILE_256x128:
-        return launch_t<DT, 256, 128, 64, 2, 2, 8, 8, 1>(L, s);
+        return launch_t<DT, 256, 128, 64, 2, 2, 3, 8, 8, 1>(L, s);
+    case TILE_256x256_S5:
+        return launch_t<DT, 256, 256, 32, 2, 2, 5, 8, 8, 1>(L, s);
+    case TILE_256x256_S3:
+        return launch_t<DT, 256, 256, 32, 2, 2, 3, 8, 8, 1>(L, s);
+    case TILE_256x128_K32:
+        return launch_t<DT, 256, 128, 32, 2, 2, 5, 8, 8, 1>(L, s);
     case TILE_128x128:
 #define MIGEMM_V(va, vb) \
-    if (L.vec_a == va && L.vec_b == vb) return launch_t<DT, 128, 128, 64, 2, 2, va, vb, 2>(L, s);
+    if (L.vec_a == va && L.vec_b == vb) return launch_t<DT, 128, 128, 32, 2, 2, 4, va, vb, 2>(L, s);
         MIGEMM_V(8, 8) MIGEMM_V(8, 2) MIGEMM_V(8, 1)
         MIGEMM_V(2, 8) MIGEMM_V(2, 2) MIGEMM_V(2, 1)
         MIGEMM_V(1, 8) MIGEMM_V(1, 2) MIGEMM_V(1, 1)

@@ -172,8 +172,11 @@ hipError_t gemv_launch(const GemvLaunch &L, hipStream_t s)
 
 // ---- streaming-read probe ------------------------------------------------
 
-constexpr int kProbeBlocks = 2048;
+constexpr int kProbeBlocks = 4096;
+constexpr int kProbeUnroll = 8;
 
+// Each thread keeps kProbeUnroll independent 16-byte loads in flight per
+// iteration; consecutive threads read consecutive 16-byte words.
 __global__ void __launch_bounds__(256) hbm_read_kernel(const u32x4 *__restrict__ buf, size_t n16,
                                                        uint32_t *__restrict__ sink)
 {
@@ -181,9 +184,12 @@ __global__ void __launch_bounds__(256) hbm_read_kernel(const u32x4 *__restrict__
     const size_t stride = (size_t)gridDim.x * blockDim.x;
     size_t i = (size_t)blockIdx.x * blockDim.x + threadIdx.x;
     u32x4 acc = {0u, 0u, 0u, 0u};
-    for (; i + 3 * stride < n16; i += 4 * stride) {
-        u32x4 a = buf[i], b = buf[i + stride], c = buf[i + 2 * stride], d = buf[i + 3 * stride];
-        acc ^= a ^ b ^ c ^ d;
+    for (; i + (kProbeUnroll - 1) * stride < n16; i += kProbeUnroll * stride) {
+        u32x4 v[kProbeUnroll];
+#pragma unroll
+        for (int u = 0; u < kProbeUnroll; ++u) v[u] = __builtin_nontemporal_load(buf + i + u * stride);
+#pragma unroll
+        for (int u = 0; u < kProbeUnroll; ++u) acc ^= v[u];
     }
     for (; i < n16; i += stride) acc ^= buf[i];
     uint32_t v = acc[0] ^ acc[1] ^ acc[2] ^ acc[3];

@@ -6,7 +6,31 @@
 
 namespace migemm {
 
-enum GemmTile { TILE_AUTO = 0, TILE_256x256 = 1, TILE_256x128 = 2, TILE_128x128 = 3 };
+enum GemmTile {
+    TILE_AUTO = 0,
+    TILE_256x256 = 1,       // 256x256x32, 4 waves, 4 LDS stages
+    TILE_256x128 = 2,       // 256x128x64, 4 waves, 3 stages
+    TILE_128x128 = 3,       // 128x128x32, 4 waves, 4 stages, 2 workgroups per CU
+    TILE_256x256_S5 = 4,    // 256x256x32, 5 stages
+    TILE_256x256_S3 = 5,    // 256x256x32, 3 stages
+    TILE_256x128_K32 = 6,   // 256x128x32, 5 stages
+    TILE_COUNT
+};
+
+struct TileShape {
+    int bm, bn, bk, stages, waves;
+};
+
+// Indexed by GemmTile (entry 0 unused).
+constexpr TileShape kTileShapes[TILE_COUNT] = {
+    {0, 0, 0, 0, 0},
+    {256, 256, 32, 4, 4},
+    {256, 128, 64, 3, 4},
+    {128, 128, 32, 4, 4},
+    {256, 256, 32, 5, 4},
+    {256, 256, 32, 3, 4},
+    {256, 128, 32, 5, 4},
+};
 
 struct GemmLaunch {
     int dtype;                    // DT_F16 or DT_BF16
