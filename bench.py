@@ -43,6 +43,9 @@ def parse():
     p.add_argument("--no-cpu-baseline", action="store_true")
     p.add_argument("--cpu-seconds", type=float, default=12.0,
                    help="target CPU time of the oracle sample")
+    p.add_argument("--copy-calibration", action="store_true",
+                   help="only run a plain 1 GiB device-to-device copy 3 times (the known-size "
+                        "reference for scaling FETCH_SIZE / WRITE_SIZE counters) and exit")
     return p.parse_args()
 
 
@@ -72,6 +75,22 @@ def hbm_probe(binding, torch, stream, nbytes=4 << 30, reps=20):
     ts.sort()
     del buf
     return nbytes / ts[len(ts) // 2] / 1e9
+
+
+def measured_traffic(kernel_file, summary_file):
+    """HBM bytes per launch from a committed rocprofv3 counter summary, or
+    None when there is none or the kernel source changed since it was taken."""
+    import hashlib
+    path = os.path.join(ROOT, "profiles", summary_file)
+    src = os.path.join(ROOT, "bf16_gemm_decode_amd", "csrc", kernel_file)
+    try:
+        summ = json.load(open(path))
+        digest = hashlib.sha256(open(src, "rb").read()).hexdigest()
+    except (OSError, ValueError):
+        return None
+    if summ.get("kernel_source_sha256") != digest:
+        return None
+    return summ.get("hbm_bytes_per_launch")
 
 
 def cpu_baseline(A, B, M, N, K, target_s):
@@ -110,6 +129,15 @@ def main():
     from bf16_gemm_decode_amd import binding, roofline as rf
 
     torch.cuda.set_device(0)
+    if args.copy_calibration:
+        src = torch.full((1 << 28,), 3, dtype=torch.int32, device="cuda")   # 1 GiB
+        dst = torch.empty_like(src)
+        torch.cuda.synchronize()
+        for _ in range(3):
+            dst.copy_(src)
+        torch.cuda.synchronize()
+        print(json.dumps({"copy_calibration_bytes": src.numel() * 4, "copies": 3}))
+        return
     stream = torch.cuda.Stream()
     props = torch.cuda.get_device_properties(0)
 
@@ -192,13 +220,14 @@ def main():
                             "rows_per_block": args.rows_per_block or 8,
                             "w_copies_rotated": W_COPIES}},
         "roofline": {"bound": "mfma", "achieved": round(tflops, 2), "peak": peak,
-                     "unit": "TFLOP/s", "frac": round(tflops / peak, 4), "traffic": None,
+                     "unit": "TFLOP/s", "frac": round(tflops / peak, 4),
+                     "traffic": measured_traffic("gemm.hip", "gemm_8192x8192x16384_f16_traffic.json"),
                      "kernel": "gemm_kernel (2*M*N*K FLOP per launch)",
                      "avg_launch_ms": round(gemm_avg * 1e3, 4)},
         "gemv": {"GBps": round(gemv_GBps, 1), "avg_launch_us": round(gemv_avg * 1e6, 2),
                  "roofline": {"bound": "hbm", "achieved": round(gemv_GBps, 1), "peak": hbm,
                               "unit": "GB/s", "frac": round(gemv_GBps / hbm, 4),
-                              "traffic": None,
+                              "traffic": measured_traffic("gemv.hip", "gemv_34816x5120_bf16_n1_traffic.json"),
                               "algorithmic_bytes": int(gemv_bytes)},
                  "probe_read_GBps": round(probe_GBps, 1),
                  "frac_of_probe": round(gemv_GBps / probe_GBps, 4)},

@@ -64,8 +64,10 @@ int plan_gemm(int dtype, const uint16_t *A, const uint16_t *B, const uint16_t *C
     L.c_vec = (M % 4 == 0 && (uintptr_t)C % 8 == 0) ? 1 : 0;
     const bool wide = (L.vec_a == 8 && L.vec_b == 8);
     if (tile == TILE_AUTO) {
+        // the 256x256 tile (waves stacked along M) once it fills the 256 CUs
+        // at least twice, else 256x128, else the 128x128 tile
         if (wide && cdiv(M, 256) * cdiv(N, 256) >= 512)
-            tile = TILE_256x256;
+            tile = TILE_256x256_W41;
         else if (wide && cdiv(M, 256) * cdiv(N, 128) >= 512)
             tile = TILE_256x128;
         else

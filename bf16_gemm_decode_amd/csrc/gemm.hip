@@ -7,43 +7,41 @@
 //
 //  * one workgroup owns a BM x BN tile of C, picked by tile_coord() (XCD
 //    renumbering + the grouped ordering of the FlagGems Hygon page);
-//  * K advances in BK-wide steps through a ring of S LDS stages.  Each step's
-//    A tile (BK rows of BM m-contiguous elements) and B tile (BN rows of BK
-//    k-contiguous elements) go straight from HBM into LDS with buffer loads
-//    that write LDS directly (no VGPR staging), S-2 steps ahead of the step
-//    being computed;
+//  * K advances in 64-wide steps through two LDS stages.  Each step's A tile
+//    (64 rows of BM m-contiguous elements) and B tile go straight from HBM
+//    into LDS with buffer loads that write LDS directly (no VGPR staging),
+//    one step ahead of the step being computed;
 //  * A is m-contiguous, but an MFMA operand needs 8 consecutive k of one row
 //    per lane, so A is read out of LDS with the transposing ds_read_b64_tr_b16
-//    (lane i of each 16-lane group receives row i of a 16 x 4 block); B is
-//    already k-contiguous and is read with ds_read_b128;
+//    (lane i of each 16-lane group receives row i of a 16 x 4 block), from a
+//    row-XOR-swizzled layout that keeps the four rows of a read in different
+//    banks;
+//  * B is k-contiguous, so the loads place every 16-column x 32-k operand
+//    fragment as one KiB in exactly the order the lanes read it: the B
+//    fragment reads are linear ds_read_b128 (the fastest LDS pattern);
 //  * operand fragments are double-buffered in registers: the LDS reads of the
 //    next 32-wide k slice (including the first slice of the next step, right
-//    after the step's barrier) are issued before the MFMAs of the current one;
+//    after the step's barrier) are issued before the MFMAs of the current one,
+//    all from per-lane base addresses plus immediate offsets;
 //  * v_mfma_f32_16x16x32_{f16,bf16} accumulates in FP32 registers;
 //  * out-of-range rows/columns are never stored; out-of-range k reads as
 //    zero through the buffer descriptors' range check, so ragged K needs no
 //    separate path;
 //  * the epilogue rounds each FP32 sum once to FP16/BF16 (nearest even) and
 //    stores it directly: no FP32 copy of C ever reaches memory.
+#include <type_traits>
+
 #include "common.hpp"
 #include "tile_map.hpp"
 #include "kernels.hpp"
 
 namespace migemm {
 
-// LDS swizzles: XOR on the 16-byte chunk index within a row, so the rows a
-// 16-lane group reads in one LDS instruction fall in different banks.
-// A stage rows are k (BM elements each); B stage rows are n (BK elements).
+// A-stage swizzle: XOR on the 16-byte chunk index within a k row, so that
+// the four rows a 16-lane group reads in one transposing LDS read (and the
+// rows of the neighbouring group) fall in different banks.
 template <int BM>
 __device__ inline int swz_a(int kk) { return (((kk & 7) << 1) ^ (kk & 8)) & (BM / 8 - 1); }
-template <int BK>
-__device__ inline int swz_b(int nn)
-{
-    if constexpr (BK == 64)
-        return (nn ^ (nn >> 3)) & 7;
-    else
-        return ((nn >> 1) ^ (nn >> 3)) & 3;
-}
 
 // Raw buffer descriptor words over [base, base + nbytes), wave-uniform:
 // loads past nbytes return zero and never fault.  Word 3 selects 32-bit data
@@ -87,39 +85,54 @@ __device__ inline void wait_vmcnt()
     __builtin_amdgcn_s_waitcnt((N & 15) | ((N >> 4) << 14) | (7 << 4) | (15 << 8));
 }
 
+// acc += a * b on one 16x16x32 block, accumulating in place in AGPRs.  Written
+// as (non-volatile) inline assembly with the accumulator tied to an AGPR
+// operand: the compiler keeps each accumulator in one fixed register instead
+// of rotating it through copies, and may still schedule these freely.  It
+// does not see the MFMA's result latency, so nothing but another MFMA may
+// read an accumulator until mfma_drain() has run.
 template <int DT>
-__device__ inline f32x4 mfma16x16x32(u32x4 a, u32x4 b, f32x4 c)
+__device__ inline void mfma16x16x32(f32x4 &acc, u32x4 a, u32x4 b)
 {
     if constexpr (DT == DT_F16)
-        return __builtin_amdgcn_mfma_f32_16x16x32_f16(__builtin_bit_cast(f16x8, a),
-                                                      __builtin_bit_cast(f16x8, b), c, 0, 0, 0);
+        asm("v_mfma_f32_16x16x32_f16 %0, %1, %2, %0" : "+a"(acc) : "v"(a), "v"(b));
     else
-        return __builtin_amdgcn_mfma_f32_16x16x32_bf16(__builtin_bit_cast(bf16x8, a),
-                                                       __builtin_bit_cast(bf16x8, b), c, 0, 0, 0);
+        asm("v_mfma_f32_16x16x32_bf16 %0, %1, %2, %0" : "+a"(acc) : "v"(a), "v"(b));
 }
 
-template <int DT, int BM, int BN, int BK, int WGM, int WGN, int S, int VA, int VB, int OCC>
+// Wait states after the last MFMA before its results are read by other
+// instructions (more than the longest MFMA write-to-read requirement).
+__device__ inline void mfma_drain()
+{
+    asm volatile("s_nop 7\n\ts_nop 7\n\ts_nop 7\n\ts_nop 7" ::: "memory");
+}
+
+template <int DT, int BM, int BN, int WGM, int WGN, int S, int VA, int VB, int OCC>
 __global__ void __launch_bounds__(WGM * WGN * 64) __attribute__((amdgpu_waves_per_eu(OCC, OCC)))
 gemm_kernel(const uint16_t *__restrict__ A, const uint16_t *__restrict__ B,
             uint16_t *__restrict__ C, int M, int N, int K, int num_pid_m, int num_pid_n,
             int group_m, int num_xcd, int c_vec)
 {
+    constexpr int BK = 32;                        // K-step = one MFMA k slice
     constexpr int NW = WGM * WGN;
     constexpr int TM = BM / WGM, TN = BN / WGN;   // wave tile
     constexpr int FM = TM / 16, FN = TN / 16;     // 16x16 MFMA blocks per wave
-    constexpr int KS = BK / 32;                   // 32-wide k slices per K-step
+    constexpr int NBJ = BN / 16;                  // B fragments per step
     constexpr int A_BYTES = BK * BM * 2, B_BYTES = BN * BK * 2;
+    // LDS: a ring of S stages, each [A tile | B tile].
     constexpr int STAGE = A_BYTES + B_BYTES;
+    constexpr int LDS_BYTES = S * STAGE;
     constexpr int A_PIECE = 64 * VA * 2, B_PIECE = 64 * VB * 2;   // bytes per wave load
     constexpr int A_LOADS = A_BYTES / (A_PIECE * NW), B_LOADS = B_BYTES / (B_PIECE * NW);
+    constexpr int NLOAD = A_LOADS + B_LOADS;
     // direct-to-LDS loads per wave per K-step (single-element paths are synchronous)
     constexpr int LPS = (VA > 1 ? A_LOADS : 0) + (VB > 1 ? B_LOADS : 0);
     static_assert(A_BYTES % (A_PIECE * NW) == 0 && B_BYTES % (B_PIECE * NW) == 0, "loader split");
-    static_assert(TM % 16 == 0 && TN % 16 == 0 && BK % 32 == 0, "tile shape");
-    static_assert(S >= 3 && S * STAGE <= 163840, "LDS ring");
+    static_assert(TM % 16 == 0 && TN % 16 == 0, "tile shape");
+    static_assert(S >= 2 && LDS_BYTES <= 163840, "LDS ring");
     static_assert(LPS * (S - 2) < 64, "vmcnt range");
 
-    __shared__ __attribute__((aligned(1024))) unsigned char smem[S * STAGE];
+    __shared__ __attribute__((aligned(1024))) unsigned char smem[LDS_BYTES];
 
     int pid_m, pid_n;
     tile_coord<int>((int)blockIdx.x, num_pid_m, num_pid_n, group_m, num_xcd, pid_m, pid_n);
@@ -129,118 +142,120 @@ gemm_kernel(const uint16_t *__restrict__ A, const uint16_t *__restrict__ B,
     const int wm = wave % WGM, wn = wave / WGM;
     const int g = lane >> 4, ig = lane & 15;
 
-    // Which global element each lane fetches for each of its loads.  A load
-    // writes lane-linear LDS bytes [piece + lane*size, +size); the swizzle is
-    // applied by choosing the global source of that LDS slot.
+    // ---- where each LDS byte of a stage comes from ----
+    // A tile: row kk (k0 + kk), BM elements, 16-byte chunks XOR-swizzled.
+    // B tile: fragment jb is one KiB; its lane slot l = 16g' + i' holds
+    // B(k0 + 8g' .. +7, n0 + 16jb + i').
+    auto a_src = [&](int P, int &kk, int &m) {
+        kk = P / (BM * 2);
+        int b = P % (BM * 2);
+        m = (((b >> 4) ^ swz_a<BM>(kk)) << 3) + ((b & 15) >> 1);
+    };
+    auto b_src = [&](int P, int &kk, int &nn) {
+        int f = P >> 10, l = (P >> 4) & 63, o = P & 15;
+        kk = 8 * (l >> 4) + (o >> 1);
+        nn = 16 * f + (l & 15);
+    };
+
     uint32_t a_off[A_LOADS];
 #pragma unroll
     for (int q = 0; q < (VA > 1 ? A_LOADS : 0); ++q) {
-        int P = (q * NW + wave) * A_PIECE + lane * VA * 2;
-        int kk = P / (BM * 2), b = P % (BM * 2);
-        int m = (((b >> 4) ^ swz_a<BM>(kk)) << 3) + ((b & 15) >> 1);
+        int kk, m;
+        a_src((q * NW + wave) * A_PIECE + lane * VA * 2, kk, m);
         a_off[q] = (uint32_t)(((int64_t)kk * M + m0 + m) * 2);
     }
     uint32_t b_off[B_LOADS];
     int b_k[B_LOADS];
 #pragma unroll
     for (int q = 0; q < (VB > 1 ? B_LOADS : 0); ++q) {
-        int P = (q * NW + wave) * B_PIECE + lane * VB * 2;
-        int nn = P / (BK * 2), b = P % (BK * 2);
-        int kk = (((b >> 4) ^ swz_b<BK>(nn)) << 3) + ((b & 15) >> 1);
+        int kk, nn;
+        b_src((q * NW + wave) * B_PIECE + lane * VB * 2, kk, nn);
         b_off[q] = (uint32_t)(((int64_t)nn * K + kk) * 2);
         b_k[q] = kk;
     }
 
-    // Issue the loads of the K-step starting at k0 into stage `st`.
-    // Descriptors are rebased per step: A at column k0 with (K - k0) columns
-    // of records, so k >= K reads zero; B at column n0, row k0, where rows
-    // n >= N fall past the records and k >= K is pushed out of range.
+    // Loads of the K-step starting at k0 into stage `st`.  Descriptors are
+    // rebased per step: A at column k0 with (K - k0) columns of records, so
+    // k >= K reads zero; B at column n0, row k0, where rows n >= N fall past
+    // the records and k >= K is pushed out of range.  Load q < A_LOADS is
+    // A's q-th, the rest are B's; issue_one() issues one of them so that the
+    // loads can be spread between MFMAs.
+    struct StepDesc { u32x4 da, db; uint32_t sa, sb; int k0; };
+    auto step_desc = [&](int st, int k0) {
+        StepDesc d;
+        d.sa = (uint32_t)(uintptr_t)(MIGEMM_LDS unsigned char *)smem + st * STAGE;
+        d.sb = d.sa + A_BYTES;
+        d.k0 = k0;
+        // a step before k = 0 (the zero step that evens out the step count)
+        // gets empty descriptors: all of its loads read zeros
+        const bool live = k0 >= 0;
+        d.da = make_desc(A + (int64_t)k0 * M, live ? clamp_records((int64_t)(K - k0) * M * 2) : 0u);
+        d.db = make_desc(B + (size_t)n0 * K + k0,
+                         live ? clamp_records((int64_t)(N - n0) * K * 2 - (int64_t)k0 * 2) : 0u);
+        return d;
+    };
+    auto issue_one = [&](const StepDesc &d, int q) {
+        if (q < A_LOADS) {
+            if constexpr (VA > 1) {
+                dma_to_lds<VA * 2>(d.da, (uint32_t)uniform((int)(d.sa + (q * NW + wave) * A_PIECE)), a_off[q]);
+            } else {
+                // one element per lane through a register: zero outside the matrix
+                int P = (q * NW + wave) * A_PIECE + lane * 2, kk, m;
+                a_src(P, kk, m);
+                uint16_t v = 0;
+                if (m0 + m < M && d.k0 + kk >= 0 && d.k0 + kk < K) v = A[(size_t)(d.k0 + kk) * M + m0 + m];
+                *(MIGEMM_LDS uint16_t *)((MIGEMM_LDS unsigned char *)smem + (d.sa - (uint32_t)(uintptr_t)(MIGEMM_LDS unsigned char *)smem) + P) = v;
+            }
+        } else {
+            const int qb = q - A_LOADS;
+            if constexpr (VB > 1) {
+                uint32_t off = (d.k0 + b_k[qb] < K) ? b_off[qb] : kOutOfRange;
+                dma_to_lds<VB * 2>(d.db, (uint32_t)uniform((int)(d.sb + (qb * NW + wave) * B_PIECE)), off);
+            } else {
+                int P = (qb * NW + wave) * B_PIECE + lane * 2, kk, nn;
+                b_src(P, kk, nn);
+                uint16_t v = 0;
+                if (n0 + nn < N && d.k0 + kk >= 0 && d.k0 + kk < K) v = B[(size_t)(n0 + nn) * K + d.k0 + kk];
+                *(MIGEMM_LDS uint16_t *)((MIGEMM_LDS unsigned char *)smem + (d.sb - (uint32_t)(uintptr_t)(MIGEMM_LDS unsigned char *)smem) + P) = v;
+            }
+        }
+    };
     auto issue = [&](int st, int k0) {
-        MIGEMM_LDS unsigned char *sa = (MIGEMM_LDS unsigned char *)(smem + st * STAGE);
-        MIGEMM_LDS unsigned char *sb = sa + A_BYTES;
-        if constexpr (VA > 1) {
-            const u32x4 da = make_desc(A + (size_t)k0 * M, clamp_records((int64_t)(K - k0) * M * 2));
-            const uint32_t base = (uint32_t)(uintptr_t)sa;
+        const StepDesc d = step_desc(st, k0);
 #pragma unroll
-            for (int q = 0; q < A_LOADS; ++q)
-                dma_to_lds<VA * 2>(da, (uint32_t)uniform((int)(base + (q * NW + wave) * A_PIECE)), a_off[q]);
-        } else {
-            // one element per lane through a register: zero outside the matrix
-#pragma unroll
-            for (int q = 0; q < A_LOADS; ++q) {
-                int P = (q * NW + wave) * A_PIECE + lane * 2;
-                int kk = P / (BM * 2), b = P % (BM * 2);
-                int m = (((b >> 4) ^ swz_a<BM>(kk)) << 3) + ((b & 15) >> 1);
-                uint16_t v = 0;
-                if (m0 + m < M && k0 + kk < K) v = A[(size_t)(k0 + kk) * M + m0 + m];
-                *(MIGEMM_LDS uint16_t *)(sa + P) = v;
-            }
-        }
-        if constexpr (VB > 1) {
-            const u32x4 db = make_desc(B + (size_t)n0 * K + k0,
-                                       clamp_records((int64_t)(N - n0) * K * 2 - (int64_t)k0 * 2));
-            const uint32_t base = (uint32_t)(uintptr_t)sb;
-#pragma unroll
-            for (int q = 0; q < B_LOADS; ++q) {
-                uint32_t off = (k0 + b_k[q] < K) ? b_off[q] : kOutOfRange;
-                dma_to_lds<VB * 2>(db, (uint32_t)uniform((int)(base + (q * NW + wave) * B_PIECE)), off);
-            }
-        } else {
-#pragma unroll
-            for (int q = 0; q < B_LOADS; ++q) {
-                int P = (q * NW + wave) * B_PIECE + lane * 2;
-                int nn = P / (BK * 2), b = P % (BK * 2);
-                int kk = (((b >> 4) ^ swz_b<BK>(nn)) << 3) + ((b & 15) >> 1);
-                uint16_t v = 0;
-                if (n0 + nn < N && k0 + kk < K) v = B[(size_t)(n0 + nn) * K + k0 + kk];
-                *(MIGEMM_LDS uint16_t *)(sb + P) = v;
-            }
-        }
+        for (int q = 0; q < NLOAD; ++q) issue_one(d, q);
     };
 
-    // Wait until this wave's loads of a step have landed while at most
-    // `ahead` later steps' loads stay in flight.
-    auto wait_steps = [&](int ahead) {
-        if constexpr (S >= 5) {
-            if (ahead >= 2) { wait_vmcnt<2 * LPS>(); return; }
-        }
-        if constexpr (S >= 4) {
-            if (ahead >= 1) { wait_vmcnt<LPS>(); return; }
-        }
-        wait_vmcnt<0>();
-    };
-
-    // Operand fragments of one 32-wide k slice.
-    struct Frag { u32x4 a[FM]; u32x4 b[FN]; };
-    auto read_frag = [&](int st, int s, Frag &f) {
-        const MIGEMM_LDS unsigned char *sa = (const MIGEMM_LDS unsigned char *)(smem + st * STAGE);
-        const MIGEMM_LDS unsigned char *sb = sa + A_BYTES;
+    // ---- operand fragment reads: per-lane stage-relative addresses ----
+    // A: for block i and half h (k rows 0-3 / 4-7 of the lane group's 8), lane
+    // t of a 16-lane group points at row 8g + 4h + t/4, columns
+    // m = wm*TM + 16i + 4*(t%4) .. +3.  B: linear KiB fragments.
+    uint32_t a_rel[FM][2];
 #pragma unroll
-        for (int i = 0; i < FM; ++i) {
-            // Lane t of a 16-lane group points at row k = kb + t/4, columns
-            // m = mb + 4*(t%4) .. +3; the transposing read hands lane i the
-            // four k of column mb + i.
+    for (int i = 0; i < FM; ++i)
+#pragma unroll
+        for (int h = 0; h < 2; ++h) {
+            int kk = 8 * g + 4 * h + (ig >> 2);
             int m = wm * TM + i * 16 + 4 * (ig & 3);
-            i16x4 lo, hi;
-            {
-                int kk = 32 * s + 8 * g + (ig >> 2);
-                int byte = kk * (BM * 2) + (((m >> 3) ^ swz_a<BM>(kk)) << 4) + (m & 7) * 2;
-                lo = __builtin_amdgcn_ds_read_tr16_b64_v4i16((MIGEMM_LDS i16x4 *)(sa + byte));
-            }
-            {
-                int kk = 32 * s + 8 * g + 4 + (ig >> 2);
-                int byte = kk * (BM * 2) + (((m >> 3) ^ swz_a<BM>(kk)) << 4) + (m & 7) * 2;
-                hi = __builtin_amdgcn_ds_read_tr16_b64_v4i16((MIGEMM_LDS i16x4 *)(sa + byte));
-            }
+            a_rel[i][h] = kk * (BM * 2) + ((((m >> 3) ^ swz_a<BM>(kk))) << 4) + (m & 7) * 2;
+        }
+    const uint32_t b_rel = A_BYTES + lane * 16 + wn * FN * 1024;
+
+    // Operand fragments of one K-step.  read_one(r) issues item r of the NR
+    // items that fill it: for r < FM the two transposing reads of A block r,
+    // otherwise the linear read of B block r - FM.
+    struct Frag { u32x4 a[FM]; u32x4 b[FN]; };
+    constexpr int NR = FM + FN;
+    auto read_one = [&](uint32_t stage_off, int r, Frag &f) {
+        const MIGEMM_LDS unsigned char *base = (const MIGEMM_LDS unsigned char *)smem + stage_off;
+        if (r < FM) {
+            i16x4 lo = __builtin_amdgcn_ds_read_tr16_b64_v4i16((MIGEMM_LDS i16x4 *)(base + a_rel[r][0]));
+            i16x4 hi = __builtin_amdgcn_ds_read_tr16_b64_v4i16((MIGEMM_LDS i16x4 *)(base + a_rel[r][1]));
             typedef __attribute__((ext_vector_type(8))) short i16x8;
             i16x8 v = __builtin_shufflevector(lo, hi, 0, 1, 2, 3, 4, 5, 6, 7);
-            f.a[i] = __builtin_bit_cast(u32x4, v);
-        }
-#pragma unroll
-        for (int j = 0; j < FN; ++j) {
-            int nn = wn * TN + j * 16 + ig;
-            int byte = nn * (BK * 2) + (((4 * s + g) ^ swz_b<BK>(nn)) << 4);
-            f.b[j] = *(const MIGEMM_LDS u32x4 *)(sb + byte);
+            f.a[r] = __builtin_bit_cast(u32x4, v);
+        } else {
+            f.b[r - FM] = *(const MIGEMM_LDS u32x4 *)(base + b_rel + (r - FM) * 1024);
         }
     };
 
@@ -250,50 +265,124 @@ gemm_kernel(const uint16_t *__restrict__ A, const uint16_t *__restrict__ B,
 #pragma unroll
         for (int j = 0; j < FN; ++j) acc[i][j] = f32x4{0.f, 0.f, 0.f, 0.f};
 
-    const int KT = (K + BK - 1) / BK;
-    if (KT > 0) {
+    // K-steps, evened out: with an odd count one zero step (k0 = -BK, whose
+    // loads all read zeros) goes first, so the loop below always runs pairs.
+    const int KT_ = (((K + BK - 1) / BK) + 1) & ~1;
+    const int kbase = ((K + BK - 1) / BK) & 1 ? -BK : 0;
+
+    // The FM*FN MFMAs of one step, with `extra(x)` for x < NX (the next
+    // step's fragment reads and later steps' loads) issued between them --
+    // one item after every EV MFMAs -- and sched_barrier pinning that order,
+    // so no burst of loads or reads holds up the in-order MFMA issue.
+    auto mma = [&](const Frag &f, auto nx_c, auto every_c, auto &&extra) {
+        constexpr int NXI = decltype(nx_c)::value, EV = decltype(every_c)::value;
 #pragma unroll
-        for (int p = 0; p < S - 1; ++p)
-            if (p < KT) issue(p, p * BK);
-        wait_steps(min(S - 2, KT - 1));
-        __syncthreads();
-        Frag cur;
-        read_frag(0, 0, cur);
-        int st = 0;
-        for (int kt = 0; kt < KT; ++kt) {
+        for (int i = 0; i < FM; ++i)
 #pragma unroll
-            for (int s = 0; s < KS; ++s) {
-                Frag nxt;
-                bool more = true;
-                // The current fragments were read a whole MFMA block ago and
-                // have landed; retire them here so that the MFMAs below need
-                // no wait while the next fragments' reads are in flight (the
-                // LDS counter cannot count past 15 outstanding reads).
-                __builtin_amdgcn_s_waitcnt((7 << 4) | 0xc00f);   // lgkmcnt(0)
-                if (s + 1 < KS) {
-                    read_frag(st, s + 1, nxt);
-                } else if (kt + 1 < KT) {
-                    // Step kt+1 becomes readable once every wave's loads into
-                    // it landed.  After this barrier no wave reads step kt-1's
-                    // stage any more: refill it with step kt+S-1.
-                    wait_steps(min(S - 3, KT - 2 - kt));
-                    __syncthreads();
-                    if (kt + S - 1 < KT) issue((st + S - 1) % S, (kt + S - 1) * BK);
-                    st = (st + 1 == S) ? 0 : st + 1;
-                    read_frag(st, 0, nxt);
+            for (int j = 0; j < FN; ++j) {
+                mfma16x16x32<DT>(acc[i][j], f.a[i], f.b[j]);
+                const int t = i * FN + j;
+                if (t % EV == EV - 1 && t / EV < NXI) extra(t / EV);
+                __builtin_amdgcn_sched_barrier(0);
+            }
+        constexpr int DONE = (FM * FN / EV < NXI ? FM * FN / EV : NXI);
+#pragma unroll
+        for (int x = DONE; x < NXI; ++x) extra(x);
+    };
+
+    // One K-step: compute `cur` (step kt, stage st) while reading step kt+1
+    // into `nxt` and refilling stage st with step kt+S.  Before any of that:
+    // this wave's reads of stage st have landed (lgkmcnt), step kt+1's loads
+    // have landed (vmcnt, letting later steps' loads fly), and after the
+    // barrier no wave reads stage st any more.  On the last step the reads
+    // fetch stale data that is never used (no load is in flight then).
+    auto step = [&](int kt, int st, Frag &cur, Frag &nxt) {
+        __builtin_amdgcn_s_waitcnt((7 << 4) | 0xc00f);   // lgkmcnt(0)
+        const int ahead = min(S - 2, KT_ - 2 - kt);
+        if (kt + 1 < KT_) {
+            if constexpr (S >= 5) {
+                if (ahead >= 3) wait_vmcnt<3 * LPS>();
+                else if (ahead == 2) wait_vmcnt<2 * LPS>();
+                else if (ahead == 1) wait_vmcnt<LPS>();
+                else wait_vmcnt<0>();
+            } else if constexpr (S >= 4) {
+                if (ahead >= 2) wait_vmcnt<2 * LPS>();
+                else if (ahead == 1) wait_vmcnt<LPS>();
+                else wait_vmcnt<0>();
+            } else if constexpr (S >= 3) {
+                if (ahead >= 1) wait_vmcnt<LPS>();
+                else wait_vmcnt<0>();
+            } else {
+                wait_vmcnt<0>();
+            }
+            __syncthreads();
+        }
+        const bool refill = kt + S < KT_;
+        const StepDesc d = step_desc(st, (kt + S) * BK + kbase);
+        const int nst = (st + 1 == S) ? 0 : st + 1;
+        const uint32_t noff = (uint32_t)(nst * STAGE);
+        constexpr int NX = NLOAD + NR, NMF = FM * FN;
+        mma(cur, std::integral_constant<int, NX>{}, std::integral_constant<int, (NMF / NX > 0 ? NMF / NX : 1)>{},
+            [&](int x) {
+                // alternate reads and loads so both streams start early
+                constexpr int MN = NLOAD < NR ? NLOAD : NR;
+                if (x < 2 * MN) {
+                    if ((x & 1) == 0) {
+                        read_one(noff, x >> 1, nxt);
+                    } else {
+                        if (refill) issue_one(d, x >> 1);
+                    }
                 } else {
-                    more = false;
+                    const int t = MN + (x - 2 * MN);
+                    if constexpr (NLOAD > NR) {
+                        if (refill) issue_one(d, t);
+                    } else {
+                        read_one(noff, t, nxt);
+                    }
                 }
+            });
+        return nst;
+    };
+
+    if (KT_ > 0) {
 #pragma unroll
-                for (int i = 0; i < FM; ++i)
-#pragma unroll
-                    for (int j = 0; j < FN; ++j) acc[i][j] = mfma16x16x32<DT>(cur.a[i], cur.b[j], acc[i][j]);
-                if (more) cur = nxt;
+        for (int p = 0; p < S; ++p)
+            if (p < KT_) issue(p, p * BK + kbase);
+        // step 0 landed; steps 1 .. S-1 may fly
+        {
+            const int ahead = min(S - 1, KT_ - 1);
+            if constexpr (S >= 5) {
+                if (ahead >= 4) wait_vmcnt<4 * LPS>();
+                else if (ahead == 3) wait_vmcnt<3 * LPS>();
+                else if (ahead == 2) wait_vmcnt<2 * LPS>();
+                else if (ahead == 1) wait_vmcnt<LPS>();
+                else wait_vmcnt<0>();
+            } else if constexpr (S >= 4) {
+                if (ahead >= 3) wait_vmcnt<3 * LPS>();
+                else if (ahead == 2) wait_vmcnt<2 * LPS>();
+                else if (ahead == 1) wait_vmcnt<LPS>();
+                else wait_vmcnt<0>();
+            } else {
+                if (ahead >= 2) wait_vmcnt<2 * LPS>();
+                else if (ahead == 1) wait_vmcnt<LPS>();
+                else wait_vmcnt<0>();
             }
         }
+        __syncthreads();
+        Frag f0, f1;
+#pragma unroll
+        for (int r = 0; r < NR; ++r) read_one(0, r, f0);
+        int st = 0;
+        int kt = 0;
+        for (; kt < KT_; kt += 2) {
+            st = step(kt, st, f0, f1);
+            st = step(kt + 1, st, f1, f0);
+        }
+        wait_vmcnt<0>();   // no load may still target LDS when the workgroup ends
     }
 
     // Epilogue: lane (g, ig) of block (i, j) holds rows 4g..4g+3 of column ig.
+    mfma_drain();
 #pragma unroll
     for (int i = 0; i < FM; ++i) {
         const int m = m0 + wm * TM + i * 16 + 4 * g;
@@ -317,11 +406,11 @@ gemm_kernel(const uint16_t *__restrict__ A, const uint16_t *__restrict__ B,
 
 // ---------------------------------------------------------------------------
 
-template <int DT, int BM, int BN, int BK, int WGM, int WGN, int S, int VA, int VB, int OCC>
+template <int DT, int BM, int BN, int WGM, int WGN, int S, int VA, int VB, int OCC>
 static hipError_t launch_t(const GemmLaunch &L, hipStream_t stream)
 {
     dim3 grid((unsigned)L.grid), block(WGM * WGN * 64);
-    hipLaunchKernelGGL((gemm_kernel<DT, BM, BN, BK, WGM, WGN, S, VA, VB, OCC>), grid, block, 0,
+    hipLaunchKernelGGL((gemm_kernel<DT, BM, BN, WGM, WGN, S, VA, VB, OCC>), grid, block, 0,
                        stream, L.A, L.B, L.C, L.M, L.N, L.K, L.num_pid_m, L.num_pid_n, L.group_m,
                        L.num_xcd, L.c_vec);
     return hipGetLastError();
@@ -332,18 +421,18 @@ static hipError_t launch_dt(const GemmLaunch &L, hipStream_t s)
 {
     switch (L.tile) {
     case TILE_256x256:
-        return launch_t<DT, 256, 256, 32, 2, 2, 4, 8, 8, 1>(L, s);
+        return launch_t<DT, 256, 256, 2, 2, 4, 8, 8, 1>(L, s);
     case TILE_256x128:
-        return launch_t<DT, 256, 128, 64, 2, 2, 3, 8, 8, 1>(L, s);
+        return launch_t<DT, 256, 128, 2, 2, 5, 8, 8, 1>(L, s);
     case TILE_256x256_S5:
-        return launch_t<DT, 256, 256, 32, 2, 2, 5, 8, 8, 1>(L, s);
+        return launch_t<DT, 256, 256, 2, 2, 5, 8, 8, 1>(L, s);
+    case TILE_256x256_W41:
+        return launch_t<DT, 256, 256, 4, 1, 4, 8, 8, 1>(L, s);
     case TILE_256x256_S3:
-        return launch_t<DT, 256, 256, 32, 2, 2, 3, 8, 8, 1>(L, s);
-    case TILE_256x128_K32:
-        return launch_t<DT, 256, 128, 32, 2, 2, 5, 8, 8, 1>(L, s);
+        return launch_t<DT, 256, 256, 2, 2, 3, 8, 8, 1>(L, s);
     case TILE_128x128:
 #define MIGEMM_V(va, vb) \
-    if (L.vec_a == va && L.vec_b == vb) return launch_t<DT, 128, 128, 32, 2, 2, 4, va, vb, 2>(L, s);
+    if (L.vec_a == va && L.vec_b == vb) return launch_t<DT, 128, 128, 2, 2, 4, va, vb, 2>(L, s);
         MIGEMM_V(8, 8) MIGEMM_V(8, 2) MIGEMM_V(8, 1)
         MIGEMM_V(2, 8) MIGEMM_V(2, 2) MIGEMM_V(2, 1)
         MIGEMM_V(1, 8) MIGEMM_V(1, 2) MIGEMM_V(1, 1)

@@ -8,12 +8,12 @@ namespace migemm {
 
 enum GemmTile {
     TILE_AUTO = 0,
-    TILE_256x256 = 1,       // 256x256x32, 4 waves, 4 LDS stages
-    TILE_256x128 = 2,       // 256x128x64, 4 waves, 3 stages
-    TILE_128x128 = 3,       // 128x128x32, 4 waves, 4 stages, 2 workgroups per CU
-    TILE_256x256_S5 = 4,    // 256x256x32, 5 stages
-    TILE_256x256_S3 = 5,    // 256x256x32, 3 stages
-    TILE_256x128_K32 = 6,   // 256x128x32, 5 stages
+    TILE_256x256 = 1,           // 256x256, 4 waves as 2x2 (128x128 per wave), 4 stages
+    TILE_256x128 = 2,           // 256x128, 4 waves as 2x2, 5 stages
+    TILE_128x128 = 3,           // 128x128, 4 waves as 2x2, 4 stages, 2 workgroups per CU
+    TILE_256x256_S5 = 4,        // tile 1 with 5 stages (all 160 KiB of LDS)
+    TILE_256x256_W41 = 5,       // 256x256, 4 waves stacked along M (64x256 per wave), 4 stages
+    TILE_256x256_S3 = 6,        // tile 1 with 3 stages
     TILE_COUNT
 };
 
@@ -21,15 +21,16 @@ struct TileShape {
     int bm, bn, bk, stages, waves;
 };
 
-// Indexed by GemmTile (entry 0 unused).
+// Indexed by GemmTile (entry 0 unused).  Every tile steps K by 32 through a
+// ring of LDS stages.
 constexpr TileShape kTileShapes[TILE_COUNT] = {
     {0, 0, 0, 0, 0},
     {256, 256, 32, 4, 4},
-    {256, 128, 64, 3, 4},
+    {256, 128, 32, 5, 4},
     {128, 128, 32, 4, 4},
     {256, 256, 32, 5, 4},
+    {256, 256, 32, 4, 4},
     {256, 256, 32, 3, 4},
-    {256, 128, 32, 5, 4},
 };
 
 struct GemmLaunch {

@@ -1,0 +1,111 @@
+"""Summarise rocprofv3 CSV output into the short text/JSON files kept under
+profiles/.
+
+  kernel-stats:  python -m bf16_gemm_decode_amd.profile_summary stats \
+                     <run_kernel_stats.csv> <out.txt> --command "<rocprofv3 command>"
+  traffic:       python -m bf16_gemm_decode_amd.profile_summary traffic \
+                     --fetch <csv> --fetch-cal <csv> --write <csv> --write-cal <csv> \
+                     --kernel <name substring> --source <kernel .hip file> \
+                     --out <out.json> --commands "<cmd>" ...
+
+The traffic mode averages FETCH_SIZE and WRITE_SIZE (KiB per dispatch) over
+the matching kernel's dispatches and scales each by what the same counter
+reads for the plain 1 GiB device copy of `bench.py --copy-calibration`
+(profiled with the same counter), so that hbm_bytes_per_launch is in true
+bytes.  It records the SHA-256 of the
+kernel source so that a later change of the kernel invalidates the figure.
+"""
+import argparse
+import collections
+import csv
+import hashlib
+import json
+import sys
+
+
+def _rows(path):
+    with open(path) as f:
+        return list(csv.DictReader(f))
+
+
+def stats(args):
+    rows = _rows(args.csv)
+    keys = list(rows[0].keys()) if rows else []
+    with open(args.out, "w") as o:
+        o.write("# rocprofv3 kernel statistics\n# command: %s\n" % args.command)
+        o.write("# columns: %s\n" % ", ".join(keys))
+        for r in rows:
+            name = r.get("Name", "")
+            if args.filter and not any(f in name for f in args.filter):
+                continue
+            o.write(", ".join(str(r[k]) for k in keys) + "\n")
+    print(open(args.out).read())
+
+
+def _counter_per_dispatch(path, counter, substr):
+    per = collections.defaultdict(float)
+    names = {}
+    for r in _rows(path):
+        if r["Counter_Name"] != counter:
+            continue
+        per[r["Dispatch_Id"]] += float(r["Counter_Value"])
+        names[r["Dispatch_Id"]] = r["Kernel_Name"]
+    hit = [v for d, v in per.items() if substr in names[d]]
+    return hit, per, names
+
+
+def _median(v):
+    v = sorted(v)
+    return v[len(v) // 2]
+
+
+def traffic(args):
+    out = {"commands": args.commands, "kernel": args.kernel}
+    for counter, path, cal in (("FETCH_SIZE", args.fetch, args.fetch_cal),
+                               ("WRITE_SIZE", args.write, args.write_cal)):
+        vals, _, _ = _counter_per_dispatch(path, counter, args.kernel)
+        _, per, names = _counter_per_dispatch(cal, counter, "")
+        copy = [v for d, v in per.items() if "copy" in names[d].lower()]
+        if not vals or not copy:
+            sys.exit("no %s values for kernel %r in %s or for a copy kernel in %s"
+                     % (counter, args.kernel, path, cal))
+        # the copy moves 1 GiB each way: its reading in KiB against the true
+        # 1 GiB gives this counter's factor to bytes
+        copy_kib = _median(copy)
+        scale = (1 << 30) / (copy_kib * 1024.0)
+        kib = sum(vals) / len(vals)
+        out[counter.lower()] = {"kib_per_dispatch_raw": kib, "dispatches": len(vals),
+                                "copy_kib_raw": copy_kib, "scale_to_bytes": scale,
+                                "bytes_per_launch": kib * 1024.0 * scale}
+    out["hbm_bytes_per_launch"] = (out["fetch_size"]["bytes_per_launch"] +
+                                   out["write_size"]["bytes_per_launch"])
+    out["kernel_source"] = args.source
+    out["kernel_source_sha256"] = hashlib.sha256(open(args.source, "rb").read()).hexdigest()
+    with open(args.out, "w") as o:
+        json.dump(out, o, indent=1)
+    print(json.dumps(out, indent=1))
+
+
+def main(argv=None):
+    p = argparse.ArgumentParser()
+    sub = p.add_subparsers(dest="mode", required=True)
+    s = sub.add_parser("stats")
+    s.add_argument("csv")
+    s.add_argument("out")
+    s.add_argument("--command", required=True)
+    s.add_argument("--filter", nargs="*")
+    t = sub.add_parser("traffic")
+    t.add_argument("--fetch", required=True)
+    t.add_argument("--fetch-cal", required=True)
+    t.add_argument("--write", required=True)
+    t.add_argument("--write-cal", required=True)
+    t.add_argument("--kernel", required=True)
+    t.add_argument("--source", required=True)
+    t.add_argument("--out", required=True)
+    t.add_argument("--commands", nargs="+", required=True)
+    a = p.parse_args(argv)
+    stats(a) if a.mode == "stats" else traffic(a)
+
+
+if __name__ == "__main__":
+    main()

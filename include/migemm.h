@@ -92,12 +92,12 @@ int gemv_bf16(const uint16_t *W, const uint16_t *X, uint16_t *Y,
 /*
  * Same contract as gemm_f16 / gemm_bf16 with the tile configuration named by
  * the caller instead of chosen by the library:
- *   tile:    0 = automatic; 1 = 256x256 (K-step 32, 4 LDS stages);
- *            2 = 256x128 (K-step 64, 3 stages); 3 = 128x128 (K-step 32,
- *            4 stages); 4 = 256x256 with 5 stages; 5 = 256x256 with 3 stages;
- *            6 = 256x128 (K-step 32, 5 stages).  All use 4 waves per
- *            workgroup; tiles other than 3 need M and K to be multiples of 8
- *            and A, B 16-byte aligned (else MIGEMM_ERR_CONFIG);
+ *   tile:    0 = automatic; 1 = 256x256 (4 waves as 2x2, 4 LDS stages);
+ *            2 = 256x128 (5 stages); 3 = 128x128 (4 stages, two workgroups
+ *            per CU); 4 = tile 1 with 5 stages; 5 = 256x256 with the 4 waves
+ *            stacked along M; 6 = tile 1 with 3 stages.  All step K by 32;
+ *            tiles other than 3 need M and K to be multiples of 8 and A, B
+ *            16-byte aligned (else MIGEMM_ERR_CONFIG);
  *   group_m: width of the grouped tile ordering (FlagGems "Hygon 优化" page,
  *            section "分组调度"), >= 1, or 0 for automatic;
  *   xcd_remap: 1 to place consecutive tiles of the ordering on one XCD's L2,

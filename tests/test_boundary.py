@@ -65,7 +65,8 @@ def test_gemm_ex_config_errors():
     L = binding.lib()
     args = (P, P + 0x100000, P + 0x200000, 64, 64, 64)
     assert L.gemm_ex(2, *args, 0, 0, 1, None) == -5
-    assert L.gemm_ex(0, *args, 4, 0, 1, None) == -5
+    assert L.gemm_ex(0, *args, 99, 0, 1, None) == -5
+    assert L.gemm_ex(0, *args, -1, 0, 1, None) == -5
     assert L.gemm_ex(0, *args, 0, -1, 1, None) == -5
     assert L.gemm_ex(0, *args, 0, 0, 2, None) == -5
     # 256-row tiles need 16-byte loads: M = 5000 has them, K = 4100 does not
@@ -90,6 +91,7 @@ def test_plan_choices():
     code, p = binding.gemm_plan(0, P, P + 2 ** 30, P + 2 ** 31, 8192, 8192, 16384)
     assert code == 0 and (p["tile_m"], p["tile_n"], p["vec_a"], p["vec_b"], p["grid"]) == \
         (256, 256, 8, 8, 1024)
+    assert p["tile_k"] == 32
     assert p["lds_bytes"] <= 160 * 1024
     # ragged: M = 5000 keeps 16-byte A loads, K = 4100 drops B to 4-byte loads
     code, p = binding.gemm_plan(1, P, P + 2 ** 30, P + 2 ** 31, 5000, 3000, 4100)
