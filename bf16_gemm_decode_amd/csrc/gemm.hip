@@ -7,10 +7,11 @@
 //
 //  * one workgroup owns a BM x BN tile of C, picked by tile_coord() (XCD
 //    renumbering + the grouped ordering of the FlagGems Hygon page);
-//  * K advances in 64-wide steps through two LDS stages.  Each step's A tile
-//    (64 rows of BM m-contiguous elements) and B tile go straight from HBM
-//    into LDS with buffer loads that write LDS directly (no VGPR staging),
-//    one step ahead of the step being computed;
+//  * K advances in 32-wide steps through a ring of S LDS stages (S = 3..5).
+//    Each step's A tile (32 k-rows of BM m-contiguous elements) and B tile
+//    go straight from HBM into LDS with buffer loads that write LDS directly
+//    (no VGPR staging), issued S steps ahead of the step being computed, with
+//    explicit vmcnt waits and one barrier per step;
 //  * A is m-contiguous, but an MFMA operand needs 8 consecutive k of one row
 //    per lane, so A is read out of LDS with the transposing ds_read_b64_tr_b16
 //    (lane i of each 16-lane group receives row i of a 16 x 4 block), from a
@@ -20,10 +21,11 @@
 //    fragment as one KiB in exactly the order the lanes read it: the B
 //    fragment reads are linear ds_read_b128 (the fastest LDS pattern);
 //  * operand fragments are double-buffered in registers: the LDS reads of the
-//    next 32-wide k slice (including the first slice of the next step, right
-//    after the step's barrier) are issued before the MFMAs of the current one,
-//    all from per-lane base addresses plus immediate offsets;
-//  * v_mfma_f32_16x16x32_{f16,bf16} accumulates in FP32 registers;
+//    next step and the loads of step + S are interleaved between the MFMAs of
+//    the current step at fixed positions (sched_barrier), all from per-lane
+//    base addresses plus immediate offsets;
+//  * v_mfma_f32_16x16x32_{f16,bf16} accumulates in FP32 AGPRs, each
+//    accumulator tied to a fixed register;
 //  * out-of-range rows/columns are never stored; out-of-range k reads as
 //    zero through the buffer descriptors' range check, so ragged K needs no
 //    separate path;
