@@ -10,7 +10,9 @@ Printed: one JSON line.  `value` is the GEMM's TFLOP/s (2*M*N*K per launch over
 the average launch time measured with HIP events on the launch stream); the
 GEMV's HBM GB/s is reported beside it with its own roofline, against both the
 8 TB/s nominal peak and the read bandwidth measured here by the streaming-read
-probe.  `cpu_baseline` times the CPU oracle on a bounded sample of the same
+probe; its launch duration comes from a burst of back-to-back launches on the
+same stream (inside a step the events also hold the dispatch gap, reported as
+in_step_avg_us).  `cpu_baseline` times the CPU oracle on a bounded sample of the same
 GEMM (sampled output entries), scaled to TFLOP/s.
 
 Usage: python bench.py [--gpus 1] [--steps 20] [--warmup 5] [--no-cpu-baseline]
@@ -77,18 +79,16 @@ def hbm_probe(binding, torch, stream, nbytes=4 << 30, reps=20):
     return nbytes / ts[len(ts) // 2] / 1e9
 
 
-def measured_traffic(kernel_file, summary_file):
+def measured_traffic(sources, summary_file):
     """HBM bytes per launch from a committed rocprofv3 counter summary, or
-    None when there is none or the kernel source changed since it was taken."""
-    import hashlib
+    None when there is none or the kernel's sources changed since it was taken."""
+    from bf16_gemm_decode_amd.profile_summary import source_digest
     path = os.path.join(ROOT, "profiles", summary_file)
-    src = os.path.join(ROOT, "bf16_gemm_decode_amd", "csrc", kernel_file)
     try:
         summ = json.load(open(path))
-        digest = hashlib.sha256(open(src, "rb").read()).hexdigest()
     except (OSError, ValueError):
         return None
-    if summ.get("kernel_source_sha256") != digest:
+    if summ.get("kernel_sources") != sources or summ.get("kernel_sources_sha256") != source_digest(sources):
         return None
     return summ.get("hbm_bytes_per_launch")
 
@@ -127,6 +127,7 @@ def main():
 
     import synth
     from bf16_gemm_decode_amd import binding, roofline as rf
+    from bf16_gemm_decode_amd.profile_summary import GEMM_SOURCES, GEMV_SOURCES
 
     torch.cuda.set_device(0)
     if args.copy_calibration:
@@ -170,6 +171,10 @@ def main():
         return L.gemv_bf16_ex(dW[i % W_COPIES].data_ptr(), dX.data_ptr(), dY.data_ptr(),
                               GM, GK, gn, args.rows_per_block, h)
 
+    code, plan = binding.gemm_plan(binding.F16, dA.data_ptr(), dB.data_ptr(), dC.data_ptr(),
+                                   M, N, K, args.tile, args.group_m, args.xcd_remap)
+    assert code == 0, code
+    kernel = "gemm_fl_kernel" if plan["tile"] >= 7 else "gemm_kernel"
     for i in range(args.warmup):
         assert gemm() == 0 and gemv(i) == 0
     stream.synchronize()
@@ -192,7 +197,20 @@ def main():
 
     gemm_s = [e[0].elapsed_time(e[1]) / 1e3 for e in ev]
     gemv_s = [e[2].elapsed_time(e[3]) / 1e3 for e in ev]
-    gemm_avg, gemv_avg = sum(gemm_s) / len(gemm_s), sum(gemv_s) / len(gemv_s)
+    gemm_avg, gemv_step_avg = sum(gemm_s) / len(gemm_s), sum(gemv_s) / len(gemv_s)
+
+    # The GEMV's launch duration: inside a step its events also hold the
+    # dispatch gap (a few microseconds, a few percent of a ~50 us kernel), so
+    # it is timed again as a burst of back-to-back launches over the rotated
+    # W copies, on the same stream.
+    nburst = max(4 * args.steps, 40)
+    b0, b1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+    b0.record(stream)
+    for i in range(nburst):
+        assert gemv(i) == 0
+    b1.record(stream)
+    stream.synchronize()
+    gemv_avg = b0.elapsed_time(b1) / 1e3 / nburst
     tflops = rf.gemm_flop(M, N, K) / gemm_avg / 1e12
     gemv_bytes = rf.gemv_bytes(GM, GK, gn)
     gemv_GBps = gemv_bytes / gemv_avg / 1e9
@@ -214,20 +232,23 @@ def main():
         "data": "synthetic",
         "config": {"workload": "%s + %s (n=%d)" % (GEMM_CFG, GEMV_CFG, gn),
                    "gemm": {"M": M, "N": N, "K": K, "dtype": "f16", "layout": "column-major",
-                            "tile": args.tile, "group_m": args.group_m,
-                            "xcd_remap": args.xcd_remap},
+                            "tile": plan["tile"], "tile_mnk": [plan["tile_m"], plan["tile_n"], plan["tile_k"]],
+                            "waves": plan["waves"], "lds_bytes": plan["lds_bytes"],
+                            "group_m": plan["group_m"], "xcd_remap": plan["xcd_remap"],
+                            "grid": plan["grid"]},
                    "gemv": {"M": GM, "K": GK, "n": gn, "dtype": "bf16",
-                            "rows_per_block": args.rows_per_block or 8,
+                            "rows_per_block": args.rows_per_block or 2,
                             "w_copies_rotated": W_COPIES}},
         "roofline": {"bound": "mfma", "achieved": round(tflops, 2), "peak": peak,
                      "unit": "TFLOP/s", "frac": round(tflops / peak, 4),
-                     "traffic": measured_traffic("gemm.hip", "gemm_8192x8192x16384_f16_traffic.json"),
-                     "kernel": "gemm_kernel (2*M*N*K FLOP per launch)",
+                     "traffic": measured_traffic(GEMM_SOURCES, "gemm_8192x8192x16384_f16_traffic.json"),
+                     "kernel": "%s (2*M*N*K FLOP per launch)" % kernel,
                      "avg_launch_ms": round(gemm_avg * 1e3, 4)},
         "gemv": {"GBps": round(gemv_GBps, 1), "avg_launch_us": round(gemv_avg * 1e6, 2),
+                 "launches_timed": nburst, "in_step_avg_us": round(gemv_step_avg * 1e6, 2),
                  "roofline": {"bound": "hbm", "achieved": round(gemv_GBps, 1), "peak": hbm,
                               "unit": "GB/s", "frac": round(gemv_GBps / hbm, 4),
-                              "traffic": measured_traffic("gemv.hip", "gemv_34816x5120_bf16_n1_traffic.json"),
+                              "traffic": measured_traffic(GEMV_SOURCES, "gemv_34816x5120_bf16_n1_traffic.json"),
                               "algorithmic_bytes": int(gemv_bytes)},
                  "probe_read_GBps": round(probe_GBps, 1),
                  "frac_of_probe": round(gemv_GBps / probe_GBps, 4)},

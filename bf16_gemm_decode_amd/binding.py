@@ -33,7 +33,7 @@ class Plan(ctypes.Structure):
     _fields_ = [("tile_m", ctypes.c_int), ("tile_n", ctypes.c_int), ("tile_k", ctypes.c_int),
                 ("waves", ctypes.c_int), ("group_m", ctypes.c_int), ("xcd_remap", ctypes.c_int),
                 ("vec_a", ctypes.c_int), ("vec_b", ctypes.c_int), ("grid", ctypes.c_int64),
-                ("lds_bytes", ctypes.c_int)]
+                ("lds_bytes", ctypes.c_int), ("tile", ctypes.c_int), ("a_kmajor", ctypes.c_int)]
 
     def as_dict(self):
         return {f: getattr(self, f) for f, _ in self._fields_}
@@ -50,10 +50,14 @@ SIGNATURES = {
     "gemm_bf16": (_I, [_P, _P, _P, _I, _I, _I, _P]),
     "gemv_bf16": (_I, [_P, _P, _P, _I, _I, _I, _P]),
     "gemm_ex": (_I, [_I, _P, _P, _P, _I, _I, _I, _I, _I, _I, _P]),
+    "gemm_tn_f16": (_I, [_P, _P, _P, _I, _I, _I, _P]),
+    "gemm_tn_bf16": (_I, [_P, _P, _P, _I, _I, _I, _P]),
+    "gemm_tn_ex": (_I, [_I, _P, _P, _P, _I, _I, _I, _I, _I, _I, _P]),
     "gemv_bf16_ex": (_I, [_P, _P, _P, _I, _I, _I, _I, _P]),
     "migemm_tile_coord": (_I, [_I64, _I64, _I64, _I64, _I64,
                                ctypes.POINTER(_I64), ctypes.POINTER(_I64)]),
     "migemm_gemm_plan_for": (_I, [_I, _P, _P, _P, _I, _I, _I, _I, _I, _I, ctypes.POINTER(Plan)]),
+    "migemm_gemm_tn_plan_for": (_I, [_I, _P, _P, _P, _I, _I, _I, _I, _I, _I, ctypes.POINTER(Plan)]),
     "migemm_strerror": (ctypes.c_char_p, [_I]),
     "migemm_abi_version": (_I, []),
     "migemm_hbm_read": (_I, [_P, ctypes.c_size_t, _P, _P]),
@@ -95,6 +99,10 @@ def gemm_ex_ptr(dtype, A, B, C, M, N, K, tile=0, group_m=0, xcd_remap=1, stream=
     return lib().gemm_ex(dtype, A, B, C, M, N, K, tile, group_m, xcd_remap, stream or None)
 
 
+def gemm_tn_ex_ptr(dtype, At, B, C, M, N, K, tile=0, group_m=0, xcd_remap=1, stream=0):
+    return lib().gemm_tn_ex(dtype, At, B, C, M, N, K, tile, group_m, xcd_remap, stream or None)
+
+
 def gemv_bf16_ptr(W, X, Y, M, K, n, stream=0):
     return lib().gemv_bf16(W, X, Y, M, K, n, stream or None)
 
@@ -110,10 +118,10 @@ def tile_coord(wg, num_pid_m, num_pid_n, group_m, num_xcd):
     return pm.value, pn.value
 
 
-def gemm_plan(dtype, A, B, C, M, N, K, tile=0, group_m=0, xcd_remap=1):
+def gemm_plan(dtype, A, B, C, M, N, K, tile=0, group_m=0, xcd_remap=1, a_kmajor=False):
     p = Plan()
-    code = lib().migemm_gemm_plan_for(dtype, A, B, C, M, N, K, tile, group_m, xcd_remap,
-                                      ctypes.byref(p))
+    fn = lib().migemm_gemm_tn_plan_for if a_kmajor else lib().migemm_gemm_plan_for
+    code = fn(dtype, A, B, C, M, N, K, tile, group_m, xcd_remap, ctypes.byref(p))
     return code, p.as_dict()
 
 

@@ -38,7 +38,8 @@ int64_t cdiv(int64_t a, int64_t b) { return (a + b - 1) / b; }
 // *launch = true) when a kernel must run, 0 with *launch = false for an empty
 // output, or a negative MIGEMM_ERR_* code.
 int plan_gemm(int dtype, const uint16_t *A, const uint16_t *B, const uint16_t *C, int M, int N,
-              int K, int tile, int group_m, int xcd_remap, GemmLaunch &L, bool &launch)
+              int K, int tile, int group_m, int xcd_remap, GemmLaunch &L, bool &launch,
+              bool a_kmajor = false)
 {
     launch = false;
     if (dtype != DT_F16 && dtype != DT_BF16) return MIGEMM_ERR_CONFIG;
@@ -59,15 +60,26 @@ int plan_gemm(int dtype, const uint16_t *A, const uint16_t *B, const uint16_t *C
     L.M = M;
     L.N = N;
     L.K = K;
-    L.vec_a = vec_width(A, M);
+    L.vec_a = vec_width(A, a_kmajor ? K : M);
     L.vec_b = vec_width(B, K);
     L.c_vec = (M % 4 == 0 && (uintptr_t)C % 8 == 0) ? 1 : 0;
+    L.a_kmajor = a_kmajor ? 1 : 0;
     const bool wide = (L.vec_a == 8 && L.vec_b == 8);
-    if (tile == TILE_AUTO) {
-        // the 256x256 tile (waves stacked along M) once it fills the 256 CUs
+    if (a_kmajor) {
+        // k-major A: the full-line tiles only, 16-byte rows of A and B
+        if (!wide) return MIGEMM_ERR_ALIGN;
+        if (tile == TILE_AUTO) {
+            tile = cdiv(M, 256) * cdiv(N, 256) >= 512 ? TILE_256x256_FL8
+                   : TILE_256x128_FL;
+        } else if (tile != TILE_256x256_FL && tile != TILE_256x256_FL22 &&
+                   tile != TILE_256x128_FL && tile != TILE_256x256_FL8) {
+            return MIGEMM_ERR_CONFIG;
+        }
+    } else if (tile == TILE_AUTO) {
+        // the 256x256 full-line tile with 8 waves once it fills the 256 CUs
         // at least twice, else 256x128, else the 128x128 tile
         if (wide && cdiv(M, 256) * cdiv(N, 256) >= 512)
-            tile = TILE_256x256_W41;
+            tile = TILE_256x256_FL8;
         else if (wide && cdiv(M, 256) * cdiv(N, 128) >= 512)
             tile = TILE_256x128;
         else
@@ -124,16 +136,36 @@ int gemm_bf16(const uint16_t *A, const uint16_t *B, uint16_t *C, int M, int N, i
     return gemm_ex(DT_BF16, A, B, C, M, N, K, TILE_AUTO, 0, 1, stream);
 }
 
-int migemm_gemm_plan_for(int dtype, const uint16_t *A, const uint16_t *B, const uint16_t *C,
-                         int M, int N, int K, int tile, int group_m, int xcd_remap,
-                         migemm_gemm_plan *plan)
+int gemm_tn_ex(int dtype, const uint16_t *At, const uint16_t *B, uint16_t *C, int M, int N, int K,
+               int tile, int group_m, int xcd_remap, void *stream)
 {
     GemmLaunch L;
     bool launch;
-    int rc = plan_gemm(dtype, A, B, C, M, N, K, tile, group_m, xcd_remap, L, launch);
+    int rc = plan_gemm(dtype, At, B, C, M, N, K, tile, group_m, xcd_remap, L, launch, true);
+    if (rc != MIGEMM_OK || !launch) return rc;
+    return finish(gemm_launch(L, (hipStream_t)stream), stream);
+}
+
+int gemm_tn_f16(const uint16_t *At, const uint16_t *B, uint16_t *C, int M, int N, int K, void *stream)
+{
+    return gemm_tn_ex(DT_F16, At, B, C, M, N, K, TILE_AUTO, 0, 1, stream);
+}
+
+int gemm_tn_bf16(const uint16_t *At, const uint16_t *B, uint16_t *C, int M, int N, int K, void *stream)
+{
+    return gemm_tn_ex(DT_BF16, At, B, C, M, N, K, TILE_AUTO, 0, 1, stream);
+}
+
+static int plan_for(int dtype, const uint16_t *A, const uint16_t *B, const uint16_t *C,
+                    int M, int N, int K, int tile, int group_m, int xcd_remap,
+                    migemm_gemm_plan *plan, bool a_kmajor)
+{
+    GemmLaunch L;
+    bool launch;
+    int rc = plan_gemm(dtype, A, B, C, M, N, K, tile, group_m, xcd_remap, L, launch, a_kmajor);
     if (rc != MIGEMM_OK || !plan) return rc;
     memset(plan, 0, sizeof(*plan));
-    const TileShape &t = kTileShapes[L.tile];
+    const TileShape &t = a_kmajor ? kTileShapesKmajorA[L.tile] : kTileShapes[L.tile];
     plan->tile_m = t.bm;
     plan->tile_n = t.bn;
     plan->tile_k = t.bk;
@@ -143,8 +175,24 @@ int migemm_gemm_plan_for(int dtype, const uint16_t *A, const uint16_t *B, const 
     plan->vec_a = L.vec_a;
     plan->vec_b = L.vec_b;
     plan->grid = launch ? L.grid : 0;
-    plan->lds_bytes = t.stages * t.bk * (t.bm + t.bn) * 2;
+    plan->lds_bytes = tile_lds_bytes(t, a_kmajor);
+    plan->tile = L.tile;
+    plan->a_kmajor = a_kmajor ? 1 : 0;
     return rc;
+}
+
+int migemm_gemm_plan_for(int dtype, const uint16_t *A, const uint16_t *B, const uint16_t *C,
+                         int M, int N, int K, int tile, int group_m, int xcd_remap,
+                         migemm_gemm_plan *plan)
+{
+    return plan_for(dtype, A, B, C, M, N, K, tile, group_m, xcd_remap, plan, false);
+}
+
+int migemm_gemm_tn_plan_for(int dtype, const uint16_t *At, const uint16_t *B, const uint16_t *C,
+                            int M, int N, int K, int tile, int group_m, int xcd_remap,
+                            migemm_gemm_plan *plan)
+{
+    return plan_for(dtype, At, B, C, M, N, K, tile, group_m, xcd_remap, plan, true);
 }
 
 int gemv_bf16_ex(const uint16_t *W, const uint16_t *X, uint16_t *Y, int M, int K, int n,
@@ -164,7 +212,7 @@ int gemv_bf16_ex(const uint16_t *W, const uint16_t *X, uint16_t *Y, int M, int K
     L.W = W;
     L.M = M;
     L.K = K;
-    L.rows_per_block = rows_per_block ? rows_per_block : 8;
+    L.rows_per_block = rows_per_block ? rows_per_block : 2;
     L.vec = (K % 8 == 0 && (uintptr_t)W % 16 == 0 && (uintptr_t)X % 16 == 0) ? 8 : 1;
     L.grid = cdiv(M, L.rows_per_block);
     // Token blocks of 16, 8, 4, 2, 1: each launch streams W once.
@@ -211,7 +259,7 @@ const char *migemm_strerror(int code)
     return code > 0 ? "HIP runtime error (code is a hipError_t)" : "unknown error";
 }
 
-int migemm_abi_version(void) { return 1; }
+int migemm_abi_version(void) { return 2; }
 
 int migemm_hbm_read(const void *buf, size_t bytes, uint32_t *sink, void *stream)
 {

@@ -407,6 +407,355 @@ gemm_kernel(const uint16_t *__restrict__ A, const uint16_t *__restrict__ B,
 }
 
 // ---------------------------------------------------------------------------
+// Full-line variant: A as above (a ring of SA stages of 32 k-rows), B through
+// its own ring of SB stages that each hold 64 k of every tile column.
+//
+// Why: an MFMA B operand spans 16 columns x 32 k, i.e. half of each column's
+// 128-byte line, so a wave load that fills one operand touches 16 lines half
+// each.  A wave load over eight columns x 64 k touches 8 whole lines instead,
+// and the fetch path (L1, L2) then moves the same bytes in markedly less
+// time.  In the B stage, column c sits at byte c*128 with its eight 16-byte
+// k-chunks permuted: chunk x at position x ^ ((c >> 1) & 7).  A wave load
+// fills eight consecutive columns (lane l: column 8p + l/8, position l%8),
+// so each group of 8 lanes fetches one whole line; an operand read (lane
+// (g, i): column 16j + i, chunk 4s + g) then spreads every 16 lanes over all
+// LDS banks.
+//
+// Sub-step j (32 k) reads A stage j % SA and half j & 1 of B stage
+// (j / 2) % SB.  Sub-step j issues the A loads of sub-step j + SA, then half
+// of the B loads of one B stage: for odd j the first half of pair
+// (j-1)/2 + SB, for even j the second half of pair (j-2)/2 + SB (both into
+// the stage freed by pair (j-1)/2 resp. (j-2)/2), so every sub-step issues
+// the same number of loads.  The prologue issues what the sub-steps before 0
+// would have.  fl_loads_after() counts, from that fixed order, how many
+// loads may still fly when a sub-step's data is needed.
+template <bool AK, int SA, int SB, int LA, int LBH>
+constexpr int fl_loads_after(int j, int need_a, int need_b)
+{
+    int n = 0;
+    for (int i = j - 1; i >= -2 * (SA + SB) - 4; --i) {
+        // sub-step i issued its A part, then one half of a B stage: undo in
+        // reverse.  The A part is sub-step i + SA (m-major A) or one half of
+        // A stage base + SA (k-major A), like B.
+        const int base = (i & 1) ? (i - 1) / 2 : (i - 2) / 2;
+        const int p = base + SB;
+        if (p >= 0) {
+            if (p == need_b) return n;
+            n += LBH;
+        }
+        const int a = AK ? base + SA : i + SA;
+        if (a >= 0) {
+            if (a == need_a) return n;
+            n += LA;
+        }
+    }
+    return -1;
+}
+
+// AK = false: A m-major (A(m,k) = A[m + k*M]), A ring of SA stages of 32 k
+// rows read with transposing LDS reads.  AK = true: A k-major (A(m,k) =
+// A[k + m*K]), A ring of SA stages of 64 k laid out, loaded and read exactly
+// like B (rows of A in place of columns of B).
+template <int DT, bool AK, int BM, int BN, int WGM, int WGN, int SA, int SB>
+__global__ void __launch_bounds__(WGM * WGN * 64)
+__attribute__((amdgpu_waves_per_eu(WGM * WGN / 4, WGM * WGN / 4)))
+gemm_fl_kernel(const uint16_t *__restrict__ A, const uint16_t *__restrict__ B,
+               uint16_t *__restrict__ C, int M, int N, int K, int num_pid_m, int num_pid_n,
+               int group_m, int num_xcd, int c_vec)
+{
+    constexpr int BK = 32;                        // sub-step = one MFMA k slice
+    constexpr int NW = WGM * WGN;
+    constexpr int TM = BM / WGM, TN = BN / WGN;
+    constexpr int FM = TM / 16, FN = TN / 16;
+    constexpr int A_BYTES = AK ? BM * 128 : BK * BM * 2;   // one A stage
+    constexpr int B_BYTES = BN * 128;             // one B stage: 64 k of each column
+    constexpr int B_BASE = SA * A_BYTES;
+    constexpr int LDS_BYTES = B_BASE + SB * B_BYTES;
+    // A loads per wave per sub-step (m-major) or per half stage (k-major)
+    constexpr int LA = AK ? A_BYTES / (2048 * NW) : A_BYTES / (1024 * NW);
+    constexpr int LB = B_BYTES / (1024 * NW);     // B loads per wave per B stage
+    constexpr int LBH = LB / 2;                   // ... per sub-step
+    static_assert(A_BYTES % ((AK ? 2048 : 1024) * NW) == 0 && B_BYTES % (2048 * NW) == 0, "loader split");
+    static_assert(TM % 16 == 0 && TN % 16 == 0 && BN % 16 == 0, "tile shape");
+    static_assert(LDS_BYTES <= 163840, "LDS rings");
+    constexpr int W_EVEN = fl_loads_after<AK, SA, SB, LA, LBH>(64, AK ? 32 : 65, 32);
+    constexpr int W_ODD = fl_loads_after<AK, SA, SB, LA, LBH>(65, AK ? 33 : 66, 33);
+    constexpr int W_PRO = fl_loads_after<AK, SA, SB, LA, LBH>(0, 0, 0);
+    static_assert(W_EVEN >= 0 && W_EVEN < 64 && W_ODD >= 0 && W_ODD < 64 && W_PRO >= 0 && W_PRO < 64,
+                  "vmcnt range");
+
+    __shared__ __attribute__((aligned(1024))) unsigned char smem[LDS_BYTES];
+
+    int pid_m, pid_n;
+    tile_coord<int>((int)blockIdx.x, num_pid_m, num_pid_n, group_m, num_xcd, pid_m, pid_n);
+    const int m0 = pid_m * BM, n0 = pid_n * BN;
+    const int lane = threadIdx.x & 63;
+    const int wave = uniform(threadIdx.x >> 6);
+    const int wm = wave % WGM, wn = wave / WGM;
+    const int g = lane >> 4, ig = lane & 15;
+    const uint32_t lds0 = (uint32_t)(uintptr_t)(MIGEMM_LDS unsigned char *)smem;
+
+    // k-major loads (B, and A when AK): lane l of load q fills row/column
+    // c = 8p + l/8 of the tile at chunk position l%8, i.e. k chunk
+    // x = (l%8) ^ ((c >> 1) & 7) of the stage's 64 k
+    auto kmajor_lane = [&](int q, int stride, uint32_t &off, int &kk) {
+        const int c = 8 * (q * NW + wave) + (lane >> 3);
+        const int x = (lane & 7) ^ ((c >> 1) & 7);
+        off = (uint32_t)(((int64_t)c * stride + 8 * x) * 2);
+        kk = 8 * x;
+    };
+    constexpr int NAO = AK ? 2 * LA : LA;
+    uint32_t a_off[NAO];
+    int a_k[AK ? NAO : 1];
+#pragma unroll
+    for (int q = 0; q < NAO; ++q) {
+        if constexpr (AK) {
+            kmajor_lane(q, K, a_off[q], a_k[q]);
+        } else {
+            // m-major A: piece P = (q*NW + wave) KiB of the stage, row kk,
+            // swizzled 16-byte chunks
+            const int P = (q * NW + wave) * 1024 + lane * 16;
+            const int kk = P / (BM * 2), b = P % (BM * 2);
+            const int m = (((b >> 4) ^ swz_a<BM>(kk)) << 3);
+            a_off[q] = (uint32_t)(((int64_t)kk * M + m0 + m) * 2);
+        }
+    }
+    uint32_t b_off[LB];
+    int b_k[LB];
+#pragma unroll
+    for (int q = 0; q < LB; ++q) kmajor_lane(q, K, b_off[q], b_k[q]);
+
+    // Sub-steps, evened out: with an odd count a zero sub-step (k0 = -BK,
+    // every element read as zero) goes first.  P_ = number of 64-k stages.
+    const int J = (((K + BK - 1) / BK) + 1) & ~1;
+    const int P_ = J / 2;
+    const int kbase = ((K + BK - 1) / BK) & 1 ? -BK : 0;
+
+    // Descriptors.  m-major A: rebased at sub-step jj's first k row (k >= K
+    // reads zero; the leading zero sub-step gets no records).  k-major
+    // operands: rebased at X + r0*K + k0 elements for the stage starting at
+    // k0 (k0 may be -BK: the lanes below k = 0 are sent out of range, so
+    // nothing below X is read), with rows/columns >= R past the records.
+    auto desc_kmajor = [&](const uint16_t *X, int r0, int R, int pp) {
+        const int k0 = kbase + pp * 2 * BK;
+        const uint64_t base = (uint64_t)(uintptr_t)X + ((int64_t)r0 * K + k0) * 2;
+        return make_desc((const void *)(uintptr_t)base,
+                         clamp_records((int64_t)(R - r0) * K * 2 - (int64_t)k0 * 2));
+    };
+    auto desc_a = [&](int jj) {
+        if constexpr (AK) {
+            return desc_kmajor(A, m0, M, jj);
+        } else {
+            const int k0 = kbase + jj * BK;
+            return make_desc(A + (int64_t)k0 * M, k0 >= 0 ? clamp_records((int64_t)(K - k0) * M * 2) : 0u);
+        }
+    };
+    auto desc_b = [&](int pp) { return desc_kmajor(B, n0, N, pp); };
+    auto kmajor_off = [&](int pp, int kk, uint32_t off) {
+        const int k = kbase + pp * 2 * BK + kk;
+        return (k >= 0 && k < K) ? off : kOutOfRange;
+    };
+    // issue_a: m-major: load q of sub-step jj into A stage sa; k-major: load
+    // q (of 2*LA) of A stage jj into stage sa
+    auto issue_a = [&](const u32x4 &d, int jj, int sa, int q) {
+        uint32_t off = a_off[q];
+        if constexpr (AK) off = kmajor_off(jj, a_k[q], off);
+        dma_to_lds<16>(d, (uint32_t)uniform((int)(lds0 + sa * A_BYTES + (q * NW + wave) * 1024)), off);
+    };
+    auto issue_b = [&](const u32x4 &d, int pp, int sb, int q) {
+        dma_to_lds<16>(d, (uint32_t)uniform((int)(lds0 + B_BASE + sb * B_BYTES + (q * NW + wave) * 1024)),
+                       kmajor_off(pp, b_k[q], b_off[q]));
+    };
+
+    // operand reads (stage-relative): m-major A through transposing reads;
+    // k-major operands per half s of the stage
+    uint32_t a_rel[AK ? 2 : FM][2];
+    if constexpr (AK) {
+#pragma unroll
+        for (int s = 0; s < 2; ++s)
+            a_rel[s][0] = (wm * TM + ig) * 128 + 16 * ((4 * s + g) ^ ((ig >> 1) & 7));
+    } else {
+#pragma unroll
+        for (int i = 0; i < FM; ++i)
+#pragma unroll
+            for (int h = 0; h < 2; ++h) {
+                int kk = 8 * g + 4 * h + (ig >> 2);
+                int m = wm * TM + i * 16 + 4 * (ig & 3);
+                a_rel[i][h] = kk * (BM * 2) + ((((m >> 3) ^ swz_a<BM>(kk))) << 4) + (m & 7) * 2;
+            }
+    }
+    uint32_t b_rel[2];
+#pragma unroll
+    for (int s = 0; s < 2; ++s)
+        b_rel[s] = B_BASE + (wn * TN + ig) * 128 + 16 * ((4 * s + g) ^ ((ig >> 1) & 7));
+
+    struct Frag { u32x4 a[FM]; u32x4 b[FN]; };
+    constexpr int NR = FM + FN;
+    // item r of the NR reads that fill a fragment set: A block r or B block
+    // r - FM, from A stage sa and B stage sb (half s of the 64-k stages)
+    auto read_one = [&](int sa, int sb, int s, int r, Frag &f) {
+        const MIGEMM_LDS unsigned char *base = (const MIGEMM_LDS unsigned char *)smem;
+        if (r < FM) {
+            const MIGEMM_LDS unsigned char *ab = base + sa * A_BYTES;
+            if constexpr (AK) {
+                f.a[r] = *(const MIGEMM_LDS u32x4 *)(ab + a_rel[s][0] + r * 2048);
+            } else {
+                i16x4 lo = __builtin_amdgcn_ds_read_tr16_b64_v4i16((MIGEMM_LDS i16x4 *)(ab + a_rel[r][0]));
+                i16x4 hi = __builtin_amdgcn_ds_read_tr16_b64_v4i16((MIGEMM_LDS i16x4 *)(ab + a_rel[r][1]));
+                typedef __attribute__((ext_vector_type(8))) short i16x8;
+                i16x8 v = __builtin_shufflevector(lo, hi, 0, 1, 2, 3, 4, 5, 6, 7);
+                f.a[r] = __builtin_bit_cast(u32x4, v);
+            }
+        } else {
+            f.b[r - FM] = *(const MIGEMM_LDS u32x4 *)(base + sb * B_BYTES + b_rel[s] + (r - FM) * 2048);
+        }
+    };
+
+    f32x4 acc[FM][FN];
+#pragma unroll
+    for (int i = 0; i < FM; ++i)
+#pragma unroll
+        for (int j = 0; j < FN; ++j) acc[i][j] = f32x4{0.f, 0.f, 0.f, 0.f};
+
+    auto mma = [&](const Frag &f, auto nx_c, auto every_c, auto &&extra) {
+        constexpr int NXI = decltype(nx_c)::value, EV = decltype(every_c)::value;
+#pragma unroll
+        for (int i = 0; i < FM; ++i)
+#pragma unroll
+            for (int j = 0; j < FN; ++j) {
+                mfma16x16x32<DT>(acc[i][j], f.a[i], f.b[j]);
+                const int t = i * FN + j;
+                if (t % EV == EV - 1 && t / EV < NXI) extra(t / EV);
+                __builtin_amdgcn_sched_barrier(0);
+            }
+        constexpr int DONE = (FM * FN / EV < NXI ? FM * FN / EV : NXI);
+#pragma unroll
+        for (int x = DONE; x < NXI; ++x) extra(x);
+    };
+
+    // Sub-step j (parity PAR) on fragments `cur`.  Ring positions: sa / sb
+    // the stages of sub-step j, sap / sbp the 64-k stages before them.
+    // Reads sub-step j+1 into `nxt`, refills A (m-major: stage sa with
+    // sub-step j+SA; k-major: half of a freed stage, like B) and half of a
+    // freed B stage.  Before that, this wave's reads have landed (lgkmcnt),
+    // sub-step j+1's loads have landed (vmcnt: exact count while every load
+    // of the fixed order was issued, else all), and after the barrier no
+    // wave reads the stages being refilled.
+    auto step = [&](int j, auto par_c, int &sa, int &sap, int &sb, int &sbp, Frag &cur, Frag &nxt) {
+        constexpr int PAR = decltype(par_c)::value;
+        __builtin_amdgcn_s_waitcnt((7 << 4) | 0xc00f);   // lgkmcnt(0)
+        const int base_prev = PAR ? (j - 3) / 2 : (j - 2) / 2;   // stage base issued in sub-step j-1
+        const int base_cur = PAR ? (j - 1) / 2 : (j - 2) / 2;    // ... in sub-step j
+        if (j + 1 < J) {
+            const bool a_all = AK ? (base_prev + SA < P_) : (j - 1 + SA < J);
+            const bool exact = a_all && (base_prev + SB < P_);
+            if (exact) wait_vmcnt<PAR ? W_ODD : W_EVEN>();
+            else wait_vmcnt<0>();
+            __syncthreads();
+        }
+        const int ja = AK ? base_cur + SA : j + SA;     // A unit refilled
+        const bool ra = AK ? ja < P_ : ja < J;
+        const int sar = AK ? (PAR ? sa : sap) : sa;
+        const int pr = base_cur + SB;                  // B stage refilled
+        const bool rb = pr < P_;
+        const int sbr = PAR ? sb : sbp;
+        const u32x4 da = desc_a(ja), db = desc_b(pr);
+        const int nsa = AK ? (PAR ? ((sa + 1 == SA) ? 0 : sa + 1) : sa) : ((sa + 1 == SA) ? 0 : sa + 1);
+        const int nsb = PAR ? ((sb + 1 == SB) ? 0 : sb + 1) : sb;
+        constexpr int NL = LA + LBH;
+        constexpr int NX = NL + NR, NMF = FM * FN;
+        mma(cur, std::integral_constant<int, NX>{}, std::integral_constant<int, (NMF / NX > 0 ? NMF / NX : 1)>{},
+            [&](int x) {
+                constexpr int MN = NL < NR ? NL : NR;
+                auto load = [&](int q) {
+                    if (q < LA) {
+                        if (ra) issue_a(da, ja, sar, (AK && !PAR ? LA : 0) + q);
+                    } else {
+                        if (rb) issue_b(db, pr, sbr, (PAR ? 0 : LBH) + q - LA);
+                    }
+                };
+                if (x < 2 * MN) {
+                    if ((x & 1) == 0) read_one(nsa, nsb, 1 - PAR, x >> 1, nxt);
+                    else load(x >> 1);
+                } else {
+                    const int t = MN + (x - 2 * MN);
+                    if constexpr (NL > NR) load(t);
+                    else read_one(nsa, nsb, 1 - PAR, t, nxt);
+                }
+            });
+        if (PAR) {
+            sbp = sb;
+            if constexpr (AK) sap = sa;
+        }
+        sa = nsa;
+        sb = nsb;
+    };
+
+    if (J > 0) {
+        // prologue: the loads of the sub-steps before 0, in the fixed order
+#pragma unroll
+        for (int i = -2 * (SA + SB) - 4; i < 0; ++i) {
+            const int base = (i & 1) ? (i - 1) / 2 : (i - 2) / 2;
+            const int a = AK ? base + SA : i + SA;
+            if (a >= 0 && a < (AK ? P_ : J)) {
+                const u32x4 d = desc_a(a);
+#pragma unroll
+                for (int q = 0; q < LA; ++q) issue_a(d, a, a, (AK && !(i & 1) ? LA : 0) + q);
+            }
+            const int p = base + SB;
+            if (p >= 0 && p < P_) {
+                const u32x4 d = desc_b(p);
+#pragma unroll
+                for (int q = 0; q < LBH; ++q) issue_b(d, p, p, ((i & 1) ? 0 : LBH) + q);
+            }
+        }
+        if ((AK ? SA - 1 < P_ : SA - 1 < J) && SB - 1 < P_) wait_vmcnt<W_PRO>();
+        else wait_vmcnt<0>();
+        __syncthreads();
+        Frag f0, f1;
+#pragma unroll
+        for (int r = 0; r < NR; ++r) read_one(0, 0, 0, r, f0);
+        int sa = 0, sap = SA - 1, sb = 0, sbp = SB - 1;
+        for (int j = 0; j < J; j += 2) {
+            step(j, std::integral_constant<int, 0>{}, sa, sap, sb, sbp, f0, f1);
+            step(j + 1, std::integral_constant<int, 1>{}, sa, sap, sb, sbp, f1, f0);
+        }
+        wait_vmcnt<0>();   // no load may still target LDS when the workgroup ends
+    }
+
+    mfma_drain();
+#pragma unroll
+    for (int i = 0; i < FM; ++i) {
+        const int m = m0 + wm * TM + i * 16 + 4 * g;
+#pragma unroll
+        for (int j = 0; j < FN; ++j) {
+            const int n = n0 + wn * TN + j * 16 + ig;
+            if (n >= N) continue;
+            uint16_t *dst = C + (size_t)n * M + m;
+            if (c_vec && m + 3 < M) {
+                u16x4 v = {to_out<DT>(acc[i][j][0]), to_out<DT>(acc[i][j][1]),
+                           to_out<DT>(acc[i][j][2]), to_out<DT>(acc[i][j][3])};
+                *(u16x4 *)dst = v;
+            } else {
+#pragma unroll
+                for (int r = 0; r < 4; ++r)
+                    if (m + r < M) dst[r] = to_out<DT>(acc[i][j][r]);
+            }
+        }
+    }
+}
+
+template <int DT, bool AK, int BM, int BN, int WGM, int WGN, int SA, int SB>
+static hipError_t launch_fl(const GemmLaunch &L, hipStream_t stream)
+{
+    dim3 grid((unsigned)L.grid), block(WGM * WGN * 64);
+    hipLaunchKernelGGL((gemm_fl_kernel<DT, AK, BM, BN, WGM, WGN, SA, SB>), grid, block, 0, stream,
+                       L.A, L.B, L.C, L.M, L.N, L.K, L.num_pid_m, L.num_pid_n, L.group_m,
+                       L.num_xcd, L.c_vec);
+    return hipGetLastError();
+}
+
+// ---------------------------------------------------------------------------
 
 template <int DT, int BM, int BN, int WGM, int WGN, int S, int VA, int VB, int OCC>
 static hipError_t launch_t(const GemmLaunch &L, hipStream_t stream)
@@ -432,6 +781,18 @@ static hipError_t launch_dt(const GemmLaunch &L, hipStream_t s)
         return launch_t<DT, 256, 256, 4, 1, 4, 8, 8, 1>(L, s);
     case TILE_256x256_S3:
         return launch_t<DT, 256, 256, 2, 2, 3, 8, 8, 1>(L, s);
+    case TILE_256x256_FL:
+        return L.a_kmajor ? launch_fl<DT, true, 256, 256, 4, 1, 2, 3>(L, s)
+                          : launch_fl<DT, false, 256, 256, 4, 1, 4, 3>(L, s);
+    case TILE_256x256_FL22:
+        return L.a_kmajor ? launch_fl<DT, true, 256, 256, 2, 2, 2, 3>(L, s)
+                          : launch_fl<DT, false, 256, 256, 2, 2, 4, 3>(L, s);
+    case TILE_256x128_FL:
+        return L.a_kmajor ? launch_fl<DT, true, 256, 128, 4, 1, 3, 4>(L, s)
+                          : launch_fl<DT, false, 256, 128, 4, 1, 4, 4>(L, s);
+    case TILE_256x256_FL8:
+        return L.a_kmajor ? launch_fl<DT, true, 256, 256, 4, 2, 2, 3>(L, s)
+                          : launch_fl<DT, false, 256, 256, 4, 2, 4, 3>(L, s);
     case TILE_128x128:
 #define MIGEMM_V(va, vb) \
     if (L.vec_a == va && L.vec_b == vb) return launch_t<DT, 128, 128, 2, 2, 4, va, vb, 2>(L, s);

@@ -11,7 +11,9 @@
 // Mapping: a wave owns RW consecutive rows of W.  Each lane covers 8
 // consecutive k of every 512-wide chunk of K (one 16-byte load per row per
 // chunk, one wave instruction = 1 KiB of a row, fully coalesced), and U chunks
-// are loaded before any is consumed.  X is small and read through the caches.
+// are loaded before any is consumed.  W is read once, with non-temporal loads
+// (measured: they keep W from displacing other lines and raise the streaming
+// rate); X is small and read through the caches.
 // Products are exact in FP32 (BF16 widens by a shift) and accumulate with FP32
 // fused multiply-adds; the 64 per-lane partial sums of each output
 // are then added across the wave with cross-lane shuffles, and the result is
@@ -79,7 +81,7 @@ gemv_kernel(const uint16_t *__restrict__ W, const uint16_t *__restrict__ X,
             for (int u = 0; u < U; ++u)
 #pragma unroll
                 for (int r = 0; r < RW; ++r)
-                    w[u][r] = *(const u32x4 *)(wr[r] + (t + u) * CH + lk);
+                    w[u][r] = __builtin_nontemporal_load((const u32x4 *)(wr[r] + (t + u) * CH + lk));
 #pragma unroll
             for (int u = 0; u < U; ++u)
 #pragma unroll
@@ -92,7 +94,7 @@ gemv_kernel(const uint16_t *__restrict__ W, const uint16_t *__restrict__ X,
         for (; t < nfull; ++t) {
             u32x4 w[RW];
 #pragma unroll
-            for (int r = 0; r < RW; ++r) w[r] = *(const u32x4 *)(wr[r] + t * CH + lk);
+            for (int r = 0; r < RW; ++r) w[r] = __builtin_nontemporal_load((const u32x4 *)(wr[r] + t * CH + lk));
 #pragma unroll
             for (int i = 0; i < NT; ++i) {
                 u32x4 x = *(const u32x4 *)(X + (size_t)i * K + t * CH + lk);
@@ -172,39 +174,42 @@ hipError_t gemv_launch(const GemvLaunch &L, hipStream_t s)
 
 // ---- streaming-read probe ------------------------------------------------
 
-constexpr int kProbeBlocks = 4096;
-constexpr int kProbeUnroll = 8;
+constexpr int kProbeWaves = 8192;        // one-wave workgroups, 32 per CU
+constexpr int kProbeChunk = 8 * 64;      // 16-byte words per wave per step (8 KiB)
 
-// Each thread keeps kProbeUnroll independent 16-byte loads in flight per
-// iteration; consecutive threads read consecutive 16-byte words.
-__global__ void __launch_bounds__(256) hbm_read_kernel(const u32x4 *__restrict__ buf, size_t n16,
-                                                       uint32_t *__restrict__ sink)
+// Wave w reads the 8 KiB chunks w, w + kProbeWaves, ...: each lane keeps
+// eight 16-byte non-temporal loads in flight, a wave's loads of one chunk
+// cover it contiguously.  The words past the last whole chunk are read
+// grid-stride.  sink[w] receives the XOR of every 32-bit word wave w read,
+// so the XOR of all sink words equals the XOR of the buffer.
+__global__ void __launch_bounds__(64) hbm_read_kernel(const u32x4 *__restrict__ buf, size_t n16,
+                                                      uint32_t *__restrict__ sink)
 {
-    __shared__ uint32_t part[4];
-    const size_t stride = (size_t)gridDim.x * blockDim.x;
-    size_t i = (size_t)blockIdx.x * blockDim.x + threadIdx.x;
+    const int lane = threadIdx.x;
     u32x4 acc = {0u, 0u, 0u, 0u};
-    for (; i + (kProbeUnroll - 1) * stride < n16; i += kProbeUnroll * stride) {
-        u32x4 v[kProbeUnroll];
+    const size_t chunks = n16 / kProbeChunk;
+    for (size_t c = blockIdx.x; c < chunks; c += kProbeWaves) {
+        const u32x4 *p = buf + c * kProbeChunk + lane;
+        u32x4 v[8];
 #pragma unroll
-        for (int u = 0; u < kProbeUnroll; ++u) v[u] = __builtin_nontemporal_load(buf + i + u * stride);
+        for (int u = 0; u < 8; ++u) v[u] = __builtin_nontemporal_load(p + u * 64);
 #pragma unroll
-        for (int u = 0; u < kProbeUnroll; ++u) acc ^= v[u];
+        for (int u = 0; u < 8; ++u) acc ^= v[u];
     }
-    for (; i < n16; i += stride) acc ^= buf[i];
+    for (size_t i = chunks * kProbeChunk + (size_t)blockIdx.x * 64 + lane; i < n16;
+         i += (size_t)kProbeWaves * 64)
+        acc ^= buf[i];
     uint32_t v = acc[0] ^ acc[1] ^ acc[2] ^ acc[3];
 #pragma unroll
     for (int s = 32; s >= 1; s >>= 1) v ^= __shfl_xor(v, s, 64);
-    if ((threadIdx.x & 63) == 0) part[threadIdx.x >> 6] = v;
-    __syncthreads();
-    if (threadIdx.x == 0) sink[blockIdx.x] = part[0] ^ part[1] ^ part[2] ^ part[3];
+    if (lane == 0) sink[blockIdx.x] = v;
 }
 
-int hbm_read_sink_words() { return kProbeBlocks; }
+int hbm_read_sink_words() { return kProbeWaves; }
 
 hipError_t hbm_read_launch(const void *buf, size_t bytes, uint32_t *sink, hipStream_t s)
 {
-    hipLaunchKernelGGL(hbm_read_kernel, dim3(kProbeBlocks), dim3(256), 0, s,
+    hipLaunchKernelGGL(hbm_read_kernel, dim3(kProbeWaves), dim3(64), 0, s,
                        (const u32x4 *)buf, bytes / 16, sink);
     return hipGetLastError();
 }

@@ -14,24 +14,55 @@ enum GemmTile {
     TILE_256x256_S5 = 4,        // tile 1 with 5 stages (all 160 KiB of LDS)
     TILE_256x256_W41 = 5,       // 256x256, 4 waves stacked along M (64x256 per wave), 4 stages
     TILE_256x256_S3 = 6,        // tile 1 with 3 stages
+    TILE_256x256_FL = 7,        // 256x256, waves along M, full-line B ring (A 4 x 32 k, B 3 x 64 k)
+    TILE_256x256_FL22 = 8,      // as 7 with 4 waves as 2x2
+    TILE_256x128_FL = 9,        // 256x128, waves along M, full-line B ring (A 4 x 32 k, B 4 x 64 k)
+    TILE_256x256_FL8 = 10,      // as 7 with 8 waves (4 x 2, two per SIMD), 64x128 per wave
     TILE_COUNT
 };
 
+// stages: ring stages of 32 k (A and B together, or A alone when b_stages
+// > 0); b_stages: B ring stages of 64 k in the full-line variants.
 struct TileShape {
-    int bm, bn, bk, stages, waves;
+    int bm, bn, bk, stages, waves, b_stages;
 };
 
-// Indexed by GemmTile (entry 0 unused).  Every tile steps K by 32 through a
-// ring of LDS stages.
+// Indexed by GemmTile (entry 0 unused).  Every tile steps K by 32.
 constexpr TileShape kTileShapes[TILE_COUNT] = {
-    {0, 0, 0, 0, 0},
-    {256, 256, 32, 4, 4},
-    {256, 128, 32, 5, 4},
-    {128, 128, 32, 4, 4},
-    {256, 256, 32, 5, 4},
-    {256, 256, 32, 4, 4},
-    {256, 256, 32, 3, 4},
+    {0, 0, 0, 0, 0, 0},
+    {256, 256, 32, 4, 4, 0},
+    {256, 128, 32, 5, 4, 0},
+    {128, 128, 32, 4, 4, 0},
+    {256, 256, 32, 5, 4, 0},
+    {256, 256, 32, 4, 4, 0},
+    {256, 256, 32, 3, 4, 0},
+    {256, 256, 32, 4, 4, 3},
+    {256, 256, 32, 4, 4, 3},
+    {256, 128, 32, 4, 4, 4},
+    {256, 256, 32, 4, 8, 3},
 };
+
+// The full-line tiles with A k-major: stages = A ring stages of 64 k.
+constexpr TileShape kTileShapesKmajorA[TILE_COUNT] = {
+    {0, 0, 0, 0, 0, 0},
+    {0, 0, 0, 0, 0, 0},
+    {0, 0, 0, 0, 0, 0},
+    {0, 0, 0, 0, 0, 0},
+    {0, 0, 0, 0, 0, 0},
+    {0, 0, 0, 0, 0, 0},
+    {0, 0, 0, 0, 0, 0},
+    {256, 256, 32, 2, 4, 3},
+    {256, 256, 32, 2, 4, 3},
+    {256, 128, 32, 3, 4, 4},
+    {256, 256, 32, 2, 8, 3},
+};
+
+constexpr int tile_lds_bytes(const TileShape &t, bool a_kmajor = false)
+{
+    return a_kmajor ? (t.stages * t.bm + t.b_stages * t.bn) * 2 * t.bk * 2
+           : t.b_stages ? t.stages * t.bk * t.bm * 2 + t.b_stages * 2 * t.bk * t.bn * 2
+                        : t.stages * t.bk * (t.bm + t.bn) * 2;
+}
 
 struct GemmLaunch {
     int dtype;                    // DT_F16 or DT_BF16
@@ -43,6 +74,7 @@ struct GemmLaunch {
     int group_m, num_xcd;
     int vec_a, vec_b;             // elements per global->LDS load (8, 2 or 1)
     int c_vec;                    // 1: 8-byte stores of 4 rows are aligned
+    int a_kmajor;                 // 1: A(m,k) = A[k + m*K] (full-line tiles only)
     int64_t grid;
 };
 

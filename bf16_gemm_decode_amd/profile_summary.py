@@ -5,22 +5,38 @@ profiles/.
                      <run_kernel_stats.csv> <out.txt> --command "<rocprofv3 command>"
   traffic:       python -m bf16_gemm_decode_amd.profile_summary traffic \
                      --fetch <csv> --fetch-cal <csv> --write <csv> --write-cal <csv> \
-                     --kernel <name substring> --source <kernel .hip file> \
+                     --kernel <name substring> --source <source files...> \
                      --out <out.json> --commands "<cmd>" ...
 
 The traffic mode averages FETCH_SIZE and WRITE_SIZE (KiB per dispatch) over
 the matching kernel's dispatches and scales each by what the same counter
 reads for the plain 1 GiB device copy of `bench.py --copy-calibration`
 (profiled with the same counter), so that hbm_bytes_per_launch is in true
-bytes.  It records the SHA-256 of the
-kernel source so that a later change of the kernel invalidates the figure.
+bytes.  It records a SHA-256 over the sources that decide what the kernel
+does (source_digest), so that a later change of them invalidates the figure.
 """
 import argparse
 import collections
 import csv
 import hashlib
 import json
+import os
 import sys
+
+CSRC = os.path.join(os.path.dirname(os.path.abspath(__file__)), "csrc")
+# the sources whose change invalidates a kernel's recorded counters
+GEMM_SOURCES = ["gemm.hip", "api.hip", "kernels.hpp", "tile_map.hpp", "common.hpp"]
+GEMV_SOURCES = ["gemv.hip", "api.hip", "kernels.hpp", "common.hpp"]
+
+
+def source_digest(names):
+    """SHA-256 over the named csrc/ files (name and content, in order)."""
+    h = hashlib.sha256()
+    for n in names:
+        h.update(n.encode() + b"\0")
+        with open(os.path.join(CSRC, n), "rb") as f:
+            h.update(f.read())
+    return h.hexdigest()
 
 
 def _rows(path):
@@ -79,8 +95,8 @@ def traffic(args):
                                 "bytes_per_launch": kib * 1024.0 * scale}
     out["hbm_bytes_per_launch"] = (out["fetch_size"]["bytes_per_launch"] +
                                    out["write_size"]["bytes_per_launch"])
-    out["kernel_source"] = args.source
-    out["kernel_source_sha256"] = hashlib.sha256(open(args.source, "rb").read()).hexdigest()
+    out["kernel_sources"] = args.source
+    out["kernel_sources_sha256"] = source_digest(args.source)
     with open(args.out, "w") as o:
         json.dump(out, o, indent=1)
     print(json.dumps(out, indent=1))
@@ -100,7 +116,8 @@ def main(argv=None):
     t.add_argument("--write", required=True)
     t.add_argument("--write-cal", required=True)
     t.add_argument("--kernel", required=True)
-    t.add_argument("--source", required=True)
+    t.add_argument("--source", nargs="+", required=True,
+                   help="csrc/ file names, e.g. the GEMM_SOURCES list")
     t.add_argument("--out", required=True)
     t.add_argument("--commands", nargs="+", required=True)
     a = p.parse_args(argv)

@@ -2,7 +2,7 @@
 
 Usage (on a GPU machine):
   python -m bf16_gemm_decode_amd.sweep --shape 4096,34816,5120 --dtype bf16 \
-      --tiles 1,2,3 --group-m 1,4,8,16 --xcd 1
+      --tiles 1,2,3 --group-m 1,4,8,16 --xcd 1 [--tn]
 
 Prints one JSON line per configuration: average kernel time over --reps
 launches (HIP events on the launch stream) and TFLOP/s = 2*M*N*K / time,
@@ -25,6 +25,8 @@ def main(argv=None):
     p.add_argument("--xcd", default="1")
     p.add_argument("--reps", type=int, default=10)
     p.add_argument("--warmup", type=int, default=3)
+    p.add_argument("--tn", action="store_true",
+                   help="time gemm_tn_ex (A supplied k-major) instead of gemm_ex")
     a = p.parse_args(argv)
 
     import torch
@@ -42,9 +44,11 @@ def main(argv=None):
     for tile in (int(t) for t in a.tiles.split(",")):
         for gm in (int(v) for v in a.group_m.split(",")):
             for xcd in (int(v) for v in a.xcd.split(",")):
+                fn = L.gemm_tn_ex if a.tn else L.gemm_ex
+
                 def run():
-                    return L.gemm_ex(code_dt, A.data_ptr(), B.data_ptr(), C.data_ptr(), M, N, K,
-                                     tile, gm, xcd, s.cuda_stream)
+                    return fn(code_dt, A.data_ptr(), B.data_ptr(), C.data_ptr(), M, N, K,
+                              tile, gm, xcd, s.cuda_stream)
                 rc = run()
                 if rc != 0:
                     print(json.dumps({"tile": tile, "group_m": gm, "xcd_remap": xcd, "error": rc}))
@@ -60,9 +64,10 @@ def main(argv=None):
                 s.synchronize()
                 t = e0.elapsed_time(e1) / 1e3 / a.reps
                 _, plan = binding.gemm_plan(code_dt, A.data_ptr(), B.data_ptr(), C.data_ptr(),
-                                            M, N, K, tile, gm, xcd)
+                                            M, N, K, tile, gm, xcd, a_kmajor=a.tn)
                 tf = flop / t / 1e12
-                print(json.dumps({"shape": [M, N, K], "dtype": a.dtype, "tile": tile,
+                print(json.dumps({"shape": [M, N, K], "dtype": a.dtype, "a_layout": "k-major" if a.tn else "m-major",
+                                  "tile": tile,
                                   "tile_mnk": [plan["tile_m"], plan["tile_n"], plan["tile_k"]],
                                   "group_m": plan["group_m"], "xcd_remap": xcd,
                                   "grid": plan["grid"], "ms": round(t * 1e3, 4),

@@ -95,8 +95,12 @@ int gemv_bf16(const uint16_t *W, const uint16_t *X, uint16_t *Y,
  *   tile:    0 = automatic; 1 = 256x256 (4 waves as 2x2, 4 LDS stages);
  *            2 = 256x128 (5 stages); 3 = 128x128 (4 stages, two workgroups
  *            per CU); 4 = tile 1 with 5 stages; 5 = 256x256 with the 4 waves
- *            stacked along M; 6 = tile 1 with 3 stages.  All step K by 32;
- *            tiles other than 3 need M and K to be multiples of 8 and A, B
+ *            stacked along M; 6 = tile 1 with 3 stages; 7 = 256x256, waves
+ *            along M, B loaded as whole 128-byte column lines (64 k) into
+ *            its own 3-stage ring, A in a 4-stage ring; 8 = tile 7 with the
+ *            waves as 2x2; 9 = 256x128 like tile 7 with a 4-stage B ring;
+ *            10 = tile 7 with 8 waves (4 x 2, two per SIMD).
+ *            All step K by 32; tiles other than 3 need M and K to be multiples of 8 and A, B
  *            16-byte aligned (else MIGEMM_ERR_CONFIG);
  *   group_m: width of the grouped tile ordering (FlagGems "Hygon 优化" page,
  *            section "分组调度"), >= 1, or 0 for automatic;
@@ -107,6 +111,26 @@ int gemv_bf16(const uint16_t *W, const uint16_t *X, uint16_t *Y,
 int gemm_ex(int dtype, const uint16_t *A, const uint16_t *B, uint16_t *C,
             int M, int N, int K, int tile, int group_m, int xcd_remap,
             void *stream);
+
+/*
+ * GEMM with A supplied k-major ("TN"): C(m,n) = C[m + n*M] =
+ * RNE( sum_k At[k + m*K] * B[k + n*K] ), FP32 accumulation, i.e. C = A x B
+ * with A(m,k) = At[k + m*K] (A row-major, M x K).  Called with At = W
+ * (row-major [M, K]), B = X (row-major [N, K]) and C = Y it computes the
+ * DCU decode page's Y = X W^T (section 6.1) for a batch of N token rows,
+ * with Y row-major [N, M] -- the GEMV's own layout.  Same argument checks,
+ * ownership and completion rules as gemm_f16 / gemm_bf16.  Runs on the
+ * full-line tiles only: tile 0 (automatic), 7, 8, 9 or 10 (A takes B's
+ * 64-k ring layout; MIGEMM_ERR_CONFIG for other tiles).  K must be a
+ * multiple of 8 and At, B 16-byte aligned (else MIGEMM_ERR_ALIGN).
+ */
+int gemm_tn_f16(const uint16_t *At, const uint16_t *B, uint16_t *C,
+                int M, int N, int K, void *stream);
+int gemm_tn_bf16(const uint16_t *At, const uint16_t *B, uint16_t *C,
+                 int M, int N, int K, void *stream);
+int gemm_tn_ex(int dtype, const uint16_t *At, const uint16_t *B, uint16_t *C,
+               int M, int N, int K, int tile, int group_m, int xcd_remap,
+               void *stream);
 
 /*
  * Same contract as gemv_bf16 with rows_per_block (output rows of W per
@@ -138,6 +162,8 @@ typedef struct {
     int vec_a, vec_b;             /* elements per global->LDS load of A, B */
     int64_t grid;                 /* workgroups launched                  */
     int lds_bytes;                /* LDS per workgroup                    */
+    int tile;                     /* tile configuration id (as gemm_ex's) */
+    int a_kmajor;                 /* 1 for gemm_tn_ex's k-major A         */
 } migemm_gemm_plan;
 
 /* Fill *plan for gemm_ex's arguments (pointers are inspected for alignment
@@ -146,6 +172,10 @@ typedef struct {
 int migemm_gemm_plan_for(int dtype, const uint16_t *A, const uint16_t *B,
                          const uint16_t *C, int M, int N, int K, int tile,
                          int group_m, int xcd_remap, migemm_gemm_plan *plan);
+/* The same for gemm_tn_ex. */
+int migemm_gemm_tn_plan_for(int dtype, const uint16_t *At, const uint16_t *B,
+                            const uint16_t *C, int M, int N, int K, int tile,
+                            int group_m, int xcd_remap, migemm_gemm_plan *plan);
 
 /* Human-readable text for a return code (static storage). */
 const char *migemm_strerror(int code);
@@ -157,10 +187,12 @@ int migemm_abi_version(void);
 
 /*
  * Streaming-read bandwidth probe: reads `bytes` bytes from device buffer
- * `buf` once with 16-byte loads and writes one 32-bit checksum per workgroup
- * to `sink` (device, at least migemm_hbm_read_sink_words() words).  `bytes`
- * must be a multiple of 16 and `buf` 16-byte aligned.  Used to measure the
- * achievable HBM read bandwidth that the GEMV is compared with.
+ * `buf` once (each wave reads contiguous 8 KiB chunks with eight 16-byte
+ * non-temporal loads per lane in flight) and writes one 32-bit XOR
+ * checksum per wave to `sink` (device, migemm_hbm_read_sink_words() words;
+ * the XOR of all of them is the XOR of the buffer's 32-bit words).
+ * `bytes` must be a multiple of 16 and `buf` 16-byte aligned.  Used to
+ * measure the achievable HBM read bandwidth that the GEMV is compared with.
  */
 int migemm_hbm_read(const void *buf, size_t bytes, uint32_t *sink, void *stream);
 int migemm_hbm_read_sink_words(void);

@@ -54,6 +54,28 @@ def gemm_gpu(A_bits, B_bits, M, N, K, fmt, tile=0, group_m=0, xcd_remap=1, strea
     return C.out(), C.guards_intact(), unchanged
 
 
+def gemm_tn_gpu(At_bits, B_bits, M, N, K, fmt, tile=0, group_m=0, xcd_remap=1, stream=0):
+    """gemm_tn_ex through the C ABI (A given k-major: A(m,k) = At[k + m*K]);
+    returns (C bits, guards ok, inputs unchanged)."""
+    import torch
+    from bf16_gemm_decode_amd import binding
+    dA, dB = dev(At_bits), dev(B_bits)
+    cA, cB = dA.clone(), dB.clone()
+    C = Guarded(M * N)
+    code = binding.gemm_tn_ex_ptr(binding.F16 if fmt == "f16" else binding.BF16,
+                                  dA.data_ptr(), dB.data_ptr(), C.ptr, M, N, K,
+                                  tile, group_m, xcd_remap, stream)
+    assert code == 0, "gemm_tn_ex returned %d" % code
+    torch.cuda.synchronize()
+    unchanged = bool(torch.equal(dA, cA) and torch.equal(dB, cB))
+    return C.out(), C.guards_intact(), unchanged
+
+
+def kmajor_to_colmajor(At_bits, M, K):
+    """A(m,k) = At[k + m*K]  ->  column-major A[m + k*M] (a pure relayout)."""
+    return np.ascontiguousarray(np.asarray(At_bits).reshape(M, K).T).reshape(-1)
+
+
 def gemv_gpu(W_bits, X_bits, M, K, n, rows_per_block=0, stream=0):
     import torch
     from bf16_gemm_decode_amd import binding

@@ -27,7 +27,7 @@ def test_library_exports_every_declared_function():
     for n in names:
         assert hasattr(L, n), n
     assert names == set(binding.SIGNATURES), names ^ set(binding.SIGNATURES)
-    assert L.migemm_abi_version() == 1
+    assert L.migemm_abi_version() == 2
 
 
 P = 0x10000        # a fake, aligned device address: never dereferenced on error paths
@@ -73,6 +73,44 @@ def test_gemm_ex_config_errors():
     assert L.gemm_ex(1, P, P + 0x10000000, P + 0x20000000, 5000, 3000, 4100, 1, 0, 1, None) == -5
 
 
+def test_every_tile_plan_fits_lds():
+    # every explicit tile plans at a wide shape, fits the 160 KiB of LDS, and
+    # reports its own tile extents
+    want = {1: (256, 256), 2: (256, 128), 3: (128, 128), 4: (256, 256), 5: (256, 256),
+            6: (256, 256), 7: (256, 256), 8: (256, 256), 9: (256, 128), 10: (256, 256)}
+    for tile, (tm, tn) in want.items():
+        code, p = binding.gemm_plan(0, P, P + 2 ** 30, P + 2 ** 31, 1024, 1024, 1024, tile)
+        assert code == 0, tile
+        assert (p["tile_m"], p["tile_n"], p["tile_k"]) == (tm, tn, 32), tile
+        assert 0 < p["lds_bytes"] <= 160 * 1024, tile
+    # the full-line tiles: A ring of 4 x 32 k plus B ring of 64 k stages
+    assert binding.gemm_plan(0, P, P + 2 ** 30, P + 2 ** 31, 1024, 1024, 1024, 7)[1]["lds_bytes"] == \
+        4 * 32 * 256 * 2 + 3 * 64 * 256 * 2
+    assert binding.gemm_plan(0, P, P + 2 ** 30, P + 2 ** 31, 1024, 1024, 1024, 9)[1]["lds_bytes"] == \
+        4 * 32 * 256 * 2 + 4 * 64 * 128 * 2
+
+
+def test_tn_plan_and_errors():
+    L = binding.lib()
+    # automatic tile: 256x256 full-line once it fills the chip twice, else 256x128
+    code, p = binding.gemm_plan(0, P, P + 2 ** 30, P + 2 ** 31, 8192, 8192, 16384, a_kmajor=True)
+    assert code == 0 and (p["tile_m"], p["tile_n"], p["vec_a"], p["vec_b"]) == (256, 256, 8, 8)
+    assert p["lds_bytes"] == 2 * 64 * 256 * 2 + 3 * 64 * 256 * 2 and p["waves"] == 8
+    code, p = binding.gemm_plan(1, P, P + 2 ** 30, P + 2 ** 31, 34816, 16, 5120, a_kmajor=True)
+    assert code == 0 and (p["tile_m"], p["tile_n"]) == (256, 128) and p["grid"] == 136
+    # only the full-line tiles take a k-major A
+    for tile in (1, 2, 3, 4, 5, 6, 11):
+        assert L.gemm_tn_ex(0, P, P + 0x100000, P + 0x200000, 64, 64, 64, tile, 0, 1, None) == -5
+    # K not a multiple of 8, or a misaligned operand: no 16-byte rows
+    assert L.gemm_tn_ex(0, P, P + 0x100000, P + 0x200000, 64, 64, 60, 7, 0, 1, None) == -4
+    assert L.gemm_tn_ex(0, P + 2, P + 0x100000, P + 0x200000, 64, 64, 64, 7, 0, 1, None) == -4
+    # the shared checks
+    assert L.gemm_tn_f16(P, P + 0x100000, P + 0x200000, -1, 64, 64, None) == -1
+    assert L.gemm_tn_bf16(None, P + 0x100000, P + 0x200000, 64, 64, 64, None) == -2
+    assert L.gemm_tn_f16(P, P + 0x100000, P + 16, 64, 64, 64, None) == -3
+    assert L.gemm_tn_f16(None, None, None, 0, 0, 64, None) == 0
+
+
 def test_gemv_argument_errors():
     L = binding.lib()
     assert L.gemv_bf16(P, P + 0x100000, P + 0x200000, -1, 8, 1, None) == -1
@@ -91,7 +129,7 @@ def test_plan_choices():
     code, p = binding.gemm_plan(0, P, P + 2 ** 30, P + 2 ** 31, 8192, 8192, 16384)
     assert code == 0 and (p["tile_m"], p["tile_n"], p["vec_a"], p["vec_b"], p["grid"]) == \
         (256, 256, 8, 8, 1024)
-    assert p["tile_k"] == 32
+    assert p["tile_k"] == 32 and p["tile"] == 10 and p["waves"] == 8 and p["a_kmajor"] == 0
     assert p["lds_bytes"] <= 160 * 1024
     # ragged: M = 5000 keeps 16-byte A loads, K = 4100 drops B to 4-byte loads
     code, p = binding.gemm_plan(1, P, P + 2 ** 30, P + 2 ** 31, 5000, 3000, 4100)

@@ -55,13 +55,28 @@ def test_shape_sweep_random_triples():
         _full_case(M, N, K, fmt, seed=200 + i)
 
 
-@pytest.mark.parametrize("tile", [1, 2, 3])
+ALL_TILES = list(range(1, 11))
+FULL_LINE_TILES = [7, 8, 9, 10]
+
+
+@pytest.mark.parametrize("tile", ALL_TILES)
 @pytest.mark.parametrize("fmt", FMTS)
 def test_each_tile_config_ragged(tile, fmt):
     # M, K multiples of 8 (the 256-row tiles need 16-byte loads); N ragged,
     # several tiles in each direction, partial last tiles, K tail.
     print("case tile", tile, fmt, flush=True)
     _full_case(520, 600, 200, fmt, seed=300 + tile, tile=tile)
+
+
+@pytest.mark.parametrize("tile", FULL_LINE_TILES)
+def test_full_line_tiles_short_and_ragged_k(tile):
+    # few sub-steps (the ring never fills: waits fall back to "all landed"),
+    # odd sub-step counts (leading zero sub-step, B stage straddling k = 0),
+    # K tails inside a 64-k B stage, and N past the tile edge
+    for i, K in enumerate([8, 32, 40, 64, 72, 96, 136, 200, 264, 520]):
+        fmt = FMTS[i % 2]
+        print("case tile", tile, "K", K, fmt, flush=True)
+        _full_case(264, 300, K, fmt, seed=700 + K, tile=tile)
 
 
 def test_misaligned_vector_widths():
@@ -155,7 +170,7 @@ def test_integer_exact_full_size(fmt):
 @pytest.mark.parametrize("fmt", FMTS)
 def test_small_integers_exact_every_tile(fmt):
     rng = np.random.default_rng(5)
-    for tile in (1, 2, 3):
+    for tile in ALL_TILES:
         M, N, K = 520, 392, 64
         a = synth.small_ints(rng, M * K, -3, 3)
         b = synth.small_ints(rng, K * N, -3, 3)
@@ -233,7 +248,7 @@ def test_tile_orderings_bit_identical_and_repeatable():
     M, N, K = 2048, 4352, 1024
     A, B = synth.gemm_operands(M, N, K, "bf16", ("normal", 1.0, 0.02), seed=11)
     base = None
-    for tile in (1, 2):
+    for tile in (1, 2, 5, 7, 9, 10):
         outs = []
         for gm in (1, 4, 8, 16):
             for xcd in (0, 1):

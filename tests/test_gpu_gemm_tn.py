@@ -1,0 +1,98 @@
+"""GPU parity of gemm_tn_* (A supplied k-major: A(m,k) = At[k + m*K]) through
+the C ABI against the CPU oracle, which takes the same matrix column-major:
+every element at small sizes, K tails inside a 64-k stage, ragged M and N,
+bit-identical agreement with gemm_ex on the same tile (same MFMA order), and
+the DCU page's Y = X W^T in its own row-major layout for a batch of tokens."""
+import numpy as np
+import pytest
+
+import oracle
+import synth
+from helpers import assert_parity, gemm_gpu, gemm_tn_gpu, gemv_gpu, kmajor_to_colmajor
+
+pytestmark = pytest.mark.gpu
+
+FMTS = ["f16", "bf16"]
+TN_TILES = [0, 7, 8, 9, 10]
+
+
+def _tn_case(M, N, K, fmt, seed, tile=0, dist=("normal", 1.0, 1.0)):
+    rng_seed = seed
+    At, B = synth.gemm_operands(M, N, K, fmt, dist, rng_seed)   # At drawn as M*K values
+    got, guards, unchanged = gemm_tn_gpu(At, B, M, N, K, fmt, tile=tile)
+    assert guards, "write outside C for %s" % ((M, N, K, fmt, tile),)
+    assert unchanged, "inputs modified"
+    ref = oracle.gemm(kmajor_to_colmajor(At, M, K), B, M, N, K, fmt)
+    assert_parity(got, ref, fmt, "tn %s tile %d" % ((M, N, K, fmt), tile))
+    return At, B, got
+
+
+@pytest.mark.parametrize("tile", TN_TILES)
+@pytest.mark.parametrize("fmt", FMTS)
+def test_tn_each_tile_ragged(tile, fmt):
+    print("case tn tile", tile, fmt, flush=True)
+    _tn_case(520, 600, 200, fmt, seed=800 + tile, tile=tile)
+
+
+@pytest.mark.parametrize("tile", [7, 9, 10])
+def test_tn_short_and_ragged_k(tile):
+    for i, K in enumerate([8, 32, 40, 64, 72, 96, 136, 264, 520]):
+        fmt = FMTS[i % 2]
+        print("case tn tile", tile, "K", K, fmt, flush=True)
+        _tn_case(300, 264, K, fmt, seed=900 + K, tile=tile)
+
+
+def test_tn_small_and_odd_shapes():
+    for (M, N, K) in [(1, 1, 8), (17, 5, 16), (255, 257, 64), (257, 31, 128), (64, 1000, 24)]:
+        for fmt in FMTS:
+            print("case tn", M, N, K, fmt, flush=True)
+            _tn_case(M, N, K, fmt, seed=M + N + K)
+
+
+def test_tn_matches_column_major_path_bit_for_bit():
+    # same tile, same MFMA order over k: the two layouts of A must give the
+    # same bits
+    M, N, K = 1024, 768, 1000
+    for fmt in FMTS:
+        At, B = synth.gemm_operands(M, N, K, fmt, ("uniform", 1.0, 1.0), seed=31)
+        A = kmajor_to_colmajor(At, M, K)
+        for tile in (7, 8, 10):
+            print("case bitwise tile", tile, fmt, flush=True)
+            tn, _, _ = gemm_tn_gpu(At, B, M, N, K, fmt, tile=tile)
+            cm, _, _ = gemm_gpu(A, B, M, N, K, fmt, tile=tile)
+            assert np.array_equal(tn, cm), "tile %d %s" % (tile, fmt)
+
+
+def test_tn_small_integers_exact():
+    rng = np.random.default_rng(17)
+    M, N, K = 520, 392, 128
+    for fmt in FMTS:
+        At = synth.to_bits(synth.small_ints(rng, M * K, -3, 3), fmt)
+        B = synth.to_bits(synth.small_ints(rng, K * N, -3, 3), fmt)
+        want = oracle.gemm(kmajor_to_colmajor(At, M, K), B, M, N, K, fmt).bits
+        for tile in TN_TILES:
+            got, _, _ = gemm_tn_gpu(At, B, M, N, K, fmt, tile=tile)
+            assert np.array_equal(got, want), (tile, fmt)
+
+
+def test_tn_is_the_decode_product_for_a_token_batch():
+    # gemm_tn(At = W, B = X, C = Y) is Y = X W^T with W, X, Y row-major: the
+    # GEMV's layout.  16 tokens of the decode shape: sampled entries against
+    # the oracle GEMV, and agreement with gemv_bf16 within the tolerance.
+    M, K, n = 34816, 5120, 16
+    W, X = synth.gemv_operands(M, K, n, seed=3)
+    print("case tn decode batch", M, K, n, flush=True)
+    got, guards, unchanged = gemm_tn_gpu(W, X, M, n, K, "bf16")
+    assert guards and unchanged
+    idx = synth.sample_indices(M, n, 3, 2048)
+    ref = oracle.gemm_sampled(kmajor_to_colmajor(W, M, K), X, M, n, K, idx, "bf16")
+    assert_parity(got[idx], ref, "bf16", "tn decode batch sampled")
+    gv, _, _ = gemv_gpu(W, X, M, K, n)
+    refv = oracle.gemv(W, X, M, K, n, "bf16")
+    assert_parity(gv, refv, "bf16", "gemv decode batch")
+    # both are within the oracle's bound of the same exact value; directly,
+    # they differ by at most twice the bound
+    a = synth.from_bits(got, "bf16").astype(np.float64)
+    b = synth.from_bits(gv, "bf16").astype(np.float64)
+    bound = 2 * (2e-3 * refv.sabs + oracle.ulp_out(refv.exact, "bf16"))
+    assert np.all(np.abs(a - b) <= bound)

@@ -87,13 +87,15 @@ def test_k_zero_writes_zero():
 
 
 def test_hbm_probe_checksum():
+    # every word read exactly once: whole 8 KiB chunks, and a ragged tail
     import torch
     from bf16_gemm_decode_amd import hbm_read, hbm_read_sink_words
-    n = 1 << 24
-    buf = torch.randint(0, 2 ** 31 - 1, (n,), dtype=torch.int32, device="cuda")
-    sink = torch.zeros(hbm_read_sink_words(), dtype=torch.int32, device="cuda")
-    hbm_read(buf, sink)
-    torch.cuda.synchronize()
-    x = np.bitwise_xor.reduce(sink.cpu().numpy().view(np.uint32))
-    want = np.bitwise_xor.reduce(buf.cpu().numpy().view(np.uint32))
-    assert x == want
+    for n in (1 << 24, (1 << 22) + 12, 4):
+        print("case probe words", n, flush=True)
+        buf = torch.randint(0, 2 ** 31 - 1, (n,), dtype=torch.int32, device="cuda")
+        sink = torch.zeros(hbm_read_sink_words(), dtype=torch.int32, device="cuda")
+        hbm_read(buf, sink)
+        torch.cuda.synchronize()
+        x = np.bitwise_xor.reduce(sink.cpu().numpy().view(np.uint32))
+        want = np.bitwise_xor.reduce(buf.cpu().numpy().view(np.uint32))
+        assert x == want, n
