@@ -69,10 +69,10 @@ int plan_gemm(int dtype, const uint16_t *A, const uint16_t *B, const uint16_t *C
         // k-major A: the full-line tiles only, 16-byte rows of A and B
         if (!wide) return MIGEMM_ERR_ALIGN;
         if (tile == TILE_AUTO) {
-            tile = cdiv(M, 256) * cdiv(N, 256) >= 512 ? TILE_256x256_FL8
-                   : TILE_256x128_FL;
-        } else if (tile != TILE_256x256_FL && tile != TILE_256x256_FL22 &&
-                   tile != TILE_256x128_FL && tile != TILE_256x256_FL8) {
+            tile = N <= kSkinnyMaxTokens ? TILE_SKINNY
+                   : cdiv(M, 256) * cdiv(N, 256) >= 512 ? TILE_256x256_FL8
+                                                        : TILE_256x128_FL;
+        } else if (tile < TILE_256x256_FL || (tile == TILE_SKINNY && N > kSkinnyMaxTokens)) {
             return MIGEMM_ERR_CONFIG;
         }
     } else if (tile == TILE_AUTO) {
@@ -84,11 +84,14 @@ int plan_gemm(int dtype, const uint16_t *A, const uint16_t *B, const uint16_t *C
             tile = TILE_256x128;
         else
             tile = TILE_128x128;
+    } else if (tile == TILE_SKINNY) {
+        return MIGEMM_ERR_CONFIG;   // only with a k-major A (gemm_tn_ex)
     } else if (tile != TILE_128x128 && !wide) {
         return MIGEMM_ERR_CONFIG;   // the 256-row tiles load only 16-byte vectors
     }
     L.tile = tile;
-    const int bm = kTileShapes[tile].bm, bn = kTileShapes[tile].bn;
+    int bm = kTileShapes[tile].bm, bn = kTileShapes[tile].bn;
+    if (tile == TILE_SKINNY) bn = N <= 4 ? 4 : 8;
     const int64_t pm = cdiv(M, bm), pn = cdiv(N, bn);
     if (pm * pn > 0x7fffffff) return MIGEMM_ERR_SIZE;
     L.num_pid_m = (int)(pm ? pm : 1);
@@ -143,6 +146,12 @@ int gemm_tn_ex(int dtype, const uint16_t *At, const uint16_t *B, uint16_t *C, in
     bool launch;
     int rc = plan_gemm(dtype, At, B, C, M, N, K, tile, group_m, xcd_remap, L, launch, true);
     if (rc != MIGEMM_OK || !launch) return rc;
+    if (L.tile == TILE_SKINNY) {
+        // C(m,n) = sum_k At[k + m*K] B[k + n*K] is Y = X W^T with W = At,
+        // X = B, Y = C, all row-major: the skinny kernel's contract
+        SkinnyLaunch S{dtype, At, B, C, M, K, N, L.c_vec};
+        return finish(skinny_launch(S, (hipStream_t)stream), stream);
+    }
     return finish(gemm_launch(L, (hipStream_t)stream), stream);
 }
 
@@ -166,6 +175,21 @@ static int plan_for(int dtype, const uint16_t *A, const uint16_t *B, const uint1
     if (rc != MIGEMM_OK || !plan) return rc;
     memset(plan, 0, sizeof(*plan));
     const TileShape &t = a_kmajor ? kTileShapesKmajorA[L.tile] : kTileShapes[L.tile];
+    if (L.tile == TILE_SKINNY) {
+        plan->tile_m = 32;                      // 4 waves x 2 groups of 4 rows
+        plan->tile_n = N <= 4 ? 4 : 8;
+        plan->tile_k = 128;
+        plan->waves = 4;
+        plan->group_m = 1;
+        plan->xcd_remap = 0;
+        plan->vec_a = L.vec_a;
+        plan->vec_b = L.vec_b;
+        plan->grid = launch ? L.grid : 0;
+        plan->lds_bytes = 0;
+        plan->tile = L.tile;
+        plan->a_kmajor = 1;
+        return rc;
+    }
     plan->tile_m = t.bm;
     plan->tile_n = t.bn;
     plan->tile_k = t.bk;
@@ -208,12 +232,23 @@ int gemv_bf16_ex(const uint16_t *W, const uint16_t *X, uint16_t *Y, int M, int K
     if (overlaps(Y, ybytes, W, wbytes) || overlaps(Y, ybytes, X, xbytes)) return MIGEMM_ERR_OVERLAP;
     if (M == 0 || n == 0) return MIGEMM_OK;
 
+    const bool vec = (K % 8 == 0 && (uintptr_t)W % 16 == 0 && (uintptr_t)X % 16 == 0);
+    if (rows_per_block == 0 && vec && n >= kSkinnyMinTokens) {
+        // Y = X W^T is gemm_tn with At = W, B = X, C = Y (all row-major):
+        // up to kSkinnyMaxTokens tokens on the 4x4x4 MFMA kernel, more on
+        // the full-line 256x128 tile (measured faster from 16 tokens on)
+        if (n > kSkinnyMaxTokens)
+            return gemm_tn_ex(DT_BF16, W, X, Y, M, n, K, TILE_256x128_FL, 0, 1, stream);
+        SkinnyLaunch S{DT_BF16, W, X, Y, M, K, n, (M % 4 == 0 && (uintptr_t)Y % 8 == 0) ? 1 : 0};
+        return finish(skinny_launch(S, (hipStream_t)stream), stream);
+    }
+
     GemvLaunch L{};
     L.W = W;
     L.M = M;
     L.K = K;
     L.rows_per_block = rows_per_block ? rows_per_block : 2;
-    L.vec = (K % 8 == 0 && (uintptr_t)W % 16 == 0 && (uintptr_t)X % 16 == 0) ? 8 : 1;
+    L.vec = vec ? 8 : 1;
     L.grid = cdiv(M, L.rows_per_block);
     // Token blocks of 16, 8, 4, 2, 1: each launch streams W once.
     int done = 0;

@@ -456,9 +456,9 @@ constexpr int fl_loads_after(int j, int need_a, int need_b)
 // rows read with transposing LDS reads.  AK = true: A k-major (A(m,k) =
 // A[k + m*K]), A ring of SA stages of 64 k laid out, loaded and read exactly
 // like B (rows of A in place of columns of B).
-template <int DT, bool AK, int BM, int BN, int WGM, int WGN, int SA, int SB>
+template <int DT, bool AK, int BM, int BN, int WGM, int WGN, int SA, int SB, int OCC>
 __global__ void __launch_bounds__(WGM * WGN * 64)
-__attribute__((amdgpu_waves_per_eu(WGM * WGN / 4, WGM * WGN / 4)))
+__attribute__((amdgpu_waves_per_eu(OCC, OCC)))
 gemm_fl_kernel(const uint16_t *__restrict__ A, const uint16_t *__restrict__ B,
                uint16_t *__restrict__ C, int M, int N, int K, int num_pid_m, int num_pid_n,
                int group_m, int num_xcd, int c_vec)
@@ -745,11 +745,14 @@ gemm_fl_kernel(const uint16_t *__restrict__ A, const uint16_t *__restrict__ B,
     }
 }
 
-template <int DT, bool AK, int BM, int BN, int WGM, int WGN, int SA, int SB>
+// OCC: waves per SIMD the kernel is compiled for (its register budget is
+// 512 / OCC per lane); 0 = one workgroup's waves spread one per SIMD.
+template <int DT, bool AK, int BM, int BN, int WGM, int WGN, int SA, int SB, int OCC = 0>
 static hipError_t launch_fl(const GemmLaunch &L, hipStream_t stream)
 {
+    constexpr int OC = OCC ? OCC : WGM * WGN / 4;
     dim3 grid((unsigned)L.grid), block(WGM * WGN * 64);
-    hipLaunchKernelGGL((gemm_fl_kernel<DT, AK, BM, BN, WGM, WGN, SA, SB>), grid, block, 0, stream,
+    hipLaunchKernelGGL((gemm_fl_kernel<DT, AK, BM, BN, WGM, WGN, SA, SB, OC>), grid, block, 0, stream,
                        L.A, L.B, L.C, L.M, L.N, L.K, L.num_pid_m, L.num_pid_n, L.group_m,
                        L.num_xcd, L.c_vec);
     return hipGetLastError();
@@ -793,6 +796,15 @@ static hipError_t launch_dt(const GemmLaunch &L, hipStream_t s)
     case TILE_256x256_FL8:
         return L.a_kmajor ? launch_fl<DT, true, 256, 256, 4, 2, 2, 3>(L, s)
                           : launch_fl<DT, false, 256, 256, 4, 2, 4, 3>(L, s);
+    case TILE_64x32_SK:
+        return L.a_kmajor ? launch_fl<DT, true, 64, 32, 2, 1, 4, 2, 2>(L, s)
+                          : launch_fl<DT, false, 64, 32, 2, 1, 4, 2, 2>(L, s);
+    case TILE_64x64_SK:
+        return L.a_kmajor ? launch_fl<DT, true, 64, 64, 2, 1, 4, 2, 2>(L, s)
+                          : launch_fl<DT, false, 64, 64, 2, 1, 4, 2, 2>(L, s);
+    case TILE_128x128_SK:
+        return L.a_kmajor ? launch_fl<DT, true, 128, 128, 2, 2, 4, 3, 1>(L, s)
+                          : launch_fl<DT, false, 128, 128, 2, 2, 4, 3, 1>(L, s);
     case TILE_128x128:
 #define MIGEMM_V(va, vb) \
     if (L.vec_a == va && L.vec_b == vb) return launch_t<DT, 128, 128, 2, 2, 4, va, vb, 2>(L, s);

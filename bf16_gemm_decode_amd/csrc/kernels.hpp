@@ -18,6 +18,10 @@ enum GemmTile {
     TILE_256x256_FL22 = 8,      // as 7 with 4 waves as 2x2
     TILE_256x128_FL = 9,        // 256x128, waves along M, full-line B ring (A 4 x 32 k, B 4 x 64 k)
     TILE_256x256_FL8 = 10,      // as 7 with 8 waves (4 x 2, two per SIMD), 64x128 per wave
+    TILE_64x32_SK = 11,         // skinny: 64x32, 2 waves along M, full-line rings, 4 WG per CU
+    TILE_64x64_SK = 12,         // skinny: 64x64, 2 waves along M, 3 WG per CU
+    TILE_128x128_SK = 13,       // 128x128, 4 waves as 2x2, full-line rings
+    TILE_SKINNY = 14,           // few columns: W straight into 4x4x4 MFMA registers (skinny.hip)
     TILE_COUNT
 };
 
@@ -40,6 +44,10 @@ constexpr TileShape kTileShapes[TILE_COUNT] = {
     {256, 256, 32, 4, 4, 3},
     {256, 128, 32, 4, 4, 4},
     {256, 256, 32, 4, 8, 3},
+    {64, 32, 32, 4, 2, 2},
+    {64, 64, 32, 4, 2, 2},
+    {128, 128, 32, 4, 4, 3},
+    {32, 64, 32, 0, 4, 0},
 };
 
 // The full-line tiles with A k-major: stages = A ring stages of 64 k.
@@ -55,6 +63,10 @@ constexpr TileShape kTileShapesKmajorA[TILE_COUNT] = {
     {256, 256, 32, 2, 4, 3},
     {256, 128, 32, 3, 4, 4},
     {256, 256, 32, 2, 8, 3},
+    {64, 32, 32, 4, 2, 2},
+    {64, 64, 32, 4, 2, 2},
+    {128, 128, 32, 4, 4, 3},
+    {32, 64, 32, 0, 4, 0},
 };
 
 constexpr int tile_lds_bytes(const TileShape &t, bool a_kmajor = false)
@@ -90,6 +102,19 @@ struct GemvLaunch {
 };
 
 hipError_t gemv_launch(const GemvLaunch &L, hipStream_t stream);
+
+// Y = X W^T on MFMA for n <= kSkinnyMaxTokens token rows (skinny.hip).
+constexpr int kSkinnyMaxTokens = 8;
+constexpr int kSkinnyMinTokens = 3;    // the automatic GEMV switches to MFMA from here
+struct SkinnyLaunch {
+    int dtype;
+    const uint16_t *W, *X;        // W row-major [M, K], X row-major [n, K]
+    uint16_t *Y;                  // Y row-major [n, M]
+    int M, K, n;
+    int y_vec;                    // 1: 8-byte stores of 4 consecutive rows are aligned
+};
+
+hipError_t skinny_launch(const SkinnyLaunch &L, hipStream_t stream);
 
 hipError_t hbm_read_launch(const void *buf, size_t bytes, uint32_t *sink, hipStream_t stream);
 int hbm_read_sink_words();

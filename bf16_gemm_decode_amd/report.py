@@ -1,0 +1,226 @@
+"""Per-workload timing report of the hot path on one GPU.
+
+Measures every workload of the method's test matrix with the seeded synthetic
+inputs of `synth` (the same recipes the parity tests use):
+
+  * 512^3 FP16 GEMM (launch-latency bound), the 8192 x 8192 x 16384 FP16 GEMM,
+    the ragged 5000 x 3000 x 4100 BF16 GEMM;
+  * the decode GEMV Y = X W^T (W 34816 x 5120 BF16) at n = 1, 4, 16 tokens,
+    and the same product at n = 16 .. 256 through gemm_tn_bf16 (MFMA);
+  * the prefill GEMM 4096 x 34816 x 5120 BF16 over the grouped-ordering width
+    GROUP_M in {1, 4, 8, 16} x the tiles that fit it, in both of its layouts
+    (column-major X through gemm_ex, row-major X and W through gemm_tn_ex);
+  * the streaming-read probe.
+
+Times are kernel durations from HIP events around back-to-back launches on
+one stream (median and minimum of `--rounds` rounds).  TFLOP/s use the
+algorithmic 2*M*N*K, GB/s the algorithmic bytes; "util" is the fraction of
+the 2.5 PFLOP/s dense FP16/BF16 MFMA peak (of 8 TB/s for the GEMV).  Outputs
+are not checked here: the test suite does that.
+
+Usage (GPU):  python -m bf16_gemm_decode_amd.report [--out report.md] [--rounds 5]
+"""
+import argparse
+import json
+import os
+import subprocess
+import sys
+
+from . import binding, roofline as rf
+
+ROOT = os.path.dirname(os.path.dirname(os.path.abspath(__file__)))
+
+
+def _timer(torch, stream, fn, launches, rounds):
+    for _ in range(2):
+        fn(0)
+    stream.synchronize()
+    ts = []
+    for r in range(rounds):
+        e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+        e0.record(stream)
+        for i in range(launches):
+            code = fn(i)
+            assert code == 0, code
+        e1.record(stream)
+        stream.synchronize()
+        ts.append(e0.elapsed_time(e1) / 1e3 / launches)
+    ts.sort()
+    return ts[len(ts) // 2], ts[0]
+
+
+def _dev(torch, bits):
+    import numpy as np
+    return torch.from_numpy(np.ascontiguousarray(bits).view(np.int16)).cuda()
+
+
+def _smi():
+    """Clock / power / temperature as printed by amd-smi, if it runs here."""
+    for cmd in (["amd-smi", "metric", "-g", "0", "--clock", "--power", "--temperature"],
+                ["rocm-smi", "--showclocks", "--showpower", "--showtemp"]):
+        try:
+            out = subprocess.run(cmd, capture_output=True, text=True, timeout=30)
+        except (OSError, subprocess.TimeoutExpired):
+            continue
+        if out.returncode == 0 and out.stdout.strip():
+            return "$ " + " ".join(cmd) + "\n" + out.stdout.strip()
+    return "(no amd-smi / rocm-smi output available)"
+
+
+def main(argv=None):
+    p = argparse.ArgumentParser()
+    p.add_argument("--out", default=None, help="write a markdown summary here")
+    p.add_argument("--rounds", type=int, default=5)
+    p.add_argument("--skip-prefill-grid", action="store_true")
+    p.add_argument("--sections", default="gemm,decode,prefill",
+                   help="comma list of gemm, decode, prefill")
+    p.add_argument("--decode-tiles", default="0",
+                   help="gemm_tn tiles to time for the decode batches (0 = automatic)")
+    a = p.parse_args(argv)
+
+    import numpy as np
+    import torch
+    sys.path.insert(0, ROOT)
+    import synth
+
+    torch.cuda.set_device(0)
+    s = torch.cuda.Stream()
+    h = s.cuda_stream
+    L = binding.lib()
+    rows = []
+    peak = rf.MI355X["mfma_f16_tflops"]
+    hbm = rf.MI355X["hbm_GBps"]
+    smi_before = _smi()
+
+    def gemm_row(name, code_dt, dA, dB, dC, M, N, K, tile=0, gm=0, tn=False, launches=None):
+        fn_c = L.gemm_tn_ex if tn else L.gemm_ex
+        launches = launches or max(3, min(200, int(2e-3 / max(rf.gemm_flop(M, N, K) / 1.0e15, 1e-6))))
+        med, mn = _timer(torch, s, lambda i: fn_c(code_dt, dA.data_ptr(), dB.data_ptr(), dC.data_ptr(),
+                                                  M, N, K, tile, gm, 1, h), launches, a.rounds)
+        _, plan = binding.gemm_plan(code_dt, dA.data_ptr(), dB.data_ptr(), dC.data_ptr(), M, N, K,
+                                    tile, gm, 1, a_kmajor=tn)
+        tf = rf.gemm_flop(M, N, K) / med / 1e12
+        r = {"workload": name, "M": M, "N": N, "K": K, "layout": "A k-major" if tn else "column-major",
+             "tile": plan["tile"], "tile_mnk": [plan["tile_m"], plan["tile_n"], plan["tile_k"]],
+             "group_m": plan["group_m"], "grid": plan["grid"], "launches": launches,
+             "median_us": round(med * 1e6, 2), "min_us": round(mn * 1e6, 2),
+             "tflops": round(tf, 1), "util": round(tf / peak, 4)}
+        rows.append(r)
+        print(json.dumps(r), flush=True)
+        return r
+
+    def operands(name):
+        w = synth.WORKLOADS[name]
+        A, B = synth.workload_operands(name)
+        code_dt = binding.F16 if w["fmt"] == "f16" else binding.BF16
+        return w, code_dt, _dev(torch, A), _dev(torch, B)
+
+    sections = a.sections.split(",")
+    # --- GEMMs ------------------------------------------------------------
+    for name in (("gemm_512_f16", "gemm_8192x8192x16384_f16", "gemm_5000x3000x4100_bf16")
+                 if "gemm" in sections else ()):
+        w, code_dt, dA, dB = operands(name)
+        dC = torch.empty(w["M"] * w["N"], dtype=torch.int16, device="cuda")
+        gemm_row(name, code_dt, dA, dB, dC, w["M"], w["N"], w["K"])
+        del dA, dB, dC
+
+    # --- decode GEMV and its batched MFMA form ------------------------------
+    wv = synth.WORKLOADS["gemv_34816x5120_bf16"]
+    if "decode" not in sections:
+        wv = None
+    M, K = (wv["M"], wv["K"]) if wv else (0, 0)
+    W, _ = synth.gemv_operands(M, K, 1, seed=wv["seed"]) if wv else (None, None)
+    copies = [_dev(torch, W)] if wv else []
+    for _ in range(3 if wv else 0):
+        copies.append(copies[0].clone())        # 4 x 356.5 MB: W cannot stay in the MALL
+    probe_buf = torch.empty((4 << 30) // 4, dtype=torch.int32, device="cuda")
+    probe_buf.fill_(7)
+    sink = torch.zeros(binding.hbm_read_sink_words(), dtype=torch.int32, device="cuda")
+    pmed, pmin = _timer(torch, s, lambda i: L.migemm_hbm_read(probe_buf.data_ptr(), 4 << 30,
+                                                               sink.data_ptr(), h), 5, a.rounds)
+    probe = (4 << 30) / pmed / 1e9
+    del probe_buf
+    rows.append({"workload": "hbm_read probe (4 GiB)", "median_us": round(pmed * 1e6, 1),
+                 "GBps": round(probe, 1), "util": round(probe / hbm, 4)})
+    print(json.dumps(rows[-1]), flush=True)
+    for n in ((1, 2, 3, 4, 8, 16) if wv else ()):
+        _, X = synth.gemv_operands(M, K, n, seed=wv["seed"])
+        dX = _dev(torch, X)
+        dY = torch.empty(n * M, dtype=torch.int16, device="cuda")
+        # rows_per_block 0: the automatic path; 2: the row-blocked vector kernel
+        for rpb, path in ((0, "gemv_bf16 (automatic)"), (2, "gemv_bf16_ex vector kernel, rows_per_block 2")):
+            med, mn = _timer(torch, s, lambda i: L.gemv_bf16_ex(copies[i % 4].data_ptr(), dX.data_ptr(),
+                                                                 dY.data_ptr(), M, K, n, rpb, h),
+                             40, a.rounds)
+            gb = rf.gemv_bytes(M, K, n) / med / 1e9
+            r = {"workload": "gemv_34816x5120_bf16: " + path, "n": n, "median_us": round(med * 1e6, 2),
+                 "min_us": round(mn * 1e6, 2), "GBps": round(gb, 1), "util": round(gb / hbm, 4),
+                 "frac_of_probe": round(gb / probe, 4)}
+            rows.append(r)
+            print(json.dumps(r), flush=True)
+    for n in ((4, 8, 16, 32, 64, 128, 256) if wv else ()):
+        _, X = synth.gemv_operands(M, K, n, seed=wv["seed"])
+        dX = _dev(torch, X)
+        dY = torch.empty(n * M, dtype=torch.int16, device="cuda")
+        for tile in (int(t) for t in a.decode_tiles.split(",")):
+            if binding.gemm_plan(binding.BF16, copies[0].data_ptr(), dX.data_ptr(), dY.data_ptr(),
+                                 M, n, K, tile, 0, 1, a_kmajor=True)[0] != 0:
+                continue
+            med, mn = _timer(torch, s, lambda i: L.gemm_tn_ex(binding.BF16, copies[i % 4].data_ptr(),
+                                                               dX.data_ptr(), dY.data_ptr(), M, n, K,
+                                                               tile, 0, 1, h), 20, a.rounds)
+            gb = rf.gemv_bytes(M, K, n) / med / 1e9
+            tf = rf.gemm_flop(M, n, K) / med / 1e12
+            _, plan = binding.gemm_plan(binding.BF16, copies[0].data_ptr(), dX.data_ptr(),
+                                        dY.data_ptr(), M, n, K, tile, 0, 1, a_kmajor=True)
+            r = {"workload": "decode batch Y = X W^T via gemm_tn_bf16", "n": n, "tile": plan["tile"],
+                 "tile_mnk": [plan["tile_m"], plan["tile_n"], plan["tile_k"]], "grid": plan["grid"],
+                 "median_us": round(med * 1e6, 2), "min_us": round(mn * 1e6, 2), "GBps": round(gb, 1),
+                 "util": round(gb / hbm, 4), "frac_of_probe": round(gb / probe, 4), "tflops": round(tf, 1)}
+            rows.append(r)
+            print(json.dumps(r), flush=True)
+    del copies
+
+    # --- prefill: GROUP_M x tile ------------------------------------------
+    if not a.skip_prefill_grid and "prefill" in sections:
+        w, code_dt, dA, dB = operands("prefill_4096x34816x5120_bf16")
+        Mp, Np, Kp = w["M"], w["N"], w["K"]
+        dC = torch.empty(Mp * Np, dtype=torch.int16, device="cuda")
+        for tile in (10, 9, 2, 3):
+            for gm in (1, 4, 8, 16):
+                gemm_row("prefill_4096x34816x5120_bf16", code_dt, dA, dB, dC, Mp, Np, Kp, tile, gm,
+                         launches=10)
+        # row-major X [4096, 5120] and W [34816, 5120] as gemm_tn(At = W, B = X): Y row-major
+        At = dB                                           # W row-major: B(k,n) = W[n][k]
+        Xr = dA.view(Kp, Mp).t().contiguous().view(-1)   # X row-major [4096, 5120]
+        Y = torch.empty(Mp * Np, dtype=torch.int16, device="cuda")
+        for tile in (10, 7, 9):
+            for gm in (1, 4, 8, 16):
+                gemm_row("prefill_4096x34816x5120_bf16 (Y = X W^T, row-major)", code_dt, At, Xr, Y,
+                         Np, Mp, Kp, tile, gm, tn=True, launches=10)
+
+    smi_after = _smi()
+    if a.out:
+        with open(a.out, "w") as f:
+            f.write("# Per-workload report\n\n")
+            f.write("command: `python -m bf16_gemm_decode_amd.report --out %s --rounds %d`\n\n"
+                    % (os.path.relpath(a.out, ROOT), a.rounds))
+            f.write("Kernel durations from HIP events around back-to-back launches (median / min of "
+                    "%d rounds); util = fraction of 2.5 PFLOP/s (GEMM) or 8 TB/s (GEMV, probe).\n\n"
+                    % a.rounds)
+            f.write("| workload | shape / n | layout | tile | GROUP_M | median us | min us | TFLOP/s | GB/s | util | of probe |\n")
+            f.write("|---|---|---|---|---|---|---|---|---|---|---|\n")
+            for r in rows:
+                shape = "%dx%dx%d" % (r["M"], r["N"], r["K"]) if "M" in r else ("n=%d" % r["n"] if "n" in r else "")
+                tile = ("%d (%s)" % (r["tile"], "x".join(str(v) for v in r["tile_mnk"]))
+                        if "tile_mnk" in r else str(r.get("tile", "")))
+                f.write("| %s | %s | %s | %s | %s | %s | %s | %s | %s | %s | %s |\n" % (
+                    r["workload"], shape, r.get("layout", ""), tile, r.get("group_m", ""),
+                    r.get("median_us", ""), r.get("min_us", ""), r.get("tflops", ""),
+                    r.get("GBps", ""), r.get("util", ""), r.get("frac_of_probe", "")))
+            f.write("\n## GPU state\n\nbefore:\n```\n%s\n```\nafter:\n```\n%s\n```\n" % (smi_before, smi_after))
+        print("wrote", a.out)
+
+
+if __name__ == "__main__":
+    main()

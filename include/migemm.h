@@ -81,8 +81,12 @@ int gemm_bf16(const uint16_t *A, const uint16_t *B, uint16_t *C,
  *
  * W and X are read only.  n == 0 or M == 0 returns 0 without a launch;
  * K == 0 writes +0.0 to Y.  Errors as for the GEMM (Y must not overlap W, X).
- * n may be any positive value; the kernel is built for n <= 16 tokens per
- * pass and loops over larger n.
+ * n may be any positive value.  n <= 2 (or K not a multiple of 8, or W, X
+ * not 16-byte aligned) runs the row-blocked vector kernel; from 3 tokens on,
+ * with 16-byte rows, the multiply-adds run on MFMA: up to 8 tokens on the
+ * 4x4x4 MFMA with W streamed straight into operand registers, beyond that
+ * as gemm_tn_bf16 on the 256x128 full-line tile.  gemv_bf16_ex with a
+ * non-zero rows_per_block always runs the vector kernel.
  */
 int gemv_bf16(const uint16_t *W, const uint16_t *X, uint16_t *Y,
               int M, int K, int n, void *stream);
@@ -99,7 +103,11 @@ int gemv_bf16(const uint16_t *W, const uint16_t *X, uint16_t *Y,
  *            along M, B loaded as whole 128-byte column lines (64 k) into
  *            its own 3-stage ring, A in a 4-stage ring; 8 = tile 7 with the
  *            waves as 2x2; 9 = 256x128 like tile 7 with a 4-stage B ring;
- *            10 = tile 7 with 8 waves (4 x 2, two per SIMD).
+ *            10 = tile 7 with 8 waves (4 x 2, two per SIMD); skinny tiles for
+ *            few columns (decode batches): 11 = 64x32 and 12 = 64x64 (2 waves,
+ *            several workgroups per CU), 13 = 128x128 (4 waves as 2x2), all
+ *            with tile 7's full-line B ring; 14 = the skinny 4x4x4 MFMA kernel
+ *            of gemv_bf16 (gemm_tn_* only, N <= 8).
  *            All step K by 32; tiles other than 3 need M and K to be multiples of 8 and A, B
  *            16-byte aligned (else MIGEMM_ERR_CONFIG);
  *   group_m: width of the grouped tile ordering (FlagGems "Hygon 优化" page,
@@ -120,8 +128,8 @@ int gemm_ex(int dtype, const uint16_t *A, const uint16_t *B, uint16_t *C,
  * DCU decode page's Y = X W^T (section 6.1) for a batch of N token rows,
  * with Y row-major [N, M] -- the GEMV's own layout.  Same argument checks,
  * ownership and completion rules as gemm_f16 / gemm_bf16.  Runs on the
- * full-line tiles only: tile 0 (automatic), 7, 8, 9 or 10 (A takes B's
- * 64-k ring layout; MIGEMM_ERR_CONFIG for other tiles).  K must be a
+ * full-line tiles only: tile 0 (automatic) or 7 .. 13 (A takes B's 64-k
+ * ring layout; MIGEMM_ERR_CONFIG for other tiles).  K must be a
  * multiple of 8 and At, B 16-byte aligned (else MIGEMM_ERR_ALIGN).
  */
 int gemm_tn_f16(const uint16_t *At, const uint16_t *B, uint16_t *C,
@@ -134,8 +142,8 @@ int gemm_tn_ex(int dtype, const uint16_t *At, const uint16_t *B, uint16_t *C,
 
 /*
  * Same contract as gemv_bf16 with rows_per_block (output rows of W per
- * workgroup: 2, 4, 8, 16 or 32; 0 = automatic), the knob swept on the DCU
- * decode page, section 6.2.
+ * workgroup of the vector kernel: 2, 4, 8, 16 or 32), the knob swept on the
+ * DCU decode page, section 6.2; 0 = automatic (as gemv_bf16).
  */
 int gemv_bf16_ex(const uint16_t *W, const uint16_t *X, uint16_t *Y,
                  int M, int K, int n, int rows_per_block, void *stream);

@@ -77,7 +77,8 @@ def test_every_tile_plan_fits_lds():
     # every explicit tile plans at a wide shape, fits the 160 KiB of LDS, and
     # reports its own tile extents
     want = {1: (256, 256), 2: (256, 128), 3: (128, 128), 4: (256, 256), 5: (256, 256),
-            6: (256, 256), 7: (256, 256), 8: (256, 256), 9: (256, 128), 10: (256, 256)}
+            6: (256, 256), 7: (256, 256), 8: (256, 256), 9: (256, 128), 10: (256, 256),
+            11: (64, 32), 12: (64, 64), 13: (128, 128)}
     for tile, (tm, tn) in want.items():
         code, p = binding.gemm_plan(0, P, P + 2 ** 30, P + 2 ** 31, 1024, 1024, 1024, tile)
         assert code == 0, tile
@@ -96,10 +97,17 @@ def test_tn_plan_and_errors():
     code, p = binding.gemm_plan(0, P, P + 2 ** 30, P + 2 ** 31, 8192, 8192, 16384, a_kmajor=True)
     assert code == 0 and (p["tile_m"], p["tile_n"], p["vec_a"], p["vec_b"]) == (256, 256, 8, 8)
     assert p["lds_bytes"] == 2 * 64 * 256 * 2 + 3 * 64 * 256 * 2 and p["waves"] == 8
-    code, p = binding.gemm_plan(1, P, P + 2 ** 30, P + 2 ** 31, 34816, 16, 5120, a_kmajor=True)
-    assert code == 0 and (p["tile_m"], p["tile_n"]) == (256, 128) and p["grid"] == 136
+    code, p = binding.gemm_plan(1, P, P + 2 ** 30, P + 2 ** 31, 34816, 200, 5120, a_kmajor=True)
+    assert code == 0 and (p["tile_m"], p["tile_n"]) == (256, 128) and p["grid"] == 272
+    # the skinny tile: few columns only, and only with a k-major A
+    code, p = binding.gemm_plan(1, P, P + 2 ** 30, P + 2 ** 31, 34816, 8, 5120, a_kmajor=True)
+    assert code == 0 and (p["tile"], p["tile_m"], p["tile_n"], p["waves"], p["grid"]) == (14, 32, 8, 4, 1088)
+    assert binding.gemm_plan(1, P, P + 2 ** 30, P + 2 ** 31, 34816, 5, 5120, a_kmajor=True)[1]["tile_n"] == 8
+    assert binding.gemm_plan(1, P, P + 2 ** 30, P + 2 ** 31, 34816, 9, 5120, a_kmajor=True)[1]["tile"] != 14
+    assert L.gemm_tn_ex(0, P, P + 0x100000, P + 0x200000, 64, 9, 64, 14, 0, 1, None) == -5
+    assert L.gemm_ex(0, P, P + 0x100000, P + 0x200000, 64, 16, 64, 14, 0, 1, None) == -5
     # only the full-line tiles take a k-major A
-    for tile in (1, 2, 3, 4, 5, 6, 11):
+    for tile in (1, 2, 3, 4, 5, 6, 15):
         assert L.gemm_tn_ex(0, P, P + 0x100000, P + 0x200000, 64, 64, 64, tile, 0, 1, None) == -5
     # K not a multiple of 8, or a misaligned operand: no 16-byte rows
     assert L.gemm_tn_ex(0, P, P + 0x100000, P + 0x200000, 64, 64, 60, 7, 0, 1, None) == -4

@@ -55,8 +55,8 @@ def test_shape_sweep_random_triples():
         _full_case(M, N, K, fmt, seed=200 + i)
 
 
-ALL_TILES = list(range(1, 11))
-FULL_LINE_TILES = [7, 8, 9, 10]
+ALL_TILES = list(range(1, 14))
+FULL_LINE_TILES = [7, 8, 9, 10, 11, 12, 13]
 
 
 @pytest.mark.parametrize("tile", ALL_TILES)
@@ -248,7 +248,7 @@ def test_tile_orderings_bit_identical_and_repeatable():
     M, N, K = 2048, 4352, 1024
     A, B = synth.gemm_operands(M, N, K, "bf16", ("normal", 1.0, 0.02), seed=11)
     base = None
-    for tile in (1, 2, 5, 7, 9, 10):
+    for tile in (1, 2, 5, 7, 9, 10, 11, 13):
         outs = []
         for gm in (1, 4, 8, 16):
             for xcd in (0, 1):

@@ -13,7 +13,7 @@ from helpers import assert_parity, gemm_gpu, gemm_tn_gpu, gemv_gpu, kmajor_to_co
 pytestmark = pytest.mark.gpu
 
 FMTS = ["f16", "bf16"]
-TN_TILES = [0, 7, 8, 9, 10]
+TN_TILES = [0, 7, 8, 9, 10, 11, 12, 13]
 
 
 def _tn_case(M, N, K, fmt, seed, tile=0, dist=("normal", 1.0, 1.0)):
@@ -34,7 +34,7 @@ def test_tn_each_tile_ragged(tile, fmt):
     _tn_case(520, 600, 200, fmt, seed=800 + tile, tile=tile)
 
 
-@pytest.mark.parametrize("tile", [7, 9, 10])
+@pytest.mark.parametrize("tile", [7, 9, 10, 11, 12, 13])
 def test_tn_short_and_ragged_k(tile):
     for i, K in enumerate([8, 32, 40, 64, 72, 96, 136, 264, 520]):
         fmt = FMTS[i % 2]
@@ -56,7 +56,7 @@ def test_tn_matches_column_major_path_bit_for_bit():
     for fmt in FMTS:
         At, B = synth.gemm_operands(M, N, K, fmt, ("uniform", 1.0, 1.0), seed=31)
         A = kmajor_to_colmajor(At, M, K)
-        for tile in (7, 8, 10):
+        for tile in (7, 8, 10, 11, 12, 13):
             print("case bitwise tile", tile, fmt, flush=True)
             tn, _, _ = gemm_tn_gpu(At, B, M, N, K, fmt, tile=tile)
             cm, _, _ = gemm_gpu(A, B, M, N, K, fmt, tile=tile)
@@ -73,6 +73,28 @@ def test_tn_small_integers_exact():
         for tile in TN_TILES:
             got, _, _ = gemm_tn_gpu(At, B, M, N, K, fmt, tile=tile)
             assert np.array_equal(got, want), (tile, fmt)
+
+
+@pytest.mark.parametrize("fmt", FMTS)
+def test_skinny_tile_every_token_count_and_ragged_edges(fmt):
+    # tile 14 (W straight into 4x4x4 MFMA registers, 128-wide k chunks): token
+    # counts across the 4-slot groups, rows off the 8-row wave blocks, K tails
+    # inside a chunk and K shorter than one chunk
+    for (M, N, K) in [(100, 1, 64), (37, 3, 40), (64, 5, 520), (300, 8, 264), (260, 7, 136),
+                      (96, 6, 8), (1000, 8, 1000), (33, 4, 24), (7, 2, 128), (9, 8, 5120)]:
+        print("case skinny", M, N, K, fmt, flush=True)
+        _tn_case(M, N, K, fmt, seed=1000 + M + N + K, tile=14)
+
+
+def test_skinny_matches_exact_integers():
+    rng = np.random.default_rng(23)
+    M, N, K = 520, 7, 1024
+    for fmt in FMTS:
+        At = synth.to_bits(synth.small_ints(rng, M * K, -3, 3), fmt)
+        B = synth.to_bits(synth.small_ints(rng, K * N, -3, 3), fmt)
+        want = oracle.gemm(kmajor_to_colmajor(At, M, K), B, M, N, K, fmt).bits
+        got, _, _ = gemm_tn_gpu(At, B, M, N, K, fmt, tile=14)
+        assert np.array_equal(got, want), fmt
 
 
 def test_tn_is_the_decode_product_for_a_token_batch():

@@ -29,8 +29,10 @@ def test_small_shapes():
 
 
 def test_ragged_shapes_and_token_counts():
+    # n <= 2 the vector kernel, 3..8 the 4x4x4 MFMA kernel, more the
+    # full-line GEMM tile (K a multiple of 8); K % 8 != 0 always the vector one
     for (M, K) in [(7, 13), (100, 512), (129, 1031), (1000, 5120), (77, 5128), (31, 4096)]:
-        for n in (1, 2, 3, 5, 16, 17, 33):
+        for n in (1, 2, 3, 4, 5, 8, 9, 16, 17, 33):
             print("case", M, K, n, flush=True)
             _case(M, K, n, seed=M * 7 + K + n)
 
@@ -55,6 +57,20 @@ def test_rows_per_block_bit_identical(n):
     for o in outs[1:]:
         assert np.array_equal(o, outs[0])
     assert_parity(outs[0], oracle.gemv(W, X, M, K, n), "bf16", "rows_per_block")
+
+
+def test_every_route_against_the_vector_kernel():
+    # the automatic routes (MFMA for n >= 3) and the vector kernel
+    # (rows_per_block given) both meet the oracle's bound at the decode width
+    M, K = 2051, 5120
+    for n in (3, 6, 8, 12, 40):
+        W, X = synth.gemv_operands(M, K, n, seed=40 + n)
+        ref = oracle.gemv(W, X, M, K, n)
+        auto, g1, _ = gemv_gpu(W, X, M, K, n, 0)
+        vec, g2, _ = gemv_gpu(W, X, M, K, n, 2)
+        assert g1 and g2
+        assert_parity(auto, ref, "bf16", "automatic n=%d" % n)
+        assert_parity(vec, ref, "bf16", "vector n=%d" % n)
 
 
 def test_one_hot_selects_column_exactly():
