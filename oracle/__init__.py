@@ -1,4 +1,4 @@
-"""CPU oracle for the column-major GEMM and the decode GEMV.
+"""CPU oracle for the column-major GEMM, the decode GEMV and decode attention.
 
 TEST INFRASTRUCTURE ONLY.  Only the test suite, ``__graft_entry__.smoke()``
 and the CPU-baseline leg of ``bench.py`` may import this package.  The HIP
@@ -6,6 +6,10 @@ library never imports, links or calls it, and it shares no code with the
 HIP path.  The arithmetic lives in ``oracle.c`` (FP64 triple loop, exact
 16-bit decode, single RNE rounding); this module only marshals numpy arrays
 and implements the acceptance rule.
+
+Decode attention (DCU decode page, sections 6.1 and 6.3) uses the same
+rule with S_abs = sum_l p_l |v_ld| and a relative factor derived per output
+from L, D and the scores' magnitude (``attention_rel``).
 
 Acceptance rule (per checked element, C_ref the oracle's rounded result):
     |C_gpu - C_ref| <= 2e-3 * S_abs + ulp_out(C_ref)
@@ -62,6 +66,13 @@ def lib():
                                   ctypes.c_int, ctypes.c_int, ctypes.c_int]
         L.oracle_grouped_tile.restype = None
         L.oracle_grouped_tile.argtypes = [ctypes.c_int64] * 4 + [i64p, i64p]
+        i32p = ctypes.POINTER(ctypes.c_int32)
+        L.oracle_attention.restype = ctypes.c_int64
+        L.oracle_attention.argtypes = [ctypes.c_int, u16p, u16p, u16p, i32p, i32p] + \
+            [ctypes.c_int] * 6 + [ctypes.c_double, u16p, f64p, f64p, f64p]
+        L.oracle_attention_segmented.restype = None
+        L.oracle_attention_segmented.argtypes = [ctypes.c_int, u16p, u16p, u16p, i32p, i32p] + \
+            [ctypes.c_int] * 6 + [ctypes.c_double, ctypes.c_int, u16p, f64p]
         _lib = L
     return _lib
 
@@ -146,6 +157,77 @@ def gemv(W, X, M, K, n, fmt="bf16") -> GemmResult:
                              _p(Y, ctypes.c_uint16), _p(Yx, ctypes.c_double),
                              _p(S, ctypes.c_double), M, K, n)
     return GemmResult(Y, Yx, S, macs)
+
+
+class AttentionResult(GemmResult):
+    """Oracle attention output: ``bits``, ``exact`` (double), ``sabs``
+    (sum_l p_l |v_ld|), ``macs``, and ``qk_abs`` per (b, h): the largest
+    |scale| * sum_d |q_d k_ld| over the cached tokens."""
+
+    def __init__(self, bits, exact, sabs, macs, qk_abs):
+        super().__init__(bits, exact, sabs, macs)
+        self.qk_abs = qk_abs
+
+
+def _att_args(Q, Kc, Vc, block_table, seq_lens):
+    Q, Kc, Vc = _u16(Q).ravel(), _u16(Kc).ravel(), _u16(Vc).ravel()
+    bt = np.ascontiguousarray(block_table, np.int32).ravel()
+    sl = np.ascontiguousarray(seq_lens, np.int32).ravel()
+    return Q, Kc, Vc, bt, sl
+
+
+def attention(Q, Kc, Vc, block_table, seq_lens, B, Hq, Hkv, D, block_size, max_blocks,
+              scale, fmt="bf16") -> AttentionResult:
+    """Decode attention, the plain definition (DCU decode page, section 6.1):
+    out[b,h,:] = softmax(scale * q K^T) V over the seq_lens[b] cached tokens
+    of kv head h // (Hq // Hkv).  Q, out: [B, Hq, D]; Kc, Vc: paged
+    [block, token_in_block, Hkv, D]; block_table: [B, max_blocks] page ids."""
+    Q, Kc, Vc, bt, sl = _att_args(Q, Kc, Vc, block_table, seq_lens)
+    n = B * Hq * D
+    out = np.empty(n, np.uint16)
+    ox = np.empty(n, np.float64)
+    S = np.empty(n, np.float64)
+    qka = np.empty(B * Hq, np.float64)
+    macs = lib().oracle_attention(fmt_id(fmt), _p(Q, ctypes.c_uint16), _p(Kc, ctypes.c_uint16),
+                                  _p(Vc, ctypes.c_uint16), _p(bt, ctypes.c_int32),
+                                  _p(sl, ctypes.c_int32), B, Hq, Hkv, D, block_size, max_blocks,
+                                  scale, _p(out, ctypes.c_uint16), _p(ox, ctypes.c_double),
+                                  _p(S, ctypes.c_double), _p(qka, ctypes.c_double))
+    return AttentionResult(out, ox, S, macs, qka)
+
+
+def attention_segmented(Q, Kc, Vc, block_table, seq_lens, B, Hq, Hkv, D, block_size,
+                        max_blocks, scale, nseg, fmt="bf16"):
+    """The page's segmented algorithm (section 6.3) in double: returns
+    (rounded bits, double values)."""
+    Q, Kc, Vc, bt, sl = _att_args(Q, Kc, Vc, block_table, seq_lens)
+    n = B * Hq * D
+    out = np.empty(n, np.uint16)
+    ox = np.empty(n, np.float64)
+    lib().oracle_attention_segmented(fmt_id(fmt), _p(Q, ctypes.c_uint16), _p(Kc, ctypes.c_uint16),
+                                     _p(Vc, ctypes.c_uint16), _p(bt, ctypes.c_int32),
+                                     _p(sl, ctypes.c_int32), B, Hq, Hkv, D, block_size,
+                                     max_blocks, scale, nseg, _p(out, ctypes.c_uint16),
+                                     _p(ox, ctypes.c_double))
+    return out, ox
+
+
+def gamma(n, u=2.0 ** -24):
+    """Higham's gamma_n = n u / (1 - n u)."""
+    return n * u / (1.0 - n * u)
+
+
+def attention_rel(ref: AttentionResult, seq_lens, Hq, D):
+    """Relative bound, per output element, for an FP32 evaluation of decode
+    attention in any order (scores summed over D, exponentials, sums over L,
+    one merge): 2 * |scale| * gamma_D * sum_d |q k| (a score error scales
+    both numerator and denominator terms by up to e^eps) + 2 * gamma_L (the
+    sums of numerator and denominator) + 16 u (exp, division, merge)."""
+    sl = np.asarray(seq_lens, np.int64)
+    B = sl.size
+    L = np.repeat(sl, Hq)                                   # per (b, h)
+    rel = 2 * ref.qk_abs * gamma(D) + 2 * np.array([gamma(max(int(x), 1)) for x in L]) + 16 * 2.0 ** -24
+    return np.repeat(rel, D).reshape(B * Hq * D)
 
 
 def grouped_tile(pid, num_pid_m, num_pid_n, group_m):

@@ -17,6 +17,12 @@
  *    the linear layer Y = X W^T with X:[n,k], W:[m,k], Y:[n,m].
  *  - FlagGems "Hygon 优化" page, section "分组调度" (grouped scheduling): the
  *    GROUP_M map from a flat program id to an output tile.
+ *  - "DCU decode" page, section 6.1 (attention shapes: per query head
+ *    scores = Q K^T over the L cached tokens, prob = softmax(scores),
+ *    out = prob V; KV cache kept in pages [block, token_in_block, kv_head,
+ *    head_dim]) and section 6.3 (the split of K/V along L into contiguous
+ *    segments, each with a local max, a local softmax denominator and a
+ *    local prob V, merged with a numerically stable global reduction).
  *
  * Arithmetic: every 16-bit input is decoded exactly to double; every product
  * of two decoded inputs is exact in double (11+11 or 8+8 significand bits);
@@ -220,4 +226,134 @@ void oracle_grouped_tile(int64_t pid, int64_t num_pid_m, int64_t num_pid_n,
     *pid_n = local / rows;
 }
 
-int oracle_abi_version(void) { return 1; }
+/* ---- decode attention (DCU decode page, sections 6.1 and 6.3) ---------- */
+
+/* Row (b, token l, kv head kvh) of a paged cache laid out
+ * [block][token_in_block][kv_head][head_dim]: token l of sequence b sits in
+ * page block_table[b * max_blocks + l / block_size] at slot l % block_size. */
+static const uint16_t *kv_row(const uint16_t *cache, const int32_t *block_table, int b, int64_t l,
+                              int kvh, int Hkv, int D, int block_size, int max_blocks)
+{
+    int64_t blk = block_table[(int64_t)b * max_blocks + l / block_size];
+    int64_t slot = l % block_size;
+    return cache + ((blk * block_size + slot) * Hkv + kvh) * (int64_t)D;
+}
+
+/* The plain definition, one query token per sequence: for sequence b and
+ * query head h (kv head h / (Hq / Hkv)),
+ *     s_l = scale * sum_d q_d k_ld          (l < L = seq_lens[b])
+ *     out_d = sum_l exp(s_l - max s) v_ld / sum_l exp(s_l - max s)
+ * in double; out rounded once.  Also S_d = sum_l p_l |v_ld| (the scale of
+ * the terms the tolerance is relative to) and QKabs[b][h] = max_l |scale| *
+ * sum_d |q_d k_ld| (what bounds a score's summation error).  L = 0 gives
+ * out = 0.  Q, Out: [B][Hq][D].  Returns the multiply-adds (2 per (l, d)). */
+int64_t oracle_attention(int fmt, const uint16_t *Q, const uint16_t *Kc, const uint16_t *Vc,
+                         const int32_t *block_table, const int32_t *seq_lens, int B, int Hq,
+                         int Hkv, int D, int block_size, int max_blocks, double scale,
+                         uint16_t *Out, double *Ox, double *S, double *QKabs)
+{
+    int64_t total = 0;
+    const int G = Hq / Hkv;
+    #pragma omp parallel for collapse(2) schedule(dynamic, 1) reduction(+ : total)
+    for (int b = 0; b < B; ++b) {
+        for (int h = 0; h < Hq; ++h) {
+            const int L = seq_lens[b], kvh = h / G;
+            const uint16_t *q = Q + ((int64_t)b * Hq + h) * D;
+            double *sc = (double *)malloc(sizeof(double) * (L > 0 ? L : 1));
+            double mx = -INFINITY, qka = 0.0;
+            for (int64_t l = 0; l < L; ++l) {
+                const uint16_t *k = kv_row(Kc, block_table, b, l, kvh, Hkv, D, block_size, max_blocks);
+                double s = 0.0, sa = 0.0;
+                for (int d = 0; d < D; ++d) {
+                    const double qd = oracle_decode(fmt, q[d]), kd = oracle_decode(fmt, k[d]);
+                    s += qd * kd;
+                    sa += fabs(qd * kd);
+                }
+                sc[l] = scale * s;
+                if (sc[l] > mx) mx = sc[l];
+                if (fabs(scale) * sa > qka) qka = fabs(scale) * sa;
+                total += D;
+            }
+            if (QKabs) QKabs[(int64_t)b * Hq + h] = qka;
+            double z = 0.0;
+            for (int64_t l = 0; l < L; ++l) { sc[l] = exp(sc[l] - mx); z += sc[l]; }
+            for (int d = 0; d < D; ++d) {
+                double o = 0.0, sa = 0.0;
+                for (int64_t l = 0; l < L; ++l) {
+                    double v = oracle_decode(fmt, kv_row(Vc, block_table, b, l, kvh, Hkv, D, block_size, max_blocks)[d]);
+                    o += sc[l] * v;
+                    sa += sc[l] * fabs(v);
+                }
+                total += L;
+                const int64_t i = ((int64_t)b * Hq + h) * D + d;
+                const double out = L > 0 ? o / z : 0.0;
+                if (Out) Out[i] = oracle_encode(fmt, out);
+                if (Ox) Ox[i] = out;
+                if (S) S[i] = L > 0 ? sa / z : 0.0;
+            }
+            free(sc);
+        }
+    }
+    return total;
+}
+
+/* The page's segmented algorithm (section 6.3), in its own steps: tokens
+ * [0, L) split into nseg contiguous segments of ceil(L / nseg) tokens (the
+ * last ones shorter or empty).  Segment i keeps its local max m_i, local
+ * denominator l_i = sum exp(s - m_i) and local o_i = sum exp(s - m_i) v;
+ * the merge takes M = max m_i and out = sum_i o_i e^(m_i - M) /
+ * sum_i l_i e^(m_i - M).  Empty segments (m_i = -inf) contribute nothing.
+ * Equal to oracle_attention up to double rounding. */
+void oracle_attention_segmented(int fmt, const uint16_t *Q, const uint16_t *Kc, const uint16_t *Vc,
+                                const int32_t *block_table, const int32_t *seq_lens, int B, int Hq,
+                                int Hkv, int D, int block_size, int max_blocks, double scale,
+                                int nseg, uint16_t *Out, double *Ox)
+{
+    const int G = Hq / Hkv;
+    #pragma omp parallel for collapse(2) schedule(dynamic, 1)
+    for (int b = 0; b < B; ++b) {
+        for (int h = 0; h < Hq; ++h) {
+            const int L = seq_lens[b], kvh = h / G;
+            const int64_t seg = (L + nseg - 1) / nseg;
+            const uint16_t *q = Q + ((int64_t)b * Hq + h) * D;
+            double *m = (double *)malloc(sizeof(double) * nseg);
+            double *ls = (double *)malloc(sizeof(double) * nseg);
+            double *o = (double *)calloc((size_t)nseg * D, sizeof(double));
+            for (int i = 0; i < nseg; ++i) {
+                const int64_t l0 = i * seg, l1 = (l0 + seg < L) ? l0 + seg : L;
+                m[i] = -INFINITY;
+                ls[i] = 0.0;
+                for (int64_t l = l0; l < l1; ++l) {
+                    const uint16_t *k = kv_row(Kc, block_table, b, l, kvh, Hkv, D, block_size, max_blocks);
+                    double s = 0.0;
+                    for (int d = 0; d < D; ++d) s += oracle_decode(fmt, q[d]) * oracle_decode(fmt, k[d]);
+                    if (scale * s > m[i]) m[i] = scale * s;
+                }
+                for (int64_t l = l0; l < l1; ++l) {
+                    const uint16_t *k = kv_row(Kc, block_table, b, l, kvh, Hkv, D, block_size, max_blocks);
+                    const uint16_t *v = kv_row(Vc, block_table, b, l, kvh, Hkv, D, block_size, max_blocks);
+                    double s = 0.0;
+                    for (int d = 0; d < D; ++d) s += oracle_decode(fmt, q[d]) * oracle_decode(fmt, k[d]);
+                    const double p = exp(scale * s - m[i]);
+                    ls[i] += p;
+                    for (int d = 0; d < D; ++d) o[(int64_t)i * D + d] += p * oracle_decode(fmt, v[d]);
+                }
+            }
+            double M = -INFINITY;
+            for (int i = 0; i < nseg; ++i) if (m[i] > M) M = m[i];
+            double z = 0.0;
+            for (int i = 0; i < nseg; ++i) if (ls[i] > 0.0) z += ls[i] * exp(m[i] - M);
+            for (int d = 0; d < D; ++d) {
+                double acc = 0.0;
+                for (int i = 0; i < nseg; ++i) if (ls[i] > 0.0) acc += o[(int64_t)i * D + d] * exp(m[i] - M);
+                const int64_t idx = ((int64_t)b * Hq + h) * D + d;
+                const double out = z > 0.0 ? acc / z : 0.0;
+                if (Out) Out[idx] = oracle_encode(fmt, out);
+                if (Ox) Ox[idx] = out;
+            }
+            free(m); free(ls); free(o);
+        }
+    }
+}
+
+int oracle_abi_version(void) { return 2; }

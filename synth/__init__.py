@@ -33,6 +33,12 @@ WORKLOADS = {
                                  n_values=(1, 4, 16), seed=3),
     "prefill_4096x34816x5120_bf16": dict(kind="gemm", M=4096, N=34816, K=5120, fmt=BF16,
                                          dist=("normal", 1.0, 0.02), seed=4),
+    # decode attention of the DCU page's head shape (16 query heads, 4 KV
+    # heads, head dim 256, BF16, pages of 784 tokens), one query token,
+    # Q, K, V ~ N(0, 1), scale 1/sqrt(D)
+    "attention_decode_16q4kv_d256_bf16": dict(kind="attention", Hq=16, Hkv=4, D=256,
+                                              block_size=784, lengths=(8192, 16384, 32768),
+                                              B=1, fmt=BF16, seed=5),
 }
 
 
@@ -89,6 +95,32 @@ def workload_operands(name, n=None):
     if w["kind"] == "gemm":
         return gemm_operands(w["M"], w["N"], w["K"], w["fmt"], w["dist"], w["seed"])
     return gemv_operands(w["M"], w["K"], n, seed=w["seed"], fmt=w["fmt"])
+
+
+def attention_operands(B, Hq, Hkv, D, seq_lens, block_size, seed, sigma=1.0, spare_blocks=3,
+                       fmt=BF16):
+    """Decode-attention inputs.  Q [B, Hq, D] and the paged caches K, V
+    [num_blocks, block_size, Hkv, D] ~ N(0, sigma) (drawn in that order, flat
+    storage order); block_table [B, max_blocks] int32: each sequence takes
+    ceil(L / block_size) pages from a seeded permutation of all pages (so
+    pages are scattered), unused entries -1."""
+    rng = np.random.default_rng(seed)
+    seq_lens = [int(x) for x in seq_lens]
+    need = [-(-L // block_size) for L in seq_lens]
+    max_blocks = max(1, max(need) if need else 1)
+    nblocks = sum(need) + spare_blocks
+    Q = to_bits(rng.normal(0.0, sigma, B * Hq * D), fmt)
+    K = to_bits(rng.normal(0.0, sigma, nblocks * block_size * Hkv * D), fmt)
+    V = to_bits(rng.normal(0.0, sigma, nblocks * block_size * Hkv * D), fmt)
+    perm = rng.permutation(nblocks)
+    bt = np.full((B, max_blocks), -1, np.int32)
+    pos = 0
+    for b in range(B):
+        bt[b, :need[b]] = perm[pos:pos + need[b]]
+        pos += need[b]
+    return dict(Q=Q, K=K, V=V, block_table=bt, seq_lens=np.array(seq_lens, np.int32),
+                max_blocks=max_blocks, num_blocks=nblocks, B=B, Hq=Hq, Hkv=Hkv, D=D,
+                block_size=block_size)
 
 
 def sample_indices(M, N, seed, count=4096):

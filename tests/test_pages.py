@@ -73,3 +73,16 @@ def test_mi355x_peaks():
     assert rf.MI355X["mfma_bf16_tflops"] == 2500.0 and rf.MI355X["hbm_GBps"] == 8000.0
     # dense FP16/BF16 MFMA: 256 CUs x 4096 FLOP/clk x 2.4 GHz
     assert close(256 * 4096 * 2.4e9 / 1e12, 2516.6, 1e-4)
+
+
+def test_attention_segment_table():
+    # the section 7 table and its stated conclusions: 32 segments lose at 8K,
+    # win by about 10% at 16K and about 21% at 32K, so 32 segments pay off
+    # only above a length between 8K and 16K (the page sets 12,288)
+    a = P["attention_segments"]
+    assert a["ms_32"]["8192"] > a["ms_16"]["8192"]
+    for L, stated in (("16384", a["stated_speedup_16k"]), ("32768", a["stated_speedup_32k"])):
+        gain = 1.0 - a["ms_32"][L] / a["ms_16"][L]
+        assert abs(gain - stated) <= a["speedup_tol"], (L, gain)
+    assert 8192 < a["use_32_from_length"] <= 16384
+    assert a["heads_q"] % a["heads_kv"] == 0
