@@ -16,7 +16,7 @@ _PKG = os.path.dirname(os.path.abspath(__file__))
 LIB_PATH = os.path.join(_PKG, "libmigemm.so")
 
 ERRORS = {0: "ok", -1: "negative dimension", -2: "null pointer with a non-zero extent",
-          -3: "output overlaps an input", -4: "pointer not 2-byte aligned",
+          -3: "output overlaps an input", -4: "pointer or size not aligned as the entry point requires",
           -5: "configuration not offered", -6: "dimension beyond the supported range"}
 
 F16, BF16 = 0, 1
@@ -61,6 +61,10 @@ SIGNATURES = {
     "migemm_strerror": (ctypes.c_char_p, [_I]),
     "migemm_abi_version": (_I, []),
     "migemm_hbm_read": (_I, [_P, ctypes.c_size_t, _P, _P]),
+    "attention_decode_bf16": (_I, [_P, _P, _P, _P, _P, _P] + [_I] * 7 +
+                              [ctypes.c_float, _I, _I, _P, ctypes.c_size_t, _P]),
+    "migemm_attention_segments": (_I, [_I, _I, _I]),
+    "migemm_attention_workspace_bytes": (ctypes.c_size_t, [_I, _I, _I, _I]),
     "migemm_hbm_read_sink_words": (_I, []),
 }
 
@@ -208,3 +212,32 @@ def hbm_read(buf, sink, stream=None):
 
 def hbm_read_sink_words():
     return lib().migemm_hbm_read_sink_words()
+
+
+def attention_decode(Q, Kc, Vc, block_table, seq_lens, Out, Hkv, block_size, scale,
+                     max_seq_len, num_segments=0, workspace=None, stream=None):
+    """Tensor wrapper of attention_decode_bf16.  Q, Out: [B, Hq, D] bfloat16
+    CUDA tensors; Kc, Vc: [num_blocks, block_size, Hkv, D] bfloat16;
+    block_table: [B, max_blocks] int32; seq_lens: [B] int32.  Allocates the
+    workspace when none is given (a uint8 CUDA tensor of the needed size)."""
+    import torch
+    B, Hq, D = Q.shape
+    num_blocks = Kc.shape[0]
+    max_blocks = block_table.shape[1]
+    for t in (Q, Kc, Vc, Out):
+        if t.dtype != torch.bfloat16 or not t.is_cuda or not t.is_contiguous():
+            raise ValueError("Q, Kc, Vc, Out must be contiguous bfloat16 CUDA tensors")
+    for t in (block_table, seq_lens):
+        if t.dtype != torch.int32 or not t.is_cuda or not t.is_contiguous():
+            raise ValueError("block_table and seq_lens must be contiguous int32 CUDA tensors")
+    S = num_segments or lib().migemm_attention_segments(B, Hkv, max_seq_len)
+    need = lib().migemm_attention_workspace_bytes(B, Hq, D, S)
+    if workspace is None:
+        workspace = torch.empty(max(need, 16), dtype=torch.uint8, device=Q.device)
+    _check(lib().attention_decode_bf16(Q.data_ptr(), Kc.data_ptr(), Vc.data_ptr(),
+                                       block_table.data_ptr(), seq_lens.data_ptr(), Out.data_ptr(),
+                                       B, Hq, Hkv, D, block_size, max_blocks, num_blocks, scale,
+                                       max_seq_len, S, workspace.data_ptr(),
+                                       workspace.numel() * workspace.element_size(),
+                                       _stream_handle(stream)), "attention_decode_bf16")
+    return Out

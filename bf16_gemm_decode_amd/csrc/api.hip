@@ -270,6 +270,62 @@ int gemv_bf16(const uint16_t *W, const uint16_t *X, uint16_t *Y, int M, int K, i
     return gemv_bf16_ex(W, X, Y, M, K, n, 0, stream);
 }
 
+int migemm_attention_segments(int B, int Hkv, int max_seq_len)
+{
+    if (B <= 0 || Hkv <= 0) return 1;
+    // about 1024 workgroups (4 per CU) when the sequences allow it, and at
+    // least 128 tokens per segment
+    int S = 1;
+    while (S < 256 && (int64_t)B * Hkv * S < 1024) S <<= 1;
+    while (S > 1 && (max_seq_len + S - 1) / S < 128) S >>= 1;
+    return S;
+}
+
+size_t migemm_attention_workspace_bytes(int B, int Hq, int D, int num_segments)
+{
+    if (B < 0 || Hq < 0 || D < 0 || num_segments < 1) return 0;
+    return attention_workspace_bytes(B, Hq, D, num_segments);
+}
+
+int attention_decode_bf16(const uint16_t *Q, const uint16_t *Kc, const uint16_t *Vc,
+                          const int32_t *block_table, const int32_t *seq_lens, uint16_t *Out,
+                          int B, int Hq, int Hkv, int D, int block_size, int max_blocks,
+                          int num_blocks, float scale, int max_seq_len, int num_segments,
+                          void *workspace, size_t workspace_bytes, void *stream)
+{
+    if (B < 0 || Hq < 0 || Hkv < 0 || D < 0 || block_size < 0 || max_blocks < 0 ||
+        num_blocks < 0 || max_seq_len < 0 || num_segments < 0)
+        return MIGEMM_ERR_DIM;
+    if (B == 0 || Hq == 0) return MIGEMM_OK;
+    if (Hkv == 0 || Hq % Hkv != 0 || block_size == 0 || max_blocks == 0 || num_blocks == 0)
+        return MIGEMM_ERR_DIM;
+    const int G = Hq / Hkv;
+    if (!(D == 64 || D == 128 || D == 256) || !(G == 1 || G == 2 || G == 4 || G == 8) ||
+        num_segments > 1024)
+        return MIGEMM_ERR_CONFIG;
+    // grid (segments, kv heads, sequences); token positions held in int
+    if (B > 65535 || Hkv > 65535 || (int64_t)max_blocks * block_size > INT32_MAX)
+        return MIGEMM_ERR_SIZE;
+    if (!Q || !Kc || !Vc || !block_table || !seq_lens || !Out || !workspace) return MIGEMM_ERR_NULL;
+    if (((uintptr_t)Q | (uintptr_t)Kc | (uintptr_t)Vc | (uintptr_t)workspace) % 16 ||
+        ((uintptr_t)block_table | (uintptr_t)seq_lens) % 4 || (uintptr_t)Out % 2)
+        return MIGEMM_ERR_ALIGN;
+    const int S = num_segments ? num_segments : migemm_attention_segments(B, Hkv, max_seq_len);
+    const size_t need = attention_workspace_bytes(B, Hq, D, S);
+    if (workspace_bytes < need) return MIGEMM_ERR_SIZE;
+    const size_t qb = (size_t)B * Hq * D * 2;
+    const size_t cb = (size_t)num_blocks * block_size * Hkv * D * 2;
+    if (overlaps(Out, qb, Q, qb) || overlaps(Out, qb, Kc, cb) || overlaps(Out, qb, Vc, cb) ||
+        overlaps(Out, qb, workspace, need) || overlaps(workspace, need, Q, qb) ||
+        overlaps(workspace, need, Kc, cb) || overlaps(workspace, need, Vc, cb) ||
+        overlaps(Out, qb, block_table, (size_t)B * max_blocks * 4) ||
+        overlaps(Out, qb, seq_lens, (size_t)B * 4))
+        return MIGEMM_ERR_OVERLAP;
+    AttentionLaunch A{Q, Kc, Vc, block_table, seq_lens, Out, B, Hq, Hkv, D, block_size,
+                      max_blocks, num_blocks, scale, S, workspace};
+    return finish(attention_launch(A, (hipStream_t)stream), stream);
+}
+
 int migemm_tile_coord(int64_t wg, int64_t num_pid_m, int64_t num_pid_n, int64_t group_m,
                       int64_t num_xcd, int64_t *pid_m, int64_t *pid_n)
 {
@@ -287,7 +343,7 @@ const char *migemm_strerror(int code)
     case MIGEMM_ERR_DIM: return "negative dimension";
     case MIGEMM_ERR_NULL: return "null pointer with a non-zero extent";
     case MIGEMM_ERR_OVERLAP: return "output overlaps an input";
-    case MIGEMM_ERR_ALIGN: return "pointer not 2-byte aligned";
+    case MIGEMM_ERR_ALIGN: return "pointer or size not aligned as the entry point requires";
     case MIGEMM_ERR_CONFIG: return "configuration not offered";
     case MIGEMM_ERR_SIZE: return "dimension beyond the supported range";
     }

@@ -116,6 +116,20 @@ struct SkinnyLaunch {
 
 hipError_t skinny_launch(const SkinnyLaunch &L, hipStream_t stream);
 
+// Decode attention over a paged KV cache, split into S segments (attention.hip).
+struct AttentionLaunch {
+    const uint16_t *Q, *Kc, *Vc;          // Q [B][Hq][D]; caches [block][token][Hkv][D]
+    const int32_t *block_table, *seq_lens; // [B][max_blocks], [B]
+    uint16_t *Out;                        // [B][Hq][D]
+    int B, Hq, Hkv, D, block_size, max_blocks, num_blocks;
+    float scale;
+    int S;                                // segments per (sequence, kv head)
+    void *workspace;                      // attention_workspace_bytes(B, Hq, D, S)
+};
+
+size_t attention_workspace_bytes(int B, int Hq, int D, int S);
+hipError_t attention_launch(const AttentionLaunch &A, hipStream_t stream);
+
 hipError_t hbm_read_launch(const void *buf, size_t bytes, uint32_t *sink, hipStream_t stream);
 int hbm_read_sink_words();
 

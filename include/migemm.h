@@ -38,7 +38,7 @@ extern "C" {
 #define MIGEMM_ERR_DIM      (-1)  /* a dimension is negative                     */
 #define MIGEMM_ERR_NULL     (-2)  /* NULL pointer where the extent is non-zero   */
 #define MIGEMM_ERR_OVERLAP  (-3)  /* the output overlaps an input's byte range   */
-#define MIGEMM_ERR_ALIGN    (-4)  /* a pointer is not 2-byte aligned             */
+#define MIGEMM_ERR_ALIGN    (-4)  /* a pointer or size is not aligned as needed  */
 #define MIGEMM_ERR_CONFIG   (-5)  /* an explicit configuration is not offered    */
 #define MIGEMM_ERR_SIZE     (-6)  /* a dimension exceeds the supported range     */
 
@@ -90,6 +90,52 @@ int gemm_bf16(const uint16_t *A, const uint16_t *B, uint16_t *C,
  */
 int gemv_bf16(const uint16_t *W, const uint16_t *X, uint16_t *Y,
               int M, int K, int n, void *stream);
+
+/*
+ * attention_decode_bf16 -- decode attention over a paged KV cache (bfloat16).
+ *
+ * Defined by the DCU decode page (forum.sourcefind.cn db785961): section 6.1
+ * gives, per query head, scores = q K^T over the L cached tokens, prob =
+ * softmax(scores), out = prob V, and the paged cache layout [block,
+ * token_in_block, kv_head, head_dim]; section 6.3 splits the L tokens into
+ * contiguous segments, each with a local max, local softmax denominator and
+ * local prob V, merged with a numerically stable global reduction (section 7
+ * measures 16 vs 32 segments).  Here, one query token per sequence:
+ *     out[b][h][:] = softmax(scale * Q[b][h] . K[l], l < seq_lens[b]) V[l]
+ * with K[l], V[l] the rows of kv head h / (Hq / Hkv) for token l, found in
+ * page block_table[b * max_blocks + l / block_size] at slot l % block_size.
+ * FP32 arithmetic, one rounding to bfloat16.
+ *   Q, Out:      [B][Hq][D] row-major; Q, Kc, Vc 16-byte aligned.
+ *   Kc, Vc:      [num_blocks][block_size][Hkv][D] (device).
+ *   block_table: [B][max_blocks] int32 page ids (device); seq_lens: [B]
+ *                int32 (device), clamped to max_blocks * block_size.
+ *                Tokens on a page id outside [0, num_blocks) are skipped.
+ *   D in {64, 128, 256}; Hq / Hkv in {1, 2, 4, 8}.
+ *   max_seq_len: host-side upper bound of seq_lens (for the automatic
+ *                segment count); num_segments: 0 = automatic
+ *                (migemm_attention_segments), else 1 .. 1024.
+ *   workspace:   device, 16-byte aligned, at least
+ *                migemm_attention_workspace_bytes(B, Hq, D, segments) bytes
+ *                (the per-segment FP32 partials); owned by the caller.
+ * A sequence with seq_lens[b] == 0 gets zeros.  Errors: MIGEMM_ERR_DIM,
+ * _NULL, _ALIGN, _CONFIG (D, group size, segments), _SIZE (workspace too
+ * small; B or Hkv above 65535; max_blocks * block_size above 2^31 - 1),
+ * _OVERLAP (Out or workspace intersecting an input).  B == 0 is a
+ * no-op.  Completion as for the GEMM (NULL stream: synchronous).
+ */
+int attention_decode_bf16(const uint16_t *Q, const uint16_t *Kc, const uint16_t *Vc,
+                          const int32_t *block_table, const int32_t *seq_lens,
+                          uint16_t *Out, int B, int Hq, int Hkv, int D, int block_size,
+                          int max_blocks, int num_blocks, float scale, int max_seq_len,
+                          int num_segments, void *workspace, size_t workspace_bytes,
+                          void *stream);
+
+/* Segments the automatic choice uses (host only): about 1024 workgroups of
+ * (segment, kv head, sequence) when the lengths allow, at least 128 tokens
+ * per segment, at most 256 segments. */
+int migemm_attention_segments(int B, int Hkv, int max_seq_len);
+/* Workspace bytes attention_decode_bf16 needs for that many segments. */
+size_t migemm_attention_workspace_bytes(int B, int Hq, int D, int num_segments);
 
 /* ---- explicit-configuration variants (tuning sweeps) --------------------- */
 

@@ -184,3 +184,36 @@ def test_tile_coord_rejects_bad_input():
         binding.tile_coord(15, 5, 3, 2, 1)
     with pytest.raises(binding.MigemmError):
         binding.tile_coord(0, 5, 3, 0, 1)
+
+
+def test_attention_argument_errors_and_segments():
+    L = binding.lib()
+    ws = 1 << 20
+    args = lambda **k: dict(dict(Q=P, Kc=P + 0x1000000, Vc=P + 0x2000000, bt=P + 0x3000000,
+                                 sl=P + 0x3100000, Out=P + 0x3200000, B=1, Hq=16, Hkv=4, D=256,
+                                 bs=784, maxb=2, nb=4, scale=0.0625, maxlen=1000, S=16,
+                                 ws=P + 0x4000000, wsb=ws), **k)
+
+    def call(a):
+        return L.attention_decode_bf16(a["Q"], a["Kc"], a["Vc"], a["bt"], a["sl"], a["Out"], a["B"],
+                                       a["Hq"], a["Hkv"], a["D"], a["bs"], a["maxb"], a["nb"],
+                                       a["scale"], a["maxlen"], a["S"], a["ws"], a["wsb"], None)
+    assert call(args(B=0)) == 0                       # nothing to do, nothing touched
+    assert call(args(Hq=-1)) == -1
+    assert call(args(Hq=6)) == -1                     # Hq not a multiple of Hkv
+    assert call(args(D=96)) == -5                     # head dim not built
+    assert call(args(Hq=64)) == -5                    # group of 16 heads not built
+    assert call(args(S=2000)) == -5
+    assert call(args(Q=None)) == -2
+    assert call(args(Kc=P + 0x1000008)) == -4         # caches need 16-byte rows
+    assert call(args(wsb=1000)) == -6                 # workspace too small
+    assert call(args(Out=P + 8)) == -3                # Out inside Q
+    assert call(args(B=70000, wsb=1 << 40)) == -6     # grid z limit
+    assert call(args(maxb=1 << 22, bs=1024)) == -6    # token positions past int
+    # workspace: partial max, denominator and D outputs per (b, h, segment)
+    assert L.migemm_attention_workspace_bytes(2, 16, 256, 32) == 2 * 16 * 32 * 258 * 4
+    # automatic segments: ~1024 workgroups, >= 128 tokens each, <= 256
+    assert L.migemm_attention_segments(1, 4, 32768) == 256
+    assert L.migemm_attention_segments(1, 4, 8192) == 64
+    assert L.migemm_attention_segments(8, 4, 32768) == 32
+    assert L.migemm_attention_segments(1, 4, 100) == 1
