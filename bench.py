@@ -15,6 +15,12 @@ same stream (inside a step the events also hold the dispatch gap, reported as
 in_step_avg_us).  `cpu_baseline` times the CPU oracle on a bounded sample of the same
 GEMM (sampled output entries), scaled to TFLOP/s.
 
+Beside the step, `attention` reports split-KV decode attention over the paged
+BF16 cache (16 query / 4 KV heads, head dim 256, pages of 784 tokens, one
+sequence of 32768 cached tokens, automatic segment count) from a burst of
+launches rotating over 5 disjoint copies of the cache (5 x 134 MB), as HBM
+GB/s of the algorithmic bytes (K and V read once, Q, block table, output).
+
 Usage: python bench.py [--gpus 1] [--steps 20] [--warmup 5] [--no-cpu-baseline]
 """
 import argparse
@@ -30,6 +36,9 @@ METRIC = "GEMM TFLOP/s at 8192x8192x16384 (% MFMA peak); decode GEMV HBM GB/s (%
 GEMM_CFG = "gemm_8192x8192x16384_f16"
 GEMV_CFG = "gemv_34816x5120_bf16"
 W_COPIES = 4
+ATT_CFG = "attention_decode_16q4kv_d256_bf16"
+ATT_LEN = 32768
+ATT_COPIES = 5
 
 
 def parse():
@@ -127,7 +136,7 @@ def main():
 
     import synth
     from bf16_gemm_decode_amd import binding, roofline as rf
-    from bf16_gemm_decode_amd.profile_summary import GEMM_SOURCES, GEMV_SOURCES
+    from bf16_gemm_decode_amd.profile_summary import ATTENTION_SOURCES, GEMM_SOURCES, GEMV_SOURCES
 
     torch.cuda.set_device(0)
     if args.copy_calibration:
@@ -156,6 +165,19 @@ def main():
         dW.append(dW[0].clone())
     dX = dev(X)
     dY = torch.empty(gn * GM, dtype=torch.int16, device="cuda")
+    torch.cuda.synchronize()
+
+    wa = synth.WORKLOADS[ATT_CFG]
+    Hq, Hkv, D, bs = wa["Hq"], wa["Hkv"], wa["D"], wa["block_size"]
+    op = synth.attention_operands(1, Hq, Hkv, D, [ATT_LEN], bs, seed=wa["seed"])
+    nb, mb = op["num_blocks"], op["max_blocks"]
+    aK = torch.cat([dev(op["K"])] * ATT_COPIES)        # copy c holds pages c*nb .. c*nb+nb-1
+    aV = torch.cat([dev(op["V"])] * ATT_COPIES)
+    aQ = dev(op["Q"])
+    abt = torch.from_numpy(np.concatenate([op["block_table"] + c * nb for c in range(ATT_COPIES)])
+                           .astype(np.int32)).cuda()
+    asl = torch.full((ATT_COPIES,), ATT_LEN, dtype=torch.int32, device="cuda")
+    aO = torch.empty(Hq * D, dtype=torch.int16, device="cuda")
     torch.cuda.synchronize()
 
     probe_GBps = hbm_probe(binding, torch, stream)
@@ -211,6 +233,30 @@ def main():
     b1.record(stream)
     stream.synchronize()
     gemv_avg = b0.elapsed_time(b1) / 1e3 / nburst
+    # decode attention, burst over the cache copies
+    segs = L.migemm_attention_segments(1, Hq, Hkv, ATT_LEN)
+    wsb = L.migemm_attention_workspace_bytes(1, Hq, D, segs)
+    aws = torch.empty(wsb, dtype=torch.uint8, device="cuda")
+
+    def attention(i):
+        c = i % ATT_COPIES
+        return L.attention_decode_bf16(aQ.data_ptr(), aK.data_ptr(), aV.data_ptr(),
+                                        abt.data_ptr() + c * mb * 4, asl.data_ptr() + c * 4,
+                                        aO.data_ptr(), 1, Hq, Hkv, D, bs, mb, nb * ATT_COPIES,
+                                        1.0 / D ** 0.5, ATT_LEN, 0, aws.data_ptr(), wsb, h)
+    for i in range(ATT_COPIES):
+        assert attention(i) == 0
+    natt = max(4 * args.steps, 40)
+    a0, a1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+    a0.record(stream)
+    for i in range(natt):
+        assert attention(i) == 0
+    a1.record(stream)
+    stream.synchronize()
+    att_avg = a0.elapsed_time(a1) / 1e3 / natt
+    att_bytes = rf.attention_bytes([ATT_LEN], Hq, Hkv, D, bs)
+    att_GBps = att_bytes / att_avg / 1e9
+
     tflops = rf.gemm_flop(M, N, K) / gemm_avg / 1e12
     gemv_bytes = rf.gemv_bytes(GM, GK, gn)
     gemv_GBps = gemv_bytes / gemv_avg / 1e9
@@ -252,6 +298,16 @@ def main():
                               "algorithmic_bytes": int(gemv_bytes)},
                  "probe_read_GBps": round(probe_GBps, 1),
                  "frac_of_probe": round(gemv_GBps / probe_GBps, 4)},
+        "attention": {"workload": "%s, 1 sequence of %d tokens" % (ATT_CFG, ATT_LEN),
+                      "segments": segs, "avg_call_us": round(att_avg * 1e6, 2),
+                      "calls_timed": natt, "kernels": "attn_segment_kernel + attn_merge_kernel",
+                      "GBps": round(att_GBps, 1), "algorithmic_bytes": int(att_bytes),
+                      "roofline": {"bound": "hbm", "achieved": round(att_GBps, 1), "peak": hbm,
+                                   "unit": "GB/s", "frac": round(att_GBps / hbm, 4),
+                                   "traffic_segment_kernel": measured_traffic(
+                                       ATTENTION_SOURCES,
+                                       "attention_16q4kv_d256_l32768_traffic.json")},
+                      "frac_of_probe": round(att_GBps / probe_GBps, 4)},
         "device": {"name": props.name, "cus": props.multi_processor_count},
     }
     if not args.no_cpu_baseline:

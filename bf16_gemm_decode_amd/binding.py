@@ -63,7 +63,7 @@ SIGNATURES = {
     "migemm_hbm_read": (_I, [_P, ctypes.c_size_t, _P, _P]),
     "attention_decode_bf16": (_I, [_P, _P, _P, _P, _P, _P] + [_I] * 7 +
                               [ctypes.c_float, _I, _I, _P, ctypes.c_size_t, _P]),
-    "migemm_attention_segments": (_I, [_I, _I, _I]),
+    "migemm_attention_segments": (_I, [_I, _I, _I, _I]),
     "migemm_attention_workspace_bytes": (ctypes.c_size_t, [_I, _I, _I, _I]),
     "migemm_hbm_read_sink_words": (_I, []),
 }
@@ -230,7 +230,7 @@ def attention_decode(Q, Kc, Vc, block_table, seq_lens, Out, Hkv, block_size, sca
     for t in (block_table, seq_lens):
         if t.dtype != torch.int32 or not t.is_cuda or not t.is_contiguous():
             raise ValueError("block_table and seq_lens must be contiguous int32 CUDA tensors")
-    S = num_segments or lib().migemm_attention_segments(B, Hkv, max_seq_len)
+    S = num_segments or lib().migemm_attention_segments(B, Hq, Hkv, max_seq_len)
     need = lib().migemm_attention_workspace_bytes(B, Hq, D, S)
     if workspace is None:
         workspace = torch.empty(max(need, 16), dtype=torch.uint8, device=Q.device)

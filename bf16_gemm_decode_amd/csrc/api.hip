@@ -270,14 +270,19 @@ int gemv_bf16(const uint16_t *W, const uint16_t *X, uint16_t *Y, int M, int K, i
     return gemv_bf16_ex(W, X, Y, M, K, n, 0, stream);
 }
 
-int migemm_attention_segments(int B, int Hkv, int max_seq_len)
+int migemm_attention_segments(int B, int Hq, int Hkv, int max_seq_len)
 {
-    if (B <= 0 || Hkv <= 0) return 1;
-    // about 1024 workgroups (4 per CU) when the sequences allow it, and at
-    // least 128 tokens per segment
+    if (B <= 0 || Hq <= 0 || Hkv <= 0 || Hq % Hkv) return 1;
+    // Double S while the segment workgroups still fit in one round of
+    // residency (2 per CU at the segment kernel's register use) and every
+    // segment keeps at least 128 tokens; measured best on the
+    // 16 Q / 4 KV / head-dim-256 shape for 1 x 8K .. 32K and 8 x 8K,
+    // 32 x 4K tokens.
+    const int64_t per_s = (int64_t)B * Hkv * ((Hq / Hkv + 3) / 4);   // workgroups per segment
+    const int64_t resident = 2 * 256;
     int S = 1;
-    while (S < 256 && (int64_t)B * Hkv * S < 1024) S <<= 1;
-    while (S > 1 && (max_seq_len + S - 1) / S < 128) S >>= 1;
+    while (S < 1024 && per_s * 2 * S <= resident && (max_seq_len + 2 * S - 1) / (2 * S) >= 128)
+        S <<= 1;
     return S;
 }
 
@@ -303,14 +308,15 @@ int attention_decode_bf16(const uint16_t *Q, const uint16_t *Kc, const uint16_t 
     if (!(D == 64 || D == 128 || D == 256) || !(G == 1 || G == 2 || G == 4 || G == 8) ||
         num_segments > 1024)
         return MIGEMM_ERR_CONFIG;
-    // grid (segments, kv heads, sequences); token positions held in int
-    if (B > 65535 || Hkv > 65535 || (int64_t)max_blocks * block_size > INT32_MAX)
+    // grid (kv heads, segments, sequences); token positions (plus a few
+    // steps of look-ahead) held in int
+    if (B > 65535 || Hkv > 65535 || (int64_t)max_blocks * block_size > (1 << 30))
         return MIGEMM_ERR_SIZE;
     if (!Q || !Kc || !Vc || !block_table || !seq_lens || !Out || !workspace) return MIGEMM_ERR_NULL;
     if (((uintptr_t)Q | (uintptr_t)Kc | (uintptr_t)Vc | (uintptr_t)workspace) % 16 ||
         ((uintptr_t)block_table | (uintptr_t)seq_lens) % 4 || (uintptr_t)Out % 2)
         return MIGEMM_ERR_ALIGN;
-    const int S = num_segments ? num_segments : migemm_attention_segments(B, Hkv, max_seq_len);
+    const int S = num_segments ? num_segments : migemm_attention_segments(B, Hq, Hkv, max_seq_len);
     const size_t need = attention_workspace_bytes(B, Hq, D, S);
     if (workspace_bytes < need) return MIGEMM_ERR_SIZE;
     const size_t qb = (size_t)B * Hq * D * 2;
@@ -350,7 +356,7 @@ const char *migemm_strerror(int code)
     return code > 0 ? "HIP runtime error (code is a hipError_t)" : "unknown error";
 }
 
-int migemm_abi_version(void) { return 2; }
+int migemm_abi_version(void) { return 3; }
 
 int migemm_hbm_read(const void *buf, size_t bytes, uint32_t *sink, void *stream)
 {

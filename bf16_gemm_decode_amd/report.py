@@ -10,7 +10,12 @@ inputs of `synth` (the same recipes the parity tests use):
   * the prefill GEMM 4096 x 34816 x 5120 BF16 over the grouped-ordering width
     GROUP_M in {1, 4, 8, 16} x the tiles that fit it, in both of its layouts
     (column-major X through gemm_ex, row-major X and W through gemm_tn_ex);
-  * the streaming-read probe.
+  * the streaming-read probe;
+  * split-KV decode attention at 16 query / 4 KV heads, head dim 256, pages
+    of 784 tokens, for 1 sequence of 8K, 16K, 32K tokens and batches of 8 x 8K
+    and 32 x 4K, at 16, 32 and the automatic number of segments (the caches
+    rotate over disjoint page sets of > 600 MB so they do not stay in the
+    MALL).
 
 Times are kernel durations from HIP events around back-to-back launches on
 one stream (median and minimum of `--rounds` rounds).  TFLOP/s use the
@@ -72,10 +77,12 @@ def main(argv=None):
     p.add_argument("--out", default=None, help="write a markdown summary here")
     p.add_argument("--rounds", type=int, default=5)
     p.add_argument("--skip-prefill-grid", action="store_true")
-    p.add_argument("--sections", default="gemm,decode,prefill",
-                   help="comma list of gemm, decode, prefill")
+    p.add_argument("--sections", default="gemm,decode,prefill,attention",
+                   help="comma list of gemm, decode, prefill, attention")
     p.add_argument("--decode-tiles", default="0",
                    help="gemm_tn tiles to time for the decode batches (0 = automatic)")
+    p.add_argument("--attn-segments", default="16,32,0",
+                   help="segment counts to time for the attention (0 = automatic)")
     a = p.parse_args(argv)
 
     import numpy as np
@@ -199,19 +206,61 @@ def main(argv=None):
                 gemm_row("prefill_4096x34816x5120_bf16 (Y = X W^T, row-major)", code_dt, At, Xr, Y,
                          Np, Mp, Kp, tile, gm, tn=True, launches=10)
 
+    # --- decode attention over the paged cache ------------------------------
+    wa = synth.WORKLOADS["attention_decode_16q4kv_d256_bf16"]
+    for B, Lq in (((1, 8192), (1, 16384), (1, 32768), (8, 8192), (32, 4096))
+                  if "attention" in sections else ()):
+        Hq, Hkv, D, bs = wa["Hq"], wa["Hkv"], wa["D"], wa["block_size"]
+        per = 2 * 2 * Lq * Hkv * D                      # KV bytes of one sequence
+        copies = max(1, -(-(600 << 20) // (per * B)))    # > 2x the MALL across rotations
+        op = synth.attention_operands(B * copies, Hq, Hkv, D, [Lq] * (B * copies), bs,
+                                      seed=wa["seed"])
+        dQ, dK, dV = _dev(torch, op["Q"]), _dev(torch, op["K"]), _dev(torch, op["V"])
+        bt = torch.from_numpy(np.ascontiguousarray(op["block_table"], np.int32)).cuda()
+        sl = torch.from_numpy(np.ascontiguousarray(op["seq_lens"], np.int32)).cuda()
+        out = torch.empty(B * copies * Hq * D, dtype=torch.int16, device="cuda")
+        mb = op["max_blocks"]
+        nbytes = rf.attention_bytes([Lq] * B, Hq, Hkv, D, bs)
+        for S in (int(x) for x in a.attn_segments.split(",")):
+            segs = S or L.migemm_attention_segments(B, Hq, Hkv, Lq)
+            wsb = L.migemm_attention_workspace_bytes(B, Hq, D, segs)
+            ws = torch.empty(wsb, dtype=torch.uint8, device="cuda")
+
+            def call(i, S=S, ws=ws, wsb=wsb):
+                c = i % copies                           # sequences c*B .. c*B+B-1
+                return L.attention_decode_bf16(
+                    dQ.data_ptr() + c * B * Hq * D * 2, dK.data_ptr(), dV.data_ptr(),
+                    bt.data_ptr() + c * B * mb * 4, sl.data_ptr() + c * B * 4,
+                    out.data_ptr() + c * B * Hq * D * 2, B, Hq, Hkv, D, bs, mb, op["num_blocks"],
+                    1.0 / np.sqrt(D), Lq, S, ws.data_ptr(), wsb, h)
+            med, mn = _timer(torch, s, call, 40, a.rounds)
+            gb = nbytes / med / 1e9
+            r = {"workload": "attention_decode_16q4kv_d256_bf16 (page 784)", "B": B, "L": Lq,
+                 "segments": segs, "requested": S, "median_us": round(med * 1e6, 2),
+                 "min_us": round(mn * 1e6, 2), "GBps": round(gb, 1), "util": round(gb / hbm, 4),
+                 "frac_of_probe": round(gb / probe, 4),
+                 "workspace_bytes": wsb}
+            rows.append(r)
+            print(json.dumps(r), flush=True)
+        del dQ, dK, dV, op
+
     smi_after = _smi()
     if a.out:
         with open(a.out, "w") as f:
             f.write("# Per-workload report\n\n")
-            f.write("command: `python -m bf16_gemm_decode_amd.report --out %s --rounds %d`\n\n"
-                    % (os.path.relpath(a.out, ROOT), a.rounds))
+            f.write("command: `python -m bf16_gemm_decode_amd.report %s`\n\n"
+                    % " ".join(sys.argv[1:] if argv is None else argv))
             f.write("Kernel durations from HIP events around back-to-back launches (median / min of "
-                    "%d rounds); util = fraction of 2.5 PFLOP/s (GEMM) or 8 TB/s (GEMV, probe).\n\n"
+                    "%d rounds); util = fraction of 2.5 PFLOP/s (GEMM) or 8 TB/s (GEMV, attention, "
+                    "probe); for the attention GB/s counts the algorithmic bytes (K and V read once, "
+                    "Q, block table, output), the workspace partials not included.\n\n"
                     % a.rounds)
             f.write("| workload | shape / n | layout | tile | GROUP_M | median us | min us | TFLOP/s | GB/s | util | of probe |\n")
             f.write("|---|---|---|---|---|---|---|---|---|---|---|\n")
             for r in rows:
-                shape = "%dx%dx%d" % (r["M"], r["N"], r["K"]) if "M" in r else ("n=%d" % r["n"] if "n" in r else "")
+                shape = ("%dx%dx%d" % (r["M"], r["N"], r["K"]) if "M" in r else
+                         "n=%d" % r["n"] if "n" in r else
+                         "B=%d L=%d S=%d" % (r["B"], r["L"], r["segments"]) if "L" in r else "")
                 tile = ("%d (%s)" % (r["tile"], "x".join(str(v) for v in r["tile_mnk"]))
                         if "tile_mnk" in r else str(r.get("tile", "")))
                 f.write("| %s | %s | %s | %s | %s | %s | %s | %s | %s | %s | %s |\n" % (

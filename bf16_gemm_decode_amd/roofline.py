@@ -61,3 +61,17 @@ def ridge(peak_tflops, bw_GBps):
 
 def seconds_at(amount, rate):
     return amount / rate
+
+
+def attention_bytes(seq_lens, Hq, Hkv, D, block_size, elt=2):
+    """Decode attention (one query token per sequence): every cached K and V
+    row of the kv heads read once, Q read once, the output written once, and
+    the block-table entries of the used pages read once."""
+    kv = sum(2.0 * elt * int(L) * Hkv * D for L in seq_lens)
+    pages = sum(4.0 * (-(-int(L) // block_size)) for L in seq_lens)
+    return kv + pages + 2.0 * elt * len(seq_lens) * Hq * D
+
+
+def attention_flop(seq_lens, Hq, D):
+    """q.k and prob*v: 4 * L * Hq * D per sequence (softmax not counted)."""
+    return sum(4.0 * int(L) * Hq * D for L in seq_lens)

@@ -119,7 +119,7 @@ int gemv_bf16(const uint16_t *W, const uint16_t *X, uint16_t *Y,
  *                (the per-segment FP32 partials); owned by the caller.
  * A sequence with seq_lens[b] == 0 gets zeros.  Errors: MIGEMM_ERR_DIM,
  * _NULL, _ALIGN, _CONFIG (D, group size, segments), _SIZE (workspace too
- * small; B or Hkv above 65535; max_blocks * block_size above 2^31 - 1),
+ * small; B or Hkv above 65535; max_blocks * block_size above 2^30),
  * _OVERLAP (Out or workspace intersecting an input).  B == 0 is a
  * no-op.  Completion as for the GEMM (NULL stream: synchronous).
  */
@@ -130,10 +130,11 @@ int attention_decode_bf16(const uint16_t *Q, const uint16_t *Kc, const uint16_t 
                           int num_segments, void *workspace, size_t workspace_bytes,
                           void *stream);
 
-/* Segments the automatic choice uses (host only): about 1024 workgroups of
- * (segment, kv head, sequence) when the lengths allow, at least 128 tokens
- * per segment, at most 256 segments. */
-int migemm_attention_segments(int B, int Hkv, int max_seq_len);
+/* Segments the automatic choice uses (host only): the largest power of two
+ * that keeps the segment workgroups (B * Hkv * ceil(Hq / Hkv / 4) per
+ * segment) within one round of residency on 256 CUs (512) and at least
+ * 128 tokens per segment; 1 when the lengths are short. */
+int migemm_attention_segments(int B, int Hq, int Hkv, int max_seq_len);
 /* Workspace bytes attention_decode_bf16 needs for that many segments. */
 size_t migemm_attention_workspace_bytes(int B, int Hq, int D, int num_segments);
 

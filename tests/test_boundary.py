@@ -27,7 +27,7 @@ def test_library_exports_every_declared_function():
     for n in names:
         assert hasattr(L, n), n
     assert names == set(binding.SIGNATURES), names ^ set(binding.SIGNATURES)
-    assert L.migemm_abi_version() == 2
+    assert L.migemm_abi_version() == 3
 
 
 P = 0x10000        # a fake, aligned device address: never dereferenced on error paths
@@ -213,7 +213,11 @@ def test_attention_argument_errors_and_segments():
     # workspace: partial max, denominator and D outputs per (b, h, segment)
     assert L.migemm_attention_workspace_bytes(2, 16, 256, 32) == 2 * 16 * 32 * 258 * 4
     # automatic segments: ~1024 workgroups, >= 128 tokens each, <= 256
-    assert L.migemm_attention_segments(1, 4, 32768) == 256
-    assert L.migemm_attention_segments(1, 4, 8192) == 64
-    assert L.migemm_attention_segments(8, 4, 32768) == 32
-    assert L.migemm_attention_segments(1, 4, 100) == 1
+    assert L.migemm_attention_segments(1, 16, 4, 32768) == 128
+    assert L.migemm_attention_segments(1, 16, 4, 16384) == 128
+    assert L.migemm_attention_segments(1, 16, 4, 8192) == 64
+    assert L.migemm_attention_segments(8, 16, 4, 8192) == 16
+    assert L.migemm_attention_segments(32, 16, 4, 4096) == 4
+    assert L.migemm_attention_segments(1, 32, 4, 32768) == 64   # groups of 8: 2 workgroups each
+    assert L.migemm_attention_segments(1, 16, 4, 100) == 1
+    assert L.migemm_attention_segments(1000, 16, 4, 32768) == 1

@@ -26,7 +26,7 @@ def _gpu(op, scale, S, max_seq_len=None):
     guard = 256
     out = torch.full((B * Hq * D + 2 * guard,), -1, dtype=torch.int16, device="cuda")
     mlen = int(max(op["seq_lens"])) if max_seq_len is None else max_seq_len
-    segs = S or L.migemm_attention_segments(B, Hkv, mlen)
+    segs = S or L.migemm_attention_segments(B, Hq, Hkv, mlen)
     need = L.migemm_attention_workspace_bytes(B, Hq, D, segs)
     ws = torch.empty(max(need, 16), dtype=torch.uint8, device="cuda")
     code = L.attention_decode_bf16(dQ.data_ptr(), dK.data_ptr(), dV.data_ptr(), bt.data_ptr(),
