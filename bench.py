@@ -54,6 +54,9 @@ def parse():
     p.add_argument("--no-cpu-baseline", action="store_true")
     p.add_argument("--cpu-seconds", type=float, default=12.0,
                    help="target CPU time of the oracle sample")
+    p.add_argument("--cpu-all", action="store_true",
+                   help="CPU baseline only: time the oracle on every workload (full or sampled) "
+                        "and print one JSON line per workload; uses no GPU")
     p.add_argument("--copy-calibration", action="store_true",
                    help="only run a plain 1 GiB device-to-device copy 3 times (the known-size "
                         "reference for scaling FETCH_SIZE / WRITE_SIZE counters) and exit")
@@ -125,12 +128,73 @@ def cpu_baseline(A, B, M, N, K, target_s):
                       "(K = 16384 multiply-adds each, FP64 accumulation)" % n}
 
 
+def cpu_all():
+    """The oracle timed on every workload: full where it finishes in seconds
+    (512^3 GEMM, the GEMV at n = 1, 4, 16, decode attention at 8K-32K
+    tokens), else on the 4096 sampled outputs of the parity tests, with the
+    full-size time extrapolated from the sampled rate."""
+    import oracle
+    import synth
+    from bf16_gemm_decode_amd import roofline as rf
+    cores = int(os.environ.get("OMP_NUM_THREADS", len(os.sched_getaffinity(0))))
+
+    def line(**kw):
+        kw["cores"] = cores
+        kw["kind"] = "oracle"
+        print(json.dumps(kw), flush=True)
+
+    for name in ("gemm_512_f16", "gemm_8192x8192x16384_f16", "gemm_5000x3000x4100_bf16",
+                 "prefill_4096x34816x5120_bf16"):
+        w = synth.WORKLOADS[name]
+        M, N, K = w["M"], w["N"], w["K"]
+        A, B = synth.workload_operands(name)
+        if M * N * K <= 1 << 28:
+            t0 = time.perf_counter()
+            oracle.gemm(A, B, M, N, K, w["fmt"])
+            dt = time.perf_counter() - t0
+            line(workload=name, sample="full", seconds=round(dt, 4),
+                 GFLOPs=round(rf.gemm_flop(M, N, K) / dt / 1e9, 3))
+        else:
+            idx = synth.sample_indices(M, N, w["seed"])
+            t0 = time.perf_counter()
+            oracle.gemm_sampled(A, B, M, N, K, idx, w["fmt"])
+            dt = time.perf_counter() - t0
+            rate = 2.0 * K * idx.size / dt
+            line(workload=name, sample="%d sampled outputs" % idx.size, seconds=round(dt, 4),
+                 GFLOPs=round(rate / 1e9, 3),
+                 extrapolated_full_seconds=round(rf.gemm_flop(M, N, K) / rate, 1))
+    wv = synth.WORKLOADS["gemv_34816x5120_bf16"]
+    for n in (1, 4, 16):
+        W, X = synth.gemv_operands(wv["M"], wv["K"], n, seed=wv["seed"])
+        t0 = time.perf_counter()
+        oracle.gemv(W, X, wv["M"], wv["K"], n)
+        dt = time.perf_counter() - t0
+        line(workload="gemv_34816x5120_bf16", n=n, sample="full", seconds=round(dt, 4),
+             GBps=round(rf.gemv_bytes(wv["M"], wv["K"], n) / dt / 1e9, 3))
+    wa = synth.WORKLOADS["attention_decode_16q4kv_d256_bf16"]
+    for L in wa["lengths"]:
+        op = synth.attention_operands(1, wa["Hq"], wa["Hkv"], wa["D"], [L], wa["block_size"],
+                                      seed=wa["seed"])
+        t0 = time.perf_counter()
+        oracle.attention(op["Q"], op["K"], op["V"], op["block_table"], op["seq_lens"], 1,
+                         wa["Hq"], wa["Hkv"], wa["D"], wa["block_size"], op["max_blocks"],
+                         1.0 / wa["D"] ** 0.5)
+        dt = time.perf_counter() - t0
+        line(workload="attention_decode_16q4kv_d256_bf16", B=1, L=L, sample="full",
+             seconds=round(dt, 4),
+             GBps=round(rf.attention_bytes([L], wa["Hq"], wa["Hkv"], wa["D"], wa["block_size"])
+                        / dt / 1e9, 3))
+
+
 def main():
     args = parse()
     if args.gpus != 1:
         print("bench.py measures one GPU: the path runs on a single MI355X and has no "
               "multi-GPU mode (--gpus %d requested)" % args.gpus, file=sys.stderr)
         sys.exit(2)
+    if args.cpu_all:
+        cpu_all()
+        return
     import numpy as np
     import torch
 
