@@ -69,10 +69,12 @@ int plan_gemm(int dtype, const uint16_t *A, const uint16_t *B, const uint16_t *C
         // k-major A: the full-line tiles only, 16-byte rows of A and B
         if (!wide) return MIGEMM_ERR_ALIGN;
         if (tile == TILE_AUTO) {
-            tile = N <= kSkinnyMaxTokens ? TILE_SKINNY
+            tile = N <= kSkinnyAutoMax ? TILE_SKINNY
+                   : N <= kBatchAutoMax ? TILE_BATCH
                    : cdiv(M, 256) * cdiv(N, 256) >= 512 ? TILE_256x256_FL8
                                                         : TILE_256x128_FL;
-        } else if (tile < TILE_256x256_FL || (tile == TILE_SKINNY && N > kSkinnyMaxTokens)) {
+        } else if (tile < TILE_256x256_FL || (tile == TILE_SKINNY && N > kSkinnyMaxTokens) ||
+                   (tile == TILE_BATCH && N > kBatchMaxTokens)) {
             return MIGEMM_ERR_CONFIG;
         }
     } else if (tile == TILE_AUTO) {
@@ -84,7 +86,7 @@ int plan_gemm(int dtype, const uint16_t *A, const uint16_t *B, const uint16_t *C
             tile = TILE_256x128;
         else
             tile = TILE_128x128;
-    } else if (tile == TILE_SKINNY) {
+    } else if (tile == TILE_SKINNY || tile == TILE_BATCH) {
         return MIGEMM_ERR_CONFIG;   // only with a k-major A (gemm_tn_ex)
     } else if (tile != TILE_128x128 && !wide) {
         return MIGEMM_ERR_CONFIG;   // the 256-row tiles load only 16-byte vectors
@@ -92,6 +94,7 @@ int plan_gemm(int dtype, const uint16_t *A, const uint16_t *B, const uint16_t *C
     L.tile = tile;
     int bm = kTileShapes[tile].bm, bn = kTileShapes[tile].bn;
     if (tile == TILE_SKINNY) bn = N <= 4 ? 4 : 8;
+    if (tile == TILE_BATCH) bn = batch_tile_n(N);
     const int64_t pm = cdiv(M, bm), pn = cdiv(N, bn);
     if (pm * pn > 0x7fffffff) return MIGEMM_ERR_SIZE;
     L.num_pid_m = (int)(pm ? pm : 1);
@@ -146,11 +149,12 @@ int gemm_tn_ex(int dtype, const uint16_t *At, const uint16_t *B, uint16_t *C, in
     bool launch;
     int rc = plan_gemm(dtype, At, B, C, M, N, K, tile, group_m, xcd_remap, L, launch, true);
     if (rc != MIGEMM_OK || !launch) return rc;
-    if (L.tile == TILE_SKINNY) {
+    if (L.tile == TILE_SKINNY || L.tile == TILE_BATCH) {
         // C(m,n) = sum_k At[k + m*K] B[k + n*K] is Y = X W^T with W = At,
-        // X = B, Y = C, all row-major: the skinny kernel's contract
+        // X = B, Y = C, all row-major: the skinny and batch kernels' contract
         SkinnyLaunch S{dtype, At, B, C, M, K, N, L.c_vec};
-        return finish(skinny_launch(S, (hipStream_t)stream), stream);
+        return finish((L.tile == TILE_SKINNY ? skinny_launch : batch_launch)(S, (hipStream_t)stream),
+                      stream);
     }
     return finish(gemm_launch(L, (hipStream_t)stream), stream);
 }
@@ -186,6 +190,21 @@ static int plan_for(int dtype, const uint16_t *A, const uint16_t *B, const uint1
         plan->vec_b = L.vec_b;
         plan->grid = launch ? L.grid : 0;
         plan->lds_bytes = 0;
+        plan->tile = L.tile;
+        plan->a_kmajor = 1;
+        return rc;
+    }
+    if (L.tile == TILE_BATCH) {
+        plan->tile_m = 64;                      // 4 waves x 16 rows
+        plan->tile_n = batch_tile_n(N);
+        plan->tile_k = 128;
+        plan->waves = 4;
+        plan->group_m = 1;
+        plan->xcd_remap = 0;
+        plan->vec_a = L.vec_a;
+        plan->vec_b = L.vec_b;
+        plan->grid = launch ? L.grid : 0;
+        plan->lds_bytes = batch_lds_bytes(N);
         plan->tile = L.tile;
         plan->a_kmajor = 1;
         return rc;
@@ -235,12 +254,14 @@ int gemv_bf16_ex(const uint16_t *W, const uint16_t *X, uint16_t *Y, int M, int K
     const bool vec = (K % 8 == 0 && (uintptr_t)W % 16 == 0 && (uintptr_t)X % 16 == 0);
     if (rows_per_block == 0 && vec && n >= kSkinnyMinTokens) {
         // Y = X W^T is gemm_tn with At = W, B = X, C = Y (all row-major):
-        // up to kSkinnyMaxTokens tokens on the 4x4x4 MFMA kernel, more on
-        // the full-line 256x128 tile (measured faster from 16 tokens on)
-        if (n > kSkinnyMaxTokens)
+        // up to kSkinnyAutoMax tokens on the 4x4x4 MFMA kernel, up to
+        // kBatchAutoMax on the 16x16x32 batch kernel, more on the
+        // full-line 256x128 tile
+        if (n > kBatchAutoMax)
             return gemm_tn_ex(DT_BF16, W, X, Y, M, n, K, TILE_256x128_FL, 0, 1, stream);
         SkinnyLaunch S{DT_BF16, W, X, Y, M, K, n, (M % 4 == 0 && (uintptr_t)Y % 8 == 0) ? 1 : 0};
-        return finish(skinny_launch(S, (hipStream_t)stream), stream);
+        return finish((n > kSkinnyAutoMax ? batch_launch : skinny_launch)(S, (hipStream_t)stream),
+                      stream);
     }
 
     GemvLaunch L{};

@@ -1,0 +1,216 @@
+// batch.hip -- Y = X W^T for a decode batch of 9 .. 128 token rows on the
+// 16x16x32 MFMA, streaming W from HBM once.
+//
+// The product of the DCU decode page (forum.sourcefind.cn db785961), section
+// 6.1: W row-major [M, K], X row-major [n, K], Y row-major [n, M], FP32
+// accumulation, one rounding.  With a few dozen tokens the work per W element
+// is still small (2n FLOP per 2 bytes), so the kernel is built to stream W at
+// HBM speed with enough MFMA throughput to spare:
+//
+//  * A workgroup of 4 waves owns 64 rows of W (16 per wave) and a block of up
+//    to 16*NTT tokens; K is walked in chunks of 128.
+//  * W is read as whole 128-byte lines: each load instruction covers 8 rows x
+//    128 bytes (lane l: row l/8, bytes 16*(l%8)); a wave's 16 rows x 128 k of
+//    a chunk are 4 such loads, non-temporal, U chunks in flight in
+//    registers.  (Loads of 64 bytes per row, the A operand's own shape,
+//    stream W at two thirds of this rate.)  Each chunk goes through a
+//    wave-private 4 KB LDS area -- row r's 16-byte piece x at
+//    r*256 + 16*(x ^ r), so the line writes and the operand reads both spread
+//    over all banks -- and comes back as A operands of v_mfma_f32_16x16x32
+//    (lane l: row l%16, k 32*j + 8*(l/16) .. +7).
+//  * The chunk of X (the block's tokens x 128 k) is staged once per
+//    workgroup in LDS, double-buffered, token rows padded to 272 bytes so the
+//    16 rows a B-operand read touches fall in distinct banks; each wave reads
+//    its B operands (token l%16, k 32*j + 8*(l/16)) with ds_read_b128.
+//  * One barrier per chunk; X is fetched from L2 two chunks ahead, into
+//    alternating staging registers, ahead of the W loads issued with it.
+//  * The chunk count is rounded up to a multiple of U; chunks past K (and k
+//    past K inside the last real chunk) read as zero (from a zero block), rows past M are
+//    clamped on load and never stored, tokens past n read as zero and are
+//    never stored.
+#include "common.hpp"
+#include "kernels.hpp"
+
+namespace migemm {
+
+namespace {
+
+constexpr int kKC = 128;                  // k per chunk
+constexpr int kXRow = kKC * 2 + 16;       // LDS bytes per staged token row
+
+// 16 zero bytes in device memory.  A masked lane loads from here instead of
+// selecting zero after its load: a select placed on the loaded value makes
+// the compiler wait for that load wherever it puts the select.
+__device__ const uint16_t kZeros[8] = {0, 0, 0, 0, 0, 0, 0, 0};
+
+// 16-byte loads through a global-address-space pointer (a select between a
+// kernel argument and kZeros would otherwise leave a generic pointer and a
+// flat load, which also counts against the LDS counter)
+typedef const __attribute__((address_space(1))) u32x4 *gptr16;
+__device__ inline u32x4 load16(const void *p) { return *(gptr16)p; }
+__device__ inline u32x4 load16_nt(const void *p) { return __builtin_nontemporal_load((gptr16)p); }
+
+template <int DT>
+__device__ inline void mfma_16x16x32(f32x4 &acc, u32x4 a, u32x4 b)
+{
+    if constexpr (DT == DT_F16)
+        acc = __builtin_amdgcn_mfma_f32_16x16x32_f16(__builtin_bit_cast(f16x8, a),
+                                                     __builtin_bit_cast(f16x8, b), acc, 0, 0, 0);
+    else
+        acc = __builtin_amdgcn_mfma_f32_16x16x32_bf16(__builtin_bit_cast(bf16x8, a),
+                                                      __builtin_bit_cast(bf16x8, b), acc, 0, 0, 0);
+}
+
+}  // namespace
+
+template <int DT, int NTT, int U>
+__global__ void __launch_bounds__(256)
+batch_kernel(const uint16_t *__restrict__ W, const uint16_t *__restrict__ X,
+             uint16_t *__restrict__ Y, int M, int K, int n, int y_vec)
+{
+    constexpr int XP = NTT;                       // 16-byte X pieces per thread and chunk
+    __shared__ __attribute__((aligned(16))) uint8_t xs[2][NTT * 16][kXRow];
+    __shared__ __attribute__((aligned(16))) uint8_t ws[4][16 * 256];   // per wave
+
+    const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
+    const int g = lane >> 4, r16 = lane & 15;
+    const int row0 = blockIdx.x * 64 + wave * 16;
+    const int tok0 = blockIdx.y * (NTT * 16);
+    const int chunks = (K + kKC - 1) / kKC;
+    const int padded = (chunks + U - 1) / U * U;
+
+    // W loads: instruction 2h + q reads rows 8h + l/8 (clamped) at k
+    // 64q + 8*(l%8) of the chunk; piece x = 8q + l%8 of row rw
+    const int lr = lane >> 3, lc = lane & 7;
+    const uint16_t *wrow0 = W + (size_t)min(row0 + lr, M - 1) * K;
+    const uint16_t *wrow1 = W + (size_t)min(row0 + 8 + lr, M - 1) * K;
+    auto load_w = [&](int c, u32x4 (&w)[4]) {
+#pragma unroll
+        for (int i = 0; i < 4; ++i) {
+            const int k = c * kKC + 64 * (i & 1) + 8 * lc;
+            w[i] = load16_nt(k < K ? (i < 2 ? wrow0 : wrow1) + k : kZeros);
+        }
+    };
+    uint8_t *wsw = ws[wave];
+    // write a chunk's 4 loads into the wave's area, read back the 4 A operands
+    auto relayout_w = [&](const u32x4 (&w)[4], u32x4 (&a)[4]) {
+#pragma unroll
+        for (int i = 0; i < 4; ++i) {
+            const int rw = 8 * (i >> 1) + lr, x = 8 * (i & 1) + lc;
+            *(u32x4 *)(wsw + rw * 256 + 16 * (x ^ rw)) = w[i];
+        }
+        // the area is private to the wave and LDS runs a wave's accesses in
+        // order; the wait only keeps the compiler from reordering
+        __builtin_amdgcn_s_waitcnt(0xc07f);      // lgkmcnt(0)
+#pragma unroll
+        for (int j = 0; j < 4; ++j) {
+            const int x = 4 * j + g;
+            a[j] = *(const u32x4 *)(wsw + r16 * 256 + 16 * (x ^ r16));
+        }
+    };
+    auto load_x = [&](int c, u32x4 (&xr)[XP]) {
+#pragma unroll
+        for (int p = 0; p < XP; ++p) {
+            const int e = p * 256 + tid;
+            const int t = e >> 4, ch = e & 15;
+            const int k = c * kKC + ch * 8;
+            const bool ok = tok0 + t < n && k < K;
+            xr[p] = load16(ok ? X + (size_t)(tok0 + t) * K + k : kZeros);
+        }
+    };
+    auto store_x = [&](int buf, const u32x4 (&xr)[XP]) {
+#pragma unroll
+        for (int p = 0; p < XP; ++p) {
+            const int e = p * 256 + tid;
+            *(u32x4 *)&xs[buf][e >> 4][(e & 15) * 16] = xr[p];
+        }
+    };
+
+    f32x4 acc[NTT];
+#pragma unroll
+    for (int t = 0; t < NTT; ++t) acc[t] = f32x4{0.f, 0.f, 0.f, 0.f};
+
+    // Chunk c's X sits in LDS buffer c & 1 and, before that, in staging
+    // registers xr[c & 1] (U is even, so c & 1 == u & 1 is static).  Per
+    // chunk: W from w[u] through the wave's LDS area into A operands; the X
+    // loads of chunk c + 2 and the W loads of chunk c + U (into the freed
+    // w[u]); the MFMAs; the store of chunk c + 1's X (fetched a chunk ago,
+    // ahead of the previous W loads, so waiting for it leaves the W loads in
+    // flight); one barrier.
+    static_assert(U % 2 == 0, "U even");
+    u32x4 w[U][4];
+    u32x4 xr[2][XP];
+    load_x(0, xr[0]);
+    load_x(1, xr[1]);
+#pragma unroll
+    for (int u = 0; u < U; ++u) load_w(u, w[u]);
+    store_x(0, xr[0]);
+    __syncthreads();
+
+    for (int c0 = 0; c0 < padded; c0 += U) {
+#pragma unroll
+        for (int u = 0; u < U; ++u) {
+            const int c = c0 + u, buf = u & 1;
+            u32x4 a[4];
+            relayout_w(w[u], a);
+            load_x(c + 2, xr[buf]);
+            load_w(c + U, w[u]);
+#pragma unroll
+            for (int j = 0; j < 4; ++j)
+#pragma unroll
+                for (int t = 0; t < NTT; ++t) {
+                    const u32x4 b = *(const u32x4 *)&xs[buf][t * 16 + r16][(32 * j + 8 * g) * 2];
+                    mfma_16x16x32<DT>(acc[t], a[j], b);
+                }
+            store_x(buf ^ 1, xr[buf ^ 1]);
+            __syncthreads();
+        }
+    }
+
+    // lane (g, r16) holds rows 4g .. 4g+3 of the wave's 16 for token r16 of
+    // each 16-token tile
+    const int m = row0 + 4 * g;
+    if (m >= M) return;
+#pragma unroll
+    for (int t = 0; t < NTT; ++t) {
+        const int tok = tok0 + t * 16 + r16;
+        if (tok >= n) continue;
+        uint16_t *dst = Y + (size_t)tok * M + m;
+        if (y_vec && m + 3 < M) {
+            u16x4 v = {to_out<DT>(acc[t][0]), to_out<DT>(acc[t][1]), to_out<DT>(acc[t][2]),
+                       to_out<DT>(acc[t][3])};
+            *(u16x4 *)dst = v;
+        } else {
+#pragma unroll
+            for (int i = 0; i < 4; ++i)
+                if (m + i < M) dst[i] = to_out<DT>(acc[t][i]);
+        }
+    }
+}
+
+template <int DT, int NTT>
+static hipError_t launch_ntt(const SkinnyLaunch &L, hipStream_t s)
+{
+    constexpr int U = 4;
+    const dim3 grid((unsigned)((L.M + 63) / 64), (unsigned)((L.n + NTT * 16 - 1) / (NTT * 16)));
+    hipLaunchKernelGGL((batch_kernel<DT, NTT, U>), grid, dim3(256), 0, s, L.W, L.X, L.Y, L.M, L.K,
+                       L.n, L.y_vec);
+    return hipGetLastError();
+}
+
+template <int DT>
+static hipError_t launch_dt(const SkinnyLaunch &L, hipStream_t s)
+{
+    if (L.n <= 16) return launch_ntt<DT, 1>(L, s);
+    if (L.n <= 32) return launch_ntt<DT, 2>(L, s);
+    if (L.n <= 64) return launch_ntt<DT, 4>(L, s);
+    return launch_ntt<DT, 8>(L, s);
+}
+
+hipError_t batch_launch(const SkinnyLaunch &L, hipStream_t s)
+{
+    if (L.n < 1 || L.n > kBatchMaxTokens) return hipErrorInvalidValue;
+    return L.dtype == DT_F16 ? launch_dt<DT_F16>(L, s) : launch_dt<DT_BF16>(L, s);
+}
+
+}  // namespace migemm

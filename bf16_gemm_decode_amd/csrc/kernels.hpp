@@ -22,6 +22,7 @@ enum GemmTile {
     TILE_64x64_SK = 12,         // skinny: 64x64, 2 waves along M, 3 WG per CU
     TILE_128x128_SK = 13,       // 128x128, 4 waves as 2x2, full-line rings
     TILE_SKINNY = 14,           // few columns: W straight into 4x4x4 MFMA registers (skinny.hip)
+    TILE_BATCH = 15,            // 9..128 columns: W into 16x16x32 MFMA registers, X in LDS (batch.hip)
     TILE_COUNT
 };
 
@@ -48,6 +49,7 @@ constexpr TileShape kTileShapes[TILE_COUNT] = {
     {64, 64, 32, 4, 2, 2},
     {128, 128, 32, 4, 4, 3},
     {32, 64, 32, 0, 4, 0},
+    {64, 128, 128, 0, 4, 0},
 };
 
 // The full-line tiles with A k-major: stages = A ring stages of 64 k.
@@ -67,6 +69,7 @@ constexpr TileShape kTileShapesKmajorA[TILE_COUNT] = {
     {64, 64, 32, 4, 2, 2},
     {128, 128, 32, 4, 4, 3},
     {32, 64, 32, 0, 4, 0},
+    {64, 128, 128, 0, 4, 0},
 };
 
 constexpr int tile_lds_bytes(const TileShape &t, bool a_kmajor = false)
@@ -106,6 +109,15 @@ hipError_t gemv_launch(const GemvLaunch &L, hipStream_t stream);
 // Y = X W^T on MFMA for n <= kSkinnyMaxTokens token rows (skinny.hip).
 constexpr int kSkinnyMaxTokens = 8;
 constexpr int kSkinnyMinTokens = 3;    // the automatic GEMV switches to MFMA from here
+// Y = X W^T on the 16x16x32 MFMA with X staged in LDS (batch.hip), for up
+// to kBatchMaxTokens tokens.
+constexpr int kBatchMaxTokens = 128;
+// Automatic choice (measured on W 34816 x 5120): the 4x4x4 kernel up to 4
+// tokens, the batch kernel up to 32 (its 64- and 128-token blocks hold too
+// much LDS and too many registers per workgroup to keep W streaming), then
+// the GEMM's 256x128 tile.
+constexpr int kSkinnyAutoMax = 4;
+constexpr int kBatchAutoMax = 32;
 struct SkinnyLaunch {
     int dtype;
     const uint16_t *W, *X;        // W row-major [M, K], X row-major [n, K]
@@ -115,6 +127,12 @@ struct SkinnyLaunch {
 };
 
 hipError_t skinny_launch(const SkinnyLaunch &L, hipStream_t stream);
+hipError_t batch_launch(const SkinnyLaunch &L, hipStream_t stream);
+// token columns of one batch-kernel workgroup for n tokens (16, 32, 64, 128)
+constexpr int batch_tile_n(int n) { return n <= 16 ? 16 : n <= 32 ? 32 : n <= 64 ? 64 : 128; }
+// its LDS bytes: two staged chunks of tile_n token rows of 272 bytes, and
+// the 4 waves' 4 KB areas that re-lay W out
+constexpr int batch_lds_bytes(int n) { return 2 * batch_tile_n(n) * (128 * 2 + 16) + 4 * 4096; }
 
 // Decode attention over a paged KV cache, split into S segments (attention.hip).
 struct AttentionLaunch {

@@ -165,7 +165,7 @@ skinny_kernel(const uint16_t *__restrict__ W, const uint16_t *__restrict__ X,
 template <int DT, int TG>
 static hipError_t launch_tg(const SkinnyLaunch &L, hipStream_t s)
 {
-    constexpr int RW = 2, U = 8;
+    constexpr int RW = 2, U = 4;
     const unsigned grid = (unsigned)((L.M + 16 * RW - 1) / (16 * RW));   // 4 waves x 4*RW rows
     hipLaunchKernelGGL((skinny_kernel<DT, RW, TG, U>), dim3(grid), dim3(256), 0, s,
                        L.W, L.X, L.Y, L.M, L.K, L.n, L.y_vec);

@@ -83,10 +83,12 @@ int gemm_bf16(const uint16_t *A, const uint16_t *B, uint16_t *C,
  * K == 0 writes +0.0 to Y.  Errors as for the GEMM (Y must not overlap W, X).
  * n may be any positive value.  n <= 2 (or K not a multiple of 8, or W, X
  * not 16-byte aligned) runs the row-blocked vector kernel; from 3 tokens on,
- * with 16-byte rows, the multiply-adds run on MFMA: up to 8 tokens on the
- * 4x4x4 MFMA with W streamed straight into operand registers, beyond that
- * as gemm_tn_bf16 on the 256x128 full-line tile.  gemv_bf16_ex with a
- * non-zero rows_per_block always runs the vector kernel.
+ * with 16-byte rows, the multiply-adds run on MFMA: up to 4 tokens on the
+ * 4x4x4 MFMA with W streamed straight into operand registers, up to 32 on
+ * the 16x16x32 MFMA with W read as whole cache lines and the token block of
+ * X staged in LDS (tile 15 below), beyond that as gemm_tn_bf16 on the
+ * 256x128 full-line tile.  gemv_bf16_ex with a non-zero rows_per_block always runs
+ * the vector kernel.
  */
 int gemv_bf16(const uint16_t *W, const uint16_t *X, uint16_t *Y,
               int M, int K, int n, void *stream);
@@ -154,7 +156,10 @@ size_t migemm_attention_workspace_bytes(int B, int Hq, int D, int num_segments);
  *            few columns (decode batches): 11 = 64x32 and 12 = 64x64 (2 waves,
  *            several workgroups per CU), 13 = 128x128 (4 waves as 2x2), all
  *            with tile 7's full-line B ring; 14 = the skinny 4x4x4 MFMA kernel
- *            of gemv_bf16 (gemm_tn_* only, N <= 8).
+ *            of gemv_bf16 (gemm_tn_* only, N <= 8); 15 = the batch kernel
+ *            of gemv_bf16 (gemm_tn_* only, N <= 128: 64 rows x 16..128
+ *            columns per workgroup, 16x16x32 MFMA, A read as whole lines and
+ *            re-laid out through LDS, B staged in LDS).
  *            All step K by 32; tiles other than 3 need M and K to be multiples of 8 and A, B
  *            16-byte aligned (else MIGEMM_ERR_CONFIG);
  *   group_m: width of the grouped tile ordering (FlagGems "Hygon 优化" page,
@@ -175,8 +180,10 @@ int gemm_ex(int dtype, const uint16_t *A, const uint16_t *B, uint16_t *C,
  * DCU decode page's Y = X W^T (section 6.1) for a batch of N token rows,
  * with Y row-major [N, M] -- the GEMV's own layout.  Same argument checks,
  * ownership and completion rules as gemm_f16 / gemm_bf16.  Runs on the
- * full-line tiles only: tile 0 (automatic) or 7 .. 13 (A takes B's 64-k
- * ring layout; MIGEMM_ERR_CONFIG for other tiles).  K must be a
+ * full-line tiles only: tile 0 (automatic: 14 for N <= 4, 15 for
+ * N <= 32, else 10 or 9) or 7 .. 15 (A takes B's 64-k ring layout;
+ * MIGEMM_ERR_CONFIG for other tiles, and for 14 with N > 8 or 15 with
+ * N > 128).  K must be a
  * multiple of 8 and At, B 16-byte aligned (else MIGEMM_ERR_ALIGN).
  */
 int gemm_tn_f16(const uint16_t *At, const uint16_t *B, uint16_t *C,

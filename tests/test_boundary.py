@@ -100,14 +100,25 @@ def test_tn_plan_and_errors():
     code, p = binding.gemm_plan(1, P, P + 2 ** 30, P + 2 ** 31, 34816, 200, 5120, a_kmajor=True)
     assert code == 0 and (p["tile_m"], p["tile_n"]) == (256, 128) and p["grid"] == 272
     # the skinny tile: few columns only, and only with a k-major A
-    code, p = binding.gemm_plan(1, P, P + 2 ** 30, P + 2 ** 31, 34816, 8, 5120, a_kmajor=True)
+    code, p = binding.gemm_plan(1, P, P + 2 ** 30, P + 2 ** 31, 34816, 8, 5120, 14, a_kmajor=True)
     assert code == 0 and (p["tile"], p["tile_m"], p["tile_n"], p["waves"], p["grid"]) == (14, 32, 8, 4, 1088)
-    assert binding.gemm_plan(1, P, P + 2 ** 30, P + 2 ** 31, 34816, 5, 5120, a_kmajor=True)[1]["tile_n"] == 8
-    assert binding.gemm_plan(1, P, P + 2 ** 30, P + 2 ** 31, 34816, 9, 5120, a_kmajor=True)[1]["tile"] != 14
+    assert binding.gemm_plan(1, P, P + 2 ** 30, P + 2 ** 31, 34816, 5, 5120, 14, a_kmajor=True)[1]["tile_n"] == 8
+    code, p = binding.gemm_plan(1, P, P + 2 ** 30, P + 2 ** 31, 34816, 4, 5120, a_kmajor=True)
+    assert code == 0 and (p["tile"], p["tile_n"]) == (14, 4)          # automatic up to 4 columns
+    assert binding.gemm_plan(1, P, P + 2 ** 30, P + 2 ** 31, 34816, 5, 5120, a_kmajor=True)[1]["tile"] == 15
     assert L.gemm_tn_ex(0, P, P + 0x100000, P + 0x200000, 64, 9, 64, 14, 0, 1, None) == -5
     assert L.gemm_ex(0, P, P + 0x100000, P + 0x200000, 64, 16, 64, 14, 0, 1, None) == -5
+    # the batch tile: 9 .. 128 columns, 64 rows per workgroup, token blocks of 16 .. 128
+    for n, tn in ((9, 16), (16, 16), (17, 32), (33, 64), (64, 64), (65, 128), (128, 128)):
+        code, p = binding.gemm_plan(1, P, P + 2 ** 30, P + 2 ** 31, 34816, n, 5120, 15, a_kmajor=True)
+        assert code == 0 and (p["tile"], p["tile_m"], p["tile_n"], p["tile_k"], p["waves"]) == (15, 64, tn, 128, 4)
+        assert p["grid"] == 544 and p["lds_bytes"] == 2 * tn * 272 + 4 * 4096
+    assert binding.gemm_plan(1, P, P + 2 ** 30, P + 2 ** 31, 34816, 32, 5120, a_kmajor=True)[1]["tile"] == 15
+    assert binding.gemm_plan(1, P, P + 2 ** 30, P + 2 ** 31, 34816, 33, 5120, a_kmajor=True)[1]["tile"] == 9
+    assert L.gemm_tn_ex(0, P, P + 0x100000, P + 0x200000, 64, 129, 64, 15, 0, 1, None) == -5
+    assert L.gemm_ex(0, P, P + 0x100000, P + 0x200000, 64, 16, 64, 15, 0, 1, None) == -5
     # only the full-line tiles take a k-major A
-    for tile in (1, 2, 3, 4, 5, 6, 15):
+    for tile in (1, 2, 3, 4, 5, 6, 16):
         assert L.gemm_tn_ex(0, P, P + 0x100000, P + 0x200000, 64, 64, 64, tile, 0, 1, None) == -5
     # K not a multiple of 8, or a misaligned operand: no 16-byte rows
     assert L.gemm_tn_ex(0, P, P + 0x100000, P + 0x200000, 64, 64, 60, 7, 0, 1, None) == -4

@@ -97,6 +97,31 @@ def test_skinny_matches_exact_integers():
         assert np.array_equal(got, want), fmt
 
 
+@pytest.mark.parametrize("fmt", FMTS)
+def test_batch_tile_token_blocks_and_ragged_edges(fmt):
+    # tile 15 (W straight into 16x16x32 MFMA registers, the token block of B
+    # staged in LDS, 128-wide k chunks, chunk count padded to a multiple of
+    # 4): every token-block width (16, 32, 64, 128) with ragged token counts,
+    # rows off the 64-row workgroup block, K tails inside a chunk, K shorter
+    # than one chunk, padded and unpadded chunk counts
+    for (M, N, K) in [(100, 9, 64), (37, 16, 40), (64, 17, 520), (300, 32, 264), (260, 33, 136),
+                      (96, 64, 8), (1000, 65, 1000), (33, 100, 24), (130, 128, 1160),
+                      (9, 128, 5120), (2051, 40, 5120), (65, 1, 128)]:
+        print("case batch", M, N, K, fmt, flush=True)
+        _tn_case(M, N, K, fmt, seed=2000 + M + N + K, tile=15)
+
+
+def test_batch_matches_exact_integers():
+    rng = np.random.default_rng(29)
+    M, N, K = 520, 77, 1032
+    for fmt in FMTS:
+        At = synth.to_bits(synth.small_ints(rng, M * K, -3, 3), fmt)
+        B = synth.to_bits(synth.small_ints(rng, K * N, -3, 3), fmt)
+        want = oracle.gemm(kmajor_to_colmajor(At, M, K), B, M, N, K, fmt).bits
+        got, _, _ = gemm_tn_gpu(At, B, M, N, K, fmt, tile=15)
+        assert np.array_equal(got, want), fmt
+
+
 def test_tn_is_the_decode_product_for_a_token_batch():
     # gemm_tn(At = W, B = X, C = Y) is Y = X W^T with W, X, Y row-major: the
     # GEMV's layout.  16 tokens of the decode shape: sampled entries against

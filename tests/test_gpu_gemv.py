@@ -60,10 +60,12 @@ def test_rows_per_block_bit_identical(n):
 
 
 def test_every_route_against_the_vector_kernel():
-    # the automatic routes (MFMA for n >= 3) and the vector kernel
+    # the automatic routes (4x4x4 MFMA for 3..8 tokens, the batch kernel for
+    # 9..128, the GEMM tile beyond) and the vector kernel
     # (rows_per_block given) both meet the oracle's bound at the decode width
     M, K = 2051, 5120
-    for n in (3, 6, 8, 12, 40):
+    for n in (3, 6, 8, 12, 40, 100, 129):
+        print("case route n", n, flush=True)
         W, X = synth.gemv_operands(M, K, n, seed=40 + n)
         ref = oracle.gemv(W, X, M, K, n)
         auto, g1, _ = gemv_gpu(W, X, M, K, n, 0)
