@@ -20,6 +20,7 @@ ERRORS = {0: "ok", -1: "negative dimension", -2: "null pointer with a non-zero e
           -5: "configuration not offered", -6: "dimension beyond the supported range"}
 
 F16, BF16 = 0, 1
+F8E4M3, F8E5M2, I8 = 2, 3, 4          # 8-bit inputs of gemm_tn_q_ex
 
 
 class MigemmError(RuntimeError):
@@ -54,6 +55,10 @@ SIGNATURES = {
     "gemm_tn_bf16": (_I, [_P, _P, _P, _I, _I, _I, _P]),
     "gemm_tn_ex": (_I, [_I, _P, _P, _P, _I, _I, _I, _I, _I, _I, _P]),
     "gemv_bf16_ex": (_I, [_P, _P, _P, _I, _I, _I, _I, _P]),
+    "gemm_tn_fp8_e4m3": (_I, [_P, _P, _P, _I, _I, _I, ctypes.c_float, _P]),
+    "gemm_tn_fp8_e5m2": (_I, [_P, _P, _P, _I, _I, _I, ctypes.c_float, _P]),
+    "gemm_tn_i8": (_I, [_P, _P, _P, _I, _I, _I, ctypes.c_float, _P]),
+    "gemm_tn_q_ex": (_I, [_I, _P, _P, _P, _I, _I, _I, ctypes.c_float, _I, _I, _I, _P]),
     "migemm_tile_coord": (_I, [_I64, _I64, _I64, _I64, _I64,
                                ctypes.POINTER(_I64), ctypes.POINTER(_I64)]),
     "migemm_gemm_plan_for": (_I, [_I, _P, _P, _P, _I, _I, _I, _I, _I, _I, ctypes.POINTER(Plan)]),

@@ -42,7 +42,18 @@ int plan_gemm(int dtype, const uint16_t *A, const uint16_t *B, const uint16_t *C
               bool a_kmajor = false)
 {
     launch = false;
-    if (dtype != DT_F16 && dtype != DT_BF16) return MIGEMM_ERR_CONFIG;
+    if (dtype < DT_F16 || dtype > DT_I8 || (dt_is_8bit(dtype) && !a_kmajor)) return MIGEMM_ERR_CONFIG;
+    const bool q8 = dt_is_8bit(dtype);
+    if (q8) {
+        // 8-bit elements: the kernels count K in 2-byte units; rows must be
+        // whole 16-byte pieces
+        if (K < 0) return MIGEMM_ERR_DIM;
+        if (K % 16) return MIGEMM_ERR_ALIGN;
+        K /= 2;
+        if (!(tile == TILE_AUTO || tile == TILE_256x128_FL || tile == TILE_256x256_FL8 ||
+              tile == TILE_128x128_SK))
+            return MIGEMM_ERR_CONFIG;
+    }
     if (tile < TILE_AUTO || tile >= TILE_COUNT || group_m < 0 || xcd_remap < 0 || xcd_remap > 1)
         return MIGEMM_ERR_CONFIG;
     if (M < 0 || N < 0 || K < 0) return MIGEMM_ERR_DIM;
@@ -65,7 +76,13 @@ int plan_gemm(int dtype, const uint16_t *A, const uint16_t *B, const uint16_t *C
     L.c_vec = (M % 4 == 0 && (uintptr_t)C % 8 == 0) ? 1 : 0;
     L.a_kmajor = a_kmajor ? 1 : 0;
     const bool wide = (L.vec_a == 8 && L.vec_b == 8);
-    if (a_kmajor) {
+    if (a_kmajor && q8) {
+        if (!wide) return MIGEMM_ERR_ALIGN;
+        if (tile == TILE_AUTO)
+            tile = cdiv(M, 256) * cdiv(N, 256) >= 512   ? TILE_256x256_FL8
+                   : cdiv(M, 256) * cdiv(N, 128) >= 256 ? TILE_256x128_FL
+                                                        : TILE_128x128_SK;
+    } else if (a_kmajor) {
         // k-major A: the full-line tiles only, 16-byte rows of A and B
         if (!wide) return MIGEMM_ERR_ALIGN;
         if (tile == TILE_AUTO) {
@@ -145,6 +162,7 @@ int gemm_bf16(const uint16_t *A, const uint16_t *B, uint16_t *C, int M, int N, i
 int gemm_tn_ex(int dtype, const uint16_t *At, const uint16_t *B, uint16_t *C, int M, int N, int K,
                int tile, int group_m, int xcd_remap, void *stream)
 {
+    if (dt_is_8bit(dtype)) return MIGEMM_ERR_CONFIG;   // gemm_tn_q_ex takes the scale
     GemmLaunch L;
     bool launch;
     int rc = plan_gemm(dtype, At, B, C, M, N, K, tile, group_m, xcd_remap, L, launch, true);
@@ -157,6 +175,37 @@ int gemm_tn_ex(int dtype, const uint16_t *At, const uint16_t *B, uint16_t *C, in
                       stream);
     }
     return finish(gemm_launch(L, (hipStream_t)stream), stream);
+}
+
+int gemm_tn_q_ex(int qtype, const void *At, const void *B, uint16_t *C, int M, int N, int K,
+                 float scale, int tile, int group_m, int xcd_remap, void *stream)
+{
+    if (!dt_is_8bit(qtype) || qtype > DT_I8) return MIGEMM_ERR_CONFIG;
+    GemmLaunch L;
+    bool launch;
+    int rc = plan_gemm(qtype, (const uint16_t *)At, (const uint16_t *)B, C, M, N, K, tile, group_m,
+                       xcd_remap, L, launch, true);
+    if (rc != MIGEMM_OK || !launch) return rc;
+    L.scale = scale;
+    return finish(gemm_launch(L, (hipStream_t)stream), stream);
+}
+
+int gemm_tn_fp8_e4m3(const uint8_t *At, const uint8_t *B, uint16_t *C, int M, int N, int K,
+                     float scale, void *stream)
+{
+    return gemm_tn_q_ex(DT_F8E4M3, At, B, C, M, N, K, scale, TILE_AUTO, 0, 1, stream);
+}
+
+int gemm_tn_fp8_e5m2(const uint8_t *At, const uint8_t *B, uint16_t *C, int M, int N, int K,
+                     float scale, void *stream)
+{
+    return gemm_tn_q_ex(DT_F8E5M2, At, B, C, M, N, K, scale, TILE_AUTO, 0, 1, stream);
+}
+
+int gemm_tn_i8(const int8_t *At, const int8_t *B, uint16_t *C, int M, int N, int K, float scale,
+               void *stream)
+{
+    return gemm_tn_q_ex(DT_I8, At, B, C, M, N, K, scale, TILE_AUTO, 0, 1, stream);
 }
 
 int gemm_tn_f16(const uint16_t *At, const uint16_t *B, uint16_t *C, int M, int N, int K, void *stream)
@@ -211,7 +260,7 @@ static int plan_for(int dtype, const uint16_t *A, const uint16_t *B, const uint1
     }
     plan->tile_m = t.bm;
     plan->tile_n = t.bn;
-    plan->tile_k = t.bk;
+    plan->tile_k = dt_is_8bit(dtype) ? 2 * t.bk : t.bk;   // in elements
     plan->waves = t.waves;
     plan->group_m = L.group_m;
     plan->xcd_remap = L.num_xcd > 1;

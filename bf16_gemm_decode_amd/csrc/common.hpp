@@ -16,7 +16,10 @@ typedef __attribute__((ext_vector_type(4))) unsigned int u32x4;
 
 #define MIGEMM_LDS __attribute__((address_space(3)))
 
-enum { DT_F16 = 0, DT_BF16 = 1 };
+// Element types: 16-bit (in and out), and 8-bit inputs (OCP FP8 E4M3, OCP
+// FP8 E5M2, INT8) whose GEMMs write BF16 of scale x accumulator.
+enum { DT_F16 = 0, DT_BF16 = 1, DT_F8E4M3 = 2, DT_F8E5M2 = 3, DT_I8 = 4 };
+constexpr bool dt_is_8bit(int dt) { return dt >= DT_F8E4M3; }
 
 // Offsets at or beyond a buffer descriptor's record count read as zero; this
 // value is beyond every record count the library builds (they are < 2^31).
@@ -47,6 +50,21 @@ __device__ inline unsigned short to_out(float x)
     } else {
         __bf16 h = (__bf16)x;
         return __builtin_bit_cast(unsigned short, h);
+    }
+}
+
+// The 16-bit output of one accumulator: 16-bit inputs round it to their own
+// format; 8-bit inputs write BF16 of scale x accumulator (an INT8
+// accumulator holds the bits of an int32; it is converted to FP32 first).
+template <int DT>
+__device__ inline unsigned short out16(float acc, float scale)
+{
+    if constexpr (!dt_is_8bit(DT)) {
+        return to_out<DT>(acc);
+    } else if constexpr (DT == DT_I8) {
+        return to_out<DT_BF16>((float)__builtin_bit_cast(int, acc) * scale);
+    } else {
+        return to_out<DT_BF16>(acc * scale);
     }
 }
 

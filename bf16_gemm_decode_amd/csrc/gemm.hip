@@ -93,13 +93,34 @@ __device__ inline void wait_vmcnt()
 // of rotating it through copies, and may still schedule these freely.  It
 // does not see the MFMA's result latency, so nothing but another MFMA may
 // read an accumulator until mfma_drain() has run.
+//
+// The 16-byte fragments are the same bytes for every element type; only the
+// instruction changes.  8-bit types: a fragment is 16 k of INT8 (one
+// v_mfma_i32_16x16x64_i8 takes the 16 bytes of every lane, 64 k) or two
+// 8-k halves of FP8 (two v_mfma_f32_16x16x32_{fp8,bf8} take bytes 0-7, then
+// 8-15).  A and B fragments pair the same bytes of the same lanes, so which
+// k a byte holds inside a step does not matter, and the 16x16 result layout
+// is the same for all of them.
 template <int DT>
 __device__ inline void mfma16x16x32(f32x4 &acc, u32x4 a, u32x4 b)
 {
-    if constexpr (DT == DT_F16)
+    typedef __attribute__((ext_vector_type(2))) unsigned u32x2;
+    if constexpr (DT == DT_F16) {
         asm("v_mfma_f32_16x16x32_f16 %0, %1, %2, %0" : "+a"(acc) : "v"(a), "v"(b));
-    else
+    } else if constexpr (DT == DT_BF16) {
         asm("v_mfma_f32_16x16x32_bf16 %0, %1, %2, %0" : "+a"(acc) : "v"(a), "v"(b));
+    } else if constexpr (DT == DT_I8) {
+        asm("v_mfma_i32_16x16x64_i8 %0, %1, %2, %0" : "+a"(acc) : "v"(a), "v"(b));
+    } else {
+        const u32x2 alo = {a[0], a[1]}, ahi = {a[2], a[3]}, blo = {b[0], b[1]}, bhi = {b[2], b[3]};
+        if constexpr (DT == DT_F8E4M3) {
+            asm("v_mfma_f32_16x16x32_fp8_fp8 %0, %1, %2, %0" : "+a"(acc) : "v"(alo), "v"(blo));
+            asm("v_mfma_f32_16x16x32_fp8_fp8 %0, %1, %2, %0" : "+a"(acc) : "v"(ahi), "v"(bhi));
+        } else {
+            asm("v_mfma_f32_16x16x32_bf8_bf8 %0, %1, %2, %0" : "+a"(acc) : "v"(alo), "v"(blo));
+            asm("v_mfma_f32_16x16x32_bf8_bf8 %0, %1, %2, %0" : "+a"(acc) : "v"(ahi), "v"(bhi));
+        }
+    }
 }
 
 // Wait states after the last MFMA before its results are read by other
@@ -461,8 +482,11 @@ __global__ void __launch_bounds__(WGM * WGN * 64)
 __attribute__((amdgpu_waves_per_eu(OCC, OCC)))
 gemm_fl_kernel(const uint16_t *__restrict__ A, const uint16_t *__restrict__ B,
                uint16_t *__restrict__ C, int M, int N, int K, int num_pid_m, int num_pid_n,
-               int group_m, int num_xcd, int c_vec)
+               int group_m, int num_xcd, int c_vec, float scale)
 {
+    // K counts 2-byte units: for 8-bit element types the caller passes half
+    // the element count, and each unit holds two elements.
+    static_assert(AK || !dt_is_8bit(DT), "8-bit types take a k-major A");
     constexpr int BK = 32;                        // sub-step = one MFMA k slice
     constexpr int NW = WGM * WGN;
     constexpr int TM = BM / WGM, TN = BN / WGN;
@@ -733,13 +757,13 @@ gemm_fl_kernel(const uint16_t *__restrict__ A, const uint16_t *__restrict__ B,
             if (n >= N) continue;
             uint16_t *dst = C + (size_t)n * M + m;
             if (c_vec && m + 3 < M) {
-                u16x4 v = {to_out<DT>(acc[i][j][0]), to_out<DT>(acc[i][j][1]),
-                           to_out<DT>(acc[i][j][2]), to_out<DT>(acc[i][j][3])};
+                u16x4 v = {out16<DT>(acc[i][j][0], scale), out16<DT>(acc[i][j][1], scale),
+                           out16<DT>(acc[i][j][2], scale), out16<DT>(acc[i][j][3], scale)};
                 *(u16x4 *)dst = v;
             } else {
 #pragma unroll
                 for (int r = 0; r < 4; ++r)
-                    if (m + r < M) dst[r] = to_out<DT>(acc[i][j][r]);
+                    if (m + r < M) dst[r] = out16<DT>(acc[i][j][r], scale);
             }
         }
     }
@@ -754,7 +778,7 @@ static hipError_t launch_fl(const GemmLaunch &L, hipStream_t stream)
     dim3 grid((unsigned)L.grid), block(WGM * WGN * 64);
     hipLaunchKernelGGL((gemm_fl_kernel<DT, AK, BM, BN, WGM, WGN, SA, SB, OC>), grid, block, 0, stream,
                        L.A, L.B, L.C, L.M, L.N, L.K, L.num_pid_m, L.num_pid_n, L.group_m,
-                       L.num_xcd, L.c_vec);
+                       L.num_xcd, L.c_vec, L.scale);
     return hipGetLastError();
 }
 
@@ -817,9 +841,30 @@ static hipError_t launch_dt(const GemmLaunch &L, hipStream_t s)
     return hipErrorInvalidValue;
 }
 
+// 8-bit inputs: the k-major full-line tiles 9 (256x128), 10 (256x256, 8
+// waves) and 13 (128x128); L.K is in 2-byte units.
+template <int DT>
+static hipError_t launch_q(const GemmLaunch &L, hipStream_t s)
+{
+    if (!L.a_kmajor) return hipErrorInvalidValue;
+    switch (L.tile) {
+    case TILE_256x128_FL: return launch_fl<DT, true, 256, 128, 4, 1, 3, 4>(L, s);
+    case TILE_256x256_FL8: return launch_fl<DT, true, 256, 256, 4, 2, 2, 3>(L, s);
+    case TILE_128x128_SK: return launch_fl<DT, true, 128, 128, 2, 2, 4, 3, 1>(L, s);
+    }
+    return hipErrorInvalidValue;
+}
+
 hipError_t gemm_launch(const GemmLaunch &L, hipStream_t stream)
 {
-    return L.dtype == DT_F16 ? launch_dt<DT_F16>(L, stream) : launch_dt<DT_BF16>(L, stream);
+    switch (L.dtype) {
+    case DT_F16: return launch_dt<DT_F16>(L, stream);
+    case DT_BF16: return launch_dt<DT_BF16>(L, stream);
+    case DT_F8E4M3: return launch_q<DT_F8E4M3>(L, stream);
+    case DT_F8E5M2: return launch_q<DT_F8E5M2>(L, stream);
+    case DT_I8: return launch_q<DT_I8>(L, stream);
+    }
+    return hipErrorInvalidValue;
 }
 
 }  // namespace migemm

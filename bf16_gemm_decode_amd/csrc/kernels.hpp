@@ -91,6 +91,7 @@ struct GemmLaunch {
     int c_vec;                    // 1: 8-byte stores of 4 rows are aligned
     int a_kmajor;                 // 1: A(m,k) = A[k + m*K] (full-line tiles only)
     int64_t grid;
+    float scale;                  // 8-bit types: C = BF16(scale x accumulator)
 };
 
 hipError_t gemm_launch(const GemmLaunch &L, hipStream_t stream);

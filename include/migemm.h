@@ -140,6 +140,30 @@ int migemm_attention_segments(int B, int Hq, int Hkv, int max_seq_len);
 /* Workspace bytes attention_decode_bf16 needs for that many segments. */
 size_t migemm_attention_workspace_bytes(int B, int Hq, int D, int num_segments);
 
+/*
+ * 8-bit GEMMs in the k-major ("TN") layout: C(m,n) = C[m + n*M] =
+ *     BF16_RNE( scale * sum_k A(m,k) * B(k,n) ),   A(m,k) = At[k + m*K],
+ *                                                  B(k,n) = B[k + n*K],
+ * i.e. A row-major M x K and B given as its N columns of K contiguous
+ * elements (with At = W [M, K] and B = X [N, K] it is Y = X W^T of the DCU
+ * decode page, section 6.1, on 8-bit data).  The element types are those
+ * the survey's instruction table lists for this GEMM (FP8 E4M3 / E5M2 and
+ * INT8; OCP FP8 encodings, both operands in the same format): products and
+ * sums in FP32 (FP8) or exact INT32 (INT8), then one FP32 multiply by
+ * `scale` (the dequantisation factor, e.g. the product of per-tensor
+ * scales; for INT8 the INT32 sum is converted to FP32 first), one RNE
+ * rounding to bfloat16.  K must be a multiple of 16 and At, B 16-byte
+ * aligned (else MIGEMM_ERR_ALIGN); C 2-byte aligned; other checks,
+ * ownership and completion as for gemm_f16.  INT8 sums are exact for
+ * K * 127 * 128 < 2^31.
+ */
+int gemm_tn_fp8_e4m3(const uint8_t *At, const uint8_t *B, uint16_t *C,
+                     int M, int N, int K, float scale, void *stream);
+int gemm_tn_fp8_e5m2(const uint8_t *At, const uint8_t *B, uint16_t *C,
+                     int M, int N, int K, float scale, void *stream);
+int gemm_tn_i8(const int8_t *At, const int8_t *B, uint16_t *C,
+               int M, int N, int K, float scale, void *stream);
+
 /* ---- explicit-configuration variants (tuning sweeps) --------------------- */
 
 /*
@@ -194,6 +218,15 @@ int gemm_tn_ex(int dtype, const uint16_t *At, const uint16_t *B, uint16_t *C,
                int M, int N, int K, int tile, int group_m, int xcd_remap,
                void *stream);
 
+/* The 8-bit GEMMs with an explicit configuration: qtype 2 = FP8 E4M3,
+ * 3 = FP8 E5M2, 4 = INT8 (the dtype codes of migemm_gemm_tn_plan_for);
+ * tile 0 (automatic: 10 when the 256x256 tiles fill the chip twice, 9 when
+ * 256x128 tiles fill it once, else 13), 9, 10 or 13; group_m and xcd_remap
+ * as for gemm_ex.  gemm_tn_ex rejects these dtypes (it has no scale). */
+int gemm_tn_q_ex(int qtype, const void *At, const void *B, uint16_t *C,
+                 int M, int N, int K, float scale, int tile, int group_m,
+                 int xcd_remap, void *stream);
+
 /*
  * Same contract as gemv_bf16 with rows_per_block (output rows of W per
  * workgroup of the vector kernel: 2, 4, 8, 16 or 32), the knob swept on the
@@ -234,7 +267,8 @@ typedef struct {
 int migemm_gemm_plan_for(int dtype, const uint16_t *A, const uint16_t *B,
                          const uint16_t *C, int M, int N, int K, int tile,
                          int group_m, int xcd_remap, migemm_gemm_plan *plan);
-/* The same for gemm_tn_ex. */
+/* The same for gemm_tn_ex, and with dtype 2, 3, 4 for gemm_tn_q_ex (K in
+ * elements; tile_k reported in elements). */
 int migemm_gemm_tn_plan_for(int dtype, const uint16_t *At, const uint16_t *B,
                             const uint16_t *C, int M, int N, int K, int tile,
                             int group_m, int xcd_remap, migemm_gemm_plan *plan);

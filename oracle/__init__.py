@@ -73,6 +73,14 @@ def lib():
         L.oracle_attention_segmented.restype = None
         L.oracle_attention_segmented.argtypes = [ctypes.c_int, u16p, u16p, u16p, i32p, i32p] + \
             [ctypes.c_int] * 6 + [ctypes.c_double, ctypes.c_int, u16p, f64p]
+        u8p = ctypes.POINTER(ctypes.c_uint8)
+        L.oracle_decode8.restype = ctypes.c_double
+        L.oracle_decode8.argtypes = [ctypes.c_int, ctypes.c_uint8]
+        L.oracle_decode8_array.argtypes = [ctypes.c_int, u8p, f64p, ctypes.c_int64]
+        L.oracle_gemm_tn_q.restype = ctypes.c_int64
+        L.oracle_gemm_tn_q.argtypes = [ctypes.c_int, u8p, u8p, ctypes.c_int, ctypes.c_int,
+                                       ctypes.c_int, ctypes.c_float, i64p, ctypes.c_int64,
+                                       u16p, f64p, f64p]
         _lib = L
     return _lib
 
@@ -210,6 +218,42 @@ def attention_segmented(Q, Kc, Vc, block_table, seq_lens, B, Hq, Hkv, D, block_s
                                      max_blocks, scale, nseg, _p(out, ctypes.c_uint16),
                                      _p(ox, ctypes.c_double))
     return out, ox
+
+
+Q_FMT = {"f8e4m3": 2, "f8e5m2": 3, "i8": 4}
+
+
+def _u8(a):
+    a = np.ascontiguousarray(a)
+    if a.dtype != np.uint8:
+        a = a.view(np.uint8) if a.dtype == np.int8 else a.astype(np.uint8)
+    return a.ravel()
+
+
+def decode8(bits, fmt) -> np.ndarray:
+    """Exact values of 8-bit codes: OCP FP8 E4M3 / E5M2 or INT8."""
+    b = _u8(bits)
+    out = np.empty(b.size, np.float64)
+    lib().oracle_decode8_array(Q_FMT[fmt], _p(b, ctypes.c_uint8), _p(out, ctypes.c_double), b.size)
+    return out
+
+
+def gemm_tn_q(At, B, M, N, K, fmt, scale, idx=None) -> GemmResult:
+    """8-bit GEMM, A k-major: C(m,n) = BF16(scale * sum_k At[k+m*K] B[k+n*K])
+    (INT8: through FP32 as the output is defined; see oracle.c), column-major
+    M x N, or the entries at flat indices idx.  sabs = |scale| sum |a||b|."""
+    At, B = _u8(At), _u8(B)
+    count = M * N if idx is None else len(idx)
+    ix = None if idx is None else np.ascontiguousarray(idx, np.int64)
+    bits = np.empty(count, np.uint16)
+    ex = np.empty(count, np.float64)
+    S = np.empty(count, np.float64)
+    macs = lib().oracle_gemm_tn_q(Q_FMT[fmt], _p(At, ctypes.c_uint8), _p(B, ctypes.c_uint8),
+                                  M, N, K, scale,
+                                  None if ix is None else _p(ix, ctypes.c_int64), count,
+                                  _p(bits, ctypes.c_uint16), _p(ex, ctypes.c_double),
+                                  _p(S, ctypes.c_double))
+    return GemmResult(bits, ex, S, macs)
 
 
 def gamma(n, u=2.0 ** -24):

@@ -17,6 +17,9 @@
  *    the linear layer Y = X W^T with X:[n,k], W:[m,k], Y:[n,m].
  *  - FlagGems "Hygon 优化" page, section "分组调度" (grouped scheduling): the
  *    GROUP_M map from a flat program id to an output tile.
+ *  - the 8-bit GEMM (FP8 E4M3 / E5M2, INT8 inputs, the element types of the
+ *    survey's instruction table) in the k-major layout of the DCU page's
+ *    Y = X W^T, with one scale and a BF16 output (see oracle_gemm_tn_q).
  *  - "DCU decode" page, section 6.1 (attention shapes: per query head
  *    scores = Q K^T over the L cached tokens, prob = softmax(scores),
  *    out = prob V; KV cache kept in pages [block, token_in_block, kv_head,
@@ -175,6 +178,82 @@ int64_t oracle_gemm_sampled(int fmt, const uint16_t *A, const uint16_t *B,
         if (C) C[i] = oracle_encode(fmt, s);
         if (Cx) Cx[i] = s;
         if (S) S[i] = sabs;
+    }
+    return total;
+}
+
+/* ---- 8-bit element types ------------------------------------------------
+ * OCP 8-bit floating point (the survey's instruction table lists FP8 E4M3
+ * and E5M2 for this GEMM): E4M3 has 1 sign, 4 exponent (bias 7) and 3
+ * mantissa bits, no infinities, S.1111.111 is NaN (largest finite 448);
+ * E5M2 has 5 exponent bits (bias 15) and 2 mantissa bits with IEEE-style
+ * infinities and NaNs (largest finite 57344).  Both have subnormals.
+ * INT8 is two's complement. */
+#define ORACLE_F8E4M3 2
+#define ORACLE_F8E5M2 3
+#define ORACLE_I8 4
+
+double oracle_decode8(int fmt, uint8_t v)
+{
+    if (fmt == ORACLE_I8) return (double)(int8_t)v;
+    const int e4 = fmt == ORACLE_F8E4M3;
+    const int mbits = e4 ? 3 : 2, bias = e4 ? 7 : 15, emax_field = e4 ? 15 : 31;
+    const int sign = v >> 7, e = (v >> mbits) & emax_field, man = v & ((1 << mbits) - 1);
+    double x;
+    if (e == 0)
+        x = ldexp((double)man, 1 - bias - mbits);
+    else if (e4 && e == 15 && man == 7)
+        x = NAN;
+    else if (!e4 && e == 31)
+        x = man ? NAN : INFINITY;
+    else
+        x = ldexp((double)((1 << mbits) + man), e - bias - mbits);
+    return sign ? -x : x;
+}
+
+void oracle_decode8_array(int fmt, const uint8_t *in, double *out, int64_t n)
+{
+    for (int64_t i = 0; i < n; ++i)
+        out[i] = oracle_decode8(fmt, in[i]);
+}
+
+/* 8-bit GEMM with A k-major ("TN"): C(m,n) = C[m + n*M], A(m,k) =
+ * At[k + m*K], B(k,n) = B[k + n*K]; s = sum_k A(m,k) B(k,n) exactly (every
+ * 8-bit value and product is exact in double, and so are these sums).
+ * Output: FP8: BF16_RNE(scale * s), rounded once from double; INT8: the sum
+ * is an integer, taken to FP32 (RNE), multiplied by scale in FP32 (RNE),
+ * then rounded to BF16 -- the FP32 steps that define the INT8 output.
+ * Cx = the value before the BF16 rounding, S = |scale| * sum_k |a||b|.
+ * All M*N outputs (idx == NULL, column-major) or those at idx[0..count). */
+int64_t oracle_gemm_tn_q(int fmt, const uint8_t *At, const uint8_t *B, int M, int N, int K,
+                         float scale, const int64_t *idx, int64_t count,
+                         uint16_t *C, double *Cx, double *S)
+{
+    const int64_t total_out = idx ? count : (int64_t)M * N;
+    int64_t total = 0;
+    #pragma omp parallel for schedule(dynamic, 16) reduction(+ : total)
+    for (int64_t i = 0; i < total_out; ++i) {
+        const int64_t o = idx ? idx[i] : i;
+        const int64_t m = o % M, n = o / M;
+        double s = 0.0, sa = 0.0;
+        for (int64_t k = 0; k < K; ++k) {
+            double a = oracle_decode8(fmt, At[k + m * (int64_t)K]);
+            double b = oracle_decode8(fmt, B[k + n * (int64_t)K]);
+            s += a * b;
+            sa += fabs(a) * fabs(b);
+            ++total;
+        }
+        double v;
+        if (fmt == ORACLE_I8) {
+            volatile float f = (float)s;          /* FP32, round to nearest even */
+            volatile float p = f * scale;         /* one FP32 multiply */
+            v = (double)p;
+        } else {
+            v = (double)scale * s;
+        }
+        if (C) C[i] = oracle_encode(ORACLE_BF16, v);
+        if (Cx) Cx[i] = v;
+        if (S) S[i] = fabs((double)scale) * sa;
     }
     return total;
 }
@@ -356,4 +435,4 @@ void oracle_attention_segmented(int fmt, const uint16_t *Q, const uint16_t *Kc, 
     }
 }
 
-int oracle_abi_version(void) { return 2; }
+int oracle_abi_version(void) { return 3; }

@@ -123,6 +123,27 @@ def attention_operands(B, Hq, Hkv, D, seq_lens, block_size, seed, sigma=1.0, spa
                 block_size=block_size)
 
 
+def q8_operands(M, N, K, fmt, seed, sigma=1.0):
+    """8-bit operands of the k-major GEMM: At row-major [M, K] then B as N
+    columns of K, flat uint8 codes.  FP8 (fmt 'f8e4m3' / 'f8e5m2'): N(0,
+    sigma) drawn in float32 and converted to torch's OCP float8 types
+    (nearest even); INT8 ('i8'): integers uniform in [-128, 127]."""
+    rng = np.random.default_rng(seed)
+    if fmt == "i8":
+        At = rng.integers(-128, 128, M * K).astype(np.int8).view(np.uint8)
+        B = rng.integers(-128, 128, N * K).astype(np.int8).view(np.uint8)
+        return At, B
+    import torch
+    dt = {"f8e4m3": torch.float8_e4m3fn, "f8e5m2": torch.float8_e5m2}[fmt]
+
+    def enc(n):
+        x = torch.from_numpy(rng.normal(0.0, sigma, n).astype(np.float32))
+        return x.to(dt).view(torch.uint8).numpy().copy()
+    At = enc(M * K)
+    B = enc(N * K)
+    return At, B
+
+
 def sample_indices(M, N, seed, count=4096):
     """``count`` distinct flat output indices (m + n*M) drawn with
     default_rng(1000 + seed), plus the four corners, sorted."""

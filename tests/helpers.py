@@ -71,6 +71,24 @@ def gemm_tn_gpu(At_bits, B_bits, M, N, K, fmt, tile=0, group_m=0, xcd_remap=1, s
     return C.out(), C.guards_intact(), unchanged
 
 
+def gemm_tn_q_gpu(At, B, M, N, K, fmt, scale, tile=0, stream=0):
+    """gemm_tn_q_ex (8-bit At, B; BF16 C) through the C ABI; returns (C bits,
+    guards ok, inputs unchanged)."""
+    import torch
+    from bf16_gemm_decode_amd import binding
+    q = {"f8e4m3": binding.F8E4M3, "f8e5m2": binding.F8E5M2, "i8": binding.I8}[fmt]
+    dA = torch.from_numpy(np.ascontiguousarray(At).view(np.uint8)).cuda()
+    dB = torch.from_numpy(np.ascontiguousarray(B).view(np.uint8)).cuda()
+    cA, cB = dA.clone(), dB.clone()
+    C = Guarded(M * N)
+    code = binding.lib().gemm_tn_q_ex(q, dA.data_ptr(), dB.data_ptr(), C.ptr, M, N, K, scale,
+                                      tile, 0, 1, stream)
+    assert code == 0, "gemm_tn_q_ex returned %d" % code
+    torch.cuda.synchronize()
+    unchanged = bool(torch.equal(dA, cA) and torch.equal(dB, cB))
+    return C.out(), C.guards_intact(), unchanged
+
+
 def kmajor_to_colmajor(At_bits, M, K):
     """A(m,k) = At[k + m*K]  ->  column-major A[m + k*M] (a pure relayout)."""
     return np.ascontiguousarray(np.asarray(At_bits).reshape(M, K).T).reshape(-1)
