@@ -77,8 +77,8 @@ def main(argv=None):
     p.add_argument("--out", default=None, help="write a markdown summary here")
     p.add_argument("--rounds", type=int, default=5)
     p.add_argument("--skip-prefill-grid", action="store_true")
-    p.add_argument("--sections", default="gemm,decode,prefill,attention",
-                   help="comma list of gemm, decode, prefill, attention")
+    p.add_argument("--sections", default="gemm,decode,prefill,attention,q8",
+                   help="comma list of gemm, decode, prefill, attention, q8")
     p.add_argument("--decode-tiles", default="0",
                    help="gemm_tn tiles to time for the decode batches (0 = automatic)")
     p.add_argument("--attn-segments", default="16,32,0",
@@ -244,6 +244,45 @@ def main(argv=None):
             print(json.dumps(r), flush=True)
         del dQ, dK, dV, op
 
+    # --- 8-bit GEMMs (k-major A) at the headline size ---------------------
+    if "q8" in sections:
+        Mq, Nq, Kq = 8192, 8192, 16384
+        g = torch.Generator(device="cuda")
+        g.manual_seed(11)
+
+        def codes(n, fmt):
+            c = torch.randint(0, 256, (n,), dtype=torch.int32, device="cuda", generator=g)
+            if fmt == binding.F8E4M3:
+                c = torch.where((c & 0x7F) == 0x7F, c ^ 1, c)      # no NaN codes
+            elif fmt == binding.F8E5M2:
+                c = torch.where((c & 0x7C) == 0x7C, c & ~0x40, c)  # no inf / NaN codes
+            return c.to(torch.uint8)
+        dC = torch.empty(Mq * Nq, dtype=torch.int16, device="cuda")
+        for q, qname, pk in ((binding.F8E4M3, "fp8 e4m3", rf.MI355X["mfma_fp8_tflops"]),
+                             (binding.F8E5M2, "fp8 e5m2", rf.MI355X["mfma_fp8_tflops"]),
+                             (binding.I8, "int8", rf.MI355X["mfma_int8_tops"])):
+            dA, dB = codes(Mq * Kq, q), codes(Nq * Kq, q)
+            med, mn = _timer(torch, s, lambda i: L.gemm_tn_q_ex(q, dA.data_ptr(), dB.data_ptr(),
+                                                                 dC.data_ptr(), Mq, Nq, Kq, 1.0, 0,
+                                                                 0, 1, h), 10, a.rounds)
+            _, plan = binding.gemm_plan(q, dA.data_ptr(), dB.data_ptr(), dC.data_ptr(), Mq, Nq, Kq,
+                                        a_kmajor=True)
+            tf = rf.gemm_flop(Mq, Nq, Kq) / med / 1e12
+            r = {"workload": "gemm_tn %s 8192x8192x16384 (BF16 out)" % qname, "M": Mq, "N": Nq,
+                 "K": Kq, "layout": "A k-major", "tile": plan["tile"],
+                 "tile_mnk": [plan["tile_m"], plan["tile_n"], plan["tile_k"]],
+                 "group_m": plan["group_m"], "median_us": round(med * 1e6, 2),
+                 "min_us": round(mn * 1e6, 2), "tflops": round(tf, 1), "util": round(tf / pk, 4)}
+            rows.append(r)
+            print(json.dumps(r), flush=True)
+            del dA, dB
+        # the BF16 kernel on the same layout, for comparison
+        dA = torch.randn(Mq * Kq, device="cuda", generator=g).to(torch.bfloat16).view(torch.int16)
+        dB = torch.randn(Nq * Kq, device="cuda", generator=g).to(torch.bfloat16).view(torch.int16)
+        gemm_row("gemm_tn bf16 8192x8192x16384 (comparison)", binding.BF16, dA, dB, dC, Mq, Nq,
+                 Kq, tn=True, launches=10)
+        del dA, dB, dC
+
     smi_after = _smi()
     if a.out:
         with open(a.out, "w") as f:
@@ -251,7 +290,8 @@ def main(argv=None):
             f.write("command: `python -m bf16_gemm_decode_amd.report %s`\n\n"
                     % " ".join(sys.argv[1:] if argv is None else argv))
             f.write("Kernel durations from HIP events around back-to-back launches (median / min of "
-                    "%d rounds); util = fraction of 2.5 PFLOP/s (GEMM) or 8 TB/s (GEMV, attention, "
+                    "%d rounds); util = fraction of the dense peak of the row's type (2.5 PFLOP/s "
+                    "FP16/BF16, 5.0 PFLOP/s FP8, 5.0 POP/s INT8) or of 8 TB/s (GEMV, attention, "
                     "probe); for the attention GB/s counts the algorithmic bytes (K and V read once, "
                     "Q, block table, output), the workspace partials not included.\n\n"
                     % a.rounds)

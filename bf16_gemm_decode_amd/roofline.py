@@ -15,6 +15,8 @@ MI355X = {
     "hbm_GBps": 8000.0,
     "mfma_f16_tflops": 2500.0,
     "mfma_bf16_tflops": 2500.0,
+    "mfma_fp8_tflops": 5000.0,
+    "mfma_int8_tops": 5000.0,
     "valu_fp32_tflops": 157.3,
     "valu_fp64_tflops": 78.6,
 }
