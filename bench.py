@@ -15,6 +15,10 @@ same stream (inside a step the events also hold the dispatch gap, reported as
 in_step_avg_us).  `cpu_baseline` times the CPU oracle on a bounded sample of the same
 GEMM (sampled output entries), scaled to TFLOP/s.
 
+`gemm_8bit` reports the FP8 (E4M3, E5M2) and INT8 GEMMs at the same size in the
+k-major layout (random codes without NaN or infinity, BF16 output), each from a
+burst of launches, against the 5.0 PFLOP/s / 5.0 POP/s dense peaks.
+
 Beside the step, `attention` reports split-KV decode attention over the paged
 BF16 cache (16 query / 4 KV heads, head dim 256, pages of 784 tokens, one
 sequence of 32768 cached tokens, automatic segment count) from a burst of
@@ -321,6 +325,38 @@ def main():
     att_bytes = rf.attention_bytes([ATT_LEN], Hq, Hkv, D, bs)
     att_GBps = att_bytes / att_avg / 1e9
 
+    # 8-bit GEMMs at the headline size, k-major A (the layout they take)
+    gen = torch.Generator(device="cuda")
+    gen.manual_seed(11)
+    q_rows = {}
+    qC = torch.empty(M * N, dtype=torch.int16, device="cuda")
+    for q, qname, pk in ((binding.F8E4M3, "fp8_e4m3", rf.MI355X["mfma_fp8_tflops"]),
+                         (binding.F8E5M2, "fp8_e5m2", rf.MI355X["mfma_fp8_tflops"]),
+                         (binding.I8, "int8", rf.MI355X["mfma_int8_tops"])):
+        def codes(n):
+            c = torch.randint(0, 256, (n,), dtype=torch.int32, device="cuda", generator=gen)
+            if q == binding.F8E4M3:
+                c = torch.where((c & 0x7F) == 0x7F, c ^ 1, c)
+            elif q == binding.F8E5M2:
+                c = torch.where((c & 0x7C) == 0x7C, c & ~0x40, c)
+            return c.to(torch.uint8)
+        qA, qB = codes(M * K), codes(N * K)
+        for _ in range(2):
+            assert L.gemm_tn_q_ex(q, qA.data_ptr(), qB.data_ptr(), qC.data_ptr(), M, N, K, 1.0, 0, 0, 1, h) == 0
+        q0, q1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+        nq = 10
+        q0.record(stream)
+        for _ in range(nq):
+            assert L.gemm_tn_q_ex(q, qA.data_ptr(), qB.data_ptr(), qC.data_ptr(), M, N, K, 1.0, 0, 0, 1, h) == 0
+        q1.record(stream)
+        stream.synchronize()
+        qt = q0.elapsed_time(q1) / 1e3 / nq
+        qtf = rf.gemm_flop(M, N, K) / qt / 1e12
+        q_rows[qname] = {"avg_launch_ms": round(qt * 1e3, 4), "TFLOPs_or_TOPs": round(qtf, 1),
+                         "peak": pk, "frac": round(qtf / pk, 4)}
+        del qA, qB
+    del qC
+
     tflops = rf.gemm_flop(M, N, K) / gemm_avg / 1e12
     gemv_bytes = rf.gemv_bytes(GM, GK, gn)
     gemv_GBps = gemv_bytes / gemv_avg / 1e9
@@ -372,6 +408,8 @@ def main():
                                        ATTENTION_SOURCES,
                                        "attention_16q4kv_d256_l32768_traffic.json")},
                       "frac_of_probe": round(att_GBps / probe_GBps, 4)},
+        "gemm_8bit": {"shape": [M, N, K], "layout": "A k-major (gemm_tn_q_ex, automatic tile)",
+                      "output": "BF16 of scale x sum", **q_rows},
         "device": {"name": props.name, "cus": props.multi_processor_count},
     }
     if not args.no_cpu_baseline:
