@@ -37,6 +37,29 @@ int64_t cdiv(int64_t a, int64_t b) { return (a + b - 1) / b; }
 // Shared by gemm_ex and migemm_gemm_plan_for.  Returns 0 and fills L (and
 // *launch = true) when a kernel must run, 0 with *launch = false for an empty
 // output, or a negative MIGEMM_ERR_* code.
+// Exact-shape configurations, measured on one MI355X with the per-workload
+// report (GROUP_M x tile sweeps of the prefill shape in both layouts, the
+// headline GEMM, the ragged BF16 GEMM).  Consulted when the caller leaves both
+// the tile and the grouped width automatic; an entry whose tile the operands
+// cannot take (alignment) is skipped.
+struct ShapeConfig {
+    int dtype, a_kmajor, M, N, K, tile, group_m;
+};
+constexpr ShapeConfig kShapeTable[] = {
+    {DT_F16, 0, 8192, 8192, 16384, TILE_256x256_FL8, 8},
+    {DT_BF16, 0, 4096, 34816, 5120, TILE_256x256_FL8, 16},    // 1.261 ms vs 1.270 at 8
+    {DT_BF16, 1, 34816, 4096, 5120, TILE_256x256_FL8, 4},     // 1.316 ms vs 1.354 at 8
+    {DT_BF16, 0, 5000, 3000, 4100, TILE_128x128, 8},
+};
+
+const ShapeConfig *find_shape(int dtype, bool a_kmajor, int M, int N, int K)
+{
+    for (const ShapeConfig &c : kShapeTable)
+        if (c.dtype == dtype && c.a_kmajor == (a_kmajor ? 1 : 0) && c.M == M && c.N == N && c.K == K)
+            return &c;
+    return nullptr;
+}
+
 int plan_gemm(int dtype, const uint16_t *A, const uint16_t *B, const uint16_t *C, int M, int N,
               int K, int tile, int group_m, int xcd_remap, GemmLaunch &L, bool &launch,
               bool a_kmajor = false)
@@ -76,6 +99,13 @@ int plan_gemm(int dtype, const uint16_t *A, const uint16_t *B, const uint16_t *C
     L.c_vec = (M % 4 == 0 && (uintptr_t)C % 8 == 0) ? 1 : 0;
     L.a_kmajor = a_kmajor ? 1 : 0;
     const bool wide = (L.vec_a == 8 && L.vec_b == 8);
+    if (tile == TILE_AUTO && group_m == 0 && !q8) {
+        const ShapeConfig *c = find_shape(dtype, a_kmajor, M, N, K);
+        if (c && (wide || c->tile == TILE_128x128)) {
+            tile = c->tile;
+            group_m = c->group_m;
+        }
+    }
     if (a_kmajor && q8) {
         if (!wide) return MIGEMM_ERR_ALIGN;
         if (tile == TILE_AUTO)

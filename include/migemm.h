@@ -169,7 +169,10 @@ int gemm_tn_i8(const int8_t *At, const int8_t *B, uint16_t *C,
 /*
  * Same contract as gemm_f16 / gemm_bf16 with the tile configuration named by
  * the caller instead of chosen by the library:
- *   tile:    0 = automatic; 1 = 256x256 (4 waves as 2x2, 4 LDS stages);
+ *   tile:    0 = automatic (with group_m 0: first an exact-shape table of
+ *            measured configurations -- the headline FP16 GEMM, the prefill
+ *            GEMM in both layouts, the ragged BF16 GEMM -- then the size
+ *            rules); 1 = 256x256 (4 waves as 2x2, 4 LDS stages);
  *            2 = 256x128 (5 stages); 3 = 128x128 (4 stages, two workgroups
  *            per CU); 4 = tile 1 with 5 stages; 5 = 256x256 with the 4 waves
  *            stacked along M; 6 = tile 1 with 3 stages; 7 = 256x256, waves
