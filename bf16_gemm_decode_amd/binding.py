@@ -59,6 +59,9 @@ SIGNATURES = {
     "gemm_tn_fp8_e5m2": (_I, [_P, _P, _P, _I, _I, _I, ctypes.c_float, _P]),
     "gemm_tn_i8": (_I, [_P, _P, _P, _I, _I, _I, ctypes.c_float, _P]),
     "gemm_tn_q_ex": (_I, [_I, _P, _P, _P, _I, _I, _I, ctypes.c_float, _I, _I, _I, _P]),
+    "gemm_splitk_ex": (_I, [_I, _I, _P, _P, _P, _I, _I, _I, _I, _I, _I, _I, _P, ctypes.c_size_t, _P]),
+    "migemm_splitk_splits": (_I, [_I, _I, _I, _I, _I]),
+    "migemm_splitk_workspace_bytes": (ctypes.c_size_t, [_I, _I, _I]),
     "migemm_tile_coord": (_I, [_I64, _I64, _I64, _I64, _I64,
                                ctypes.POINTER(_I64), ctypes.POINTER(_I64)]),
     "migemm_gemm_plan_for": (_I, [_I, _P, _P, _P, _I, _I, _I, _I, _I, _I, ctypes.POINTER(Plan)]),

@@ -207,6 +207,71 @@ int gemm_tn_ex(int dtype, const uint16_t *At, const uint16_t *B, uint16_t *C, in
     return finish(gemm_launch(L, (hipStream_t)stream), stream);
 }
 
+int migemm_splitk_splits(int dtype, int a_kmajor, int M, int N, int K)
+{
+    if ((dtype != DT_F16 && dtype != DT_BF16) || M <= 0 || N <= 0 || K <= 0) return 1;
+    if (a_kmajor && N <= kBatchAutoMax) return 1;           // the streaming decode kernels
+    // the split runs on the 256x128 full-line tile: up to about one
+    // workgroup per CU, slices of at least 1024 k, at most 8
+    const int64_t tiles = cdiv(M, 256) * cdiv(N, 128);
+    int S = 1;
+    while (S < 8 && tiles * 2 * S <= 256 && K / (2 * S) >= 1024) S <<= 1;
+    return S;
+}
+
+size_t migemm_splitk_workspace_bytes(int M, int N, int splits)
+{
+    if (M <= 0 || N <= 0 || splits <= 1) return 0;
+    return (size_t)splits * M * N * sizeof(float);
+}
+
+int gemm_splitk_ex(int dtype, int a_kmajor, const uint16_t *A, const uint16_t *B, uint16_t *C,
+                   int M, int N, int K, int splits, int tile, int group_m, int xcd_remap,
+                   void *workspace, size_t workspace_bytes, void *stream)
+{
+    if (dtype != DT_F16 && dtype != DT_BF16) return MIGEMM_ERR_CONFIG;
+    if (splits < 0 || a_kmajor < 0 || a_kmajor > 1) return MIGEMM_ERR_CONFIG;
+    int S = splits ? splits : migemm_splitk_splits(dtype, a_kmajor, M, N, K);
+    // slices run on tiles 9, 10, 13; the automatic tile with a split is 9
+    const bool split_tile = tile == TILE_256x128_FL || tile == TILE_256x256_FL8 || tile == TILE_128x128_SK;
+    if (S > 1 && tile != TILE_AUTO && !split_tile) return MIGEMM_ERR_CONFIG;
+    GemmLaunch L;
+    bool launch;
+    int rc = plan_gemm(dtype, A, B, C, M, N, K, S > 1 && tile == TILE_AUTO ? TILE_256x128_FL : tile,
+                       group_m, xcd_remap, L, launch, a_kmajor != 0);
+    if (S > 1 && tile == TILE_AUTO && rc == MIGEMM_ERR_CONFIG) {
+        // operands without 16-byte rows take no full-line tile: no split
+        S = 1;
+        rc = plan_gemm(dtype, A, B, C, M, N, K, tile, group_m, xcd_remap, L, launch, a_kmajor != 0);
+    }
+    if (rc != MIGEMM_OK || !launch) return rc;
+    const int ks = S > 1 ? (int)(((int64_t)K + S - 1) / S + 63) / 64 * 64 : K;
+    const int S_eff = S > 1 ? (int)(((int64_t)K + ks - 1) / ks) : 1;
+    if (S_eff > 1) {
+        const size_t need = (size_t)S_eff * M * N * sizeof(float);
+        if (!workspace) return MIGEMM_ERR_NULL;
+        if ((uintptr_t)workspace % 16) return MIGEMM_ERR_ALIGN;
+        if (workspace_bytes < need) return MIGEMM_ERR_SIZE;
+        const size_t ab = (size_t)M * K * 2, bb = (size_t)K * N * 2, cb = (size_t)M * N * 2;
+        if (overlaps(workspace, need, A, ab) || overlaps(workspace, need, B, bb) ||
+            overlaps(workspace, need, C, cb))
+            return MIGEMM_ERR_OVERLAP;
+        L.splits = S_eff;
+        L.ks = ks;
+        L.part = (float *)workspace;
+        hipError_t e = gemm_launch(L, (hipStream_t)stream);
+        if (e == hipSuccess)
+            e = splitk_reduce_launch(dtype, L.part, C, (int64_t)M * N, S_eff, (hipStream_t)stream);
+        return finish(e, stream);
+    }
+    if (L.tile == TILE_SKINNY || L.tile == TILE_BATCH) {
+        SkinnyLaunch Sk{dtype, A, B, C, M, K, N, L.c_vec};
+        return finish((L.tile == TILE_SKINNY ? skinny_launch : batch_launch)(Sk, (hipStream_t)stream),
+                      stream);
+    }
+    return finish(gemm_launch(L, (hipStream_t)stream), stream);
+}
+
 int gemm_tn_q_ex(int qtype, const void *At, const void *B, uint16_t *C, int M, int N, int K,
                  float scale, int tile, int group_m, int xcd_remap, void *stream)
 {

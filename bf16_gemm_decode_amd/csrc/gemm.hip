@@ -33,6 +33,8 @@
 //    stores it directly: no FP32 copy of C ever reaches memory.
 #include <type_traits>
 
+#include <algorithm>
+
 #include "common.hpp"
 #include "tile_map.hpp"
 #include "kernels.hpp"
@@ -477,16 +479,24 @@ constexpr int fl_loads_after(int j, int need_a, int need_b)
 // rows read with transposing LDS reads.  AK = true: A k-major (A(m,k) =
 // A[k + m*K]), A ring of SA stages of 64 k laid out, loaded and read exactly
 // like B (rows of A in place of columns of B).
-template <int DT, bool AK, int BM, int BN, int WGM, int WGN, int SA, int SB, int OCC>
+template <int DT, bool AK, int BM, int BN, int WGM, int WGN, int SA, int SB, int OCC, bool SPLIT>
 __global__ void __launch_bounds__(WGM * WGN * 64)
 __attribute__((amdgpu_waves_per_eu(OCC, OCC)))
 gemm_fl_kernel(const uint16_t *__restrict__ A, const uint16_t *__restrict__ B,
-               uint16_t *__restrict__ C, int M, int N, int K, int num_pid_m, int num_pid_n,
-               int group_m, int num_xcd, int c_vec, float scale)
+               uint16_t *__restrict__ C, int M, int N, int K_total, int num_pid_m, int num_pid_n,
+               int group_m, int num_xcd, int c_vec, float scale, int ks, float *__restrict__ part)
 {
     // K counts 2-byte units: for 8-bit element types the caller passes half
     // the element count, and each unit holds two elements.
     static_assert(AK || !dt_is_8bit(DT), "8-bit types take a k-major A");
+    // SPLIT: workgroup row blockIdx.y sums k in [kb, kb + ks) (ks a multiple
+    // of 64) into FP32 partials part[blockIdx.y][n][m]; rows of k-major
+    // operands keep their full stride K_total.  Otherwise the kernel sums
+    // all of K and writes C.
+    static_assert(!SPLIT || !dt_is_8bit(DT), "split-K: 16-bit types");
+    const int kb = SPLIT ? (int)blockIdx.y * ks : 0;
+    const int K = SPLIT ? min(ks, K_total - kb) : K_total;
+    const int ldk = K_total;
     constexpr int BK = 32;                        // sub-step = one MFMA k slice
     constexpr int NW = WGM * WGN;
     constexpr int TM = BM / WGM, TN = BN / WGN;
@@ -534,7 +544,7 @@ gemm_fl_kernel(const uint16_t *__restrict__ A, const uint16_t *__restrict__ B,
 #pragma unroll
     for (int q = 0; q < NAO; ++q) {
         if constexpr (AK) {
-            kmajor_lane(q, K, a_off[q], a_k[q]);
+            kmajor_lane(q, ldk, a_off[q], a_k[q]);
         } else {
             // m-major A: piece P = (q*NW + wave) KiB of the stage, row kk,
             // swizzled 16-byte chunks
@@ -547,7 +557,7 @@ gemm_fl_kernel(const uint16_t *__restrict__ A, const uint16_t *__restrict__ B,
     uint32_t b_off[LB];
     int b_k[LB];
 #pragma unroll
-    for (int q = 0; q < LB; ++q) kmajor_lane(q, K, b_off[q], b_k[q]);
+    for (int q = 0; q < LB; ++q) kmajor_lane(q, ldk, b_off[q], b_k[q]);
 
     // Sub-steps, evened out: with an odd count a zero sub-step (k0 = -BK,
     // every element read as zero) goes first.  P_ = number of 64-k stages.
@@ -561,17 +571,18 @@ gemm_fl_kernel(const uint16_t *__restrict__ A, const uint16_t *__restrict__ B,
     // k0 (k0 may be -BK: the lanes below k = 0 are sent out of range, so
     // nothing below X is read), with rows/columns >= R past the records.
     auto desc_kmajor = [&](const uint16_t *X, int r0, int R, int pp) {
-        const int k0 = kbase + pp * 2 * BK;
-        const uint64_t base = (uint64_t)(uintptr_t)X + ((int64_t)r0 * K + k0) * 2;
+        const int k0 = kb + kbase + pp * 2 * BK;
+        const uint64_t base = (uint64_t)(uintptr_t)X + ((int64_t)r0 * ldk + k0) * 2;
         return make_desc((const void *)(uintptr_t)base,
-                         clamp_records((int64_t)(R - r0) * K * 2 - (int64_t)k0 * 2));
+                         clamp_records((int64_t)(R - r0) * ldk * 2 - (int64_t)k0 * 2));
     };
     auto desc_a = [&](int jj) {
         if constexpr (AK) {
             return desc_kmajor(A, m0, M, jj);
         } else {
             const int k0 = kbase + jj * BK;
-            return make_desc(A + (int64_t)k0 * M, k0 >= 0 ? clamp_records((int64_t)(K - k0) * M * 2) : 0u);
+            return make_desc(A + (int64_t)(kb + k0) * M,
+                             k0 >= 0 ? clamp_records((int64_t)(K - k0) * M * 2) : 0u);
         }
     };
     auto desc_b = [&](int pp) { return desc_kmajor(B, n0, N, pp); };
@@ -748,6 +759,28 @@ gemm_fl_kernel(const uint16_t *__restrict__ A, const uint16_t *__restrict__ B,
     }
 
     mfma_drain();
+    if constexpr (SPLIT) {
+        // FP32 partial sums of this k slice (16-bit types only)
+        float *pz = part + (size_t)blockIdx.y * M * N;
+#pragma unroll
+        for (int i = 0; i < FM; ++i) {
+            const int m = m0 + wm * TM + i * 16 + 4 * g;
+#pragma unroll
+            for (int j = 0; j < FN; ++j) {
+                const int n = n0 + wn * TN + j * 16 + ig;
+                if (n >= N) continue;
+                float *dst = pz + (size_t)n * M + m;
+                if (c_vec && m + 3 < M) {
+                    *(f32x4 *)dst = acc[i][j];
+                } else {
+#pragma unroll
+                    for (int r = 0; r < 4; ++r)
+                        if (m + r < M) dst[r] = acc[i][j][r];
+                }
+            }
+        }
+        return;
+    }
 #pragma unroll
     for (int i = 0; i < FM; ++i) {
         const int m = m0 + wm * TM + i * 16 + 4 * g;
@@ -771,14 +804,32 @@ gemm_fl_kernel(const uint16_t *__restrict__ A, const uint16_t *__restrict__ B,
 
 // OCC: waves per SIMD the kernel is compiled for (its register budget is
 // 512 / OCC per lane); 0 = one workgroup's waves spread one per SIMD.
+// Split-K variants exist for the tiles 9 (256x128), 10 (256x256, 8 waves)
+// and 13 (128x128) and the 16-bit types.
+template <int DT, int BM, int BN, int WGM, int WGN>
+constexpr bool kSplitTile = !dt_is_8bit(DT) && ((BM == 256 && BN == 128 && WGM * WGN == 4) ||
+                                                (BM == 256 && BN == 256 && WGM * WGN == 8) ||
+                                                (BM == 128 && BN == 128 && WGM * WGN == 4));
+
 template <int DT, bool AK, int BM, int BN, int WGM, int WGN, int SA, int SB, int OCC = 0>
 static hipError_t launch_fl(const GemmLaunch &L, hipStream_t stream)
 {
     constexpr int OC = OCC ? OCC : WGM * WGN / 4;
-    dim3 grid((unsigned)L.grid), block(WGM * WGN * 64);
-    hipLaunchKernelGGL((gemm_fl_kernel<DT, AK, BM, BN, WGM, WGN, SA, SB, OC>), grid, block, 0, stream,
-                       L.A, L.B, L.C, L.M, L.N, L.K, L.num_pid_m, L.num_pid_n, L.group_m,
-                       L.num_xcd, L.c_vec, L.scale);
+    const dim3 block(WGM * WGN * 64);
+    if (L.splits > 1) {
+        if constexpr (kSplitTile<DT, BM, BN, WGM, WGN>) {
+            hipLaunchKernelGGL((gemm_fl_kernel<DT, AK, BM, BN, WGM, WGN, SA, SB, OC, true>),
+                               dim3((unsigned)L.grid, (unsigned)L.splits), block, 0, stream, L.A, L.B,
+                               L.C, L.M, L.N, L.K, L.num_pid_m, L.num_pid_n, L.group_m, L.num_xcd,
+                               L.c_vec, L.scale, L.ks, L.part);
+            return hipGetLastError();
+        }
+        return hipErrorInvalidValue;
+    }
+    hipLaunchKernelGGL((gemm_fl_kernel<DT, AK, BM, BN, WGM, WGN, SA, SB, OC, false>),
+                       dim3((unsigned)L.grid), block, 0, stream, L.A, L.B, L.C, L.M, L.N, L.K,
+                       L.num_pid_m, L.num_pid_n, L.group_m, L.num_xcd, L.c_vec, L.scale, L.K,
+                       (float *)nullptr);
     return hipGetLastError();
 }
 
@@ -839,6 +890,51 @@ static hipError_t launch_dt(const GemmLaunch &L, hipStream_t s)
         break;
     }
     return hipErrorInvalidValue;
+}
+
+// ---------------------------------------------------------------------------
+// Split-K: C = round(sum_z part[z]) over `splits` FP32 partial matrices of
+// `count` elements each, one rounding.  VEC: 4 consecutive elements per
+// thread (count % 4 == 0, part 16-byte and C 8-byte aligned).
+
+template <int DT, bool VEC>
+__global__ void __launch_bounds__(256)
+splitk_reduce_kernel(const float *__restrict__ part, uint16_t *__restrict__ C, int64_t count, int splits)
+{
+    const int64_t stride = (int64_t)gridDim.x * 256 * (VEC ? 4 : 1);
+    for (int64_t i = ((int64_t)blockIdx.x * 256 + threadIdx.x) * (VEC ? 4 : 1); i < count; i += stride) {
+        if constexpr (VEC) {
+            f32x4 acc = *(const f32x4 *)(part + i);
+            for (int z = 1; z < splits; ++z) {
+                const f32x4 v = *(const f32x4 *)(part + (size_t)z * count + i);
+#pragma unroll
+                for (int e = 0; e < 4; ++e) acc[e] += v[e];
+            }
+            const u16x4 o = {to_out<DT>(acc[0]), to_out<DT>(acc[1]), to_out<DT>(acc[2]), to_out<DT>(acc[3])};
+            *(u16x4 *)(C + i) = o;
+        } else {
+            float acc = part[i];
+            for (int z = 1; z < splits; ++z) acc += part[(size_t)z * count + i];
+            C[i] = to_out<DT>(acc);
+        }
+    }
+}
+
+hipError_t splitk_reduce_launch(int dtype, const float *part, uint16_t *C, int64_t count, int splits,
+                                hipStream_t stream)
+{
+    if (count <= 0) return hipSuccess;
+    const bool vec = count % 4 == 0 && (uintptr_t)part % 16 == 0 && (uintptr_t)C % 8 == 0;
+    const int64_t items = vec ? count / 4 : count;
+    const unsigned grid = (unsigned)std::min<int64_t>((items + 255) / 256, 8192);
+    if (dtype == DT_F16) {
+        if (vec) hipLaunchKernelGGL((splitk_reduce_kernel<DT_F16, true>), dim3(grid), dim3(256), 0, stream, part, C, count, splits);
+        else hipLaunchKernelGGL((splitk_reduce_kernel<DT_F16, false>), dim3(grid), dim3(256), 0, stream, part, C, count, splits);
+    } else {
+        if (vec) hipLaunchKernelGGL((splitk_reduce_kernel<DT_BF16, true>), dim3(grid), dim3(256), 0, stream, part, C, count, splits);
+        else hipLaunchKernelGGL((splitk_reduce_kernel<DT_BF16, false>), dim3(grid), dim3(256), 0, stream, part, C, count, splits);
+    }
+    return hipGetLastError();
 }
 
 // 8-bit inputs: the k-major full-line tiles 9 (256x128), 10 (256x256, 8

@@ -92,7 +92,14 @@ struct GemmLaunch {
     int a_kmajor;                 // 1: A(m,k) = A[k + m*K] (full-line tiles only)
     int64_t grid;
     float scale;                  // 8-bit types: C = BF16(scale x accumulator)
+    int splits;                   // > 1: split-K over `splits` k slices of ks (full-line tiles)
+    int ks;                       // slice length, a multiple of 64 (2-byte units)
+    float *part;                  // split-K FP32 partials [splits][N][M]
 };
+
+// Sum of split-K partials: C = round(sum_z part[z][n][m]) (gemm.hip).
+hipError_t splitk_reduce_launch(int dtype, const float *part, uint16_t *C, int64_t count,
+                                int splits, hipStream_t stream);
 
 hipError_t gemm_launch(const GemmLaunch &L, hipStream_t stream);
 

@@ -164,6 +164,36 @@ int gemm_tn_fp8_e5m2(const uint8_t *At, const uint8_t *B, uint16_t *C,
 int gemm_tn_i8(const int8_t *At, const int8_t *B, uint16_t *C,
                int M, int N, int K, float scale, void *stream);
 
+/*
+ * Split-K GEMM: the product of gemm_ex (a_kmajor 0: A(m,k) = A[m + k*M]) or
+ * gemm_tn_ex (a_kmajor 1: A(m,k) = A[k + m*K]), with B(k,n) = B[k + n*K]
+ * and C(m,n) = C[m + n*M], for shapes whose output tiles do not fill the
+ * 256 CUs: K is cut into `splits` slices (of a multiple of 64 k), each slice
+ * summed in FP32 into its own M x N partial in `workspace`, then one kernel
+ * adds the partials and rounds once (RNE) to the 16-bit format.  splits 0 =
+ * automatic (migemm_splitk_splits); 1 = no split (same as gemm_ex /
+ * gemm_tn_ex).  Slices run on the full-line tiles 9, 10 and 13 (tile 0
+ * with a split means 9); another explicit tile with splits > 1 is
+ * MIGEMM_ERR_CONFIG, and operands without 16-byte rows run unsplit.
+ * workspace: device, 16-byte aligned, at least
+ * migemm_splitk_workspace_bytes(M, N, slices) bytes where slices =
+ * ceil(K / ks), ks = 64 * ceil(ceil(K / splits) / 64) (never more than
+ * `splits`), owned by the caller, not overlapping A, B or C; unused (may be
+ * NULL) without a split.  Errors as for gemm_ex, plus _NULL / _ALIGN /
+ * _SIZE / _OVERLAP for the workspace.  dtype 0 (binary16) or 1 (bfloat16).
+ */
+int gemm_splitk_ex(int dtype, int a_kmajor, const uint16_t *A, const uint16_t *B,
+                   uint16_t *C, int M, int N, int K, int splits, int tile,
+                   int group_m, int xcd_remap, void *workspace,
+                   size_t workspace_bytes, void *stream);
+/* The automatic slice count (host only): doubles while twice the 256x128
+ * tiles still fit about one workgroup per CU and slices keep >= 1024 k, at
+ * most 8; 1 for shapes that fill the chip and for the k-major decode widths
+ * (N <= 32), which stream A once anyway. */
+int migemm_splitk_splits(int dtype, int a_kmajor, int M, int N, int K);
+/* FP32 partial bytes for that many slices (0 when slices <= 1). */
+size_t migemm_splitk_workspace_bytes(int M, int N, int splits);
+
 /* ---- explicit-configuration variants (tuning sweeps) --------------------- */
 
 /*

@@ -145,6 +145,33 @@ def test_exact_shape_table():
     assert plan(1, 4096, 34816, 5128)["group_m"] == 8
 
 
+def test_splitk_rules_and_errors():
+    L = binding.lib()
+    # automatic slices: up to ~1 workgroup per CU on the 256x128 tile, >= 1024 k each, <= 8
+    assert L.migemm_splitk_splits(1, 0, 2048, 2048, 65536) == 2
+    assert L.migemm_splitk_splits(1, 0, 1024, 1024, 65536) == 8
+    assert L.migemm_splitk_splits(0, 1, 1024, 1024, 4096) == 4       # 1024 k per slice
+    assert L.migemm_splitk_splits(0, 0, 8192, 8192, 16384) == 1
+    assert L.migemm_splitk_splits(1, 1, 34816, 16, 5120) == 1      # decode widths stream A once
+    assert L.migemm_splitk_splits(2, 1, 1024, 1024, 65536) == 1    # 8-bit types: no split
+    assert L.migemm_splitk_workspace_bytes(100, 30, 4) == 4 * 100 * 30 * 4
+    assert L.migemm_splitk_workspace_bytes(100, 30, 1) == 0
+    W = P + 0x10000000
+    call = lambda **k: L.gemm_splitk_ex(*[dict(dt=0, ak=0, A=P, B=P + 0x1000000, C=P + 0x2000000, M=512,
+                                                N=512, K=4096, S=4, tile=0, gm=0, xcd=1, ws=W,
+                                                wsb=1 << 30, st=None, **{})[x] if x not in k else k[x]
+                                          for x in ("dt", "ak", "A", "B", "C", "M", "N", "K", "S",
+                                                    "tile", "gm", "xcd", "ws", "wsb", "st")])
+    assert call(dt=2) == -5 and call(ak=2) == -5 and call(S=-1) == -5
+    assert call(tile=3) == -5 and call(tile=7) == -5              # slices on tiles 9, 10, 13 only
+    assert call(ws=None) == -2
+    assert call(ws=W + 8) == -4
+    assert call(wsb=4 * 512 * 512 * 4 - 1) == -6
+    assert call(ws=P + 0x1000000) == -3                           # workspace on B
+    assert call(M=-1) == -1
+    assert call(M=0) == 0                                         # nothing to do
+
+
 def test_q8_plan_and_errors():
     L = binding.lib()
     # 8-bit GEMMs: k-major A only, K in elements (multiple of 16), tiles 9, 10, 13
