@@ -207,16 +207,35 @@ int gemm_tn_ex(int dtype, const uint16_t *At, const uint16_t *B, uint16_t *C, in
     return finish(gemm_launch(L, (hipStream_t)stream), stream);
 }
 
+// The automatic split: the 256x256 tile (10) with the smallest power-of-two
+// slice count that gives it >= 256 workgroups, else the 256x128 tile (9)
+// likewise, else tile 9 with as many slices as allowed; slices keep >= 1024
+// k and number at most 32 (measured on 1024^2 .. 8192x1024 outputs with K
+// of 16K .. 128K).  Returns the slice count, *tile the tile.
+static int splitk_choice(int M, int N, int K, int a_kmajor, int *tile)
+{
+    *tile = TILE_256x128_FL;
+    if (M <= 0 || N <= 0 || K <= 0 || (a_kmajor && N <= kBatchAutoMax)) return 1;
+    const int64_t t10 = cdiv(M, 256) * cdiv(N, 256), t9 = cdiv(M, 256) * cdiv(N, 128);
+    if (t10 >= 256) return 1;                               // fills the chip unsplit
+    auto slices = [&](int64_t tiles) {
+        int S = 1;
+        while (S < 32 && tiles * S < 256 && K / (2 * S) >= 1024) S <<= 1;
+        return S;
+    };
+    const int s10 = slices(t10);
+    if (t10 * s10 >= 256) {
+        *tile = TILE_256x256_FL8;
+        return s10;
+    }
+    return t9 >= 256 ? 1 : slices(t9);
+}
+
 int migemm_splitk_splits(int dtype, int a_kmajor, int M, int N, int K)
 {
-    if ((dtype != DT_F16 && dtype != DT_BF16) || M <= 0 || N <= 0 || K <= 0) return 1;
-    if (a_kmajor && N <= kBatchAutoMax) return 1;           // the streaming decode kernels
-    // the split runs on the 256x128 full-line tile: up to about one
-    // workgroup per CU, slices of at least 1024 k, at most 8
-    const int64_t tiles = cdiv(M, 256) * cdiv(N, 128);
-    int S = 1;
-    while (S < 8 && tiles * 2 * S <= 256 && K / (2 * S) >= 1024) S <<= 1;
-    return S;
+    if (dtype != DT_F16 && dtype != DT_BF16) return 1;
+    int tile;
+    return splitk_choice(M, N, K, a_kmajor, &tile);
 }
 
 size_t migemm_splitk_workspace_bytes(int M, int N, int splits)
@@ -231,13 +250,16 @@ int gemm_splitk_ex(int dtype, int a_kmajor, const uint16_t *A, const uint16_t *B
 {
     if (dtype != DT_F16 && dtype != DT_BF16) return MIGEMM_ERR_CONFIG;
     if (splits < 0 || a_kmajor < 0 || a_kmajor > 1) return MIGEMM_ERR_CONFIG;
-    int S = splits ? splits : migemm_splitk_splits(dtype, a_kmajor, M, N, K);
-    // slices run on tiles 9, 10, 13; the automatic tile with a split is 9
+    int auto_tile;
+    const int auto_S = splitk_choice(M, N, K, a_kmajor, &auto_tile);
+    int S = splits ? splits : auto_S;
+    // slices run on tiles 9, 10, 13; the automatic tile with a split is the
+    // rule's (9 when the caller fixed the slice count and the rule splits not)
     const bool split_tile = tile == TILE_256x128_FL || tile == TILE_256x256_FL8 || tile == TILE_128x128_SK;
     if (S > 1 && tile != TILE_AUTO && !split_tile) return MIGEMM_ERR_CONFIG;
     GemmLaunch L;
     bool launch;
-    int rc = plan_gemm(dtype, A, B, C, M, N, K, S > 1 && tile == TILE_AUTO ? TILE_256x128_FL : tile,
+    int rc = plan_gemm(dtype, A, B, C, M, N, K, S > 1 && tile == TILE_AUTO ? (auto_S > 1 ? auto_tile : TILE_256x128_FL) : tile,
                        group_m, xcd_remap, L, launch, a_kmajor != 0);
     if (S > 1 && tile == TILE_AUTO && rc == MIGEMM_ERR_CONFIG) {
         // operands without 16-byte rows take no full-line tile: no split

@@ -77,8 +77,8 @@ def main(argv=None):
     p.add_argument("--out", default=None, help="write a markdown summary here")
     p.add_argument("--rounds", type=int, default=5)
     p.add_argument("--skip-prefill-grid", action="store_true")
-    p.add_argument("--sections", default="gemm,decode,prefill,attention,q8",
-                   help="comma list of gemm, decode, prefill, attention, q8")
+    p.add_argument("--sections", default="gemm,decode,prefill,attention,q8,splitk",
+                   help="comma list of gemm, decode, prefill, attention, q8, splitk")
     p.add_argument("--decode-tiles", default="0",
                    help="gemm_tn tiles to time for the decode batches (0 = automatic)")
     p.add_argument("--attn-segments", default="16,32,0",
@@ -282,6 +282,30 @@ def main(argv=None):
         gemm_row("gemm_tn bf16 8192x8192x16384 (comparison)", binding.BF16, dA, dB, dC, Mq, Nq,
                  Kq, tn=True, launches=10)
         del dA, dB, dC
+
+    # --- split-K on shapes whose tiles do not fill the chip -----------------
+    if "splitk" in sections:
+        gk = torch.Generator(device="cuda")
+        gk.manual_seed(13)
+        ws = torch.empty(1 << 28, dtype=torch.float32, device="cuda")          # 1 GiB
+        for (Ms, Ns, Ks) in ((1024, 1024, 65536), (2048, 2048, 65536), (2048, 2048, 16384),
+                             (4096, 1024, 32768), (8192, 1024, 16384), (512, 512, 131072)):
+            dA = torch.randn(Ms * Ks, device="cuda", generator=gk).to(torch.bfloat16).view(torch.int16)
+            dB = torch.randn(Ks * Ns, device="cuda", generator=gk).to(torch.bfloat16).view(torch.int16)
+            dC = torch.empty(Ms * Ns, dtype=torch.int16, device="cuda")
+            gemm_row("gemm_ex (no split)", binding.BF16, dA, dB, dC, Ms, Ns, Ks, launches=10)
+            med, mn = _timer(torch, s, lambda i: L.gemm_splitk_ex(binding.BF16, 0, dA.data_ptr(), dB.data_ptr(),
+                                                                   dC.data_ptr(), Ms, Ns, Ks, 0, 0, 0, 1,
+                                                                   ws.data_ptr(), ws.numel() * 4, h),
+                             10, a.rounds)
+            tf = rf.gemm_flop(Ms, Ns, Ks) / med / 1e12
+            r = {"workload": "gemm_splitk_ex (automatic: %d slices)" % L.migemm_splitk_splits(binding.BF16, 0, Ms, Ns, Ks),
+                 "M": Ms, "N": Ns, "K": Ks, "layout": "column-major", "median_us": round(med * 1e6, 2),
+                 "min_us": round(mn * 1e6, 2), "tflops": round(tf, 1), "util": round(tf / peak, 4)}
+            rows.append(r)
+            print(json.dumps(r), flush=True)
+            del dA, dB, dC
+        del ws
 
     smi_after = _smi()
     if a.out:

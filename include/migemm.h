@@ -173,7 +173,8 @@ int gemm_tn_i8(const int8_t *At, const int8_t *B, uint16_t *C,
  * adds the partials and rounds once (RNE) to the 16-bit format.  splits 0 =
  * automatic (migemm_splitk_splits); 1 = no split (same as gemm_ex /
  * gemm_tn_ex).  Slices run on the full-line tiles 9, 10 and 13 (tile 0
- * with a split means 9); another explicit tile with splits > 1 is
+ * with a split: the automatic rule's tile, below); another explicit tile
+ * with splits > 1 is
  * MIGEMM_ERR_CONFIG, and operands without 16-byte rows run unsplit.
  * workspace: device, 16-byte aligned, at least
  * migemm_splitk_workspace_bytes(M, N, slices) bytes where slices =
@@ -186,10 +187,11 @@ int gemm_splitk_ex(int dtype, int a_kmajor, const uint16_t *A, const uint16_t *B
                    uint16_t *C, int M, int N, int K, int splits, int tile,
                    int group_m, int xcd_remap, void *workspace,
                    size_t workspace_bytes, void *stream);
-/* The automatic slice count (host only): doubles while twice the 256x128
- * tiles still fit about one workgroup per CU and slices keep >= 1024 k, at
- * most 8; 1 for shapes that fill the chip and for the k-major decode widths
- * (N <= 32), which stream A once anyway. */
+/* The automatic slice count (host only): the smallest power of two that
+ * gives the 256x256 tile (10) >= 256 workgroups, else the 256x128 tile (9)
+ * likewise (the automatic tile of gemm_splitk_ex follows), slices of >= 1024
+ * k, at most 32; 1 for shapes whose 256x256 tiles fill the chip and for the
+ * k-major decode widths (N <= 32), which stream A once anyway. */
 int migemm_splitk_splits(int dtype, int a_kmajor, int M, int N, int K);
 /* FP32 partial bytes for that many slices (0 when slices <= 1). */
 size_t migemm_splitk_workspace_bytes(int M, int N, int splits);

@@ -147,10 +147,12 @@ def test_exact_shape_table():
 
 def test_splitk_rules_and_errors():
     L = binding.lib()
-    # automatic slices: up to ~1 workgroup per CU on the 256x128 tile, >= 1024 k each, <= 8
-    assert L.migemm_splitk_splits(1, 0, 2048, 2048, 65536) == 2
-    assert L.migemm_splitk_splits(1, 0, 1024, 1024, 65536) == 8
-    assert L.migemm_splitk_splits(0, 1, 1024, 1024, 4096) == 4       # 1024 k per slice
+    # automatic slices: >= 256 workgroups on the 256x256 tile, else 256x128; >= 1024 k each, <= 32
+    assert L.migemm_splitk_splits(1, 0, 2048, 2048, 65536) == 4        # 64 tiles x 4
+    assert L.migemm_splitk_splits(1, 0, 8192, 1024, 16384) == 2        # 128 tiles x 2
+    assert L.migemm_splitk_splits(1, 0, 1024, 1024, 65536) == 16       # 16 tiles x 16
+    assert L.migemm_splitk_splits(1, 0, 512, 512, 131072) == 32        # 256x128: 8 tiles x 32
+    assert L.migemm_splitk_splits(0, 1, 1024, 1024, 4096) == 4         # 1024 k per slice
     assert L.migemm_splitk_splits(0, 0, 8192, 8192, 16384) == 1
     assert L.migemm_splitk_splits(1, 1, 34816, 16, 5120) == 1      # decode widths stream A once
     assert L.migemm_splitk_splits(2, 1, 1024, 1024, 65536) == 1    # 8-bit types: no split

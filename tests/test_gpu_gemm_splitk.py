@@ -20,7 +20,7 @@ def _splitk(A, B, M, N, K, fmt, a_kmajor, splits, tile=0):
     dA, dB = dev(A), dev(B)
     cA, cB = dA.clone(), dB.clone()
     C = Guarded(M * N)
-    ws_bytes = max(16, L.migemm_splitk_workspace_bytes(M, N, max(splits, 8)))
+    ws_bytes = max(16, L.migemm_splitk_workspace_bytes(M, N, max(splits, 32)))
     ws = torch.empty(ws_bytes // 4 + 4, dtype=torch.float32, device="cuda")
     code = L.gemm_splitk_ex(0 if fmt == "f16" else 1, a_kmajor, dA.data_ptr(), dB.data_ptr(), C.ptr,
                             M, N, K, splits, tile, 0, 1, ws.data_ptr(), ws_bytes, None)
