@@ -191,7 +191,9 @@ batch_kernel(const uint16_t *__restrict__ W, const uint16_t *__restrict__ X,
 template <int DT, int NTT>
 static hipError_t launch_ntt(const SkinnyLaunch &L, hipStream_t s)
 {
-    constexpr int U = 4;
+    // 4 chunks of W in flight; 2 for the 64- and 128-token blocks, whose X
+    // staging already takes the registers (measured faster there)
+    constexpr int U = NTT >= 4 ? 2 : 4;
     const dim3 grid((unsigned)((L.M + 63) / 64), (unsigned)((L.n + NTT * 16 - 1) / (NTT * 16)));
     hipLaunchKernelGGL((batch_kernel<DT, NTT, U>), grid, dim3(256), 0, s, L.W, L.X, L.Y, L.M, L.K,
                        L.n, L.y_vec);

@@ -121,11 +121,11 @@ constexpr int kSkinnyMinTokens = 3;    // the automatic GEMV switches to MFMA fr
 // to kBatchMaxTokens tokens.
 constexpr int kBatchMaxTokens = 128;
 // Automatic choice (measured on W 34816 x 5120): the 4x4x4 kernel up to 4
-// tokens, the batch kernel up to 32 (its 64- and 128-token blocks hold too
-// much LDS and too many registers per workgroup to keep W streaming), then
-// the GEMM's 256x128 tile.
+// tokens, the batch kernel up to 64 (its 128-token block holds 86 KB of LDS
+// per workgroup, too little residency to keep W streaming), then the GEMM's
+// 256x128 tile.
 constexpr int kSkinnyAutoMax = 4;
-constexpr int kBatchAutoMax = 32;
+constexpr int kBatchAutoMax = 64;
 struct SkinnyLaunch {
     int dtype;
     const uint16_t *W, *X;        // W row-major [M, K], X row-major [n, K]

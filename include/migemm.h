@@ -84,7 +84,7 @@ int gemm_bf16(const uint16_t *A, const uint16_t *B, uint16_t *C,
  * n may be any positive value.  n <= 2 (or K not a multiple of 8, or W, X
  * not 16-byte aligned) runs the row-blocked vector kernel; from 3 tokens on,
  * with 16-byte rows, the multiply-adds run on MFMA: up to 4 tokens on the
- * 4x4x4 MFMA with W streamed straight into operand registers, up to 32 on
+ * 4x4x4 MFMA with W streamed straight into operand registers, up to 64 on
  * the 16x16x32 MFMA with W read as whole cache lines and the token block of
  * X staged in LDS (tile 15 below), beyond that as gemm_tn_bf16 on the
  * 256x128 full-line tile.  gemv_bf16_ex with a non-zero rows_per_block always runs
@@ -191,7 +191,7 @@ int gemm_splitk_ex(int dtype, int a_kmajor, const uint16_t *A, const uint16_t *B
  * gives the 256x256 tile (10) >= 256 workgroups, else the 256x128 tile (9)
  * likewise (the automatic tile of gemm_splitk_ex follows), slices of >= 1024
  * k, at most 32; 1 for shapes whose 256x256 tiles fill the chip and for the
- * k-major decode widths (N <= 32), which stream A once anyway. */
+ * k-major decode widths (N <= 64), which stream A once anyway. */
 int migemm_splitk_splits(int dtype, int a_kmajor, int M, int N, int K);
 /* FP32 partial bytes for that many slices (0 when slices <= 1). */
 size_t migemm_splitk_workspace_bytes(int M, int N, int splits);
@@ -240,7 +240,7 @@ int gemm_ex(int dtype, const uint16_t *A, const uint16_t *B, uint16_t *C,
  * with Y row-major [N, M] -- the GEMV's own layout.  Same argument checks,
  * ownership and completion rules as gemm_f16 / gemm_bf16.  Runs on the
  * full-line tiles only: tile 0 (automatic: 14 for N <= 4, 15 for
- * N <= 32, else 10 or 9) or 7 .. 15 (A takes B's 64-k ring layout;
+ * N <= 64, else 10 or 9) or 7 .. 15 (A takes B's 64-k ring layout;
  * MIGEMM_ERR_CONFIG for other tiles, and for 14 with N > 8 or 15 with
  * N > 128).  K must be a
  * multiple of 8 and At, B 16-byte aligned (else MIGEMM_ERR_ALIGN).

@@ -113,8 +113,8 @@ def test_tn_plan_and_errors():
         code, p = binding.gemm_plan(1, P, P + 2 ** 30, P + 2 ** 31, 34816, n, 5120, 15, a_kmajor=True)
         assert code == 0 and (p["tile"], p["tile_m"], p["tile_n"], p["tile_k"], p["waves"]) == (15, 64, tn, 128, 4)
         assert p["grid"] == 544 and p["lds_bytes"] == 2 * tn * 272 + 4 * 4096
-    assert binding.gemm_plan(1, P, P + 2 ** 30, P + 2 ** 31, 34816, 32, 5120, a_kmajor=True)[1]["tile"] == 15
-    assert binding.gemm_plan(1, P, P + 2 ** 30, P + 2 ** 31, 34816, 33, 5120, a_kmajor=True)[1]["tile"] == 9
+    assert binding.gemm_plan(1, P, P + 2 ** 30, P + 2 ** 31, 34816, 64, 5120, a_kmajor=True)[1]["tile"] == 15
+    assert binding.gemm_plan(1, P, P + 2 ** 30, P + 2 ** 31, 34816, 65, 5120, a_kmajor=True)[1]["tile"] == 9
     assert L.gemm_tn_ex(0, P, P + 0x100000, P + 0x200000, 64, 129, 64, 15, 0, 1, None) == -5
     assert L.gemm_ex(0, P, P + 0x100000, P + 0x200000, 64, 16, 64, 15, 0, 1, None) == -5
     # only the full-line tiles take a k-major A
