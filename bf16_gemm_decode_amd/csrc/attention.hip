@@ -14,29 +14,27 @@
 //
 // Segment kernel: one workgroup (4 waves) per (kv head, segment, sequence),
 // kv heads fastest so the workgroups reading the same token rows run
-// together.  A K or V row of D BF16 values is D/8 lanes x 16 bytes, so one
-// wave load reads 64/(D/8) whole rows (2 rows of 512 B at D = 256): full
-// cache lines, every 4 lanes contiguous.  Up to 4 query heads of the kv head
-// share every K and V load.  Each lane keeps its 8 elements of q (per head,
-// pre-multiplied by scale * log2 e so that exponentials are powers of two)
-// and its 8 elements of the running output; a token's score is the dot
-// product summed across its D/8 lanes with DPP row operations (and one
-// swizzle at D = 256).  The 4 waves split the segment's tokens and walk
-// them in steps of 4 wave loads of K and of V, triple-buffered in
-// registers: while a step is computed the next two steps' rows are in
-// flight, and the page ids of the step after those (each lane reads the
-// block-table entry of its own row) are on their way.
-// Per step and head: one rescale of the running state, then exp2 and
-// prob * V, branch-free.  At the end the token slots of a wave and then
-// the 4 waves are merged, and the segment's (max, denominator,
-// unnormalised output) go to the workspace in FP32.
+// together; up to 4 query heads of the kv head share every K and V load (a
+// larger group is split over workgroups, whose second read of the rows the
+// caches serve).  A K or V row of D BF16 values is D/8 lanes x 16 bytes, so
+// one wave load reads 64/(D/8) whole rows (2 rows of 512 B at D = 256): full
+// cache lines.  The 4 waves split the segment's tokens and walk them in
+// steps of 16 tokens, double-buffered in registers (the next step's rows
+// in flight while one is computed, the page ids of the step after that on
+// their way; each lane reads the block-table entry of its own row).  Per
+// step, q K^T is one 16-token x 16-head tile on the matrix cores, the
+// online softmax runs once per (token, head), and prob V runs on the vector
+// ALUs; the details are at the kernel.  At the end the token slots of a
+// wave and then the 4 waves are merged, and the segment's (max,
+// denominator, unnormalised output) go to the workspace in FP32.
 //
 // Merge kernel: one workgroup per (query head, sequence, 64 output
 // columns); each thread merges a quarter of the segments of its column
 // online (log-sum-exp), the quarters are merged through LDS, then one
 // division and one rounding to BF16.  Empty segments (max = -inf, denominator 0) add
 // nothing; a sequence with no token gives zeros.  Tokens whose page id is
-// outside [0, num_blocks) are skipped instead of read.
+// outside [0, num_blocks) add nothing: their rows are read from a block of
+// zeros and their scores are -inf.
 #include "common.hpp"
 #include "kernels.hpp"
 
@@ -68,55 +66,56 @@ __device__ inline void merge_state(float &m, float &l, float (&o)[8], float m2, 
 
 }  // namespace
 
-// Sum over aligned groups of CPL lanes (8, 16 or 32), the total in every
-// lane of the group: DPP row rotations and quad permutes within a row of 16
-// lanes, one swizzle across the two rows of a 32-lane group.
-template <int CTRL>
-__device__ inline float dpp_f(float x)
-{
-    return __builtin_bit_cast(float, __builtin_amdgcn_update_dpp(0, __builtin_bit_cast(int, x), CTRL,
-                                                                 0xf, 0xf, true));
-}
+// 16 zero bytes in device memory: masked K and V rows load from here, so a
+// token past the range or on an invalid page contributes exact zeros (row 0
+// of a cache page could hold anything).
+__device__ const uint16_t kAttnZeros[8] = {0, 0, 0, 0, 0, 0, 0, 0};
 
-template <int CPL>
-__device__ inline float group_sum(float x)
-{
-    if constexpr (CPL >= 16) {
-        x += dpp_f<0x128>(x);                        // row_ror:8
-        x += dpp_f<0x124>(x);                        // row_ror:4
-    }
-    x += dpp_f<0x4e>(x);                             // quad_perm [2,3,0,1]
-    x += dpp_f<0xb1>(x);                             // quad_perm [1,0,3,2]
-    if constexpr (CPL == 8) x += dpp_f<0x141>(x);    // row_half_mirror: the other quad
-    if constexpr (CPL == 32)                         // lane ^ 16 within 32 lanes
-        x += __builtin_bit_cast(float, __builtin_amdgcn_ds_swizzle(__builtin_bit_cast(int, x), 0x401f));
-    return x;
-}
+typedef const __attribute__((address_space(1))) u32x4 *attn_gptr16;
 
-// G query heads per workgroup: all of a kv head's group when it has up to
-// 4 heads, else 4 of them (the workgroups of one kv head then read the same
-// K and V rows; the second read is served by the caches).
+// One step of 16 tokens:
+//  * scores: the step's K rows (loaded in the row layout) are written to a
+//    wave-private LDS tile, row t's 16-byte piece x at t*2D + 16*(x ^ f(t)),
+//    and read back as A operands of v_mfma_f32_16x16x32_bf16 (token l%16,
+//    d 32*kk + 8*(l/16)); Q^T of the G query heads is the B operand (head
+//    l%16, zero past G), read from a copy staged once in LDS;
+//  * softmax once per (token, head) in the MFMA result layout (lane l:
+//    head l%16, tokens 4*(l/16) .. +3): step max over the 16 tokens, one
+//    rescale of the running state per head (kept per lane, the same in the
+//    4 lanes of a head), exp2, the running denominator;
+//  * prob x V on the VALU in the row layout, each lane reading its token's
+//    probabilities and the step's per-head rescale from LDS.  All token
+//    slots of a wave share one running maximum, so the slots add up at the
+//    end without rescaling; the 4 waves then merge through LDS.
 template <int D, int G>
 __global__ void __launch_bounds__(kAttnWaves * 64)
 attn_segment_kernel(const uint16_t *__restrict__ Q, const uint16_t *__restrict__ Kc,
-                    const uint16_t *__restrict__ Vc, const int32_t *__restrict__ block_table,
-                    const int32_t *__restrict__ seq_lens, float *__restrict__ part_o,
-                    float *__restrict__ part_ml, int Hq, int Hkv, int group, int block_size,
-                    int max_blocks, int num_blocks, float qscale, int S)
+                 const uint16_t *__restrict__ Vc, const int32_t *__restrict__ block_table,
+                 const int32_t *__restrict__ seq_lens, float *__restrict__ part_o,
+                 float *__restrict__ part_ml, int Hq, int Hkv, int group, int block_size,
+                 int max_blocks, int num_blocks, float qscale, int S)
 {
     constexpr int CPL = D / 8;          // lanes per cached row (16 bytes each)
     constexpr int TPI = 64 / CPL;       // rows per wave load
-    constexpr int U = 4;                // wave loads of K (and of V) per step
-    constexpr int T = TPI * U;          // tokens per wave step (<= 64)
-    static_assert(D % 64 == 0 && D <= 256 && T <= 64, "head dim");
+    constexpr int T = 16;               // tokens per step: one MFMA tile
+    constexpr int U = T / TPI;          // wave loads of K (and of V) per step
+    constexpr int KS = D / 32;          // MFMA k-steps over the head dim
+    constexpr int KROW = 2 * D;         // bytes of one staged K row
+    static_assert(D % 64 == 0 && D <= 256 && G <= 4, "shape");
+    __shared__ __attribute__((aligned(16))) uint8_t kt[kAttnWaves][T * KROW];
+    __shared__ __attribute__((aligned(16))) float pt[kAttnWaves][T][4];    // probabilities [token][head]
+    __shared__ __attribute__((aligned(16))) float ct[kAttnWaves][4];       // per-head rescale of a step
+    __shared__ __attribute__((aligned(16))) float vt[kAttnWaves][T];       // 0 or -inf per token
+    __shared__ __attribute__((aligned(16))) uint16_t qt[16][D + 8];        // Q^T operand rows
     __shared__ float xs[kAttnWaves][G][2 + D];
 
-    const int parts = group / G;                        // workgroups per kv head
+    const int parts = group / G;
     const int kvh = blockIdx.x / parts, s = blockIdx.y, b = blockIdx.z;
-    const int h0 = kvh * group + (blockIdx.x % parts) * G;  // first query head
+    const int h0 = kvh * group + (blockIdx.x % parts) * G;
     const int lane = threadIdx.x & 63;
     const int wave = uniform(threadIdx.x >> 6);
     const int slot = lane / CPL, c = lane % CPL;
+    const int g = lane >> 4, r16 = lane & 15;
 
     int L = seq_lens[b];
     L = L < 0 ? 0 : (L > max_blocks * block_size ? max_blocks * block_size : L);
@@ -125,183 +124,188 @@ attn_segment_kernel(const uint16_t *__restrict__ Q, const uint16_t *__restrict__
     const int per = (l1 - l0 + kAttnWaves - 1) / kAttnWaves;
     const int w0 = min(l1, l0 + wave * per), w1 = min(l1, w0 + per);
 
-    // this lane's 8 elements of q for the G heads, in log2 units
-    float q[G][8];
-#pragma unroll
-    for (int h = 0; h < G; ++h) {
-        const u32x4 v = *(const u32x4 *)(Q + ((size_t)b * Hq + h0 + h) * D + c * 8);
-#pragma unroll
-        for (int e = 0; e < 4; ++e) {
-            q[h][2 * e] = __builtin_bit_cast(float, v[e] << 16) * qscale;
-            q[h][2 * e + 1] = __builtin_bit_cast(float, v[e] & 0xffff0000u) * qscale;
-        }
+    // Q^T as B operands, staged once in LDS: row h < G holds query head
+    // h0 + h, rows G .. 15 are zero; lane (g, h) reads Q[h0 + h][32 kk + 8 g .. +7]
+    for (int i = threadIdx.x; i < 16 * (D / 8); i += kAttnWaves * 64) {
+        const int h = i / (D / 8), x = i % (D / 8);
+        u32x4 v = {0u, 0u, 0u, 0u};
+        if (h < G) v = *(const u32x4 *)(Q + ((size_t)b * Hq + h0 + h) * D + 8 * x);
+        *(u32x4 *)&qt[h][8 * x] = v;
     }
+    __syncthreads();
 
-    float m[G], l[G], o[G][8];
+    float mrun = kNegInf, lrun = 0.f;      // head r16's running max (log2 units) and denominator
+    float o[G][8];
 #pragma unroll
-    for (int h = 0; h < G; ++h) {
-        m[h] = kNegInf;
-        l[h] = 0.f;
+    for (int h = 0; h < G; ++h)
 #pragma unroll
         for (int e = 0; e < 8; ++e) o[h][e] = 0.f;
-    }
 
     const int32_t *bt = block_table + (size_t)b * max_blocks;
-    const size_t row_stride = (size_t)Hkv * D;          // elements between tokens in a page
+    const size_t row_stride = (size_t)Hkv * D;
     const size_t lane_off = (size_t)kvh * D + c * 8;
     const float inv_bs = 1.0f / (float)block_size;
+    uint8_t *ktw = kt[wave];
+    // swizzle of a staged K row: keeps the 16 rows of an operand read in
+    // distinct banks
+    auto swz = [](int t) { return D == 64 ? (t >> 1) & 7 : t & 15; };
 
-    // Page id and slot of every row this lane loads in the step starting
-    // at token t (id -1 past the range).  Each lane reads the block-table
-    // entry of its own token (lanes on one page share the address); the
-    // read itself is unconditional, from a clamped index.
-    auto page_ids = [&](int t, int (&pg)[U], int (&in)[U]) {
+    // Page id of every row this lane loads in the step starting at t (-1
+    // past the range); each lane reads its own token's block-table entry.
+    auto page_ids = [&](int t, int (&pg)[U]) {
         const int pf = t / block_size;
         const int r0 = t - pf * block_size;
 #pragma unroll
         for (int u = 0; u < U; ++u) {
-            const int rel = r0 + TPI * u + slot;                 // < block_size + T
+            const int rel = r0 + TPI * u + slot;
             int idx = (int)((float)rel * inv_bs);
-            int i = rel - idx * block_size;
-            if (i < 0) { --idx; i += block_size; }
-            else if (i >= block_size) { ++idx; i -= block_size; }
-            in[u] = i;
+            const int i = rel - idx * block_size;
+            idx += i < 0 ? -1 : (i >= block_size ? 1 : 0);
             const int v = bt[min(pf + idx, max_blocks - 1)];
             pg[u] = t + TPI * u + slot < w1 ? v : -1;
         }
     };
-    // K and V loads (non-temporal: every row is read once) of one step.  A
-    // row past the range or on an invalid page loads row 0 of the cache
-    // (always in bounds) and is masked out by ok.
-    auto issue = [&](const int (&pg)[U], const int (&in)[U], u32x4 (&kr)[U], u32x4 (&vr)[U],
-                     bool (&ok)[U]) {
+    // K and V loads of a step (non-temporal); masked rows read zeros
+    auto issue = [&](int t, const int (&pg)[U], u32x4 (&kr)[U], u32x4 (&vr)[U], bool (&ok)[U]) {
+        const int pf = t / block_size;
+        const int r0 = t - pf * block_size;
 #pragma unroll
         for (int u = 0; u < U; ++u) {
+            const int rel = r0 + TPI * u + slot;
+            int idx = (int)((float)rel * inv_bs);
+            int in = rel - idx * block_size;
+            if (in < 0) in += block_size;
+            else if (in >= block_size) in -= block_size;
             ok[u] = pg[u] >= 0 && pg[u] < num_blocks;
-            const size_t off = ok[u] ? ((size_t)pg[u] * block_size + in[u]) * row_stride + lane_off : 0;
-            kr[u] = __builtin_nontemporal_load((const u32x4 *)(Kc + off));
-            vr[u] = __builtin_nontemporal_load((const u32x4 *)(Vc + off));
+            const size_t off = ((size_t)pg[u] * block_size + in) * row_stride + lane_off;
+            kr[u] = __builtin_nontemporal_load((attn_gptr16)(ok[u] ? Kc + off : kAttnZeros));
+            vr[u] = __builtin_nontemporal_load((attn_gptr16)(ok[u] ? Vc + off : kAttnZeros));
         }
     };
 
-    // One step: scores of the U x TPI tokens for the G heads (dot product
-    // over the CPL lanes of a row), one rescale of the running state per
-    // head, then prob * V.
     auto step = [&](const u32x4 (&kr)[U], const u32x4 (&vr)[U], const bool (&ok)[U]) {
-        float sc[U][G];
+        // K rows into the tile, token validity beside them
 #pragma unroll
         for (int u = 0; u < U; ++u) {
-            float kf[8];
+            const int t = TPI * u + slot;
+            *(u32x4 *)(ktw + t * KROW + 16 * (c ^ swz(t))) = kr[u];
+            if (c == 0) vt[wave][t] = ok[u] ? 0.f : kNegInf;
+        }
+        __builtin_amdgcn_s_waitcnt(0xc07f);             // lgkmcnt(0): wave-private tile
+        f32x4 sacc = {0.f, 0.f, 0.f, 0.f};
+#pragma unroll
+        for (int kk = 0; kk < KS; ++kk) {
+            const u32x4 a = *(const u32x4 *)(ktw + r16 * KROW + 16 * ((4 * kk + g) ^ swz(r16)));
+            sacc = __builtin_amdgcn_mfma_f32_16x16x32_bf16(__builtin_bit_cast(bf16x8, a),
+                                                          __builtin_bit_cast(bf16x8, *(const u32x4 *)&qt[r16][32 * kk + 8 * g]),
+                                                          sacc, 0, 0, 0);
+        }
+        // softmax bookkeeping for head r16 over tokens 4g .. 4g+3 of the tile
+        const f32x4 valid = *(const f32x4 *)&vt[wave][4 * g];
+        float sv[4];
+#pragma unroll
+        for (int r = 0; r < 4; ++r) sv[r] = fmaf(sacc[r], qscale, valid[r]);
+        float mt = fmaxf(fmaxf(sv[0], sv[1]), fmaxf(sv[2], sv[3]));
+        mt = fmaxf(mt, __shfl_xor(mt, 16, 64));
+        mt = fmaxf(mt, __shfl_xor(mt, 32, 64));
+        const float mn = fmaxf(mrun, mt);
+        const float ref = mn == kNegInf ? 0.f : mn;     // exp2(-inf - ref) = 0 while nothing is seen
+        const float corr = __builtin_amdgcn_exp2f(mrun - ref);
+        float p[4], psum = 0.f;
+#pragma unroll
+        for (int r = 0; r < 4; ++r) {
+            p[r] = __builtin_amdgcn_exp2f(sv[r] - ref);
+            psum += p[r];
+        }
+        psum += __shfl_xor(psum, 16, 64);
+        psum += __shfl_xor(psum, 32, 64);
+        lrun = lrun * corr + psum;
+        mrun = mn;
+        if (r16 < G) {
+#pragma unroll
+            for (int r = 0; r < 4; ++r) pt[wave][4 * g + r][r16] = p[r];
+            if (g == 0) ct[wave][r16] = corr;
+        }
+        __builtin_amdgcn_s_waitcnt(0xc07f);
+        // prob x V for this lane's tokens
+        const f32x4 cr = *(const f32x4 *)ct[wave];
+#pragma unroll
+        for (int h = 0; h < G; ++h)
+#pragma unroll
+            for (int e = 0; e < 8; ++e) o[h][e] *= cr[h];
+#pragma unroll
+        for (int u = 0; u < U; ++u) {
+            const f32x4 pp = *(const f32x4 *)pt[wave][TPI * u + slot];
 #pragma unroll
             for (int e = 0; e < 4; ++e) {
-                kf[2 * e] = __builtin_bit_cast(float, kr[u][e] << 16);
-                kf[2 * e + 1] = __builtin_bit_cast(float, kr[u][e] & 0xffff0000u);
-            }
+                const float v0 = __builtin_bit_cast(float, vr[u][e] << 16);
+                const float v1 = __builtin_bit_cast(float, vr[u][e] & 0xffff0000u);
 #pragma unroll
-            for (int h = 0; h < G; ++h) {
-                float p = 0.f;
-#pragma unroll
-                for (int e = 0; e < 8; ++e) p = fmaf(q[h][e], kf[e], p);
-                p = group_sum<CPL>(p);
-                sc[u][h] = ok[u] ? p : kNegInf;
-            }
-        }
-#pragma unroll
-        for (int h = 0; h < G; ++h) {
-            float mb = sc[0][h];
-#pragma unroll
-            for (int u = 1; u < U; ++u) mb = fmaxf(mb, sc[u][h]);
-            const float mn = fmaxf(m[h], mb);
-            // branch-free: while nothing has been seen, any finite reference
-            // gives exp2(-inf - ref) = 0 (v_exp_f32 maps -inf to +0)
-            const float ref = mn == kNegInf ? 0.f : mn;
-            const float corr = __builtin_amdgcn_exp2f(m[h] - ref);
-            l[h] *= corr;
-#pragma unroll
-            for (int e = 0; e < 8; ++e) o[h][e] *= corr;
-            m[h] = mn;
-#pragma unroll
-            for (int u = 0; u < U; ++u) {
-                const float p = __builtin_amdgcn_exp2f(sc[u][h] - ref);
-                l[h] += p;
-#pragma unroll
-                for (int e = 0; e < 4; ++e) {
-                    o[h][2 * e] = fmaf(p, __builtin_bit_cast(float, vr[u][e] << 16), o[h][2 * e]);
-                    o[h][2 * e + 1] = fmaf(p, __builtin_bit_cast(float, vr[u][e] & 0xffff0000u), o[h][2 * e + 1]);
+                for (int h = 0; h < G; ++h) {
+                    o[h][2 * e] = fmaf(pp[h], v0, o[h][2 * e]);
+                    o[h][2 * e + 1] = fmaf(pp[h], v1, o[h][2 * e + 1]);
                 }
             }
         }
     };
 
-    // Three register buffers rotate: while one step is computed, the next
-    // two steps' K and V are in flight.  The page ids of the step after
-    // those are requested before the K and V loads issued alongside, so
-    // waiting for the ids never waits for the newest loads.
-    u32x4 ka[U], va[U], kb[U], vb[U], kx[U], vx[U];
-    bool oka[U], okb[U], okx[U];
-    int pa[U], ia[U], pb[U], ib[U], px[U], ix[U];
-    page_ids(w0, pa, ia);
-    page_ids(w0 + T, pb, ib);
-    page_ids(w0 + 2 * T, px, ix);
-    issue(pa, ia, ka, va, oka);
-    issue(pb, ib, kb, vb, okb);
-    for (int t0 = w0; t0 < w1; t0 += 3 * T) {
-        page_ids(t0 + 3 * T, pa, ia);
-        issue(px, ix, kx, vx, okx);
+    // two register buffers: while one step is computed the next one's K and
+    // V are in flight; each step's page ids are requested before the loads
+    // issued alongside them
+    u32x4 ka[U], va[U], kb2[U], vb2[U];
+    bool oka[U], okb[U];
+    int pa[U], pb[U];
+    page_ids(w0, pa);
+    page_ids(w0 + T, pb);
+    issue(w0, pa, ka, va, oka);
+    for (int t0 = w0; t0 < w1; t0 += 2 * T) {
+        page_ids(t0 + 2 * T, pa);
+        issue(t0 + T, pb, kb2, vb2, okb);
         step(ka, va, oka);
         if (t0 + T >= w1) break;
-        page_ids(t0 + 4 * T, pb, ib);
-        issue(pa, ia, ka, va, oka);
-        step(kb, vb, okb);
-        if (t0 + 2 * T >= w1) break;
-        page_ids(t0 + 5 * T, px, ix);
-        issue(pb, ib, kb, vb, okb);
-        step(kx, vx, okx);
+        page_ids(t0 + 3 * T, pb);
+        issue(t0 + 2 * T, pa, ka, va, oka);
+        step(kb2, vb2, okb);
     }
 
-    // merge the token slots of the wave (lanes c, c + CPL, ...), one head
-    // at a time
+    // the token slots of a wave share the running max: add their outputs
 #pragma unroll
     for (int h = 0; h < G; ++h)
 #pragma unroll
-        for (int x = CPL; x < 64; x <<= 1) {
-            float o2[8];
+        for (int x = CPL; x < 64; x <<= 1)
 #pragma unroll
-            for (int e = 0; e < 8; ++e) o2[e] = __shfl_xor(o[h][e], x, 64);
-            merge_state(m[h], l[h], o[h], __shfl_xor(m[h], x, 64), __shfl_xor(l[h], x, 64), o2);
-        }
-    // then the waves, through LDS; wave 0 writes the segment's state
+            for (int e = 0; e < 8; ++e) o[h][e] += __shfl_xor(o[h][e], x, 64);
     if (slot == 0) {
 #pragma unroll
-        for (int h = 0; h < G; ++h) {
-            if (c == 0) {
-                xs[wave][h][0] = m[h];
-                xs[wave][h][1] = l[h];
-            }
+        for (int h = 0; h < G; ++h)
 #pragma unroll
             for (int e = 0; e < 8; ++e) xs[wave][h][2 + c * 8 + e] = o[h][e];
-        }
+    }
+    if (g == 0 && r16 < G) {
+        xs[wave][r16][0] = mrun;
+        xs[wave][r16][1] = lrun;
     }
     __syncthreads();
     if (wave != 0 || slot != 0) return;
 #pragma unroll
-    for (int h = 0; h < G; ++h)
+    for (int h = 0; h < G; ++h) {
+        float m = xs[0][h][0], l = xs[0][h][1], acc[8];
+#pragma unroll
+        for (int e = 0; e < 8; ++e) acc[e] = xs[0][h][2 + c * 8 + e];
 #pragma unroll
         for (int w = 1; w < kAttnWaves; ++w) {
             float o2[8];
 #pragma unroll
             for (int e = 0; e < 8; ++e) o2[e] = xs[w][h][2 + c * 8 + e];
-            merge_state(m[h], l[h], o[h], xs[w][h][0], xs[w][h][1], o2);
+            merge_state(m, l, acc, xs[w][h][0], xs[w][h][1], o2);
         }
-#pragma unroll
-    for (int h = 0; h < G; ++h) {
         const size_t row = ((size_t)b * Hq + h0 + h) * S + s;
         if (c == 0) {
-            part_ml[row * 2] = m[h];
-            part_ml[row * 2 + 1] = l[h];
+            part_ml[row * 2] = m;
+            part_ml[row * 2 + 1] = l;
         }
 #pragma unroll
-        for (int e = 0; e < 8; ++e) part_o[row * D + c * 8 + e] = o[h][e];
+        for (int e = 0; e < 8; ++e) part_o[row * D + c * 8 + e] = acc[e];
     }
 }
 
