@@ -49,7 +49,7 @@ constexpr ShapeConfig kShapeTable[] = {
     {DT_F16, 0, 8192, 8192, 16384, TILE_256x256_FL8, 8},
     {DT_BF16, 0, 4096, 34816, 5120, TILE_256x256_FL8, 16},    // 1.261 ms vs 1.270 at 8
     {DT_BF16, 1, 34816, 4096, 5120, TILE_256x256_FL8, 4},     // 1.316 ms vs 1.354 at 8
-    {DT_BF16, 0, 5000, 3000, 4100, TILE_128x128, 8},
+    {DT_BF16, 0, 5000, 3000, 4100, TILE_256x256_FL8, 16},    // 120 us vs 201 on 128x128
 };
 
 const ShapeConfig *find_shape(int dtype, bool a_kmajor, int M, int N, int K)
@@ -98,14 +98,41 @@ int plan_gemm(int dtype, const uint16_t *A, const uint16_t *B, const uint16_t *C
     L.vec_b = vec_width(B, K);
     L.c_vec = (M % 4 == 0 && (uintptr_t)C % 8 == 0) ? 1 : 0;
     L.a_kmajor = a_kmajor ? 1 : 0;
+    // wide: 16-byte aligned rows of A and B (every tile).  fl: 4-byte
+    // aligned rows, enough for the full-line tiles, whose 16-byte loads need
+    // dword alignment only; their k loop stops at a multiple of 8 and adds
+    // the last K % 8 k after it.
     const bool wide = (L.vec_a == 8 && L.vec_b == 8);
+    const bool fl = (L.vec_a >= 2 && L.vec_b >= 2);
+    auto is_fl = [](int t) { return t >= TILE_256x256_FL && t <= TILE_128x128_SK; };
     if (tile == TILE_AUTO && group_m == 0 && !q8) {
         const ShapeConfig *c = find_shape(dtype, a_kmajor, M, N, K);
-        if (c && (wide || c->tile == TILE_128x128)) {
+        if (c && (wide || c->tile == TILE_128x128 || (fl && is_fl(c->tile)))) {
             tile = c->tile;
             group_m = c->group_m;
         }
     }
+    // Automatic tile for a 16-bit GEMM: the least estimated time, counting
+    // rounds of workgroups over the 256 CUs.  Per round at K = 4096 (one
+    // MI355X, square and 2:1 shapes from 1024 to 8192): 256x256 with 8 waves
+    // 110 us per 256 tiles; 256x128 80 us per 256; 128x128 56 us for up to
+    // 256 tiles, then 85 us per 512 (two workgroups per CU; the full-line
+    // 128x128 takes 56 us per 256).
+    auto auto_tile = [&]() {
+        const int64_t t256 = cdiv(M, 256) * cdiv(N, 256), t2 = cdiv(M, 256) * cdiv(N, 128),
+                      t128 = cdiv(M, 128) * cdiv(N, 128);
+        int best = TILE_128x128;
+        int64_t cost = INT64_MAX;
+        auto take = [&](int t, int64_t c) {
+            if (c < cost) { cost = c; best = t; }
+        };
+        if (fl) take(TILE_256x256_FL8, cdiv(t256, 256) * 110);
+        if (wide && !a_kmajor) take(TILE_256x128, cdiv(t2, 256) * 80);
+        else if (fl) take(TILE_256x128_FL, cdiv(t2, 256) * 80);
+        if (!a_kmajor) take(TILE_128x128, t128 <= 256 ? 56 : cdiv(t128, 512) * 85);
+        else if (fl) take(TILE_128x128_SK, cdiv(t128, 256) * 56);
+        return best;
+    };
     if (a_kmajor && q8) {
         if (!wide) return MIGEMM_ERR_ALIGN;
         if (tile == TILE_AUTO)
@@ -113,30 +140,25 @@ int plan_gemm(int dtype, const uint16_t *A, const uint16_t *B, const uint16_t *C
                    : cdiv(M, 256) * cdiv(N, 128) >= 256 ? TILE_256x128_FL
                                                         : TILE_128x128_SK;
     } else if (a_kmajor) {
-        // k-major A: the full-line tiles only, 16-byte rows of A and B
-        if (!wide) return MIGEMM_ERR_ALIGN;
+        // k-major A: the full-line tiles (4-byte rows) and, with 16-byte
+        // rows, the few-token kernels
+        if (!fl) return MIGEMM_ERR_ALIGN;
         if (tile == TILE_AUTO) {
-            tile = N <= kSkinnyAutoMax ? TILE_SKINNY
-                   : N <= kBatchAutoMax ? TILE_BATCH
-                   : cdiv(M, 256) * cdiv(N, 256) >= 512 ? TILE_256x256_FL8
-                                                        : TILE_256x128_FL;
-        } else if (tile < TILE_256x256_FL || (tile == TILE_SKINNY && N > kSkinnyMaxTokens) ||
+            tile = wide && N <= kSkinnyAutoMax ? TILE_SKINNY
+                   : wide && N <= kBatchAutoMax ? TILE_BATCH
+                                                : auto_tile();
+        } else if ((tile < TILE_256x256_FL) || (tile == TILE_SKINNY && N > kSkinnyMaxTokens) ||
                    (tile == TILE_BATCH && N > kBatchMaxTokens)) {
             return MIGEMM_ERR_CONFIG;
+        } else if (!wide && !is_fl(tile)) {
+            return MIGEMM_ERR_ALIGN;
         }
     } else if (tile == TILE_AUTO) {
-        // the 256x256 full-line tile with 8 waves once it fills the 256 CUs
-        // at least twice, else 256x128, else the 128x128 tile
-        if (wide && cdiv(M, 256) * cdiv(N, 256) >= 512)
-            tile = TILE_256x256_FL8;
-        else if (wide && cdiv(M, 256) * cdiv(N, 128) >= 512)
-            tile = TILE_256x128;
-        else
-            tile = TILE_128x128;
+        tile = auto_tile();
     } else if (tile == TILE_SKINNY || tile == TILE_BATCH) {
         return MIGEMM_ERR_CONFIG;   // only with a k-major A (gemm_tn_ex)
-    } else if (tile != TILE_128x128 && !wide) {
-        return MIGEMM_ERR_CONFIG;   // the 256-row tiles load only 16-byte vectors
+    } else if (tile != TILE_128x128 && !(wide || (fl && is_fl(tile)))) {
+        return MIGEMM_ERR_CONFIG;   // the other tiles load 16-byte (full-line: 4-byte aligned) rows
     }
     L.tile = tile;
     int bm = kTileShapes[tile].bm, bn = kTileShapes[tile].bn;
@@ -261,8 +283,10 @@ int gemm_splitk_ex(int dtype, int a_kmajor, const uint16_t *A, const uint16_t *B
     bool launch;
     int rc = plan_gemm(dtype, A, B, C, M, N, K, S > 1 && tile == TILE_AUTO ? (auto_S > 1 ? auto_tile : TILE_256x128_FL) : tile,
                        group_m, xcd_remap, L, launch, a_kmajor != 0);
-    if (S > 1 && tile == TILE_AUTO && rc == MIGEMM_ERR_CONFIG) {
-        // operands without 16-byte rows take no full-line tile: no split
+    // slices need 16-byte rows of A and B (a slice's last 16-byte piece of a
+    // row must not reach into the next row); without them: no split
+    const bool wide = vec_width(A, a_kmajor ? K : M) == 8 && vec_width(B, K) == 8;
+    if (S > 1 && (!wide || (tile == TILE_AUTO && rc == MIGEMM_ERR_CONFIG))) {
         S = 1;
         rc = plan_gemm(dtype, A, B, C, M, N, K, tile, group_m, xcd_remap, L, launch, a_kmajor != 0);
     }

@@ -68,6 +68,16 @@ __device__ inline unsigned short out16(float acc, float scale)
     }
 }
 
+// 16-bit input element -> FP32 (exact)
+template <int DT>
+__device__ inline float from16(unsigned short v)
+{
+    if constexpr (DT == DT_F16)
+        return (float)__builtin_bit_cast(_Float16, v);
+    else
+        return __builtin_bit_cast(float, (unsigned)v << 16);
+}
+
 // Wave-uniform value in a scalar register.
 __device__ inline int uniform(int v) { return __builtin_amdgcn_readfirstlane(v); }
 

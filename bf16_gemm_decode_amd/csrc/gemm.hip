@@ -491,11 +491,14 @@ gemm_fl_kernel(const uint16_t *__restrict__ A, const uint16_t *__restrict__ B,
     static_assert(AK || !dt_is_8bit(DT), "8-bit types take a k-major A");
     // SPLIT: workgroup row blockIdx.y sums k in [kb, kb + ks) (ks a multiple
     // of 64) into FP32 partials part[blockIdx.y][n][m]; rows of k-major
-    // operands keep their full stride K_total.  Otherwise the kernel sums
-    // all of K and writes C.
+    // operands keep their full stride K_total.  Otherwise the k loop covers
+    // [0, ks), ks = K_total rounded down to a multiple of 8, so that every
+    // 16-byte piece of a k-major row it loads lies inside the row; one more
+    // MFMA per block adds the last K_total - ks (< 8) k, and the kernel
+    // writes C.
     static_assert(!SPLIT || !dt_is_8bit(DT), "split-K: 16-bit types");
     const int kb = SPLIT ? (int)blockIdx.y * ks : 0;
-    const int K = SPLIT ? min(ks, K_total - kb) : K_total;
+    const int K = SPLIT ? min(ks, K_total - kb) : ks;
     const int ldk = K_total;
     constexpr int BK = 32;                        // sub-step = one MFMA k slice
     constexpr int NW = WGM * WGN;
@@ -652,6 +655,45 @@ gemm_fl_kernel(const uint16_t *__restrict__ A, const uint16_t *__restrict__ B,
 #pragma unroll
         for (int j = 0; j < FN; ++j) acc[i][j] = f32x4{0.f, 0.f, 0.f, 0.f};
 
+    if constexpr (!SPLIT && !dt_is_8bit(DT)) {
+        if (K < K_total) {
+            // k in [K, K_total) (fewer than 8), before the loop: one MFMA
+            // per block on those k.  The workgroup stages them (zero past M,
+            // N and K_total) as 8 elements per A row and per B column in LDS
+            // (the rings' first bytes, refilled only after the second
+            // barrier); lanes 0-15 of each operand take their row's or
+            // column's 8, lanes 16-63 zero.
+            uint16_t *t16 = (uint16_t *)smem;
+            static_assert((BM + BN) * 16 <= LDS_BYTES, "k-tail staging");
+            for (int e = threadIdx.x; e < (BM + BN) * 8; e += NW * 64) {
+                const int k = K + (e & 7);
+                uint16_t v = 0;
+                if (e < BM * 8) {
+                    const int m = m0 + (e >> 3);
+                    if (m < M && k < K_total) v = A[AK ? (size_t)m * ldk + k : (size_t)k * M + m];
+                } else {
+                    const int n = n0 + (e >> 3) - BM;
+                    if (n < N && k < K_total) v = B[(size_t)n * ldk + k];
+                }
+                t16[e] = v;
+            }
+            __syncthreads();
+            Frag tf;
+            const u32x4 z = {0u, 0u, 0u, 0u};
+#pragma unroll
+            for (int i = 0; i < FM; ++i)
+                tf.a[i] = g == 0 ? *(const u32x4 *)&t16[(wm * TM + i * 16 + ig) * 8] : z;
+#pragma unroll
+            for (int j = 0; j < FN; ++j)
+                tf.b[j] = g == 0 ? *(const u32x4 *)&t16[(BM + wn * TN + j * 16 + ig) * 8] : z;
+#pragma unroll
+            for (int i = 0; i < FM; ++i)
+#pragma unroll
+                for (int j = 0; j < FN; ++j) mfma16x16x32<DT>(acc[i][j], tf.a[i], tf.b[j]);
+            __syncthreads();
+        }
+    }
+
     auto mma = [&](const Frag &f, auto nx_c, auto every_c, auto &&extra) {
         constexpr int NXI = decltype(nx_c)::value, EV = decltype(every_c)::value;
 #pragma unroll
@@ -757,7 +799,6 @@ gemm_fl_kernel(const uint16_t *__restrict__ A, const uint16_t *__restrict__ B,
         }
         wait_vmcnt<0>();   // no load may still target LDS when the workgroup ends
     }
-
     mfma_drain();
     if constexpr (SPLIT) {
         // FP32 partial sums of this k slice (16-bit types only)
@@ -828,7 +869,7 @@ static hipError_t launch_fl(const GemmLaunch &L, hipStream_t stream)
     }
     hipLaunchKernelGGL((gemm_fl_kernel<DT, AK, BM, BN, WGM, WGN, SA, SB, OC, false>),
                        dim3((unsigned)L.grid), block, 0, stream, L.A, L.B, L.C, L.M, L.N, L.K,
-                       L.num_pid_m, L.num_pid_n, L.group_m, L.num_xcd, L.c_vec, L.scale, L.K,
+                       L.num_pid_m, L.num_pid_n, L.group_m, L.num_xcd, L.c_vec, L.scale, L.K & ~7,
                        (float *)nullptr);
     return hipGetLastError();
 }

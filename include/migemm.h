@@ -203,8 +203,9 @@ size_t migemm_splitk_workspace_bytes(int M, int N, int splits);
  * the caller instead of chosen by the library:
  *   tile:    0 = automatic (with group_m 0: first an exact-shape table of
  *            measured configurations -- the headline FP16 GEMM, the prefill
- *            GEMM in both layouts, the ragged BF16 GEMM -- then the size
- *            rules); 1 = 256x256 (4 waves as 2x2, 4 LDS stages);
+ *            GEMM in both layouts, the ragged BF16 GEMM -- then the least
+ *            estimated time over rounds of workgroups on the 256 CUs among
+ *            tiles 10, 2 (9 without 16-byte rows) and 3); 1 = 256x256 (4 waves as 2x2, 4 LDS stages);
  *            2 = 256x128 (5 stages); 3 = 128x128 (4 stages, two workgroups
  *            per CU); 4 = tile 1 with 5 stages; 5 = 256x256 with the 4 waves
  *            stacked along M; 6 = tile 1 with 3 stages; 7 = 256x256, waves
@@ -219,8 +220,12 @@ size_t migemm_splitk_workspace_bytes(int M, int N, int splits);
  *            of gemv_bf16 (gemm_tn_* only, N <= 128: 64 rows x 16..128
  *            columns per workgroup, 16x16x32 MFMA, A read as whole lines and
  *            re-laid out through LDS, B staged in LDS).
- *            All step K by 32; tiles other than 3 need M and K to be multiples of 8 and A, B
- *            16-byte aligned (else MIGEMM_ERR_CONFIG);
+ *            All step K by 32.  Tiles 1, 2, 4, 5, 6 need 16-byte rows (M and
+ *            K multiples of 8, A and B 16-byte aligned); the full-line tiles
+ *            7 .. 13 need 4-byte rows (M and K even, A and B 4-byte
+ *            aligned): their k loop stops at K rounded down to a multiple of
+ *            8 and one more MFMA step adds the remaining k; tile 3 takes
+ *            any alignment (else MIGEMM_ERR_CONFIG);
  *   group_m: width of the grouped tile ordering (FlagGems "Hygon 优化" page,
  *            section "分组调度"), >= 1, or 0 for automatic;
  *   xcd_remap: 1 to place consecutive tiles of the ordering on one XCD's L2,
@@ -240,10 +245,11 @@ int gemm_ex(int dtype, const uint16_t *A, const uint16_t *B, uint16_t *C,
  * with Y row-major [N, M] -- the GEMV's own layout.  Same argument checks,
  * ownership and completion rules as gemm_f16 / gemm_bf16.  Runs on the
  * full-line tiles only: tile 0 (automatic: 14 for N <= 4, 15 for
- * N <= 64, else 10 or 9) or 7 .. 15 (A takes B's 64-k ring layout;
- * MIGEMM_ERR_CONFIG for other tiles, and for 14 with N > 8 or 15 with
- * N > 128).  K must be a
- * multiple of 8 and At, B 16-byte aligned (else MIGEMM_ERR_ALIGN).
+ * N <= 64, else the least estimated time among 10, 9 and 13) or 7 .. 15
+ * (A takes B's 64-k ring layout; MIGEMM_ERR_CONFIG for other tiles, and
+ * for 14 with N > 8 or 15 with N > 128).  K even and At, B 4-byte aligned
+ * (4-byte rows) for tiles 7 .. 13, K a multiple of 8 and At, B 16-byte
+ * aligned for 14 and 15 (which tile 0 then uses); else MIGEMM_ERR_ALIGN.
  */
 int gemm_tn_f16(const uint16_t *At, const uint16_t *B, uint16_t *C,
                 int M, int N, int K, void *stream);

@@ -93,12 +93,16 @@ def test_every_tile_plan_fits_lds():
 
 def test_tn_plan_and_errors():
     L = binding.lib()
-    # automatic tile: 256x256 full-line once it fills the chip twice, else 256x128
+    # automatic tile: the least estimated time over rounds of workgroups
     code, p = binding.gemm_plan(0, P, P + 2 ** 30, P + 2 ** 31, 8192, 8192, 16384, a_kmajor=True)
     assert code == 0 and (p["tile_m"], p["tile_n"], p["vec_a"], p["vec_b"]) == (256, 256, 8, 8)
     assert p["lds_bytes"] == 2 * 64 * 256 * 2 + 3 * 64 * 256 * 2 and p["waves"] == 8
     code, p = binding.gemm_plan(1, P, P + 2 ** 30, P + 2 ** 31, 34816, 200, 5120, a_kmajor=True)
-    assert code == 0 and (p["tile_m"], p["tile_n"]) == (256, 128) and p["grid"] == 272
+    assert code == 0 and (p["tile_m"], p["tile_n"]) == (256, 256) and p["grid"] == 136   # one round
+    code, p = binding.gemm_plan(1, P, P + 2 ** 30, P + 2 ** 31, 2816, 2816, 4096, a_kmajor=True)
+    assert code == 0 and (p["tile_m"], p["tile_n"]) == (256, 128) and p["grid"] == 242   # one round
+    code, p = binding.gemm_plan(1, P, P + 2 ** 30, P + 2 ** 31, 2048, 2048, 4096, a_kmajor=True)
+    assert code == 0 and (p["tile"], p["grid"]) == (13, 256)
     # the skinny tile: few columns only, and only with a k-major A
     code, p = binding.gemm_plan(1, P, P + 2 ** 30, P + 2 ** 31, 34816, 8, 5120, 14, a_kmajor=True)
     assert code == 0 and (p["tile"], p["tile_m"], p["tile_n"], p["waves"], p["grid"]) == (14, 32, 8, 4, 1088)
@@ -120,9 +124,14 @@ def test_tn_plan_and_errors():
     # only the full-line tiles take a k-major A
     for tile in (1, 2, 3, 4, 5, 6, 16):
         assert L.gemm_tn_ex(0, P, P + 0x100000, P + 0x200000, 64, 64, 64, tile, 0, 1, None) == -5
-    # K not a multiple of 8, or a misaligned operand: no 16-byte rows
-    assert L.gemm_tn_ex(0, P, P + 0x100000, P + 0x200000, 64, 64, 60, 7, 0, 1, None) == -4
+    # odd K, or an operand only 2-byte aligned: not even 4-byte rows
+    assert L.gemm_tn_ex(0, P, P + 0x100000, P + 0x200000, 64, 64, 61, 7, 0, 1, None) == -4
     assert L.gemm_tn_ex(0, P + 2, P + 0x100000, P + 0x200000, 64, 64, 64, 7, 0, 1, None) == -4
+    # K = 4 mod 8 (4-byte rows): the full-line tiles only
+    code, p = binding.gemm_plan(0, P, P + 2 ** 20, P + 2 ** 21, 64, 64, 60, 7, a_kmajor=True)
+    assert code == 0 and p["tile"] == 7 and (p["vec_a"], p["vec_b"]) == (2, 2)
+    assert binding.gemm_plan(0, P, P + 2 ** 20, P + 2 ** 21, 64, 8, 60, 14, a_kmajor=True)[0] == -4
+    assert binding.gemm_plan(0, P, P + 2 ** 20, P + 2 ** 21, 64, 64, 60, 0, a_kmajor=True)[1]["tile"] == 13
     # the shared checks
     assert L.gemm_tn_f16(P, P + 0x100000, P + 0x200000, -1, 64, 64, None) == -1
     assert L.gemm_tn_bf16(None, P + 0x100000, P + 0x200000, 64, 64, 64, None) == -2
@@ -137,7 +146,7 @@ def test_exact_shape_table():
     assert (plan(1, 4096, 34816, 5120)["tile"], plan(1, 4096, 34816, 5120)["group_m"]) == (10, 16)
     assert (plan(1, 34816, 4096, 5120, tn=True)["tile"], plan(1, 34816, 4096, 5120, tn=True)["group_m"]) == (10, 4)
     assert (plan(0, 8192, 8192, 16384)["tile"], plan(0, 8192, 8192, 16384)["group_m"]) == (10, 8)
-    assert plan(1, 5000, 3000, 4100)["tile"] == 3
+    assert (plan(1, 5000, 3000, 4100)["tile"], plan(1, 5000, 3000, 4100)["group_m"]) == (10, 16)
     # an explicit GROUP_M or tile, another dtype or shape: the heuristics
     assert plan(1, 4096, 34816, 5120, gm=8)["group_m"] == 8
     assert plan(1, 4096, 34816, 5120, tile=9)["tile"] == 9
@@ -221,10 +230,14 @@ def test_plan_choices():
         (256, 256, 8, 8, 1024)
     assert p["tile_k"] == 32 and p["tile"] == 10 and p["waves"] == 8 and p["a_kmajor"] == 0
     assert p["lds_bytes"] <= 160 * 1024
-    # ragged: M = 5000 keeps 16-byte A loads, K = 4100 drops B to 4-byte loads
+    # ragged: M = 5000 keeps 16-byte A rows, K = 4100 leaves B 4-byte rows,
+    # which the full-line tiles take (k loop to 4096, then the last 4 k)
     code, p = binding.gemm_plan(1, P, P + 2 ** 30, P + 2 ** 31, 5000, 3000, 4100)
-    assert code == 0 and (p["tile_m"], p["vec_a"], p["vec_b"]) == (128, 8, 2)
-    assert p["grid"] == 40 * 24
+    assert code == 0 and (p["tile_m"], p["vec_a"], p["vec_b"]) == (256, 8, 2)
+    assert p["grid"] == 20 * 12
+    # the 256-row tiles of the older kernel still need 16-byte rows
+    assert binding.gemm_plan(1, P, P + 2 ** 30, P + 2 ** 31, 5000, 3000, 4100, 2)[0] == -5
+    assert binding.gemm_plan(1, P, P + 2 ** 30, P + 2 ** 31, 5000, 3000, 4100, 9)[0] == 0
     # odd everything: element loads
     code, p = binding.gemm_plan(1, P + 2, P + 2 ** 30 + 2, P + 2 ** 31, 33, 17, 65)
     assert code == 0 and (p["vec_a"], p["vec_b"]) == (1, 1)

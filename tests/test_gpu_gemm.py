@@ -79,6 +79,35 @@ def test_full_line_tiles_short_and_ragged_k(tile):
         _full_case(264, 300, K, fmt, seed=700 + K, tile=tile)
 
 
+@pytest.mark.parametrize("tile", FULL_LINE_TILES)
+def test_full_line_tiles_4byte_rows(tile):
+    # rows only 4-byte aligned: K = 2, 4, 6 mod 8 (B columns start at any
+    # 4-byte offset; the k loop stops at a multiple of 8 and the last k are
+    # added after it) and M = 2 mod 8 (A's k rows)
+    for i, (M, N, K) in enumerate([(264, 300, 202), (266, 130, 100), (520, 264, 1036), (258, 70, 70)]):
+        fmt = FMTS[i % 2]
+        print("case tile", tile, (M, N, K), fmt, flush=True)
+        _full_case(M, N, K, fmt, seed=900 + K + tile, tile=tile)
+
+
+def test_k_tail_keeps_columns_apart():
+    # K = 4 mod 8 on the full-line tiles: the last 16-byte piece of a B
+    # column would also hold the next column's first elements; an infinity
+    # there must stay in its own column (and a NaN in A's last k row in its
+    # own row)
+    M, N, K = 264, 40, 100
+    a = np.ones(M * K)
+    a[7 + (K - 1) * M] = np.nan   # row 7, last k
+    b = np.ones(K * N)
+    b[0 + 5 * K] = np.inf         # column 5, k = 0
+    for fmt in FMTS:
+        A, B = synth.to_bits(a, fmt), synth.to_bits(b, fmt)
+        for tile in (0, 9, 10, 13):
+            print("case k tail non-finite", fmt, tile, flush=True)
+            got, _, _ = gemm_gpu(A, B, M, N, K, fmt, tile=tile)
+            assert_parity(got, oracle.gemm(A, B, M, N, K, fmt), fmt, "k tail %s tile %d" % (fmt, tile))
+
+
 def test_misaligned_vector_widths():
     # odd M and K force element loads; M, K = 2 mod 4 force 4-byte loads
     for (M, N, K) in [(33, 40, 65), (34, 40, 66), (130, 70, 258), (258, 130, 100)]:

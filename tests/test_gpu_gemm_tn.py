@@ -42,6 +42,32 @@ def test_tn_short_and_ragged_k(tile):
         _tn_case(300, 264, K, fmt, seed=900 + K, tile=tile)
 
 
+@pytest.mark.parametrize("tile", [0, 7, 9, 10, 11, 13])
+def test_tn_4byte_rows_and_k_tail(tile):
+    # K = 2, 4, 6 mod 8: rows of At and B start at 4-byte offsets, the k loop
+    # stops at a multiple of 8 and the last k are added after it
+    for i, (M, N, K) in enumerate([(300, 264, 202), (130, 70, 100), (264, 300, 1038)]):
+        fmt = FMTS[i % 2]
+        print("case tn 4-byte rows", tile, (M, N, K), fmt, flush=True)
+        _tn_case(M, N, K, fmt, seed=1300 + K + tile, tile=tile)
+
+
+def test_tn_k_tail_keeps_rows_apart():
+    # an infinity at the start of At's row 7 must not reach row 6 through
+    # the last 16-byte piece of row 6 (K = 4 mod 8)
+    M, N, K = 264, 40, 100
+    at = np.ones(M * K)
+    at[7 * K] = np.inf
+    b = np.ones(K * N)
+    for fmt in FMTS:
+        At, B = synth.to_bits(at, fmt), synth.to_bits(b, fmt)
+        for tile in (0, 9, 10):
+            print("case tn k tail non-finite", fmt, tile, flush=True)
+            got, _, _ = gemm_tn_gpu(At, B, M, N, K, fmt, tile=tile)
+            ref = oracle.gemm(kmajor_to_colmajor(At, M, K), B, M, N, K, fmt)
+            assert_parity(got, ref, fmt, "tn k tail %s tile %d" % (fmt, tile))
+
+
 def test_tn_small_and_odd_shapes():
     for (M, N, K) in [(1, 1, 8), (17, 5, 16), (255, 257, 64), (257, 31, 128), (64, 1000, 24)]:
         for fmt in FMTS:
