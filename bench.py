@@ -41,6 +41,8 @@ GEMM_CFG = "gemm_8192x8192x16384_f16"
 GEMV_CFG = "gemv_34816x5120_bf16"
 W_COPIES = 4
 ATT_CFG = "attention_decode_16q4kv_d256_bf16"
+# rocprofv3 MfmaUtil of the bench's GEMM kernels (profile_summary mfma)
+GEMM_MFMA_SUMMARY = "gemm_8192x8192x16384_mfma_util.json"
 ATT_LEN = 32768
 ATT_COPIES = 5
 
@@ -107,6 +109,22 @@ def measured_traffic(sources, summary_file):
     if summ.get("kernel_sources") != sources or summ.get("kernel_sources_sha256") != source_digest(sources):
         return None
     return summ.get("hbm_bytes_per_launch")
+
+
+def measured_mfma_util(sources, summary_file, label):
+    """rocprofv3's MfmaUtil (mean %, over the profiled dispatches) of one
+    kernel from a committed counter summary, or None when there is none or
+    the kernel's sources changed since it was taken."""
+    from bf16_gemm_decode_amd.profile_summary import source_digest
+    path = os.path.join(ROOT, "profiles", summary_file)
+    try:
+        summ = json.load(open(path))
+    except (OSError, ValueError):
+        return None
+    if summ.get("kernel_sources") != sources or summ.get("kernel_sources_sha256") != source_digest(sources):
+        return None
+    row = summ.get("kernels", {}).get(label)
+    return round(row["mfma_util_percent"]["mean"], 2) if row else None
 
 
 def cpu_baseline(A, B, M, N, K, target_s):
@@ -353,7 +371,9 @@ def main():
         qt = q0.elapsed_time(q1) / 1e3 / nq
         qtf = rf.gemm_flop(M, N, K) / qt / 1e12
         q_rows[qname] = {"avg_launch_ms": round(qt * 1e3, 4), "TFLOPs_or_TOPs": round(qtf, 1),
-                         "peak": pk, "frac": round(qtf / pk, 4)}
+                         "peak": pk, "frac": round(qtf / pk, 4),
+                         "mfma_util_percent": measured_mfma_util(GEMM_SOURCES, GEMM_MFMA_SUMMARY,
+                                                                 qname + "_tile10")}
         del qA, qB
     del qC
 
@@ -388,6 +408,7 @@ def main():
         "roofline": {"bound": "mfma", "achieved": round(tflops, 2), "peak": peak,
                      "unit": "TFLOP/s", "frac": round(tflops / peak, 4),
                      "traffic": measured_traffic(GEMM_SOURCES, "gemm_8192x8192x16384_f16_traffic.json"),
+                     "mfma_util_percent": measured_mfma_util(GEMM_SOURCES, GEMM_MFMA_SUMMARY, "f16_tile10"),
                      "kernel": "%s (2*M*N*K FLOP per launch)" % kernel,
                      "avg_launch_ms": round(gemm_avg * 1e3, 4)},
         "gemv": {"GBps": round(gemv_GBps, 1), "avg_launch_us": round(gemv_avg * 1e6, 2),

@@ -3,6 +3,9 @@ profiles/.
 
   kernel-stats:  python -m bf16_gemm_decode_amd.profile_summary stats \
                      <run_kernel_stats.csv> <out.txt> --command "<rocprofv3 command>"
+  mfma:          python -m bf16_gemm_decode_amd.profile_summary mfma \
+                     --util-csv <csv> --counts-csv <csv> --kernel label=<substring>:<FLOP> ... \
+                     --source <files...> --out <out.json> --commands "<cmd>" ...
   traffic:       python -m bf16_gemm_decode_amd.profile_summary traffic \
                      --fetch <csv> --fetch-cal <csv> --write <csv> --write-cal <csv> \
                      --kernel <name substring> --source <source files...> \
@@ -103,6 +106,54 @@ def traffic(args):
     print(json.dumps(out, indent=1))
 
 
+def _per_dispatch(path, counter, substr):
+    """{dispatch id: (value, duration in ns)} of one counter for the
+    dispatches whose kernel name contains substr (rocprofv3's CSV holds one
+    row per dispatch and counter, instances already combined)."""
+    out = {}
+    for r in _rows(path):
+        if r["Counter_Name"] == counter and substr in r["Kernel_Name"]:
+            out[r["Dispatch_Id"]] = (float(r["Counter_Value"]),
+                                     int(r["End_Timestamp"]) - int(r["Start_Timestamp"]))
+    return out
+
+
+def mfma(args):
+    """MFMA utilisation per kernel from a --pmc MfmaUtil run (rocprofv3's
+    derived counter: MFMA-busy SIMD cycles / (GPU-active cycles x SIMDs), in
+    %), and from a --pmc run of the raw counters the MFMA FLOP per dispatch
+    (SQ_INSTS_VALU_MFMA_MOPS_F16 + _BF16, units of 512 FLOP) against the
+    algorithmic count, and GRBM_GUI_ACTIVE per XCD over the dispatch time
+    (the clock the kernel ran at)."""
+    out = {"commands": args.commands, "kernels": {}}
+    for spec in args.kernel:
+        label, rest = spec.split("=", 1)
+        substr, flop = rest.rsplit(":", 1)
+        util = _per_dispatch(args.util_csv, "MfmaUtil", substr)
+        if not util:
+            sys.exit("no MfmaUtil values for %r in %s" % (substr, args.util_csv))
+        u = [v for v, _ in util.values()]
+        row = {"kernel_name_contains": substr, "dispatches": len(u),
+               "mfma_util_percent": {"mean": sum(u) / len(u), "min": min(u), "max": max(u)}}
+        mops = [_per_dispatch(args.counts_csv, c, substr) for c in
+                ("SQ_INSTS_VALU_MFMA_MOPS_F16", "SQ_INSTS_VALU_MFMA_MOPS_BF16")]
+        act = _per_dispatch(args.counts_csv, "GRBM_GUI_ACTIVE", substr)
+        if act:
+            ghz = [v / args.xcds / t for v, t in act.values()]
+            row["gui_active_ghz_per_xcd"] = sum(ghz) / len(ghz)
+            if float(flop) > 0:   # 16-bit kernels: the MOPS counters cover them
+                f = [sum(m.get(d, (0.0, 0))[0] for m in mops) * 512.0 for d in act]
+                row["mfma_flop_per_dispatch"] = sum(f) / len(f)
+                row["algorithmic_flop_per_dispatch"] = float(flop)
+                row["mfma_flop_over_algorithmic"] = (sum(f) / len(f)) / float(flop)
+        out["kernels"][label] = row
+    out["kernel_sources"] = args.source
+    out["kernel_sources_sha256"] = source_digest(args.source)
+    with open(args.out, "w") as o:
+        json.dump(out, o, indent=1)
+    print(json.dumps(out, indent=1))
+
+
 def main(argv=None):
     p = argparse.ArgumentParser()
     sub = p.add_subparsers(dest="mode", required=True)
@@ -121,8 +172,18 @@ def main(argv=None):
                    help="csrc/ file names, e.g. the GEMM_SOURCES list")
     t.add_argument("--out", required=True)
     t.add_argument("--commands", nargs="+", required=True)
+    m = sub.add_parser("mfma")
+    m.add_argument("--util-csv", required=True, help="counter CSV of a --pmc MfmaUtil run")
+    m.add_argument("--counts-csv", required=True,
+                   help="counter CSV of a --pmc GRBM_GUI_ACTIVE SQ_INSTS_VALU_MFMA_MOPS_F16 _BF16 run")
+    m.add_argument("--kernel", nargs="+", required=True,
+                   help="label=<kernel name substring>:<algorithmic FLOP per dispatch, 0 for 8-bit>")
+    m.add_argument("--xcds", type=int, default=8)
+    m.add_argument("--source", nargs="+", required=True)
+    m.add_argument("--out", required=True)
+    m.add_argument("--commands", nargs="+", required=True)
     a = p.parse_args(argv)
-    stats(a) if a.mode == "stats" else traffic(a)
+    {"stats": stats, "traffic": traffic, "mfma": mfma}[a.mode](a)
 
 
 if __name__ == "__main__":
