@@ -513,6 +513,7 @@ gemm_fl_kernel(const uint16_t *__restrict__ A, const uint16_t *__restrict__ B,
     constexpr int LB = B_BYTES / (1024 * NW);     // B loads per wave per B stage
     constexpr int LBH = LB / 2;                   // ... per sub-step
     static_assert(A_BYTES % ((AK ? 2048 : 1024) * NW) == 0 && B_BYTES % (2048 * NW) == 0, "loader split");
+    static_assert(NW % 2 == 0, "one chunk swizzle per wave for all its B loads");
     static_assert(TM % 16 == 0 && TN % 16 == 0 && BN % 16 == 0, "tile shape");
     static_assert(LDS_BYTES <= 163840, "LDS rings");
     constexpr int W_EVEN = fl_loads_after<AK, SA, SB, LA, LBH>(64, AK ? 32 : 65, 32);
@@ -557,10 +558,13 @@ gemm_fl_kernel(const uint16_t *__restrict__ A, const uint16_t *__restrict__ B,
             a_off[q] = (uint32_t)(((int64_t)kk * M + m0 + m) * 2);
         }
     }
-    uint32_t b_off[LB];
-    int b_k[LB];
-#pragma unroll
-    for (int q = 0; q < LB; ++q) kmajor_lane(q, ldk, b_off[q], b_k[q]);
+    // every B load of a wave has the same chunk swizzle (it depends on the
+    // column group's parity only, and NW is even): one base offset and k,
+    // load q adding q*NW column groups
+    uint32_t b_off0;
+    int b_k0;
+    kmajor_lane(0, ldk, b_off0, b_k0);
+    auto b_offq = [&](int q) { return b_off0 + (uint32_t)(8 * q * NW) * (uint32_t)uniform(ldk * 2); };
 
     // Sub-steps, evened out: with an odd count a zero sub-step (k0 = -BK,
     // every element read as zero) goes first.  P_ = number of 64-k stages.
@@ -602,7 +606,7 @@ gemm_fl_kernel(const uint16_t *__restrict__ A, const uint16_t *__restrict__ B,
     };
     auto issue_b = [&](const u32x4 &d, int pp, int sb, int q) {
         dma_to_lds<16>(d, (uint32_t)uniform((int)(lds0 + B_BASE + sb * B_BYTES + (q * NW + wave) * 1024)),
-                       kmajor_off(pp, b_k[q], b_off[q]));
+                       kmajor_off(pp, b_k0, b_offq(q)));
     };
 
     // operand reads (stage-relative): m-major A through transposing reads;
