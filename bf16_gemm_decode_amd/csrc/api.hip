@@ -163,7 +163,10 @@ int plan_gemm(int dtype, const uint16_t *A, const uint16_t *B, const uint16_t *C
     L.tile = tile;
     int bm = kTileShapes[tile].bm, bn = kTileShapes[tile].bn;
     if (tile == TILE_SKINNY) bn = N <= 4 ? 4 : 8;
-    if (tile == TILE_BATCH) bn = batch_tile_n(N);
+    if (tile == TILE_BATCH) {
+        bm = batch_tile_m(N);
+        bn = batch_tile_n(N);
+    }
     const int64_t pm = cdiv(M, bm), pn = cdiv(N, bn);
     if (pm * pn > 0x7fffffff) return MIGEMM_ERR_SIZE;
     L.num_pid_m = (int)(pm ? pm : 1);
@@ -385,10 +388,10 @@ static int plan_for(int dtype, const uint16_t *A, const uint16_t *B, const uint1
         return rc;
     }
     if (L.tile == TILE_BATCH) {
-        plan->tile_m = 64;                      // 4 waves x 16 rows
+        plan->tile_m = batch_tile_m(N);         // waves x 16 rows
         plan->tile_n = batch_tile_n(N);
         plan->tile_k = 128;
-        plan->waves = 4;
+        plan->waves = batch_waves(N);
         plan->group_m = 1;
         plan->xcd_remap = 0;
         plan->vec_a = L.vec_a;

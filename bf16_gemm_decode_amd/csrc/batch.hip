@@ -7,8 +7,9 @@
 // is still small (2n FLOP per 2 bytes), so the kernel is built to stream W at
 // HBM speed with enough MFMA throughput to spare:
 //
-//  * A workgroup of 4 waves owns 64 rows of W (16 per wave) and a block of up
-//    to 16*NTT tokens; K is walked in chunks of 128.
+//  * A workgroup of NWV waves (2 for a 16-token block, else 4) owns 16*NWV
+//    rows of W (16 per wave) and a block of up to 16*NTT tokens; K is walked
+//    in chunks of 128.
 //  * W is read as whole 128-byte lines: each load instruction covers 8 rows x
 //    128 bytes (lane l: row l/8, bytes 16*(l%8)); a wave's 16 rows x 128 k of
 //    a chunk are 4 such loads, non-temporal, U chunks in flight in
@@ -63,18 +64,18 @@ __device__ inline void mfma_16x16x32(f32x4 &acc, u32x4 a, u32x4 b)
 
 }  // namespace
 
-template <int DT, int NTT, int U>
-__global__ void __launch_bounds__(256)
+template <int DT, int NTT, int U, int NWV>
+__global__ void __launch_bounds__(64 * NWV)
 batch_kernel(const uint16_t *__restrict__ W, const uint16_t *__restrict__ X,
              uint16_t *__restrict__ Y, int M, int K, int n, int y_vec)
 {
-    constexpr int XP = NTT;                       // 16-byte X pieces per thread and chunk
+    constexpr int XP = NTT * 4 / NWV;             // 16-byte X pieces per thread and chunk
     __shared__ __attribute__((aligned(16))) uint8_t xs[2][NTT * 16][kXRow];
-    __shared__ __attribute__((aligned(16))) uint8_t ws[4][16 * 256];   // per wave
+    __shared__ __attribute__((aligned(16))) uint8_t ws[NWV][16 * 256];   // per wave
 
     const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
     const int g = lane >> 4, r16 = lane & 15;
-    const int row0 = blockIdx.x * 64 + wave * 16;
+    const int row0 = blockIdx.x * (16 * NWV) + wave * 16;
     const int tok0 = blockIdx.y * (NTT * 16);
     const int chunks = (K + kKC - 1) / kKC;
     const int padded = (chunks + U - 1) / U * U;
@@ -111,7 +112,7 @@ batch_kernel(const uint16_t *__restrict__ W, const uint16_t *__restrict__ X,
     auto load_x = [&](int c, u32x4 (&xr)[XP]) {
 #pragma unroll
         for (int p = 0; p < XP; ++p) {
-            const int e = p * 256 + tid;
+            const int e = p * (64 * NWV) + tid;
             const int t = e >> 4, ch = e & 15;
             const int k = c * kKC + ch * 8;
             const bool ok = tok0 + t < n && k < K;
@@ -121,7 +122,7 @@ batch_kernel(const uint16_t *__restrict__ W, const uint16_t *__restrict__ X,
     auto store_x = [&](int buf, const u32x4 (&xr)[XP]) {
 #pragma unroll
         for (int p = 0; p < XP; ++p) {
-            const int e = p * 256 + tid;
+            const int e = p * (64 * NWV) + tid;
             *(u32x4 *)&xs[buf][e >> 4][(e & 15) * 16] = xr[p];
         }
     };
@@ -191,11 +192,12 @@ batch_kernel(const uint16_t *__restrict__ W, const uint16_t *__restrict__ X,
 template <int DT, int NTT>
 static hipError_t launch_ntt(const SkinnyLaunch &L, hipStream_t s)
 {
+    constexpr int NWV = batch_waves(NTT * 16);
     // 4 chunks of W in flight; 2 for the 64- and 128-token blocks, whose X
     // staging already takes the registers (measured faster there)
     constexpr int U = NTT >= 4 ? 2 : 4;
-    const dim3 grid((unsigned)((L.M + 63) / 64), (unsigned)((L.n + NTT * 16 - 1) / (NTT * 16)));
-    hipLaunchKernelGGL((batch_kernel<DT, NTT, U>), grid, dim3(256), 0, s, L.W, L.X, L.Y, L.M, L.K,
+    const dim3 grid((unsigned)((L.M + 16 * NWV - 1) / (16 * NWV)), (unsigned)((L.n + NTT * 16 - 1) / (NTT * 16)));
+    hipLaunchKernelGGL((batch_kernel<DT, NTT, U, NWV>), grid, dim3(64 * NWV), 0, s, L.W, L.X, L.Y, L.M, L.K,
                        L.n, L.y_vec);
     return hipGetLastError();
 }

@@ -138,9 +138,13 @@ hipError_t skinny_launch(const SkinnyLaunch &L, hipStream_t stream);
 hipError_t batch_launch(const SkinnyLaunch &L, hipStream_t stream);
 // token columns of one batch-kernel workgroup for n tokens (16, 32, 64, 128)
 constexpr int batch_tile_n(int n) { return n <= 16 ? 16 : n <= 32 ? 32 : n <= 64 ? 64 : 128; }
+// its waves (16 rows of W each): 2 for one 16-token block (finer workgroups
+// balance the CUs better; measured 65 against 68 us at 16 tokens), else 4
+constexpr int batch_waves(int n) { return batch_tile_n(n) == 16 ? 2 : 4; }
+constexpr int batch_tile_m(int n) { return 16 * batch_waves(n); }
 // its LDS bytes: two staged chunks of tile_n token rows of 272 bytes, and
-// the 4 waves' 4 KB areas that re-lay W out
-constexpr int batch_lds_bytes(int n) { return 2 * batch_tile_n(n) * (128 * 2 + 16) + 4 * 4096; }
+// the waves' 4 KB areas that re-lay W out
+constexpr int batch_lds_bytes(int n) { return 2 * batch_tile_n(n) * (128 * 2 + 16) + batch_waves(n) * 4096; }
 
 // Decode attention over a paged KV cache, split into S segments (attention.hip).
 struct AttentionLaunch {

@@ -18,7 +18,9 @@
 //    and chunk, lane l taking row l/16 at offset 8*(l%16): 16 lanes read
 //    256 contiguous bytes of one row, so every group of 4 lanes asks for 64
 //    contiguous bytes (the address unit's fast case) and a wave reads whole
-//    cache lines, straight into registers (no LDS), U chunks in flight.  A
+//    cache lines, straight into registers (no LDS), U chunks in flight in a
+//    ring (each chunk's X requested before its W, so a wait for one chunk
+//    never covers a younger request).  A
 //    cross-lane permute (ds_bpermute, lane 4b+i <- lane 16i+b) then puts
 //    row i's chunk b where block b's A operand expects it.
 //  * X is loaded and permuted the same way (token j in place of row i),
@@ -35,6 +37,12 @@
 namespace migemm {
 
 typedef __attribute__((ext_vector_type(4))) _Float16 f16x4;
+
+// 16 zero bytes in device memory: masked lanes load from here
+__device__ const uint16_t kSkZeros[8] = {0, 0, 0, 0, 0, 0, 0, 0};
+typedef const __attribute__((address_space(1))) u32x4 *sk_gptr16;
+__device__ inline u32x4 sk_load16(const void *p) { return *(sk_gptr16)p; }
+__device__ inline u32x4 sk_load16_nt(const void *p) { return __builtin_nontemporal_load((sk_gptr16)p); }
 
 // acc += (low or high four halves of a) x (the same of b) on 16 4x4x4 blocks
 template <int DT, int HI>
@@ -90,40 +98,42 @@ skinny_kernel(const uint16_t *__restrict__ W, const uint16_t *__restrict__ X,
 #pragma unroll
         for (int t = 0; t < TG; ++t) acc[r][t] = f32x4{0.f, 0.f, 0.f, 0.f};
 
-    const u32x4 zero = {0u, 0u, 0u, 0u};
+    // Ring of U chunks in flight: chunk c + U is requested into the slot
+    // chunk c has just been read from, X before W, so that waiting for a
+    // chunk never waits for a younger request.  Lanes past K (and chunks
+    // past the end) load from a zero block instead of selecting zero after
+    // the load.
     const int chunks = (K + 127) / 128;
-    for (int c = 0; c < chunks; c += U) {
-        u32x4 w[U][RW];
+    const int padded = (chunks + U - 1) / U * U;
+    auto load_chunk = [&](int c, u32x4 (&wv)[RW], u32x4 (&xv)[TG]) {
+        const bool kok = c * 128 + 8 * lc < K;
+#pragma unroll
+        for (int t = 0; t < TG; ++t) xv[t] = sk_load16((xok[t] && kok) ? (const void *)(xr[t] + c * 128) : kSkZeros);
+#pragma unroll
+        for (int r = 0; r < RW; ++r) wv[r] = sk_load16_nt(kok ? (const void *)(wr[r] + c * 128) : kSkZeros);
+    };
+    u32x4 w[U][RW], xs[U][TG];
+#pragma unroll
+    for (int u = 0; u < U; ++u) load_chunk(u, w[u], xs[u]);
+    for (int c0 = 0; c0 < padded; c0 += U) {
 #pragma unroll
         for (int u = 0; u < U; ++u) {
-            const bool ok = (c + u < chunks) && ((c + u) * 128 + 8 * lc < K);
+            u32x4 x[TG], wv[RW];
+#pragma unroll
+            for (int t = 0; t < TG; ++t) x[t] = to_mfma4_layout(xs[u][t], perm);
+#pragma unroll
+            for (int r = 0; r < RW; ++r) wv[r] = to_mfma4_layout(w[u][r], perm);
+            load_chunk(c0 + u + U, w[u], xs[u]);
+            // all low halves, then all high halves: consecutive MFMAs
+            // never feed each other
 #pragma unroll
             for (int r = 0; r < RW; ++r)
-                w[u][r] = ok ? __builtin_nontemporal_load((const u32x4 *)(wr[r] + (c + u) * 128)) : zero;
-        }
 #pragma unroll
-        for (int u = 0; u < U; ++u) {
-            if (c + u < chunks) {
-                const bool kok = (c + u) * 128 + 8 * lc < K;
-                u32x4 x[TG];
+                for (int t = 0; t < TG; ++t) mfma4<DT, 0>(acc[r][t], wv[r], x[t]);
 #pragma unroll
-                for (int t = 0; t < TG; ++t)
-                    x[t] = to_mfma4_layout((xok[t] && kok) ? *(const u32x4 *)(xr[t] + (c + u) * 128) : zero,
-                                           perm);
-                u32x4 wv[RW];
+            for (int r = 0; r < RW; ++r)
 #pragma unroll
-                for (int r = 0; r < RW; ++r) wv[r] = to_mfma4_layout(w[u][r], perm);
-                // all low halves, then all high halves: consecutive MFMAs
-                // never feed each other
-#pragma unroll
-                for (int r = 0; r < RW; ++r)
-#pragma unroll
-                    for (int t = 0; t < TG; ++t) mfma4<DT, 0>(acc[r][t], wv[r], x[t]);
-#pragma unroll
-                for (int r = 0; r < RW; ++r)
-#pragma unroll
-                    for (int t = 0; t < TG; ++t) mfma4<DT, 1>(acc[r][t], wv[r], x[t]);
-            }
+                for (int t = 0; t < TG; ++t) mfma4<DT, 1>(acc[r][t], wv[r], x[t]);
         }
     }
 
@@ -165,7 +175,9 @@ skinny_kernel(const uint16_t *__restrict__ W, const uint16_t *__restrict__ X,
 template <int DT, int TG>
 static hipError_t launch_tg(const SkinnyLaunch &L, hipStream_t s)
 {
-    constexpr int RW = 2, U = 4;
+    // chunks in flight: 8 with one token group (84 + 48 registers), 4 with
+    // two (measured best of 4 / 6 / 8)
+    constexpr int RW = 2, U = TG == 1 ? 8 : 4;
     const unsigned grid = (unsigned)((L.M + 16 * RW - 1) / (16 * RW));   // 4 waves x 4*RW rows
     hipLaunchKernelGGL((skinny_kernel<DT, RW, TG, U>), dim3(grid), dim3(256), 0, s,
                        L.W, L.X, L.Y, L.M, L.K, L.n, L.y_vec);

@@ -112,11 +112,13 @@ def test_tn_plan_and_errors():
     assert binding.gemm_plan(1, P, P + 2 ** 30, P + 2 ** 31, 34816, 5, 5120, a_kmajor=True)[1]["tile"] == 15
     assert L.gemm_tn_ex(0, P, P + 0x100000, P + 0x200000, 64, 9, 64, 14, 0, 1, None) == -5
     assert L.gemm_ex(0, P, P + 0x100000, P + 0x200000, 64, 16, 64, 14, 0, 1, None) == -5
-    # the batch tile: 9 .. 128 columns, 64 rows per workgroup, token blocks of 16 .. 128
+    # the batch tile: 9 .. 128 columns, token blocks of 16 .. 128; 2 waves
+    # (32 rows of W) per workgroup for a 16-token block, else 4 (64 rows)
     for n, tn in ((9, 16), (16, 16), (17, 32), (33, 64), (64, 64), (65, 128), (128, 128)):
         code, p = binding.gemm_plan(1, P, P + 2 ** 30, P + 2 ** 31, 34816, n, 5120, 15, a_kmajor=True)
-        assert code == 0 and (p["tile"], p["tile_m"], p["tile_n"], p["tile_k"], p["waves"]) == (15, 64, tn, 128, 4)
-        assert p["grid"] == 544 and p["lds_bytes"] == 2 * tn * 272 + 4 * 4096
+        w = 2 if tn == 16 else 4
+        assert code == 0 and (p["tile"], p["tile_m"], p["tile_n"], p["tile_k"], p["waves"]) == (15, 16 * w, tn, 128, w)
+        assert p["grid"] == 34816 // (16 * w) and p["lds_bytes"] == 2 * tn * 272 + w * 4096
     assert binding.gemm_plan(1, P, P + 2 ** 30, P + 2 ** 31, 34816, 64, 5120, a_kmajor=True)[1]["tile"] == 15
     assert binding.gemm_plan(1, P, P + 2 ** 30, P + 2 ** 31, 34816, 65, 5120, a_kmajor=True)[1]["tile"] == 9
     assert L.gemm_tn_ex(0, P, P + 0x100000, P + 0x200000, 64, 129, 64, 15, 0, 1, None) == -5
