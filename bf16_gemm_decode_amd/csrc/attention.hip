@@ -125,14 +125,26 @@ attn_segment_kernel(const uint16_t *__restrict__ Q, const uint16_t *__restrict__
     const int w0 = min(l1, l0 + wave * per), w1 = min(l1, w0 + per);
 
     // Q^T as B operands, staged once in LDS: row h < G holds query head
-    // h0 + h, rows G .. 15 are zero; lane (g, h) reads Q[h0 + h][32 kk + 8 g .. +7]
-    for (int i = threadIdx.x; i < 16 * (D / 8); i += kAttnWaves * 64) {
+    // h0 + h, rows G .. 15 are zero; lane (g, h) reads Q[h0 + h][32 kk + 8 g .. +7].
+    // Requested first, stored after the first K/V requests, so that its
+    // latency overlaps the block-table lookups instead of preceding them.
+    constexpr int QP = (16 * (D / 8) + kAttnWaves * 64 - 1) / (kAttnWaves * 64);
+    u32x4 qv[QP];
+#pragma unroll
+    for (int p = 0; p < QP; ++p) {
+        const int i = threadIdx.x + p * kAttnWaves * 64;
         const int h = i / (D / 8), x = i % (D / 8);
-        u32x4 v = {0u, 0u, 0u, 0u};
-        if (h < G) v = *(const u32x4 *)(Q + ((size_t)b * Hq + h0 + h) * D + 8 * x);
-        *(u32x4 *)&qt[h][8 * x] = v;
+        qv[p] = *(attn_gptr16)(i < 16 * (D / 8) && h < G ? Q + ((size_t)b * Hq + h0 + h) * D + 8 * x
+                                                         : kAttnZeros);
     }
-    __syncthreads();
+    auto store_q = [&]() {
+#pragma unroll
+        for (int p = 0; p < QP; ++p) {
+            const int i = threadIdx.x + p * kAttnWaves * 64;
+            if (i < 16 * (D / 8)) *(u32x4 *)&qt[i / (D / 8)][8 * (i % (D / 8))] = qv[p];
+        }
+        __syncthreads();
+    };
 
     float mrun = kNegInf, lrun = 0.f;      // head r16's running max (log2 units) and denominator
     float o[G][8];
@@ -258,6 +270,7 @@ attn_segment_kernel(const uint16_t *__restrict__ Q, const uint16_t *__restrict__
     page_ids(w0, pa);
     page_ids(w0 + T, pb);
     issue(w0, pa, ka, va, oka);
+    store_q();
     for (int t0 = w0; t0 < w1; t0 += 2 * T) {
         page_ids(t0 + 2 * T, pa);
         issue(t0 + T, pb, kb2, vb2, okb);
