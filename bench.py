@@ -408,7 +408,8 @@ def main():
         "roofline": {"bound": "mfma", "achieved": round(tflops, 2), "peak": peak,
                      "unit": "TFLOP/s", "frac": round(tflops / peak, 4),
                      "traffic": measured_traffic(GEMM_SOURCES, "gemm_8192x8192x16384_f16_traffic.json"),
-                     "mfma_util_percent": measured_mfma_util(GEMM_SOURCES, GEMM_MFMA_SUMMARY, "f16_tile10"),
+                     "mfma_util_percent": measured_mfma_util(GEMM_SOURCES, GEMM_MFMA_SUMMARY,
+                                                             "f16_tile%d" % plan["tile"]),
                      "kernel": "%s (2*M*N*K FLOP per launch)" % kernel,
                      "avg_launch_ms": round(gemm_avg * 1e3, 4)},
         "gemv": {"GBps": round(gemv_GBps, 1), "avg_launch_us": round(gemv_avg * 1e6, 2),

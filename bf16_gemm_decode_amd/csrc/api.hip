@@ -46,10 +46,10 @@ struct ShapeConfig {
     int dtype, a_kmajor, M, N, K, tile, group_m;
 };
 constexpr ShapeConfig kShapeTable[] = {
-    {DT_F16, 0, 8192, 8192, 16384, TILE_256x256_FL8, 8},
-    {DT_BF16, 0, 4096, 34816, 5120, TILE_256x256_FL8, 16},    // 1.261 ms vs 1.270 at 8
-    {DT_BF16, 1, 34816, 4096, 5120, TILE_256x256_FL8, 4},     // 1.316 ms vs 1.354 at 8
-    {DT_BF16, 0, 5000, 3000, 4100, TILE_256x256_FL8, 16},    // 120 us vs 201 on 128x128
+    {DT_F16, 0, 8192, 8192, 16384, TILE_256x256_PP, 8},      // 1.82-1.84 ms vs 1.92-2.04 on tile 10
+    {DT_BF16, 0, 4096, 34816, 5120, TILE_256x256_PP, 16},    // 1.22-1.27 ms vs 1.30 on tile 10
+    {DT_BF16, 1, 34816, 4096, 5120, TILE_256x256_FL8, 4},    // 1.316 ms vs 1.354 at 8
+    {DT_BF16, 0, 5000, 3000, 4100, TILE_256x256_PP, 16},     // 118-129 us vs 131-148 on tile 10
 };
 
 const ShapeConfig *find_shape(int dtype, bool a_kmajor, int M, int N, int K)
@@ -104,7 +104,7 @@ int plan_gemm(int dtype, const uint16_t *A, const uint16_t *B, const uint16_t *C
     // the last K % 8 k after it.
     const bool wide = (L.vec_a == 8 && L.vec_b == 8);
     const bool fl = (L.vec_a >= 2 && L.vec_b >= 2);
-    auto is_fl = [](int t) { return t >= TILE_256x256_FL && t <= TILE_128x128_SK; };
+    auto is_fl = [](int t) { return (t >= TILE_256x256_FL && t <= TILE_128x128_SK) || t == TILE_256x256_PP; };
     if (tile == TILE_AUTO && group_m == 0 && !q8) {
         const ShapeConfig *c = find_shape(dtype, a_kmajor, M, N, K);
         if (c && (wide || c->tile == TILE_128x128 || (fl && is_fl(c->tile)))) {
@@ -115,9 +115,10 @@ int plan_gemm(int dtype, const uint16_t *A, const uint16_t *B, const uint16_t *C
     // Automatic tile for a 16-bit GEMM: the least estimated time, counting
     // rounds of workgroups over the 256 CUs.  Per round at K = 4096 (one
     // MI355X, square and 2:1 shapes from 1024 to 8192): 256x256 with 8 waves
-    // 110 us per 256 tiles; 256x128 80 us per 256; 128x128 56 us for up to
-    // 256 tiles, then 85 us per 512 (two workgroups per CU; the full-line
-    // 128x128 takes 56 us per 256).
+    // 110 us per 256 tiles (the ping-pong variant, m-major A only, 5-10%
+    // less: 102); 256x128 80 us per 256; 128x128 56 us for up to 256 tiles,
+    // then 85 us per 512 (two workgroups per CU; the full-line 128x128 takes
+    // 56 us per 256).
     auto auto_tile = [&]() {
         const int64_t t256 = cdiv(M, 256) * cdiv(N, 256), t2 = cdiv(M, 256) * cdiv(N, 128),
                       t128 = cdiv(M, 128) * cdiv(N, 128);
@@ -126,7 +127,7 @@ int plan_gemm(int dtype, const uint16_t *A, const uint16_t *B, const uint16_t *C
         auto take = [&](int t, int64_t c) {
             if (c < cost) { cost = c; best = t; }
         };
-        if (fl) take(TILE_256x256_FL8, cdiv(t256, 256) * 110);
+        if (fl) take(a_kmajor ? TILE_256x256_FL8 : TILE_256x256_PP, cdiv(t256, 256) * (a_kmajor ? 110 : 102));
         if (wide && !a_kmajor) take(TILE_256x128, cdiv(t2, 256) * 80);
         else if (fl) take(TILE_256x128_FL, cdiv(t2, 256) * 80);
         if (!a_kmajor) take(TILE_128x128, t128 <= 256 ? 56 : cdiv(t128, 512) * 85);
@@ -147,7 +148,8 @@ int plan_gemm(int dtype, const uint16_t *A, const uint16_t *B, const uint16_t *C
             tile = wide && N <= kSkinnyAutoMax ? TILE_SKINNY
                    : wide && N <= kBatchAutoMax ? TILE_BATCH
                                                 : auto_tile();
-        } else if ((tile < TILE_256x256_FL) || (tile == TILE_SKINNY && N > kSkinnyMaxTokens) ||
+        } else if ((tile < TILE_256x256_FL) || tile == TILE_256x256_PP ||
+                   (tile == TILE_SKINNY && N > kSkinnyMaxTokens) ||
                    (tile == TILE_BATCH && N > kBatchMaxTokens)) {
             return MIGEMM_ERR_CONFIG;
         } else if (!wide && !is_fl(tile)) {

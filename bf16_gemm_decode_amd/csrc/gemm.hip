@@ -479,7 +479,28 @@ constexpr int fl_loads_after(int j, int need_a, int need_b)
 // rows read with transposing LDS reads.  AK = true: A k-major (A(m,k) =
 // A[k + m*K]), A ring of SA stages of 64 k laid out, loaded and read exactly
 // like B (rows of A in place of columns of B).
-template <int DT, bool AK, int BM, int BN, int WGM, int WGN, int SA, int SB, int OCC, bool SPLIT>
+// Ping-pong tile: MFMAs of a sub-step issued in its load phase (the rest go
+// into its compute phase).
+#ifndef PP_PRE
+#define PP_PRE 8
+#endif
+
+// Ping-pong schedule (PP below): loads in flight after the last one that
+// sub-step t needs, once load phases up to L have issued.  Load phase i
+// issues A sub-step i + SA - 1 (LA loads), then half (i & 1) of B stage
+// (i >> 1) + SB - 1 (LBH loads).
+template <int SA, int SB, int LA, int LBH>
+constexpr int pp_loads_after(int L, int t)
+{
+    const int ia = t - SA + 1;                     // phase that issued A(t)
+    const int na = LBH + (L - ia) * (LA + LBH);
+    const int ib = 2 * ((t >> 1) - SB + 1) + 1;    // phase that issued B stage t/2's second half
+    const int nb = (L - ib) * (LA + LBH);
+    return na < nb ? na : nb;
+}
+
+template <int DT, bool AK, int BM, int BN, int WGM, int WGN, int SA, int SB, int OCC, bool SPLIT,
+          bool PP = false>
 __global__ void __launch_bounds__(WGM * WGN * 64)
 __attribute__((amdgpu_waves_per_eu(OCC, OCC)))
 gemm_fl_kernel(const uint16_t *__restrict__ A, const uint16_t *__restrict__ B,
@@ -772,7 +793,110 @@ gemm_fl_kernel(const uint16_t *__restrict__ A, const uint16_t *__restrict__ B,
         sb = nsb;
     };
 
-    if (J > 0) {
+    if constexpr (PP) {
+        // Ping-pong: two groups of four waves, one wave of each group per
+        // SIMD (waves w and w + 4 share a SIMD).  Each sub-step j is a load
+        // phase (issue the LDS-direct loads of a later sub-step, nothing
+        // else) and a compute phase (the FM x FN MFMAs of sub-step j, with
+        // the LDS reads of sub-step j + 1 into the other fragment set between
+        // them).  Group 1 runs one phase behind group 0, a workgroup barrier
+        // between phases, so on each SIMD one wave streams MFMAs and LDS
+        // reads while the other waits for the memory pipe to take its loads:
+        // a load stalled at issue never holds up an MFMA or an LDS read.
+        //
+        // Load phase i issues A sub-step i + SA - 1 and half (i & 1) of B
+        // stage (i >> 1) + SB - 1: the largest distances at which no load
+        // targets a stage still to be read.  Before the barrier that ends its
+        // compute phase j, a wave waits for its own loads of sub-step j + 2,
+        // which the group one phase ahead starts reading right after it.
+        static_assert(!AK && !SPLIT && NW == 8, "ping-pong: 8 waves, m-major A");
+        const int role = wave >> 2;
+        if (J > 0) {
+            auto phase_loads = [&](int i) {
+                const int ja = i + SA - 1;
+                if (ja >= 0 && ja < J) {
+                    const u32x4 d = desc_a(ja);
+#pragma unroll
+                    for (int q = 0; q < LA; ++q) issue_a(d, ja, ja % SA, q);
+                }
+                const int pb = (i >> 1) + SB - 1;
+                if (pb >= 0 && pb < P_) {
+                    const u32x4 d = desc_b(pb);
+#pragma unroll
+                    for (int q = 0; q < LBH; ++q) issue_b(d, pb, pb % SB, (i & 1) * LBH + q);
+                }
+            };
+            // wait until sub-step t's loads have landed, load phases up to L
+            // issued; the exact count holds while phase L issued every load of
+            // the fixed order (then so did all phases before it)
+            auto wait_for = [&](auto lpar_c, auto dt_c, int L) {
+                constexpr int LP = decltype(lpar_c)::value, DT_ = decltype(dt_c)::value;
+                constexpr int W = pp_loads_after<SA, SB, LA, LBH>(64 + LP, 64 + LP + DT_);
+                static_assert(W >= 0 && W < 64, "vmcnt range");
+                if (L + SA - 1 < J && (L >> 1) + SB - 1 < P_) wait_vmcnt<W>();
+                else wait_vmcnt<0>();
+            };
+            constexpr int FIRST = -(SA - 1) < -2 * (SB - 1) ? -(SA - 1) : -2 * (SB - 1);
+#pragma unroll
+            for (int i = FIRST; i < 0; ++i) phase_loads(i);
+            Frag f0, f1;
+            wait_for(std::integral_constant<int, 1>{}, std::integral_constant<int, 1>{}, -1);   // sub-step 0
+            __syncthreads();
+#pragma unroll
+            for (int r = 0; r < NR; ++r) read_one(0, 0, 0, r, f0);
+            if (J > 1) wait_for(std::integral_constant<int, 1>{}, std::integral_constant<int, 2>{}, -1);   // sub-step 1
+            __syncthreads();
+            if (role) __syncthreads();
+            // The first PRE MFMAs of sub-step j go into its load phase, after
+            // the loads: its fragments are in registers by then, and the
+            // wave would otherwise only wait for the memory pipe, so for part
+            // of every phase both waves of a SIMD issue MFMAs.
+            constexpr int NMF = FM * FN;
+            constexpr int PRE = PP_PRE < NMF ? PP_PRE : 0;
+            auto pre_mfma = [&](const Frag &cur) {
+#pragma unroll
+                for (int t = 0; t < PRE; ++t) {
+                    mfma16x16x32<DT>(acc[t / FN][t % FN], cur.a[t / FN], cur.b[t % FN]);
+                    __builtin_amdgcn_sched_barrier(0);
+                }
+            };
+            // compute phase of sub-step j on `cur` (its MFMAs from PRE on),
+            // reading sub-step j + 1 into `nxt` (one read after every EV
+            // MFMAs; after the last sub-step these read stale ring contents
+            // that are never used)
+            auto compute = [&](int j, auto par_c, Frag &cur, Frag &nxt) {
+                constexpr int PAR = decltype(par_c)::value;
+                constexpr int EV = (NMF - PRE) / NR > 0 ? (NMF - PRE) / NR : 1;
+                const int na = (j + 1) % SA, nb = ((j + 1) >> 1) % SB;
+#pragma unroll
+                for (int t = PRE; t < NMF; ++t) {
+                    mfma16x16x32<DT>(acc[t / FN][t % FN], cur.a[t / FN], cur.b[t % FN]);
+                    const int u = t - PRE;
+                    if (u % EV == EV - 1 && u / EV < NR) read_one(na, nb, 1 - PAR, u / EV, nxt);
+                    __builtin_amdgcn_sched_barrier(0);
+                }
+                constexpr int DONE = (NMF - PRE) / EV < NR ? (NMF - PRE) / EV : NR;
+#pragma unroll
+                for (int r = DONE; r < NR; ++r) read_one(na, nb, 1 - PAR, r, nxt);
+                if (j + 2 < J) wait_for(std::integral_constant<int, PAR>{}, std::integral_constant<int, 2>{}, j);
+                __syncthreads();
+            };
+            for (int j = 0; j < J; j += 2) {
+                phase_loads(j);
+                pre_mfma(f0);
+                __syncthreads();
+                compute(j, std::integral_constant<int, 0>{}, f0, f1);
+                if (j + 1 < J) {
+                    phase_loads(j + 1);
+                    pre_mfma(f1);
+                    __syncthreads();
+                    compute(j + 1, std::integral_constant<int, 1>{}, f1, f0);
+                }
+            }
+            if (!role) __syncthreads();
+            wait_vmcnt<0>();   // no load may still target LDS when the workgroup ends
+        }
+    } else if (J > 0) {
         // prologue: the loads of the sub-steps before 0, in the fixed order
 #pragma unroll
         for (int i = -2 * (SA + SB) - 4; i < 0; ++i) {
@@ -856,13 +980,13 @@ constexpr bool kSplitTile = !dt_is_8bit(DT) && ((BM == 256 && BN == 128 && WGM *
                                                 (BM == 256 && BN == 256 && WGM * WGN == 8) ||
                                                 (BM == 128 && BN == 128 && WGM * WGN == 4));
 
-template <int DT, bool AK, int BM, int BN, int WGM, int WGN, int SA, int SB, int OCC = 0>
+template <int DT, bool AK, int BM, int BN, int WGM, int WGN, int SA, int SB, int OCC = 0, bool PP = false>
 static hipError_t launch_fl(const GemmLaunch &L, hipStream_t stream)
 {
     constexpr int OC = OCC ? OCC : WGM * WGN / 4;
     const dim3 block(WGM * WGN * 64);
     if (L.splits > 1) {
-        if constexpr (kSplitTile<DT, BM, BN, WGM, WGN>) {
+        if constexpr (kSplitTile<DT, BM, BN, WGM, WGN> && !PP) {
             hipLaunchKernelGGL((gemm_fl_kernel<DT, AK, BM, BN, WGM, WGN, SA, SB, OC, true>),
                                dim3((unsigned)L.grid, (unsigned)L.splits), block, 0, stream, L.A, L.B,
                                L.C, L.M, L.N, L.K, L.num_pid_m, L.num_pid_n, L.group_m, L.num_xcd,
@@ -871,7 +995,7 @@ static hipError_t launch_fl(const GemmLaunch &L, hipStream_t stream)
         }
         return hipErrorInvalidValue;
     }
-    hipLaunchKernelGGL((gemm_fl_kernel<DT, AK, BM, BN, WGM, WGN, SA, SB, OC, false>),
+    hipLaunchKernelGGL((gemm_fl_kernel<DT, AK, BM, BN, WGM, WGN, SA, SB, OC, false, PP>),
                        dim3((unsigned)L.grid), block, 0, stream, L.A, L.B, L.C, L.M, L.N, L.K,
                        L.num_pid_m, L.num_pid_n, L.group_m, L.num_xcd, L.c_vec, L.scale, L.K & ~7,
                        (float *)nullptr);
@@ -916,6 +1040,9 @@ static hipError_t launch_dt(const GemmLaunch &L, hipStream_t s)
     case TILE_256x256_FL8:
         return L.a_kmajor ? launch_fl<DT, true, 256, 256, 4, 2, 2, 3>(L, s)
                           : launch_fl<DT, false, 256, 256, 4, 2, 4, 3>(L, s);
+    case TILE_256x256_PP:
+        return L.a_kmajor ? hipErrorInvalidValue
+                          : launch_fl<DT, false, 256, 256, 4, 2, 4, 3, 2, true>(L, s);
     case TILE_64x32_SK:
         return L.a_kmajor ? launch_fl<DT, true, 64, 32, 2, 1, 4, 2, 2>(L, s)
                           : launch_fl<DT, false, 64, 32, 2, 1, 4, 2, 2>(L, s);

@@ -23,6 +23,7 @@ enum GemmTile {
     TILE_128x128_SK = 13,       // 128x128, 4 waves as 2x2, full-line rings
     TILE_SKINNY = 14,           // few columns: W straight into 4x4x4 MFMA registers (skinny.hip)
     TILE_BATCH = 15,            // 9..128 columns: W into 16x16x32 MFMA registers, X in LDS (batch.hip)
+    TILE_256x256_PP = 16,       // as 10, m-major A, ping-pong: the two waves of a SIMD alternate MFMA and memory phases
     TILE_COUNT
 };
 
@@ -50,6 +51,7 @@ constexpr TileShape kTileShapes[TILE_COUNT] = {
     {128, 128, 32, 4, 4, 3},
     {32, 64, 32, 0, 4, 0},
     {64, 128, 128, 0, 4, 0},
+    {256, 256, 32, 4, 8, 3},
 };
 
 // The full-line tiles with A k-major: stages = A ring stages of 64 k.
@@ -70,6 +72,7 @@ constexpr TileShape kTileShapesKmajorA[TILE_COUNT] = {
     {128, 128, 32, 4, 4, 3},
     {32, 64, 32, 0, 4, 0},
     {64, 128, 128, 0, 4, 0},
+    {0, 0, 0, 0, 0, 0},
 };
 
 constexpr int tile_lds_bytes(const TileShape &t, bool a_kmajor = false)

@@ -78,7 +78,7 @@ def test_every_tile_plan_fits_lds():
     # reports its own tile extents
     want = {1: (256, 256), 2: (256, 128), 3: (128, 128), 4: (256, 256), 5: (256, 256),
             6: (256, 256), 7: (256, 256), 8: (256, 256), 9: (256, 128), 10: (256, 256),
-            11: (64, 32), 12: (64, 64), 13: (128, 128)}
+            11: (64, 32), 12: (64, 64), 13: (128, 128), 16: (256, 256)}
     for tile, (tm, tn) in want.items():
         code, p = binding.gemm_plan(0, P, P + 2 ** 30, P + 2 ** 31, 1024, 1024, 1024, tile)
         assert code == 0, tile
@@ -89,6 +89,9 @@ def test_every_tile_plan_fits_lds():
         4 * 32 * 256 * 2 + 3 * 64 * 256 * 2
     assert binding.gemm_plan(0, P, P + 2 ** 30, P + 2 ** 31, 1024, 1024, 1024, 9)[1]["lds_bytes"] == \
         4 * 32 * 256 * 2 + 4 * 64 * 128 * 2
+    # the ping-pong tile: the rings of tile 10, 8 waves, m-major A only
+    code, p = binding.gemm_plan(0, P, P + 2 ** 30, P + 2 ** 31, 1024, 1024, 1024, 16)
+    assert code == 0 and p["lds_bytes"] == 160 * 1024 and p["waves"] == 8
 
 
 def test_tn_plan_and_errors():
@@ -145,10 +148,10 @@ def test_exact_shape_table():
     # measured exact-shape configurations apply when tile and GROUP_M are automatic
     plan = lambda dt, M, N, K, tile=0, gm=0, tn=False: binding.gemm_plan(
         dt, P, P + 2 ** 30, P + 2 ** 31, M, N, K, tile, gm, a_kmajor=tn)[1]
-    assert (plan(1, 4096, 34816, 5120)["tile"], plan(1, 4096, 34816, 5120)["group_m"]) == (10, 16)
+    assert (plan(1, 4096, 34816, 5120)["tile"], plan(1, 4096, 34816, 5120)["group_m"]) == (16, 16)
     assert (plan(1, 34816, 4096, 5120, tn=True)["tile"], plan(1, 34816, 4096, 5120, tn=True)["group_m"]) == (10, 4)
-    assert (plan(0, 8192, 8192, 16384)["tile"], plan(0, 8192, 8192, 16384)["group_m"]) == (10, 8)
-    assert (plan(1, 5000, 3000, 4100)["tile"], plan(1, 5000, 3000, 4100)["group_m"]) == (10, 16)
+    assert (plan(0, 8192, 8192, 16384)["tile"], plan(0, 8192, 8192, 16384)["group_m"]) == (16, 8)
+    assert (plan(1, 5000, 3000, 4100)["tile"], plan(1, 5000, 3000, 4100)["group_m"]) == (16, 16)
     # an explicit GROUP_M or tile, another dtype or shape: the heuristics
     assert plan(1, 4096, 34816, 5120, gm=8)["group_m"] == 8
     assert plan(1, 4096, 34816, 5120, tile=9)["tile"] == 9
@@ -230,7 +233,7 @@ def test_plan_choices():
     code, p = binding.gemm_plan(0, P, P + 2 ** 30, P + 2 ** 31, 8192, 8192, 16384)
     assert code == 0 and (p["tile_m"], p["tile_n"], p["vec_a"], p["vec_b"], p["grid"]) == \
         (256, 256, 8, 8, 1024)
-    assert p["tile_k"] == 32 and p["tile"] == 10 and p["waves"] == 8 and p["a_kmajor"] == 0
+    assert p["tile_k"] == 32 and p["tile"] == 16 and p["waves"] == 8 and p["a_kmajor"] == 0
     assert p["lds_bytes"] <= 160 * 1024
     # ragged: M = 5000 keeps 16-byte A rows, K = 4100 leaves B 4-byte rows,
     # which the full-line tiles take (k loop to 4096, then the last 4 k)

@@ -55,8 +55,8 @@ def test_shape_sweep_random_triples():
         _full_case(M, N, K, fmt, seed=200 + i)
 
 
-ALL_TILES = list(range(1, 14))
-FULL_LINE_TILES = [7, 8, 9, 10, 11, 12, 13]
+ALL_TILES = list(range(1, 14)) + [16]
+FULL_LINE_TILES = [7, 8, 9, 10, 11, 12, 13, 16]
 
 
 @pytest.mark.parametrize("tile", ALL_TILES)
@@ -102,7 +102,7 @@ def test_k_tail_keeps_columns_apart():
     b[0 + 5 * K] = np.inf         # column 5, k = 0
     for fmt in FMTS:
         A, B = synth.to_bits(a, fmt), synth.to_bits(b, fmt)
-        for tile in (0, 9, 10, 13):
+        for tile in (0, 9, 10, 13, 16):
             print("case k tail non-finite", fmt, tile, flush=True)
             got, _, _ = gemm_gpu(A, B, M, N, K, fmt, tile=tile)
             assert_parity(got, oracle.gemm(A, B, M, N, K, fmt), fmt, "k tail %s tile %d" % (fmt, tile))
@@ -277,7 +277,7 @@ def test_tile_orderings_bit_identical_and_repeatable():
     M, N, K = 2048, 4352, 1024
     A, B = synth.gemm_operands(M, N, K, "bf16", ("normal", 1.0, 0.02), seed=11)
     base = None
-    for tile in (1, 2, 5, 7, 9, 10, 11, 13):
+    for tile in (1, 2, 5, 7, 9, 10, 11, 13, 16):
         outs = []
         for gm in (1, 4, 8, 16):
             for xcd in (0, 1):
