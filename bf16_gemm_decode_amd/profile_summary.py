@@ -2,7 +2,8 @@
 profiles/.
 
   kernel-stats:  python -m bf16_gemm_decode_amd.profile_summary stats \
-                     <run_kernel_stats.csv> <out.txt> --command "<rocprofv3 command>"
+                     <run_kernel_stats.csv> <out.txt> --command "<rocprofv3 command>" \
+                     [--trace <run_kernel_trace.csv> --timed <kernel substring>:<skip>:<count> ...]
   mfma:          python -m bf16_gemm_decode_amd.profile_summary mfma \
                      --util-csv <csv> --counts-csv <csv> --kernel label=<substring>:<FLOP> ... \
                      --source <files...> --out <out.json> --commands "<cmd>" ...
@@ -59,6 +60,27 @@ def stats(args):
             if args.filter and not any(f in name for f in args.filter):
                 continue
             o.write(", ".join(str(r[k]) for k in keys) + "\n")
+        # the timed region of bench.py: the kernel's dispatches after the
+        # warm-up ones, in dispatch order, from the kernel trace
+        for spec in args.timed or []:
+            substr, skip, count = spec.rsplit(":", 2)
+            d = sorted((int(r["Dispatch_Id"]), int(r["End_Timestamp"]) - int(r["Start_Timestamp"]))
+                       for r in _rows(args.trace) if substr in r["Kernel_Name"])
+            sel = [t for _, t in d[int(skip):int(skip) + int(count)]]
+            if not sel:
+                sys.exit("no dispatches of %r in %s" % (substr, args.trace))
+            o.write("# timed region: %s dispatches %d..%d of %d: average %.1f ns, min %d, max %d\n"
+                    % (substr, int(skip), int(skip) + len(sel) - 1, len(d), sum(sel) / len(sel),
+                       min(sel), max(sel)))
+        # what bench.py itself reported in the profiled run
+        if args.bench_json:
+            with open(args.bench_json) as f:
+                for line in f:
+                    if line.startswith("{") and '"roofline"' in line:
+                        b = json.loads(line)
+                        o.write("# bench.py in the same run: GEMM avg_launch_ms %s (HIP events, timed region), "
+                                "GEMV avg_launch_us %s\n" % (b["roofline"]["avg_launch_ms"],
+                                                            b["gemv"]["avg_launch_us"]))
     print(open(args.out).read())
 
 
@@ -162,6 +184,10 @@ def main(argv=None):
     s.add_argument("out")
     s.add_argument("--command", required=True)
     s.add_argument("--filter", nargs="*")
+    s.add_argument("--trace", help="the run's kernel-trace CSV, for --timed")
+    s.add_argument("--bench-json", help="stdout of the profiled bench.py run")
+    s.add_argument("--timed", nargs="*",
+                   help="<kernel name substring>:<dispatches to skip>:<count>: average over those dispatches")
     t = sub.add_parser("traffic")
     t.add_argument("--fetch", required=True)
     t.add_argument("--fetch-cal", required=True)
