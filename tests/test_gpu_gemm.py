@@ -294,6 +294,22 @@ def test_tile_orderings_bit_identical_and_repeatable():
             assert_parity(base[idx], oracle.gemm_sampled(A, B, M, N, K, idx, "bf16"), "bf16", "orderings")
 
 
+def test_pingpong_tile_bit_identical_to_tile_10():
+    # tile 16 issues the same MFMAs as tile 10 on the same fragments, each
+    # accumulator taking its k sub-steps in the same order (and the k tail
+    # first), so the two schedules must agree bit for bit: a stage read too
+    # early or refilled too soon would show here as a difference
+    for i, (M, N, K) in enumerate([(520, 600, 200), (264, 300, 72), (1024, 768, 1036), (2048, 2304, 4096),
+                                   (258, 70, 70)]):
+        fmt = FMTS[i % 2]
+        A, B = synth.gemm_operands(M, N, K, fmt, ("normal", 1.0, 1.0), seed=40 + i)
+        print("case pingpong vs tile 10", (M, N, K), fmt, flush=True)
+        g10, guards10, _ = gemm_gpu(A, B, M, N, K, fmt, tile=10)
+        g16, guards16, unchanged = gemm_gpu(A, B, M, N, K, fmt, tile=16)
+        assert guards10 and guards16 and unchanged
+        assert np.array_equal(g16, g10), (M, N, K, fmt)
+
+
 def test_tensor_wrapper_and_stream():
     import torch
     from bf16_gemm_decode_amd import gemm
