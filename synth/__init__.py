@@ -170,3 +170,16 @@ def cyclic_shift_colmajor(n, s=1):
     P = np.zeros((n, n))
     P[np.arange(n), (np.arange(n) + s) % n] = 1.0
     return P.ravel(order="F")
+
+
+def mod5_pattern(i, j, a, b):
+    """Small-integer operand pattern ((a*i + b*j) mod 5) - 2, values in
+    [-2, 2], as float64 (exact in every 16-bit format here), broadcast over
+    index arrays i and j.  For a fixed j it takes only five distinct rows
+    over i (the row for j depends on b*j mod 5 alone), so an operand of
+    billions of elements can be assembled on the device from five short rows,
+    while any of its rows or columns can be rebuilt on the host from the same
+    formula."""
+    i = np.asarray(i, dtype=np.int64)
+    j = np.asarray(j, dtype=np.int64)
+    return (((a * i + b * j) % 5) - 2).astype(np.float64)

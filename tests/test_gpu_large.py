@@ -1,0 +1,99 @@
+"""GPU parity for operands of more than 2^31 elements (about 8.6 GB each):
+byte offsets past 32 bits, the per-step rebasing of the buffer descriptors
+and the 64-bit row offsets of the decode kernels.
+
+The operands follow synth.mod5_pattern, entries in [-2, 2]: every partial
+sum is an integer below 2^24, so FP32 accumulation is exact in any order and
+the one rounding to 16 bits is deterministic -- results are compared bit for
+bit.  The pattern has five distinct rows, so the large operand is assembled
+on the device by repeating them (torch indexing: plumbing, no arithmetic of
+the method); the oracle computes the product restricted to the sampled rows
+and columns, built on the host from the same formula."""
+import numpy as np
+import pytest
+
+import oracle
+import synth
+from helpers import dev
+
+pytestmark = pytest.mark.gpu
+
+
+def _free():
+    import torch
+    torch.cuda.synchronize()
+    torch.cuda.empty_cache()
+
+
+def _edge_indices(n, extra):
+    """first, last and a few interior indices of 0..n-1, sorted, unique"""
+    return np.unique(np.array([0, 1, n // 3, n // 2, n - 2, n - 1] + extra, dtype=np.int64) % n)
+
+
+@pytest.mark.parametrize("fmt,big", [("f16", "A"), ("bf16", "B")])
+def test_gemm_operand_past_2g_elements(fmt, big):
+    import torch
+    from bf16_gemm_decode_amd import binding
+    K = 4100                                   # 4-byte rows: the k loop stops at 4096, then the tail
+    M, N = ((1 << 20) + 8, 264) if big == "A" else (264, (1 << 20) + 8)
+    assert (M if big == "A" else N) * K > 2 ** 31
+    print("case large", big, fmt, (M, N, K), flush=True)
+    # A(m, k) = ((m + 3k) mod 5) - 2: k-row k of the column-major A is row
+    # class 3k mod 5; B(k, n) = ((k + 2n) mod 5) - 2: column n is class 2n mod 5
+    arows = torch.stack([dev(synth.to_bits(synth.mod5_pattern(np.arange(M), c, 1, 1), fmt)) for c in range(5)])
+    bcols = torch.stack([dev(synth.to_bits(synth.mod5_pattern(np.arange(K), c, 1, 1), fmt)) for c in range(5)])
+    kidx = torch.arange(K, device="cuda") * 3 % 5
+    nidx = torch.arange(N, device="cuda") * 2 % 5
+    dA = arows[kidx].reshape(-1)               # [K][M]: A[m + k*M]
+    dB = bcols[nidx].reshape(-1)               # [N][K]: B[k + n*K]
+    del arows, bcols
+    dC = torch.full((M * N,), 0x7C01, dtype=torch.int16, device="cuda")   # NaN marker
+    code, plan = binding.gemm_plan(binding.F16 if fmt == "f16" else binding.BF16,
+                                   dA.data_ptr(), dB.data_ptr(), dC.data_ptr(), M, N, K)
+    assert code == 0 and plan["tile"] == 16          # the ping-pong tile, 4-byte B rows
+    print("plan tile", plan["tile"], "grid", plan["grid"], flush=True)
+    code = binding.gemm_ex_ptr(binding.F16 if fmt == "f16" else binding.BF16,
+                               dA.data_ptr(), dB.data_ptr(), dC.data_ptr(), M, N, K)
+    assert code == 0
+    torch.cuda.synchronize()
+    ms = _edge_indices(M, [(1 << 31) // K, (1 << 31) // K + 1, 257, 4095])
+    ns = _edge_indices(N, [(1 << 31) // K, 255, 256, 4097])
+    got = dC.view(M * N)[torch.from_numpy(ms[:, None] + ns[None, :] * M).cuda().reshape(-1)]
+    got = got.cpu().numpy().view(np.uint16).reshape(len(ms), len(ns))
+    # the product restricted to those rows and columns
+    kk = np.arange(K)
+    Asub = synth.to_bits(synth.mod5_pattern(ms[:, None], kk[None, :], 1, 3).ravel(order="F"), fmt)
+    Bsub = synth.to_bits(synth.mod5_pattern(kk[:, None], ns[None, :], 1, 2).ravel(order="F"), fmt)
+    ref = oracle.gemm(Asub, Bsub, len(ms), len(ns), K, fmt)
+    want = ref.bits.reshape(len(ns), len(ms)).T          # column-major [ms x ns]
+    assert np.array_equal(got, want), np.argwhere(got != want)[:8]
+    del dA, dB, dC
+    _free()
+
+
+@pytest.mark.parametrize("n", [1, 4, 16])
+def test_gemv_weight_past_2g_elements(n):
+    import torch
+    from bf16_gemm_decode_amd import binding
+    M, K = (1 << 19) + 3, 4104
+    assert M * K > 2 ** 31
+    print("case large gemv", (M, K, n), flush=True)
+    # W[j][k] = ((3k + j) mod 5) - 2: row j is class j mod 5;
+    # X[i][k] = ((k + 2i) mod 5) - 2
+    wrows = torch.stack([dev(synth.to_bits(synth.mod5_pattern(np.arange(K), c, 3, 1), "bf16")) for c in range(5)])
+    dW = wrows[torch.arange(M, device="cuda") % 5].reshape(-1)
+    del wrows
+    kk = np.arange(K)
+    X = synth.to_bits(synth.mod5_pattern(kk[None, :], np.arange(n)[:, None], 1, 2).ravel(), "bf16")
+    dX = dev(X)
+    dY = torch.full((n * M,), 0x7FC1, dtype=torch.int16, device="cuda")
+    code = binding.gemv_bf16_ptr(dW.data_ptr(), dX.data_ptr(), dY.data_ptr(), M, K, n)
+    assert code == 0
+    torch.cuda.synchronize()
+    js = _edge_indices(M, [(1 << 31) // K, (1 << 31) // K + 1, 4099])
+    got = dY.view(n, M)[:, torch.from_numpy(js).cuda()].cpu().numpy().view(np.uint16)
+    Wsub = synth.to_bits(synth.mod5_pattern(kk[None, :], js[:, None], 3, 1).ravel(), "bf16")
+    ref = oracle.gemv(Wsub, X, len(js), K, n)
+    assert np.array_equal(got, ref.bits.reshape(n, len(js)))
+    del dW, dX, dY
+    _free()
