@@ -179,7 +179,7 @@ def test_splitk_rules_and_errors():
                                           for x in ("dt", "ak", "A", "B", "C", "M", "N", "K", "S",
                                                     "tile", "gm", "xcd", "ws", "wsb", "st")])
     assert call(dt=2) == -5 and call(ak=2) == -5 and call(S=-1) == -5
-    assert call(tile=3) == -5 and call(tile=7) == -5              # slices on tiles 9, 10, 13 only
+    assert call(tile=3) == -5 and call(tile=7) == -5 and call(tile=16) == -5   # slices on 9, 10, 13 only
     assert call(ws=None) == -2
     assert call(ws=W + 8) == -4
     assert call(wsb=4 * 512 * 512 * 4 - 1) == -6
