@@ -359,6 +359,8 @@ def main():
                 c = torch.where((c & 0x7C) == 0x7C, c & ~0x40, c)
             return c.to(torch.uint8)
         qA, qB = codes(M * K), codes(N * K)
+        code, qplan = binding.gemm_plan(q, qA.data_ptr(), qB.data_ptr(), qC.data_ptr(), M, N, K, a_kmajor=True)
+        assert code == 0, code
         for _ in range(2):
             assert L.gemm_tn_q_ex(q, qA.data_ptr(), qB.data_ptr(), qC.data_ptr(), M, N, K, 1.0, 0, 0, 1, h) == 0
         q0, q1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
@@ -372,8 +374,9 @@ def main():
         qtf = rf.gemm_flop(M, N, K) / qt / 1e12
         q_rows[qname] = {"avg_launch_ms": round(qt * 1e3, 4), "TFLOPs_or_TOPs": round(qtf, 1),
                          "peak": pk, "frac": round(qtf / pk, 4),
+                         "tile": qplan["tile"],
                          "mfma_util_percent": measured_mfma_util(GEMM_SOURCES, GEMM_MFMA_SUMMARY,
-                                                                 qname + "_tile10")}
+                                                                 "%s_tile%d" % (qname, qplan["tile"]))}
         del qA, qB
     del qC
 

@@ -74,11 +74,12 @@ int plan_gemm(int dtype, const uint16_t *A, const uint16_t *B, const uint16_t *C
         if (K % 16) return MIGEMM_ERR_ALIGN;
         K /= 2;
         if (!(tile == TILE_AUTO || tile == TILE_256x128_FL || tile == TILE_256x256_FL8 ||
-              tile == TILE_128x128_SK))
+              tile == TILE_128x128_SK || (tile == TILE_256x128_F8W && dtype != DT_I8)))
             return MIGEMM_ERR_CONFIG;
     }
     if (tile < TILE_AUTO || tile >= TILE_COUNT || group_m < 0 || xcd_remap < 0 || xcd_remap > 1)
         return MIGEMM_ERR_CONFIG;
+    if (tile == TILE_256x128_F8W && !q8) return MIGEMM_ERR_CONFIG;   // FP8 only
     if (M < 0 || N < 0 || K < 0) return MIGEMM_ERR_DIM;
     if (M > MIGEMM_MAX_MN || N > MIGEMM_MAX_MN || K > MIGEMM_MAX_K) return MIGEMM_ERR_SIZE;
     const size_t abytes = (size_t)M * K * 2, bbytes = (size_t)K * N * 2, cbytes = (size_t)M * N * 2;
@@ -136,10 +137,13 @@ int plan_gemm(int dtype, const uint16_t *A, const uint16_t *B, const uint16_t *C
     };
     if (a_kmajor && q8) {
         if (!wide) return MIGEMM_ERR_ALIGN;
+        // FP8: the double-rate MFMA tile (17) once its 256x128 tiles fill
+        // the chip (8192x8192x16384: 1.06-1.08 ms against 1.30-1.43 on tile 10)
         if (tile == TILE_AUTO)
-            tile = cdiv(M, 256) * cdiv(N, 256) >= 512   ? TILE_256x256_FL8
-                   : cdiv(M, 256) * cdiv(N, 128) >= 256 ? TILE_256x128_FL
-                                                        : TILE_128x128_SK;
+            tile = dtype != DT_I8 && cdiv(M, 256) * cdiv(N, 128) >= 256 ? TILE_256x128_F8W
+                   : cdiv(M, 256) * cdiv(N, 256) >= 512                  ? TILE_256x256_FL8
+                   : cdiv(M, 256) * cdiv(N, 128) >= 256                  ? TILE_256x128_FL
+                                                                         : TILE_128x128_SK;
     } else if (a_kmajor) {
         // k-major A: the full-line tiles (4-byte rows) and, with 16-byte
         // rows, the few-token kernels

@@ -127,6 +127,24 @@ __device__ inline void mfma16x16x32(f32x4 &acc, u32x4 a, u32x4 b)
 
 // Wait states after the last MFMA before its results are read by other
 // instructions (more than the longest MFMA write-to-read requirement).
+// acc += a * b on one 16x16 block over 128 k of FP8 (E4M3 or E5M2 in both
+// operands), the double-rate gfx950 instruction: 32 bytes of A and of B per
+// lane.  Like mfma16x16x32, A and B fragments pair the same bytes of the same
+// lanes (lane l: row / column l % 16), so which k each byte holds does not
+// matter, and the result has the 16x16x32 layout.
+typedef __attribute__((ext_vector_type(8))) unsigned u32x8;
+template <int DT>
+__device__ inline void mfma16x16x128_f8(f32x4 &acc, u32x8 a, u32x8 b)
+{
+    // the accumulators stay in VGPRs: with them in AGPRs the compiler splits
+    // the 256 registers evenly and the two 32-byte fragment sets spill
+    static_assert(DT == DT_F8E4M3 || DT == DT_F8E5M2, "FP8 only");
+    if constexpr (DT == DT_F8E4M3)
+        asm("v_mfma_f32_16x16x128_f8f6f4 %0, %1, %2, %0" : "+v"(acc) : "v"(a), "v"(b));
+    else
+        asm("v_mfma_f32_16x16x128_f8f6f4 %0, %1, %2, %0 cbsz:1 blgp:1" : "+v"(acc) : "v"(a), "v"(b));
+}
+
 __device__ inline void mfma_drain()
 {
     asm volatile("s_nop 7\n\ts_nop 7\n\ts_nop 7\n\ts_nop 7" ::: "memory");
@@ -500,7 +518,7 @@ constexpr int pp_loads_after(int L, int t)
 }
 
 template <int DT, bool AK, int BM, int BN, int WGM, int WGN, int SA, int SB, int OCC, bool SPLIT,
-          bool PP = false>
+          bool PP = false, bool WIDE = false>
 __global__ void __launch_bounds__(WGM * WGN * 64)
 __attribute__((amdgpu_waves_per_eu(OCC, OCC)))
 gemm_fl_kernel(const uint16_t *__restrict__ A, const uint16_t *__restrict__ B,
@@ -793,7 +811,88 @@ gemm_fl_kernel(const uint16_t *__restrict__ A, const uint16_t *__restrict__ B,
         sb = nsb;
     };
 
-    if constexpr (PP) {
+    if constexpr (WIDE) {
+        // FP8 on the double-rate MFMA (tile 17): every step covers a whole
+        // 64-unit stage (128 FP8 k); a lane's fragment of a block is the two
+        // 16-byte chunks it reads from the stage's halves, 32 bytes, one
+        // v_mfma_f32_16x16x128 per block and step.  Fragments double-buffered
+        // (stage p + 1 is read while stage p's MFMAs run), S stages in each
+        // ring, step p loading stage p + S into the slot stage p left (read
+        // into registers during step p - 1), so a stage's loads have S - 1
+        // steps to land.
+        static_assert(AK && (DT == DT_F8E4M3 || DT == DT_F8E5M2) && SA == SB && !SPLIT && !PP,
+                      "wide steps: FP8, k-major A, equal rings");
+        constexpr int S = SA;
+        constexpr int NLS = 2 * LA + LB;                 // loads per wave per stage
+        static_assert(NLS * (S - 1) < 64, "vmcnt range");
+        struct FragW { u32x8 a[FM]; u32x8 b[FN]; };
+        auto read_w = [&](int slot, int r, FragW &f) {
+            const MIGEMM_LDS unsigned char *base = (const MIGEMM_LDS unsigned char *)smem;
+            u32x4 lo, hi;
+            if (r < FM) {
+                const MIGEMM_LDS unsigned char *ab = base + slot * A_BYTES + r * 2048;
+                lo = *(const MIGEMM_LDS u32x4 *)(ab + a_rel[0][0]);
+                hi = *(const MIGEMM_LDS u32x4 *)(ab + a_rel[1][0]);
+                f.a[r] = __builtin_shufflevector(lo, hi, 0, 1, 2, 3, 4, 5, 6, 7);
+            } else {
+                const MIGEMM_LDS unsigned char *bb = base + slot * B_BYTES + (r - FM) * 2048;
+                lo = *(const MIGEMM_LDS u32x4 *)(bb + b_rel[0]);
+                hi = *(const MIGEMM_LDS u32x4 *)(bb + b_rel[1]);
+                f.b[r - FM] = __builtin_shufflevector(lo, hi, 0, 1, 2, 3, 4, 5, 6, 7);
+            }
+        };
+        if (P_ > 0) {
+            // load item x < NLS of stage p: A loads first, then B
+            auto stage_load = [&](int p, int x, const u32x4 &da, const u32x4 &db) {
+                if (p < P_) {
+                    if (x < 2 * LA) issue_a(da, p, p % S, x);
+                    else issue_b(db, p, p % S, x - 2 * LA);
+                }
+            };
+#pragma unroll
+            for (int p = 0; p < S; ++p) {
+                const u32x4 da = desc_a(p), db = desc_b(p);
+#pragma unroll
+                for (int x = 0; x < NLS; ++x) stage_load(p, x, da, db);
+            }
+            if (S <= P_) wait_vmcnt<(S - 1) * NLS>();   // stage 0 landed
+            else wait_vmcnt<0>();
+            __syncthreads();
+            FragW f0, f1;
+#pragma unroll
+            for (int r = 0; r < NR; ++r) read_w(0, r, f0);
+            // step p: stage p + 1 landed (it was issued two steps ago; only
+            // stage p + 2's loads came after it), everyone has read stage p;
+            // then the MFMAs of stage p with the reads of stage p + 1 and the
+            // loads of stage p + S between them
+            auto wstep = [&](int p, FragW &cur, FragW &nxt) {
+                __builtin_amdgcn_s_waitcnt((7 << 4) | 0xc00f);   // lgkmcnt(0)
+                if (p + 2 < P_) wait_vmcnt<NLS>();
+                else wait_vmcnt<0>();
+                __syncthreads();
+                const int pl = p + S;
+                const u32x4 da = desc_a(pl), db = desc_b(pl);
+                const int ns = (p + 1) % S;
+#pragma unroll
+                for (int i = 0; i < FM; ++i)
+#pragma unroll
+                    for (int jj = 0; jj < FN; ++jj) {
+                        mfma16x16x128_f8<DT>(acc[i][jj], cur.a[i], cur.b[jj]);
+                        const int t = i * FN + jj;
+                        if (t < NR) read_w(ns, t, nxt);
+                        else if (t - NR < NLS) stage_load(pl, t - NR, da, db);
+                        __builtin_amdgcn_sched_barrier(0);
+                    }
+#pragma unroll
+                for (int x = (FM * FN > NR ? FM * FN - NR : 0); x < NLS; ++x) stage_load(pl, x, da, db);
+            };
+            for (int p = 0; p < P_; p += 2) {
+                wstep(p, f0, f1);
+                if (p + 1 < P_) wstep(p + 1, f1, f0);
+            }
+            wait_vmcnt<0>();   // no load may still target LDS when the workgroup ends
+        }
+    } else if constexpr (PP) {
         // Ping-pong: two groups of four waves, one wave of each group per
         // SIMD (waves w and w + 4 share a SIMD).  Each sub-step j is a load
         // phase (issue the LDS-direct loads of a later sub-step, nothing
@@ -980,13 +1079,14 @@ constexpr bool kSplitTile = !dt_is_8bit(DT) && ((BM == 256 && BN == 128 && WGM *
                                                 (BM == 256 && BN == 256 && WGM * WGN == 8) ||
                                                 (BM == 128 && BN == 128 && WGM * WGN == 4));
 
-template <int DT, bool AK, int BM, int BN, int WGM, int WGN, int SA, int SB, int OCC = 0, bool PP = false>
+template <int DT, bool AK, int BM, int BN, int WGM, int WGN, int SA, int SB, int OCC = 0, bool PP = false,
+          bool WIDE = false>
 static hipError_t launch_fl(const GemmLaunch &L, hipStream_t stream)
 {
     constexpr int OC = OCC ? OCC : WGM * WGN / 4;
     const dim3 block(WGM * WGN * 64);
     if (L.splits > 1) {
-        if constexpr (kSplitTile<DT, BM, BN, WGM, WGN> && !PP) {
+        if constexpr (kSplitTile<DT, BM, BN, WGM, WGN> && !PP && !WIDE) {
             hipLaunchKernelGGL((gemm_fl_kernel<DT, AK, BM, BN, WGM, WGN, SA, SB, OC, true>),
                                dim3((unsigned)L.grid, (unsigned)L.splits), block, 0, stream, L.A, L.B,
                                L.C, L.M, L.N, L.K, L.num_pid_m, L.num_pid_n, L.group_m, L.num_xcd,
@@ -995,7 +1095,7 @@ static hipError_t launch_fl(const GemmLaunch &L, hipStream_t stream)
         }
         return hipErrorInvalidValue;
     }
-    hipLaunchKernelGGL((gemm_fl_kernel<DT, AK, BM, BN, WGM, WGN, SA, SB, OC, false, PP>),
+    hipLaunchKernelGGL((gemm_fl_kernel<DT, AK, BM, BN, WGM, WGN, SA, SB, OC, false, PP, WIDE>),
                        dim3((unsigned)L.grid), block, 0, stream, L.A, L.B, L.C, L.M, L.N, L.K,
                        L.num_pid_m, L.num_pid_n, L.group_m, L.num_xcd, L.c_vec, L.scale, L.K & ~7,
                        (float *)nullptr);
@@ -1119,6 +1219,10 @@ static hipError_t launch_q(const GemmLaunch &L, hipStream_t s)
     case TILE_256x128_FL: return launch_fl<DT, true, 256, 128, 4, 1, 3, 4>(L, s);
     case TILE_256x256_FL8: return launch_fl<DT, true, 256, 256, 4, 2, 2, 3>(L, s);
     case TILE_128x128_SK: return launch_fl<DT, true, 128, 128, 2, 2, 4, 3, 1>(L, s);
+    case TILE_256x128_F8W:
+        if constexpr (DT == DT_F8E4M3 || DT == DT_F8E5M2)
+            return launch_fl<DT, true, 256, 128, 4, 2, 3, 3, 2, false, true>(L, s);
+        break;
     }
     return hipErrorInvalidValue;
 }

@@ -24,6 +24,7 @@ enum GemmTile {
     TILE_SKINNY = 14,           // few columns: W straight into 4x4x4 MFMA registers (skinny.hip)
     TILE_BATCH = 15,            // 9..128 columns: W into 16x16x32 MFMA registers, X in LDS (batch.hip)
     TILE_256x256_PP = 16,       // as 10, m-major A, ping-pong: the two waves of a SIMD alternate MFMA and memory phases
+    TILE_256x128_F8W = 17,      // FP8 only, k-major A: 256x128, 8 waves of 64x64, whole 64-unit steps on the 16x16x128 MFMA
     TILE_COUNT
 };
 
@@ -52,6 +53,7 @@ constexpr TileShape kTileShapes[TILE_COUNT] = {
     {32, 64, 32, 0, 4, 0},
     {64, 128, 128, 0, 4, 0},
     {256, 256, 32, 4, 8, 3},
+    {256, 128, 32, 3, 8, 3},
 };
 
 // The full-line tiles with A k-major: stages = A ring stages of 64 k.
@@ -73,6 +75,7 @@ constexpr TileShape kTileShapesKmajorA[TILE_COUNT] = {
     {32, 64, 32, 0, 4, 0},
     {64, 128, 128, 0, 4, 0},
     {0, 0, 0, 0, 0, 0},
+    {256, 128, 32, 3, 8, 3},
 };
 
 constexpr int tile_lds_bytes(const TileShape &t, bool a_kmajor = false)

@@ -190,8 +190,11 @@ def test_splitk_rules_and_errors():
 
 def test_q8_plan_and_errors():
     L = binding.lib()
-    # 8-bit GEMMs: k-major A only, K in elements (multiple of 16), tiles 9, 10, 13
+    # 8-bit GEMMs: k-major A only, K in elements (multiple of 16), tiles 9, 10, 13 (and 17 for FP8)
+    # automatic: FP8 on the double-rate tile 17 once 256x128 tiles fill the chip, INT8 on 10
     code, p = binding.gemm_plan(2, P, P + 2 ** 30, P + 2 ** 31, 8192, 8192, 16384, a_kmajor=True)
+    assert code == 0 and (p["tile"], p["tile_m"], p["tile_n"], p["tile_k"]) == (17, 256, 128, 64)
+    code, p = binding.gemm_plan(4, P, P + 2 ** 30, P + 2 ** 31, 8192, 8192, 16384, a_kmajor=True)
     assert code == 0 and (p["tile"], p["tile_m"], p["tile_n"], p["tile_k"]) == (10, 256, 256, 64)
     code, p = binding.gemm_plan(4, P, P + 2 ** 30, P + 2 ** 31, 8192, 2048, 4096, a_kmajor=True)
     assert code == 0 and p["tile"] == 9
@@ -204,12 +207,18 @@ def test_q8_plan_and_errors():
         for tile in (1, 3, 7, 8, 11, 12, 14, 15, 16):
             assert L.gemm_tn_q_ex(q, P, P + 0x100000, P + 0x200000, 64, 64, 64, 1.0, tile, 0, 1, None) == -5
         assert L.gemm_tn_ex(q, P, P + 0x100000, P + 0x200000, 64, 64, 64, 0, 0, 1, None) == -5
+        # tile 17 (the double-rate FP8 MFMA): FP8 only
+        assert (L.gemm_tn_q_ex(q, P, P + 0x100000, P + 0x200000, 64, 64, 64, 1.0, 17, 0, 1, None) == -5) == (q == 4)
         assert L.gemm_ex(q, P, P + 0x100000, P + 0x200000, 64, 64, 64, 0, 0, 1, None) == -5
         assert L.gemm_tn_q_ex(q, P, P + 0x100000, P + 0x200000, -1, 64, 64, 1.0, 0, 0, 1, None) == -1
         assert L.gemm_tn_q_ex(q, None, P + 0x100000, P + 0x200000, 64, 64, 64, 1.0, 0, 0, 1, None) == -2
         assert L.gemm_tn_q_ex(q, P, P + 0x100000, P + 16, 64, 64, 64, 1.0, 0, 0, 1, None) == -3
         assert L.gemm_tn_q_ex(q, None, None, None, 0, 0, 64, 1.0, 0, 0, 1, None) == 0
     assert L.gemm_tn_q_ex(0, P, P + 0x100000, P + 0x200000, 64, 64, 64, 1.0, 0, 0, 1, None) == -5
+    code, p = binding.gemm_plan(2, P, P + 2 ** 30, P + 2 ** 31, 8192, 8192, 16384, 17, a_kmajor=True)
+    assert code == 0 and (p["tile_m"], p["tile_n"], p["waves"], p["lds_bytes"]) == (256, 128, 8, 3 * (256 + 128) * 128)
+    assert L.gemm_ex(0, P, P + 0x100000, P + 0x200000, 64, 64, 64, 17, 0, 1, None) == -5     # not for 16-bit
+    assert L.gemm_tn_ex(1, P, P + 0x100000, P + 0x200000, 64, 64, 64, 17, 0, 1, None) == -5
     assert L.gemm_tn_q_ex(5, P, P + 0x100000, P + 0x200000, 64, 64, 64, 1.0, 0, 0, 1, None) == -5
     # C = At + 16 overlaps: At spans M*K bytes (one byte per element)
     assert L.gemm_tn_i8(P, P + 0x100000, P + 64 * 64 - 2, 64, 64, 64, 1.0, None) == -3

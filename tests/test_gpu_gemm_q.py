@@ -39,6 +39,32 @@ def test_each_tile_ragged(tile, fmt):
         _check(got, oracle.gemm_tn_q(At, B, M, N, K, fmt, scale), fmt, "%s tile %d %s" % (fmt, tile, (M, N, K)))
 
 
+@pytest.mark.parametrize("fmt", ["f8e4m3", "f8e5m2"])
+def test_fp8_wide_tile_ragged(fmt):
+    # tile 17: whole 64-unit steps on the double-rate 16x16x128 FP8 MFMA
+    # (K = 16 bytes is one stage with a leading zero half, K = 48 two stages)
+    for i, (M, N, K) in enumerate(SHAPES + [(520, 264, 4096), (256, 128, 128)]):
+        print("case q8 wide", fmt, M, N, K, flush=True)
+        At, B = synth.q8_operands(M, N, K, fmt, seed=500 + i)
+        got, guards, unchanged = gemm_tn_q_gpu(At, B, M, N, K, fmt, 0.75, 17)
+        assert guards and unchanged
+        _check(got, oracle.gemm_tn_q(At, B, M, N, K, fmt, 0.75), fmt, "%s tile 17 %s" % (fmt, (M, N, K)))
+
+
+def test_fp8_wide_tile_non_finite():
+    M, N, K = 64, 40, 256
+    At, B = synth.q8_operands(M, N, K, "f8e5m2", seed=53)
+    At[0] = 0x7C                                     # +inf in row 0
+    At[K + 130] = 0x7D                               # NaN in row 1, second stage
+    B[5 * K + 200] = 0xFC                            # -inf in column 5
+    got, _, _ = gemm_tn_q_gpu(At, B, M, N, K, "f8e5m2", 1.0, 17)
+    _check(got, oracle.gemm_tn_q(At, B, M, N, K, "f8e5m2", 1.0), "f8e5m2", "wide e5m2 non-finite")
+    At, B = synth.q8_operands(M, N, K, "f8e4m3", seed=54)
+    At[:K] = 0x7E                                    # row 0 of A: 448 everywhere
+    got, _, _ = gemm_tn_q_gpu(At, B, M, N, K, "f8e4m3", 1.0, 17)
+    _check(got, oracle.gemm_tn_q(At, B, M, N, K, "f8e4m3", 1.0), "f8e4m3", "wide e4m3 extremes")
+
+
 def test_int8_large_sums_exact():
     # all entries +-127: sums up to K * 16129 exceed 2^24 and go through FP32
     rng = np.random.default_rng(41)
