@@ -7,6 +7,8 @@ profiles/.
   mfma:          python -m bf16_gemm_decode_amd.profile_summary mfma \
                      --util-csv <csv> --counts-csv <csv> --kernel label=<substring>:<FLOP> ... \
                      --source <files...> --out <out.json> --commands "<cmd>" ...
+  sweep-mfma:    python -m bf16_gemm_decode_amd.profile_summary sweep-mfma \
+                     --util-csv <csv> --sweep-json <sweep stdout> --out <out.md> --command "<cmd>"
   traffic:       python -m bf16_gemm_decode_amd.profile_summary traffic \
                      --fetch <csv> --fetch-cal <csv> --write <csv> --write-cal <csv> \
                      --kernel <name substring> --source <source files...> \
@@ -176,6 +178,39 @@ def mfma(args):
     print(json.dumps(out, indent=1))
 
 
+def sweep_mfma(args):
+    """MfmaUtil of every configuration of a sweep.py run profiled with
+    --pmc MfmaUtil.  sweep.py launches each configuration's GEMM 1 + warmup
+    + reps times, in the order of its JSON lines; the GEMM dispatches (kernel
+    names containing 'gemm_', in dispatch order) are cut into groups of that
+    size and the timed ones (the last reps of each group) averaged."""
+    util = {}
+    names = {}
+    for r in _rows(args.util_csv):
+        if r["Counter_Name"] == "MfmaUtil" and "gemm_" in r["Kernel_Name"]:
+            util[int(r["Dispatch_Id"])] = float(r["Counter_Value"])
+            names[int(r["Dispatch_Id"])] = r["Kernel_Name"]
+    order = sorted(util)
+    cfgs = [json.loads(l) for l in open(args.sweep_json) if l.startswith("{")]
+    per = 1 + args.warmup + args.reps
+    if len(order) != per * len(cfgs):
+        sys.exit("%d GEMM dispatches for %d configurations of %d" % (len(order), len(cfgs), per))
+    with open(args.out, "w") as o:
+        o.write("# MfmaUtil per configuration (rocprofv3 derived counter: MFMA-busy SIMD cycles over\n"
+                "# GPU-active cycles x SIMDs), mean over each configuration's %d timed dispatches\n" % args.reps)
+        o.write("# command: %s\n" % args.command)
+        o.write("# sweep.py times (same run, under the counters): ms and TFLOP/s as it printed them\n\n")
+        o.write("| shape | dtype | A layout | tile | tile_mnk | GROUP_M | ms | TFLOP/s | MfmaUtil %% |\n")
+        o.write("|---|---|---|---|---|---|---|---|---|\n")
+        for i, c in enumerate(cfgs):
+            ids = order[i * per:(i + 1) * per][1 + args.warmup:]
+            u = [util[d] for d in ids]
+            o.write("| %s | %s | %s | %d | %s | %d | %s | %s | %.1f |\n" % (
+                "x".join(map(str, c["shape"])), c["dtype"], c["a_layout"], c["tile"],
+                "x".join(map(str, c["tile_mnk"])), c["group_m"], c["ms"], c["tflops"], sum(u) / len(u)))
+    print(open(args.out).read())
+
+
 def main(argv=None):
     p = argparse.ArgumentParser()
     sub = p.add_subparsers(dest="mode", required=True)
@@ -208,8 +243,15 @@ def main(argv=None):
     m.add_argument("--source", nargs="+", required=True)
     m.add_argument("--out", required=True)
     m.add_argument("--commands", nargs="+", required=True)
+    w = sub.add_parser("sweep-mfma")
+    w.add_argument("--util-csv", required=True)
+    w.add_argument("--sweep-json", required=True, help="stdout of the profiled sweep.py run")
+    w.add_argument("--warmup", type=int, default=3)
+    w.add_argument("--reps", type=int, default=10)
+    w.add_argument("--out", required=True)
+    w.add_argument("--command", required=True)
     a = p.parse_args(argv)
-    {"stats": stats, "traffic": traffic, "mfma": mfma}[a.mode](a)
+    {"stats": stats, "traffic": traffic, "mfma": mfma, "sweep-mfma": sweep_mfma}[a.mode](a)
 
 
 if __name__ == "__main__":
