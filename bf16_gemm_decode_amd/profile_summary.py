@@ -200,7 +200,7 @@ def sweep_mfma(args):
                 "# GPU-active cycles x SIMDs), mean over each configuration's %d timed dispatches\n" % args.reps)
         o.write("# command: %s\n" % args.command)
         o.write("# sweep.py times (same run, under the counters): ms and TFLOP/s as it printed them\n\n")
-        o.write("| shape | dtype | A layout | tile | tile_mnk | GROUP_M | ms | TFLOP/s | MfmaUtil %% |\n")
+        o.write("| shape | dtype | A layout | tile | tile_mnk | GROUP_M | ms | TFLOP/s | MfmaUtil % |\n")
         o.write("|---|---|---|---|---|---|---|---|---|\n")
         for i, c in enumerate(cfgs):
             ids = order[i * per:(i + 1) * per][1 + args.warmup:]
