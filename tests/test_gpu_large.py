@@ -1,14 +1,18 @@
-"""GPU parity for operands of more than 2^31 elements (about 8.6 GB each):
-byte offsets past 32 bits, the per-step rebasing of the buffer descriptors
-and the 64-bit row offsets of the decode kernels.
+"""GPU parity for operands of more than 2^31 elements (about 8.6 GB each) and
+a paged KV cache past 2^31 bytes: byte offsets past 32 bits, the per-step
+rebasing of the buffer descriptors and the 64-bit row and page offsets of the
+decode kernels.
 
-The operands follow synth.mod5_pattern, entries in [-2, 2]: every partial
-sum is an integer below 2^24, so FP32 accumulation is exact in any order and
-the one rounding to 16 bits is deterministic -- results are compared bit for
-bit.  The pattern has five distinct rows, so the large operand is assembled
-on the device by repeating them (torch indexing: plumbing, no arithmetic of
-the method); the oracle computes the product restricted to the sampled rows
-and columns, built on the host from the same formula."""
+The GEMM and GEMV operands follow synth.mod5_pattern, entries in [-2, 2]:
+every partial sum is an integer below 2^24, so FP32 accumulation is exact in
+any order and the one rounding to 16 bits is deterministic -- results are
+compared bit for bit.  The pattern has five distinct rows, so the large
+operand is assembled on the device by repeating them (torch indexing:
+plumbing, no arithmetic of the method); the oracle computes the product
+restricted to the sampled rows and columns, built on the host from the same
+formula.  The attention case places seeded pages near the end of a large,
+otherwise zero cache and checks against the oracle on the same pages
+compacted."""
 import numpy as np
 import pytest
 
@@ -96,4 +100,48 @@ def test_gemv_weight_past_2g_elements(n):
     ref = oracle.gemv(Wsub, X, len(js), K, n)
     assert np.array_equal(got, ref.bits.reshape(n, len(js)))
     del dW, dX, dY
+    _free()
+
+
+def test_attention_cache_past_2g_bytes():
+    # Paged caches of 2000 pages of 784 tokens (3.3 GB each at 4 KV heads,
+    # head dim 256): the sequences' pages sit near the end, past 2^31 bytes
+    # from the cache base.  Only those pages hold data; the oracle takes the
+    # same pages compacted, with the block table renumbered.
+    import torch
+    from bf16_gemm_decode_amd import binding
+    L = binding.lib()
+    Hq, Hkv, D, bs, NB = 16, 4, 256, 784, 2000
+    op = synth.attention_operands(2, Hq, Hkv, D, [3000, 1500], bs, seed=77)
+    page = bs * Hkv * D
+    big = np.array([NB - 1 - 7 * p for p in range(op["num_blocks"])], np.int64)   # compact page -> big page
+    assert int(big.min()) * page * 2 > 2 ** 31
+    print("case large attention cache", NB, "pages, live pages", big.tolist(), flush=True)
+    dK = torch.zeros(NB * page, dtype=torch.int16, device="cuda")
+    dV = torch.zeros(NB * page, dtype=torch.int16, device="cuda")
+    idx = torch.from_numpy(big).cuda()
+    dK.view(NB, page)[idx] = dev(op["K"]).view(-1, page)
+    dV.view(NB, page)[idx] = dev(op["V"]).view(-1, page)
+    bt = op["block_table"].astype(np.int64)
+    bt_big = np.where(bt >= 0, big[np.maximum(bt, 0)], -1).astype(np.int32)
+    dbt = torch.from_numpy(np.ascontiguousarray(bt_big)).cuda()
+    dsl = torch.from_numpy(np.ascontiguousarray(op["seq_lens"], np.int32)).cuda()
+    dQ = dev(op["Q"])
+    out = torch.full((2 * Hq * D,), -1, dtype=torch.int16, device="cuda")
+    scale = 1.0 / 16
+    for S in (0, 16):
+        segs = S or L.migemm_attention_segments(2, Hq, Hkv, 3000)
+        wsb = L.migemm_attention_workspace_bytes(2, Hq, D, segs)
+        ws = torch.empty(wsb, dtype=torch.uint8, device="cuda")
+        code = L.attention_decode_bf16(dQ.data_ptr(), dK.data_ptr(), dV.data_ptr(), dbt.data_ptr(),
+                                       dsl.data_ptr(), out.data_ptr(), 2, Hq, Hkv, D, bs, op["max_blocks"],
+                                       NB, scale, 3000, S, ws.data_ptr(), wsb, None)
+        assert code == 0
+        torch.cuda.synchronize()
+        got = out.cpu().numpy().view(np.uint16)
+        ref = oracle.attention(op["Q"], op["K"], op["V"], op["block_table"], op["seq_lens"], 2, Hq, Hkv,
+                               D, bs, op["max_blocks"], scale)
+        ok, rep = oracle.check(got, ref, "bf16", rel=oracle.attention_rel(ref, op["seq_lens"], Hq, D))
+        assert ok, ("large cache", S, rep)
+    del dK, dV
     _free()
