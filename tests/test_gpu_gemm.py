@@ -310,6 +310,23 @@ def test_pingpong_tile_bit_identical_to_tile_10():
         assert np.array_equal(g16, g10), (M, N, K, fmt)
 
 
+def test_pingpong_tile_bit_identical_random_shapes():
+    # the same property over seeded random shapes (M even: the tile takes
+    # 4-byte rows), a race detector for the ping-pong schedule's waits
+    rng = np.random.default_rng(2024)
+    for i in range(24):
+        M = 2 * int(rng.integers(1, 700))
+        N = int(rng.integers(1, 1300))
+        K = 2 * int(rng.integers(0, 600))
+        fmt = FMTS[i % 2]
+        A, B = synth.gemm_operands(M, N, K, fmt, ("normal", 1.0, 1.0), seed=900 + i)
+        print("case pingpong random", (M, N, K), fmt, flush=True)
+        g10, _, _ = gemm_gpu(A, B, M, N, K, fmt, tile=10)
+        g16, guards, _ = gemm_gpu(A, B, M, N, K, fmt, tile=16)
+        assert guards
+        assert np.array_equal(g16, g10), (M, N, K, fmt)
+
+
 def test_tensor_wrapper_and_stream():
     import torch
     from bf16_gemm_decode_amd import gemm
