@@ -42,8 +42,9 @@ def test_each_tile_ragged(tile, fmt):
 @pytest.mark.parametrize("fmt", ["f8e4m3", "f8e5m2"])
 def test_fp8_wide_tile_ragged(fmt):
     # tile 17: whole 64-unit steps on the double-rate 16x16x128 FP8 MFMA
-    # (K = 16 bytes is one stage with a leading zero half, K = 48 two stages)
-    for i, (M, N, K) in enumerate(SHAPES + [(520, 264, 4096), (256, 128, 128)]):
+    # (K = 16 or 48 bytes: one stage with a leading zero half; 160 and 192:
+    # two stages, fewer than the ring holds; 272: three)
+    for i, (M, N, K) in enumerate(SHAPES + [(520, 264, 4096), (256, 128, 128), (264, 130, 160), (300, 140, 192)]):
         print("case q8 wide", fmt, M, N, K, flush=True)
         At, B = synth.q8_operands(M, N, K, fmt, seed=500 + i)
         got, guards, unchanged = gemm_tn_q_gpu(At, B, M, N, K, fmt, 0.75, 17)
