@@ -144,6 +144,18 @@ def q8_operands(M, N, K, fmt, seed, sigma=1.0):
     return At, B
 
 
+def to_q8(values, fmt) -> np.ndarray:
+    """Codes of the 8-bit formats for values they hold exactly (small
+    integers): INT8 two's complement ('i8'), or torch's OCP float8 types
+    ('f8e4m3', 'f8e5m2'); flat uint8."""
+    v = np.asarray(values, dtype=np.float64).ravel()
+    if fmt == "i8":
+        return v.astype(np.int8).view(np.uint8)
+    import torch
+    dt = {"f8e4m3": torch.float8_e4m3fn, "f8e5m2": torch.float8_e5m2}[fmt]
+    return torch.from_numpy(v.astype(np.float32)).to(dt).view(torch.uint8).numpy().copy()
+
+
 def sample_indices(M, N, seed, count=4096):
     """``count`` distinct flat output indices (m + n*M) drawn with
     default_rng(1000 + seed), plus the four corners, sorted."""

@@ -1,5 +1,6 @@
-"""GPU parity for operands of more than 2^31 elements (about 8.6 GB each) and
-a paged KV cache past 2^31 bytes: byte offsets past 32 bits, the per-step
+"""GPU parity for operands of more than 2^31 elements (about 8.6 GB each), for
+k-major A operands (8- and 16-bit) of more than 2^32 bytes, and for a paged KV
+cache past 2^31 bytes: byte offsets past 32 bits, the per-step
 rebasing of the buffer descriptors and the 64-bit row and page offsets of the
 decode kernels.
 
@@ -69,6 +70,71 @@ def test_gemm_operand_past_2g_elements(fmt, big):
     Asub = synth.to_bits(synth.mod5_pattern(ms[:, None], kk[None, :], 1, 3).ravel(order="F"), fmt)
     Bsub = synth.to_bits(synth.mod5_pattern(kk[:, None], ns[None, :], 1, 2).ravel(order="F"), fmt)
     ref = oracle.gemm(Asub, Bsub, len(ms), len(ns), K, fmt)
+    want = ref.bits.reshape(len(ns), len(ms)).T          # column-major [ms x ns]
+    assert np.array_equal(got, want), np.argwhere(got != want)[:8]
+    del dA, dB, dC
+    _free()
+
+
+@pytest.mark.parametrize("fmt,big,tile", [("f8e4m3", "A", 17), ("f8e5m2", "B", 17), ("i8", "A", 10),
+                                          ("i8", "B", 10), ("bf16", "A", 10), ("f16", "B", 10)])
+def test_gemm_kmajor_operand_past_4g_bytes(fmt, big, tile):
+    # A k-major (At[k + m*K]), 8- or 16-bit, one operand of more than 2^32
+    # bytes, on the automatic tile (asserted).  K = 4112 units: whole 64-unit
+    # stages, then a 16-unit tail.
+    import torch
+    from bf16_gemm_decode_amd import binding
+    q8 = fmt in ("f8e4m3", "f8e5m2", "i8")
+    esize = 1 if q8 else 2
+    K = 4112
+    M, N = ((1 << 20) + 8, 264) if big == "A" else (264, (1 << 20) + 8)
+    assert (M if big == "A" else N) * K * esize > 2 ** 32
+    print("case large k-major", big, fmt, (M, N, K), flush=True)
+
+    def enc(v):
+        return synth.to_q8(v, fmt) if q8 else synth.to_bits(v, fmt)
+
+    def todev(codes):
+        return torch.from_numpy(codes if q8 else codes.view(np.int16)).cuda()
+
+    # A(m, k) = ((m + 3k) mod 5) - 2: row m of At is class m mod 5;
+    # B(k, n) = ((k + 2n) mod 5) - 2: column n is class 2n mod 5
+    kk = np.arange(K)
+    arows = torch.stack([todev(enc(synth.mod5_pattern(c, kk, 1, 3))) for c in range(5)])
+    bcols = torch.stack([todev(enc(synth.mod5_pattern(kk, c, 1, 1))) for c in range(5)])
+    dA = arows[torch.arange(M, device="cuda") % 5].reshape(-1)         # [M][K]
+    dB = bcols[torch.arange(N, device="cuda") * 2 % 5].reshape(-1)     # [N][K]
+    del arows, bcols
+    dC = torch.full((M * N,), 0x7FC1, dtype=torch.int16, device="cuda")   # NaN marker
+    dtype = {"f8e4m3": binding.F8E4M3, "f8e5m2": binding.F8E5M2, "i8": binding.I8,
+             "bf16": binding.BF16, "f16": binding.F16}[fmt]
+    code, plan = binding.gemm_plan(dtype, dA.data_ptr(), dB.data_ptr(), dC.data_ptr(), M, N, K,
+                                   a_kmajor=True)
+    assert code == 0 and plan["tile"] == tile, plan
+    print("plan tile", plan["tile"], "grid", plan["grid"], flush=True)
+    if q8:
+        code = binding.lib().gemm_tn_q_ex(dtype, dA.data_ptr(), dB.data_ptr(), dC.data_ptr(), M, N, K,
+                                          1.0, 0, 0, 1, None)
+    else:
+        code = binding.gemm_tn_ex_ptr(dtype, dA.data_ptr(), dB.data_ptr(), dC.data_ptr(), M, N, K)
+    assert code == 0
+    torch.cuda.synchronize()
+    big_dim = M if big == "A" else N
+    cross = (1 << 32) // (K * esize)           # first row / column past 2^32 bytes
+    ms = _edge_indices(M, [cross, cross + 1, 257, 4095] if big == "A" else [127, 128, 255])
+    ns = _edge_indices(N, [cross, cross + 1, 255, 4097] if big == "B" else [127, 128, 255])
+    assert big_dim - 1 > cross
+    got = dC.view(M * N)[torch.from_numpy(ms[:, None] + ns[None, :] * M).cuda().reshape(-1)]
+    got = got.cpu().numpy().view(np.uint16).reshape(len(ms), len(ns))
+    # the product restricted to those rows and columns; every partial sum is
+    # an integer below 2^24, so the results are exact and compared bit for bit
+    Asub = enc(synth.mod5_pattern(ms[:, None], kk[None, :], 1, 3).ravel())     # [ms][K]
+    Bsub = enc(synth.mod5_pattern(kk[None, :], ns[:, None], 1, 2).ravel())     # [ns][K]
+    if q8:
+        ref = oracle.gemm_tn_q(Asub, Bsub, len(ms), len(ns), K, fmt, 1.0)
+    else:
+        ref = oracle.gemm(np.ascontiguousarray(Asub.reshape(len(ms), K).T).reshape(-1), Bsub,
+                          len(ms), len(ns), K, fmt)
     want = ref.bits.reshape(len(ns), len(ms)).T          # column-major [ms x ns]
     assert np.array_equal(got, want), np.argwhere(got != want)[:8]
     del dA, dB, dC
