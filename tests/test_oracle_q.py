@@ -1,8 +1,9 @@
 """Pins of the oracle's 8-bit GEMM (OCP FP8 E4M3 / E5M2 and INT8 inputs, k-major
 A, BF16 output of scale x sum): the decoders against torch's own float8 types
 and closed forms, the sums against brute force, the addressing against the
-swapped product, the INT8 output's FP32 steps against numpy float32, and the
-special values."""
+swapped product, the INT8 output's FP32 steps against numpy float32, the
+special values, and the small-integer operands of the large-operand GPU tests
+(their 8-bit codes, and the product restricted to sampled rows and columns)."""
 import math
 
 import numpy as np
@@ -108,3 +109,34 @@ def test_sampled_entries_match_full():
         idx = np.array([0, 5, M * N - 1, 100, 257], np.int64)
         part = oracle.gemm_tn_q(At, B, M, N, K, fmt, 0.25, idx=idx)
         assert np.array_equal(part.bits, full.bits[idx]) and np.array_equal(part.exact, full.exact[idx])
+
+
+@pytest.mark.parametrize("fmt", FMTS)
+def test_to_q8_exact_on_small_integers(fmt):
+    # the large-operand GPU tests store the integers -2..2 with synth.to_q8
+    v = np.arange(-8, 9, dtype=np.float64)
+    assert np.array_equal(oracle.decode8(synth.to_q8(v, fmt), fmt), v)
+
+
+@pytest.mark.parametrize("fmt", FMTS)
+def test_mod5_rows_and_columns_restrict_the_product(fmt):
+    # the reference construction of the large-operand GPU tests: the operands
+    # assembled from five repeated rows / columns, and the product restricted
+    # to some rows and columns rebuilt from the formula, agree with the full
+    # product at those entries
+    M, N, K = 40, 30, 48
+    kk = np.arange(K)
+    arows = [synth.to_q8(synth.mod5_pattern(c, kk, 1, 3), fmt) for c in range(5)]
+    bcols = [synth.to_q8(synth.mod5_pattern(kk, c, 1, 1), fmt) for c in range(5)]
+    At = np.concatenate([arows[m % 5] for m in range(M)])
+    B = np.concatenate([bcols[2 * n % 5] for n in range(N)])
+    full = oracle.gemm_tn_q(At, B, M, N, K, fmt, 1.0).bits.reshape(N, M).T
+    ms, ns = np.array([0, 3, 17, 39]), np.array([0, 1, 12, 29])
+    Asub = synth.to_q8(synth.mod5_pattern(ms[:, None], kk[None, :], 1, 3).ravel(), fmt)
+    Bsub = synth.to_q8(synth.mod5_pattern(kk[None, :], ns[:, None], 1, 2).ravel(), fmt)
+    sub = oracle.gemm_tn_q(Asub, Bsub, len(ms), len(ns), K, fmt, 1.0).bits.reshape(len(ns), len(ms)).T
+    assert np.array_equal(full[np.ix_(ms, ns)], sub)
+    # and every entry is the exact integer sum, rounded once to BF16
+    ref = np.array([[np.sum(synth.mod5_pattern(m, kk, 1, 3) * synth.mod5_pattern(kk, n, 1, 2)) for n in ns]
+                    for m in ms])
+    assert np.array_equal(synth.to_bits(ref.ravel(), "bf16").reshape(ref.shape), sub)
