@@ -205,7 +205,7 @@ size_t migemm_splitk_workspace_bytes(int M, int N, int splits);
  *            measured configurations -- the headline FP16 GEMM, the prefill
  *            GEMM in both layouts, the ragged BF16 GEMM -- then the least
  *            estimated time over rounds of workgroups on the 256 CUs among
- *            tiles 10, 2 (9 without 16-byte rows) and 3); 1 = 256x256 (4 waves as 2x2, 4 LDS stages);
+ *            tiles 16, 2 (9 without 16-byte rows) and 3); 1 = 256x256 (4 waves as 2x2, 4 LDS stages);
  *            2 = 256x128 (5 stages); 3 = 128x128 (4 stages, two workgroups
  *            per CU); 4 = tile 1 with 5 stages; 5 = 256x256 with the 4 waves
  *            stacked along M; 6 = tile 1 with 3 stages; 7 = 256x256, waves
@@ -219,10 +219,14 @@ size_t migemm_splitk_workspace_bytes(int M, int N, int splits);
  *            of gemv_bf16 (gemm_tn_* only, N <= 8); 15 = the batch kernel
  *            of gemv_bf16 (gemm_tn_* only, N <= 128: 64 rows x 16..128
  *            columns per workgroup, 16x16x32 MFMA, A read as whole lines and
- *            re-laid out through LDS, B staged in LDS).
+ *            re-laid out through LDS, B staged in LDS); 16 = tile 10's
+ *            shape, rings and layouts with the ping-pong schedule (the two
+ *            waves of each SIMD alternate a load phase and an MFMA phase;
+ *            gemm_ex only, not split-K); 17 = the FP8 double-rate tile
+ *            (gemm_tn_q_ex only).
  *            All step K by 32.  Tiles 1, 2, 4, 5, 6 need 16-byte rows (M and
  *            K multiples of 8, A and B 16-byte aligned); the full-line tiles
- *            7 .. 13 need 4-byte rows (M and K even, A and B 4-byte
+ *            7 .. 13 and 16 need 4-byte rows (M and K even, A and B 4-byte
  *            aligned): their k loop stops at K rounded down to a multiple of
  *            8 and one more MFMA step adds the remaining k; tile 3 takes
  *            any alignment (else MIGEMM_ERR_CONFIG);
@@ -246,7 +250,8 @@ int gemm_ex(int dtype, const uint16_t *A, const uint16_t *B, uint16_t *C,
  * ownership and completion rules as gemm_f16 / gemm_bf16.  Runs on the
  * full-line tiles only: tile 0 (automatic: 14 for N <= 4, 15 for
  * N <= 64, else the least estimated time among 10, 9 and 13) or 7 .. 15
- * (A takes B's 64-k ring layout; MIGEMM_ERR_CONFIG for other tiles, and
+ * (A takes B's 64-k ring layout; MIGEMM_ERR_CONFIG for other tiles, 16 and
+ * 17 included, and
  * for 14 with N > 8 or 15 with N > 128).  K even and At, B 4-byte aligned
  * (4-byte rows) for tiles 7 .. 13, K a multiple of 8 and At, B 16-byte
  * aligned for 14 and 15 (which tile 0 then uses); else MIGEMM_ERR_ALIGN.
@@ -261,8 +266,11 @@ int gemm_tn_ex(int dtype, const uint16_t *At, const uint16_t *B, uint16_t *C,
 
 /* The 8-bit GEMMs with an explicit configuration: qtype 2 = FP8 E4M3,
  * 3 = FP8 E5M2, 4 = INT8 (the dtype codes of migemm_gemm_tn_plan_for);
- * tile 0 (automatic: 10 when the 256x256 tiles fill the chip twice, 9 when
- * 256x128 tiles fill it once, else 13), 9, 10 or 13; group_m and xcd_remap
+ * tile 0 (automatic: for FP8, 17 when its 256x128 tiles fill the chip;
+ * otherwise 10 when the 256x256 tiles fill the chip twice, 9 when 256x128
+ * tiles fill it once, else 13), 9, 10, 13, or 17 for FP8 only (256x128, 8
+ * waves, the double-rate v_mfma_f32_16x16x128 FP8 instruction on whole
+ * 64-byte k steps; MIGEMM_ERR_CONFIG for INT8); group_m and xcd_remap
  * as for gemm_ex.  gemm_tn_ex rejects these dtypes (it has no scale). */
 int gemm_tn_q_ex(int qtype, const void *At, const void *B, uint16_t *C,
                  int M, int N, int K, float scale, int tile, int group_m,
