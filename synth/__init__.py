@@ -195,3 +195,70 @@ def mod5_pattern(i, j, a, b):
     i = np.asarray(i, dtype=np.int64)
     j = np.asarray(j, dtype=np.int64)
     return (((a * i + b * j) % 5) - 2).astype(np.float64)
+
+
+def _exact_dim(h, t, L, D):
+    """Head-dim slot of logical token t in kv head h for the exact-class V:
+    h = 0: t mod D; h = 1: the run of L/D consecutive tokens t lies in
+    (together these two identify every token of a sequence of L <= D*D);
+    h = 2, 3: mixed.  Consecutive tokens never share a slot in kv head 0."""
+    t = np.asarray(t, dtype=np.int64)
+    if h % 4 == 0:
+        return t % D
+    if h % 4 == 1:
+        return (t // max(1, L // D)) % D
+    if h % 4 == 2:
+        return (t + t // 16) % D
+    return (5 * t + t // 64) % D
+
+
+def attention_exact_operands(seq_len, kind, Hq=16, Hkv=4, D=256, block_size=784, seed=7,
+                             spare_blocks=3, fmt=BF16):
+    """Decode-attention inputs whose output every correct implementation
+    with FP32 sums returns bit for bit (one sequence, power-of-two seq_len).
+
+    The page layout and the block table are those of attention_operands
+    (scattered pages); unused pages keep N(0, 1) values.  For every logical
+    token t of kv head h, V holds 1 in head-dim slot _exact_dim(h, t) and 0
+    elsewhere, so each output is (number of counted tokens mapped to its
+    slot) / (number of counted tokens): small integers over a power of two.
+      * kind "uniform": Q = 0, every score is 0, every token is counted;
+      * kind "mask": query head h holds 1024 in head-dim h mod D, zeros
+        elsewhere; in the kv head's dims of its query heads K holds 0 for
+        an exactly half of the tokens (a seeded choice per kv head) and
+        -1024 for the rest, so the scores are 0 or -2^20 * scale: weights
+        exactly 1 or (after the exponential underflows) exactly 0.
+    Returns the attention_operands dict plus 'counted' [Hkv, L] (bool)."""
+    if seq_len <= 0 or seq_len & (seq_len - 1):
+        raise ValueError("seq_len must be a power of two")
+    op = attention_operands(1, Hq, Hkv, D, [seq_len], block_size, seed, spare_blocks=spare_blocks,
+                            fmt=fmt)
+    rng = np.random.default_rng(seed + 1)
+    L, G = seq_len, Hq // Hkv
+    t = np.arange(L)
+    page = op["block_table"][0][t // block_size].astype(np.int64)
+    row = (page * block_size + t % block_size)          # cache row of logical token t
+    V = op["V"].reshape(-1, Hkv, D).copy()
+    K = op["K"].reshape(-1, Hkv, D).copy()
+    one, zero, neg = to_bits([1.0, 0.0, -1024.0], fmt)
+    counted = np.ones((Hkv, L), bool)
+    for h in range(Hkv):
+        V[row, h, :] = zero
+        V[row, h, _exact_dim(h, t, L, D)] = one
+        if kind == "mask":
+            keep = np.zeros(L, bool)
+            keep[rng.permutation(L)[:L // 2]] = True
+            counted[h] = keep
+            dims = [(h * G + j) % D for j in range(G)]
+            for d in dims:
+                K[row, h, d] = np.where(keep, zero, neg)
+    if kind == "uniform":
+        Q = np.full(Hq * D, zero, np.uint16)
+    elif kind == "mask":
+        Q = np.full((Hq, D), zero, np.uint16)
+        Q[np.arange(Hq), np.arange(Hq) % D] = to_bits([1024.0], fmt)[0]
+        Q = Q.reshape(-1)
+    else:
+        raise ValueError(kind)
+    op.update(Q=Q, K=K.reshape(-1), V=V.reshape(-1), counted=counted)
+    return op

@@ -112,3 +112,25 @@ def assert_parity(got, ref, fmt, what):
     ok, rep = oracle.check(got, ref, fmt)
     assert ok, "%s: %s" % (what, rep)
     return rep
+
+
+def attention_exact_expected(op, Hq, D):
+    """Closed form of an exact-class attention input (synth.attention_exact_operands):
+    output (h, d) = (counted tokens of kv head h's group mapped to slot d) /
+    (counted tokens), as BF16 bits.  Both counts are integers and the
+    denominator a power of two, so the value is exact before one rounding."""
+    Hkv = op["Hkv"]
+    L = int(op["seq_lens"][0])
+    t = np.arange(L)
+    exp = np.zeros((Hq, D))
+    for h in range(Hq):
+        kvh = h // (Hq // Hkv)
+        cnt = op["counted"][kvh]
+        c = np.bincount(synth._exact_dim(kvh, t[cnt], L, D), minlength=D)
+        exp[h] = c / cnt.sum()
+    return synth.to_bits(exp.ravel(), "bf16")
+
+
+def exact_mismatches(got_bits, ref_bits):
+    """Number of outputs whose bits differ (exact-class comparison)."""
+    return int(np.count_nonzero(np.asarray(got_bits, np.uint16) != np.asarray(ref_bits, np.uint16)))

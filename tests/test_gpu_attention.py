@@ -118,3 +118,38 @@ def test_page_head_shape_32_vs_16_segments(L):
     assert d.max() <= 2.44e-4 and d.mean() <= 1.58e-5, (d.max(), d.mean())
     # and the automatic choice for this chip
     _parity(op, scale, 0, "automatic L %d" % L)
+
+
+@pytest.mark.parametrize("kind", ["uniform", "mask"])
+@pytest.mark.parametrize("L", [8192, 16384, 32768])
+def test_page_head_shape_exact_class(kind, L):
+    # DCU page sections 6.3 and 7 (16 Q / 4 KV heads, head dim 256, pages of
+    # 784): inputs whose output every correct FP32 implementation returns
+    # bit for bit (synth.attention_exact_operands), with the automatic, 16
+    # and 32 segments.  One missing, extra or misread token anywhere (a
+    # segment or page tail) changes the bits: see the oracle controls.
+    from helpers import attention_exact_expected, exact_mismatches
+    w = synth.WORKLOADS["attention_decode_16q4kv_d256_bf16"]
+    op = synth.attention_exact_operands(L, kind)
+    scale = 1.0 / np.sqrt(w["D"])
+    ref = _ref(op, scale)
+    assert np.array_equal(ref.bits, attention_exact_expected(op, w["Hq"], w["D"]))
+    for S in (0, 16, 32):
+        print("case exact", kind, "L", L, "S", S, flush=True)
+        got = _gpu(op, scale, S)
+        assert exact_mismatches(got, ref.bits) == 0, (kind, L, S, exact_mismatches(got, ref.bits))
+
+
+@pytest.mark.parametrize("L", [8192, 16384, 32768])
+def test_page_head_shape_automatic_vs_16_and_32_segments(L):
+    # the automatic segment count against the page's 16 and 32 with the
+    # page's section 7 bound (max abs <= 2.44e-4, mean abs <= 1.58e-5)
+    w = synth.WORKLOADS["attention_decode_16q4kv_d256_bf16"]
+    op = synth.attention_operands(1, w["Hq"], w["Hkv"], w["D"], [L], w["block_size"], seed=w["seed"])
+    scale = 1.0 / np.sqrt(w["D"])
+    print("case auto vs 16/32 L", L, flush=True)
+    auto = oracle.decode(_gpu(op, scale, 0), "bf16")
+    for S in (16, 32):
+        other = oracle.decode(_gpu(op, scale, S), "bf16")
+        d = np.abs(auto - other)
+        assert d.max() <= 2.44e-4 and d.mean() <= 1.58e-5, (S, d.max(), d.mean())

@@ -200,3 +200,50 @@ def test_tolerance_controls():
     assert not oracle.check(bad, ref, BF, rel=rel)[0]
     off = synth.to_bits(ref.exact + 1e-2 * ref.sabs, BF)
     assert not oracle.check(off, ref, BF, rel=rel)[0]
+
+
+# ---- exact-class inputs at the DCU page's head shape (section 7: 16 query /
+# 4 KV heads, head dim 256, pages of 784, 8K-32K cached tokens).  Every
+# correct implementation with FP32 sums returns these outputs bit for bit,
+# so the GPU test compares bits; the controls below show that the
+# comparison sees one missing, extra or misread token.
+
+EXACT_W = synth.WORKLOADS["attention_decode_16q4kv_d256_bf16"]
+
+
+def _exact_ref(op):
+    return _run(op, 1.0 / math.sqrt(EXACT_W["D"]))
+
+
+@pytest.mark.parametrize("kind", ["uniform", "mask"])
+@pytest.mark.parametrize("L", [8192, 32768])
+def test_exact_class_matches_closed_form(kind, L):
+    from helpers import attention_exact_expected
+    op = synth.attention_exact_operands(L, kind)
+    ref = _exact_ref(op)
+    assert np.array_equal(ref.bits, attention_exact_expected(op, EXACT_W["Hq"], EXACT_W["D"]))
+
+
+def test_exact_class_controls_fail_the_bit_comparison():
+    """Outputs of the oracle on altered inputs differ from the true ones in
+    their bits: the last 64 tokens dropped, the last token dropped, a token
+    on a page boundary replaced by its neighbour, one masked token counted."""
+    from helpers import exact_mismatches
+    L, bs = 32768, EXACT_W["block_size"]
+    op = synth.attention_exact_operands(L, "uniform")
+    ref = _exact_ref(op)
+    for drop in (64, 1):
+        short = dict(op, seq_lens=np.array([L - drop], np.int32))
+        assert exact_mismatches(_exact_ref(short).bits, ref.bits) > 0, drop
+    # token 784 (first of the second page) read as token 783
+    V = op["V"].reshape(-1, EXACT_W["Hkv"], EXACT_W["D"]).copy()
+    bt = op["block_table"][0]
+    V[bt[1] * bs + 0] = V[bt[0] * bs + bs - 1]
+    assert exact_mismatches(_exact_ref(dict(op, V=V.reshape(-1))).bits, ref.bits) > 0
+    # mask class: one token that should score -inf-like counted
+    opm = synth.attention_exact_operands(8192, "mask")
+    refm = _exact_ref(opm)
+    t = int(np.flatnonzero(~opm["counted"][2])[0])
+    K = opm["K"].reshape(-1, EXACT_W["Hkv"], EXACT_W["D"]).copy()
+    K[opm["block_table"][0][t // bs] * bs + t % bs, 2, :] = 0
+    assert exact_mismatches(_exact_ref(dict(opm, K=K.reshape(-1))).bits, refm.bits) > 0
