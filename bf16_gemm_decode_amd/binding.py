@@ -66,6 +66,7 @@ SIGNATURES = {
                                ctypes.POINTER(_I64), ctypes.POINTER(_I64)]),
     "migemm_gemm_plan_for": (_I, [_I, _P, _P, _P, _I, _I, _I, _I, _I, _I, ctypes.POINTER(Plan)]),
     "migemm_gemm_tn_plan_for": (_I, [_I, _P, _P, _P, _I, _I, _I, _I, _I, _I, ctypes.POINTER(Plan)]),
+    "migemm_gemv_plan_for": (_I, [_P, _P, _P, _I, _I, _I, _I, ctypes.POINTER(_I)]),
     "migemm_strerror": (ctypes.c_char_p, [_I]),
     "migemm_abi_version": (_I, []),
     "migemm_hbm_read": (_I, [_P, ctypes.c_size_t, _P, _P]),
@@ -135,6 +136,14 @@ def gemm_plan(dtype, A, B, C, M, N, K, tile=0, group_m=0, xcd_remap=1, a_kmajor=
     fn = lib().migemm_gemm_tn_plan_for if a_kmajor else lib().migemm_gemm_plan_for
     code = fn(dtype, A, B, C, M, N, K, tile, group_m, xcd_remap, ctypes.byref(p))
     return code, p.as_dict()
+
+
+def gemv_route(W, X, Y, M, K, n, rows_per_block=0):
+    """(code, route) of gemv_bf16_ex's checks and kernel choice: route 0 no
+    launch, 1 vector kernel, 14 4x4x4 MFMA kernel, 15 batch kernel, 9 gemm_tn."""
+    r = _I()
+    code = lib().migemm_gemv_plan_for(W, X, Y, M, K, n, rows_per_block, ctypes.byref(r))
+    return code, r.value
 
 
 # ---- torch tensor level --------------------------------------------------------

@@ -437,9 +437,12 @@ int migemm_gemm_tn_plan_for(int dtype, const uint16_t *At, const uint16_t *B, co
     return plan_for(dtype, At, B, C, M, N, K, tile, group_m, xcd_remap, plan, true);
 }
 
-int gemv_bf16_ex(const uint16_t *W, const uint16_t *X, uint16_t *Y, int M, int K, int n,
-                 int rows_per_block, void *stream)
+// gemv_bf16_ex's argument checks and kernel choice (route codes as in
+// migemm_gemv_plan_for).
+static int plan_gemv(const uint16_t *W, const uint16_t *X, const uint16_t *Y, int M, int K, int n,
+                     int rows_per_block, int &route)
 {
+    route = 0;
     if (!(rows_per_block == 0 || rows_per_block == 2 || rows_per_block == 4 ||
           rows_per_block == 8 || rows_per_block == 16 || rows_per_block == 32))
         return MIGEMM_ERR_CONFIG;
@@ -449,19 +452,43 @@ int gemv_bf16_ex(const uint16_t *W, const uint16_t *X, uint16_t *Y, int M, int K
     if (((uintptr_t)W | (uintptr_t)X | (uintptr_t)Y) & 1) return MIGEMM_ERR_ALIGN;
     if (overlaps(Y, ybytes, W, wbytes) || overlaps(Y, ybytes, X, xbytes)) return MIGEMM_ERR_OVERLAP;
     if (M == 0 || n == 0) return MIGEMM_OK;
-
     const bool vec = (K % 8 == 0 && (uintptr_t)W % 16 == 0 && (uintptr_t)X % 16 == 0);
-    if (rows_per_block == 0 && vec && n >= kSkinnyMinTokens) {
-        // Y = X W^T is gemm_tn with At = W, B = X, C = Y (all row-major):
-        // up to kSkinnyAutoMax tokens on the 4x4x4 MFMA kernel, up to
-        // kBatchAutoMax on the 16x16x32 batch kernel, more on the
-        // full-line 256x128 tile
-        if (n > kBatchAutoMax)
-            return gemm_tn_ex(DT_BF16, W, X, Y, M, n, K, TILE_256x128_FL, 0, 1, stream);
+    // Y = X W^T is gemm_tn with At = W, B = X, C = Y (all row-major): up to
+    // kSkinnyAutoMax tokens on the 4x4x4 MFMA kernel, up to kBatchAutoMax on
+    // the 16x16x32 batch kernel, more on the full-line 256x128 tile within
+    // the GEMM's own size limits; everything else on the vector kernel
+    const bool gemm_fits = M <= MIGEMM_MAX_MN && K <= MIGEMM_MAX_K;
+    route = 1;
+    if (rows_per_block == 0 && vec && n >= kSkinnyMinTokens)
+        route = n <= kSkinnyAutoMax ? TILE_SKINNY
+                : n <= kBatchAutoMax ? TILE_BATCH
+                : gemm_fits ? TILE_256x128_FL : 1;
+    return MIGEMM_OK;
+}
+
+int migemm_gemv_plan_for(const uint16_t *W, const uint16_t *X, const uint16_t *Y, int M, int K,
+                         int n, int rows_per_block, int *route)
+{
+    int r;
+    const int rc = plan_gemv(W, X, Y, M, K, n, rows_per_block, r);
+    if (route) *route = r;
+    return rc;
+}
+
+int gemv_bf16_ex(const uint16_t *W, const uint16_t *X, uint16_t *Y, int M, int K, int n,
+                 int rows_per_block, void *stream)
+{
+    int route;
+    const int rc = plan_gemv(W, X, Y, M, K, n, rows_per_block, route);
+    if (rc != MIGEMM_OK || route == 0) return rc;
+    if (route == TILE_256x128_FL)
+        return gemm_tn_ex(DT_BF16, W, X, Y, M, n, K, TILE_256x128_FL, 0, 1, stream);
+    if (route == TILE_SKINNY || route == TILE_BATCH) {
         SkinnyLaunch S{DT_BF16, W, X, Y, M, K, n, (M % 4 == 0 && (uintptr_t)Y % 8 == 0) ? 1 : 0};
-        return finish((n > kSkinnyAutoMax ? batch_launch : skinny_launch)(S, (hipStream_t)stream),
+        return finish((route == TILE_BATCH ? batch_launch : skinny_launch)(S, (hipStream_t)stream),
                       stream);
     }
+    const bool vec = (K % 8 == 0 && (uintptr_t)W % 16 == 0 && (uintptr_t)X % 16 == 0);
 
     GemvLaunch L{};
     L.W = W;
@@ -544,6 +571,8 @@ int attention_decode_bf16(const uint16_t *Q, const uint16_t *Kc, const uint16_t 
     if (overlaps(Out, qb, Q, qb) || overlaps(Out, qb, Kc, cb) || overlaps(Out, qb, Vc, cb) ||
         overlaps(Out, qb, workspace, need) || overlaps(workspace, need, Q, qb) ||
         overlaps(workspace, need, Kc, cb) || overlaps(workspace, need, Vc, cb) ||
+        overlaps(workspace, need, block_table, (size_t)B * max_blocks * 4) ||
+        overlaps(workspace, need, seq_lens, (size_t)B * 4) ||
         overlaps(Out, qb, block_table, (size_t)B * max_blocks * 4) ||
         overlaps(Out, qb, seq_lens, (size_t)B * 4))
         return MIGEMM_ERR_OVERLAP;

@@ -7,9 +7,11 @@
 //     that the ids one XCD receives form one contiguous range of the
 //     ordering below; tiles that share A or B panels then meet in one L2.
 //  2. Grouped ordering (FlagGems "Hygon 优化" page, section "分组调度"):
-//     consecutive ids walk down a group of group_m tile rows, then move to
-//     the next tile column, so a group shares one B panel (and group_m A
-//     panels); the last group may hold fewer rows.
+//     the tile rows are cut into bands of group_m rows (the last band may be
+//     shorter); the ordering visits the bands in turn and, inside a band,
+//     every tile column in turn, taking the band's rows of that column one
+//     after another.  A band's consecutive ids therefore share one B panel
+//     and the band's A panels.
 #pragma once
 
 #include <stdint.h>
@@ -20,22 +22,29 @@ template <typename I>
 __host__ __device__ inline void tile_coord(I wg, I num_pid_m, I num_pid_n, I group_m,
                                            I num_xcd, I &pid_m, I &pid_n)
 {
-    I total = num_pid_m * num_pid_n;
     I id = wg;
     if (num_xcd > 1) {
         // XCD x receives ids x, x + num_xcd, ...: q + 1 of them when x < r.
-        I q = total / num_xcd, r = total % num_xcd;
-        I x = wg % num_xcd, slot = wg / num_xcd;
+        const I total = num_pid_m * num_pid_n;
+        const I q = total / num_xcd, r = total % num_xcd;
+        const I x = wg % num_xcd, slot = wg / num_xcd;
         id = (x < r) ? x * (q + 1) + slot : r * (q + 1) + (x - r) * q + slot;
     }
-    I per_group = group_m * num_pid_n;
-    I group = id / per_group;
-    I first_m = group * group_m;
-    I rows = num_pid_m - first_m;
-    if (rows > group_m) rows = group_m;
-    I local = id - group * per_group;
-    pid_m = first_m + local % rows;
-    pid_n = local / rows;
+    // Ids of the full bands are the mixed-radix numbers (band, column, row)
+    // with digit bases (-, num_pid_n, group_m), row least significant.
+    const I full_bands = num_pid_m / group_m;
+    const I full_ids = full_bands * group_m * num_pid_n;
+    if (id < full_ids) {
+        const I row = id % group_m, rest = id / group_m;
+        pid_n = rest % num_pid_n;
+        pid_m = (rest / num_pid_n) * group_m + row;
+    } else {
+        // the short band: its rows_left rows, again row least significant
+        const I rows_left = num_pid_m - full_bands * group_m;
+        const I local = id - full_ids;
+        pid_m = full_bands * group_m + local % rows_left;
+        pid_n = local / rows_left;
+    }
 }
 
 }  // namespace migemm

@@ -87,8 +87,10 @@ int gemm_bf16(const uint16_t *A, const uint16_t *B, uint16_t *C,
  * 4x4x4 MFMA with W streamed straight into operand registers, up to 64 on
  * the 16x16x32 MFMA with W read as whole cache lines and the token block of
  * X staged in LDS (tile 15 below), beyond that as gemm_tn_bf16 on the
- * 256x128 full-line tile.  gemv_bf16_ex with a non-zero rows_per_block always runs
- * the vector kernel.
+ * 256x128 full-line tile while M and K are within the GEMM's limits
+ * (MIGEMM_MAX_MN, MIGEMM_MAX_K; larger problems take the vector kernel).
+ * gemv_bf16_ex with a non-zero rows_per_block always runs the vector
+ * kernel.  migemm_gemv_plan_for reports the choice.
  */
 int gemv_bf16(const uint16_t *W, const uint16_t *X, uint16_t *Y,
               int M, int K, int n, void *stream);
@@ -321,6 +323,16 @@ int migemm_gemm_plan_for(int dtype, const uint16_t *A, const uint16_t *B,
 int migemm_gemm_tn_plan_for(int dtype, const uint16_t *At, const uint16_t *B,
                             const uint16_t *C, int M, int N, int K, int tile,
                             int group_m, int xcd_remap, migemm_gemm_plan *plan);
+
+/* Which kernel gemv_bf16_ex would run for these arguments (pointers are
+ * inspected for alignment only, never dereferenced): writes to *route 0 (no
+ * launch: M or n is 0), 1 (the row-blocked vector kernel), 14 (the 4x4x4
+ * MFMA kernel), 15 (the batch kernel) or 9 (gemm_tn on the 256x128
+ * full-line tile; only while M <= MIGEMM_MAX_MN and K <= MIGEMM_MAX_K,
+ * larger problems stay on the vector kernel), and returns the code
+ * gemv_bf16_ex would return for the argument checks. */
+int migemm_gemv_plan_for(const uint16_t *W, const uint16_t *X, const uint16_t *Y,
+                         int M, int K, int n, int rows_per_block, int *route);
 
 /* Human-readable text for a return code (static storage). */
 const char *migemm_strerror(int code);

@@ -66,6 +66,8 @@ def lib():
                                   ctypes.c_int, ctypes.c_int, ctypes.c_int]
         L.oracle_grouped_tile.restype = None
         L.oracle_grouped_tile.argtypes = [ctypes.c_int64] * 4 + [i64p, i64p]
+        L.oracle_grouped_order.restype = None
+        L.oracle_grouped_order.argtypes = [ctypes.c_int64] * 3 + [i64p, i64p]
         i32p = ctypes.POINTER(ctypes.c_int32)
         L.oracle_attention.restype = ctypes.c_int64
         L.oracle_attention.argtypes = [ctypes.c_int, u16p, u16p, u16p, i32p, i32p] + \
@@ -280,6 +282,17 @@ def grouped_tile(pid, num_pid_m, num_pid_n, group_m):
     lib().oracle_grouped_tile(pid, num_pid_m, num_pid_n, group_m,
                               ctypes.byref(pm), ctypes.byref(pn))
     return pm.value, pn.value
+
+
+def grouped_order(num_pid_m, num_pid_n, group_m):
+    """The whole grouped ordering as a table: entry p is program p's tile
+    (pid_m, pid_n), built by walking the tiles group by group."""
+    n = num_pid_m * num_pid_n
+    pm = np.zeros(n, np.int64)
+    pn = np.zeros(n, np.int64)
+    lib().oracle_grouped_order(num_pid_m, num_pid_n, group_m, _p(pm, ctypes.c_int64),
+                               _p(pn, ctypes.c_int64))
+    return list(zip(pm.tolist(), pn.tolist()))
 
 
 # ---- acceptance rule -------------------------------------------------------

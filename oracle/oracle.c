@@ -289,20 +289,50 @@ int64_t oracle_gemv(int fmt, const uint16_t *W, const uint16_t *X,
 
 /* ---- grouped tile ordering (FlagGems Hygon page, grouped scheduling) ---- */
 
-/* Flat program id -> output tile (pid_m, pid_n).  Consecutive ids walk down
- * a group of up to group_m tile rows before moving to the next tile column,
- * so a group shares one B panel; the last group may hold fewer rows. */
+/* The whole grouped ordering, written out by walking the tiles in the order
+ * the page's grouping visits them: tile rows taken in groups of group_m (the
+ * last group keeps what is left), inside a group every tile column in turn,
+ * inside a column the group's rows top to bottom.  Entry p of the arrays is
+ * the tile of program id p; both arrays hold num_pid_m * num_pid_n entries. */
+void oracle_grouped_order(int64_t num_pid_m, int64_t num_pid_n, int64_t group_m,
+                          int64_t *pid_m, int64_t *pid_n)
+{
+    int64_t p = 0;
+    for (int64_t first = 0; first < num_pid_m; first += group_m) {
+        int64_t last = first + group_m;
+        if (last > num_pid_m) last = num_pid_m;
+        for (int64_t col = 0; col < num_pid_n; ++col)
+            for (int64_t row = first; row < last; ++row) {
+                pid_m[p] = row;
+                pid_n[p] = col;
+                ++p;
+            }
+    }
+}
+
+/* One program id's tile: the same walk, stopped at that id. */
 void oracle_grouped_tile(int64_t pid, int64_t num_pid_m, int64_t num_pid_n,
                          int64_t group_m, int64_t *pid_m, int64_t *pid_n)
 {
-    int64_t per_group = group_m * num_pid_n;     /* programs in one group */
-    int64_t group = pid / per_group;
-    int64_t first_m = group * group_m;           /* first tile row of group */
-    int64_t rows = num_pid_m - first_m;          /* rows in this group */
-    if (rows > group_m) rows = group_m;
-    int64_t local = pid % per_group;
-    *pid_m = first_m + local % rows;
-    *pid_n = local / rows;
+    int64_t p = 0;
+    *pid_m = -1;
+    *pid_n = -1;
+    for (int64_t first = 0; first < num_pid_m; first += group_m) {
+        int64_t last = first + group_m;
+        if (last > num_pid_m) last = num_pid_m;
+        const int64_t span = (last - first) * num_pid_n;     /* ids of this group */
+        if (pid >= p + span) {
+            p += span;
+            continue;
+        }
+        for (int64_t col = 0; col < num_pid_n; ++col)
+            for (int64_t row = first; row < last; ++row, ++p)
+                if (p == pid) {
+                    *pid_m = row;
+                    *pid_n = col;
+                    return;
+                }
+    }
 }
 
 /* ---- decode attention (DCU decode page, sections 6.1 and 6.3) ---------- */

@@ -271,9 +271,13 @@ def test_tile_scheduler_bijection(group_m, num_xcd):
 
 
 def test_tile_scheduler_without_remap_is_the_grouped_ordering():
-    for npm, npn, gm in ((5, 3, 2), (16, 136, 8), (7, 9, 4), (32, 32, 16)):
-        for w in range(npm * npn):
-            assert binding.tile_coord(w, npm, npn, gm, 1) == oracle.grouped_tile(w, npm, npn, gm)
+    # the product's mixed-radix map against the oracle's table, which walks
+    # the tiles group by group, column by column, row by row
+    for npm, npn, gm in ((5, 3, 2), (16, 136, 8), (7, 9, 4), (32, 32, 16), (20, 12, 8), (3, 5, 8),
+                         (1, 7, 1), (9, 1, 4)):
+        table = oracle.grouped_order(npm, npn, gm)
+        assert [binding.tile_coord(w, npm, npn, gm, 1) for w in range(npm * npn)] == table
+        assert [oracle.grouped_tile(w, npm, npn, gm) for w in range(0, npm * npn, 7)] == table[::7]
 
 
 def test_tile_scheduler_xcd_locality():
@@ -317,6 +321,8 @@ def test_attention_argument_errors_and_segments():
     assert call(args(Kc=P + 0x1000008)) == -4         # caches need 16-byte rows
     assert call(args(wsb=1000)) == -6                 # workspace too small
     assert call(args(Out=P + 8)) == -3                # Out inside Q
+    assert call(args(ws=P + 0x3000000 - 64)) == -3    # workspace over the block table
+    assert call(args(ws=P + 0x3100000 - 16)) == -3    # workspace over seq_lens
     assert call(args(B=70000, wsb=1 << 40)) == -6     # grid z limit
     assert call(args(maxb=1 << 22, bs=1024)) == -6    # token positions past int
     # workspace: partial max, denominator and D outputs per (b, h, segment)
@@ -330,3 +336,20 @@ def test_attention_argument_errors_and_segments():
     assert L.migemm_attention_segments(1, 32, 4, 32768) == 64   # groups of 8: 2 workgroups each
     assert L.migemm_attention_segments(1, 16, 4, 100) == 1
     assert L.migemm_attention_segments(1000, 16, 4, 32768) == 1
+
+
+def test_gemv_route():
+    # the automatic route by token count (16-byte rows); non-zero
+    # rows_per_block keeps the vector kernel; beyond the GEMM's size limits
+    # many tokens stay on the vector kernel instead of failing
+    W, X, Y = P, P + (1 << 36), P + (1 << 37)
+    for n, want in ((1, 1), (2, 1), (3, 14), (4, 14), (5, 15), (64, 15), (65, 9), (1000, 9)):
+        assert binding.gemv_route(W, X, Y, 34816, 5120, n) == (0, want), n
+    assert binding.gemv_route(W, X, Y, 34816, 5120, 16, rows_per_block=8) == (0, 1)
+    assert binding.gemv_route(W, X, Y, 34816, 5122, 16) == (0, 1)          # K % 8: no MFMA route
+    assert binding.gemv_route(W, X, Y, (1 << 23) + 64, 8, 65) == (0, 1)     # M past the GEMM limit
+    assert binding.gemv_route(W, X, Y, 64, (1 << 21) + 8, 65) == (0, 1)     # K past the GEMM limit
+    assert binding.gemv_route(W, X, Y, (1 << 23) + 64, 8, 64) == (0, 15)
+    assert binding.gemv_route(W, X, Y, 0, 8, 4) == (0, 0)
+    assert binding.gemv_route(W, X, Y, 8, 8, -1)[0] == -1
+    assert binding.gemv_route(W, X, W + 2, 8, 8, 1)[0] == -3               # Y over W

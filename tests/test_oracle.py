@@ -307,8 +307,17 @@ def test_gemv_equals_gemm_with_one_row():
 
 def test_grouped_tile_hand_worked_example():
     rows = np.loadtxt(os.path.join(HERE, "golden", "grouped_tile_5x3_g2.txt"), dtype=np.int64)
+    table = oracle.grouped_order(5, 3, 2)
     for pid, pm, pn in rows:
         assert oracle.grouped_tile(int(pid), 5, 3, 2) == (pm, pn)
+        assert table[pid] == (pm, pn)
+
+
+def test_grouped_tile_one_group_is_column_major():
+    # GROUP_M >= num_pid_m: one group holding every tile row, so the ordering
+    # walks the grid column by column (pid -> (pid % rows, pid // rows))
+    for npm, npn, gm in ((5, 3, 5), (5, 3, 8), (1, 4, 2)):
+        assert oracle.grouped_order(npm, npn, gm) == [(p % npm, p // npm) for p in range(npm * npn)]
 
 
 @pytest.mark.parametrize("group_m", [1, 2, 3, 4, 8, 16])
