@@ -498,9 +498,13 @@ constexpr int fl_loads_after(int j, int need_a, int need_b)
 // A[k + m*K]), A ring of SA stages of 64 k laid out, loaded and read exactly
 // like B (rows of A in place of columns of B).
 // Ping-pong tile: MFMAs of a sub-step issued in its load phase (the rest go
-// into its compute phase).
+// into its compute phase), and the spacing, in compute-phase MFMAs, of the B
+// fragment reads there.
 #ifndef PP_PRE
-#define PP_PRE 8
+#define PP_PRE 2
+#endif
+#ifndef PP_BREAD_EVERY
+#define PP_BREAD_EVERY 2
 #endif
 
 // Ping-pong schedule (PP below): loads in flight after the last one that
@@ -895,13 +899,18 @@ gemm_fl_kernel(const uint16_t *__restrict__ A, const uint16_t *__restrict__ B,
     } else if constexpr (PP) {
         // Ping-pong: two groups of four waves, one wave of each group per
         // SIMD (waves w and w + 4 share a SIMD).  Each sub-step j is a load
-        // phase (issue the LDS-direct loads of a later sub-step, nothing
-        // else) and a compute phase (the FM x FN MFMAs of sub-step j, with
-        // the LDS reads of sub-step j + 1 into the other fragment set between
-        // them).  Group 1 runs one phase behind group 0, a workgroup barrier
-        // between phases, so on each SIMD one wave streams MFMAs and LDS
-        // reads while the other waits for the memory pipe to take its loads:
-        // a load stalled at issue never holds up an MFMA or an LDS read.
+        // phase (issue the LDS-direct loads of a later sub-step, then the
+        // transposing reads of sub-step j's own A fragments, then its first
+        // PRE MFMAs) and a compute phase (the other MFMAs of sub-step j, with
+        // the B fragment reads of sub-step j + 1 into the other fragment set
+        // between them).  Group 1 runs one phase behind group 0, a workgroup
+        // barrier between phases, so on each SIMD one wave streams MFMAs
+        // while the other waits for the memory pipe to take its loads: a load
+        // stalled at issue never holds up an MFMA.  A wave's LDS reads are
+        // split over its two phases because one wave's reads are served at
+        // a limited rate (about one KiB per 31 cycles with linear reads, 512
+        // bytes per 41 with transposing ones, measured), which with all of
+        // them in the compute phase made that phase the longest.
         //
         // Load phase i issues A sub-step i + SA - 1 and half (i & 1) of B
         // stage (i >> 1) + SB - 1: the largest distances at which no load
@@ -942,17 +951,22 @@ gemm_fl_kernel(const uint16_t *__restrict__ A, const uint16_t *__restrict__ B,
             wait_for(std::integral_constant<int, 1>{}, std::integral_constant<int, 1>{}, -1);   // sub-step 0
             __syncthreads();
 #pragma unroll
-            for (int r = 0; r < NR; ++r) read_one(0, 0, 0, r, f0);
+            for (int r = FM; r < NR; ++r) read_one(0, 0, 0, r, f0);   // its B fragments
             if (J > 1) wait_for(std::integral_constant<int, 1>{}, std::integral_constant<int, 2>{}, -1);   // sub-step 1
             __syncthreads();
             if (role) __syncthreads();
-            // The first PRE MFMAs of sub-step j go into its load phase, after
-            // the loads: its fragments are in registers by then, and the
-            // wave would otherwise only wait for the memory pipe, so for part
-            // of every phase both waves of a SIMD issue MFMAs.
+            // Load phase of sub-step j: its loads; then the A fragments of
+            // sub-step j (stage j of the A ring, complete since the barrier
+            // that ended the phase before, and refilled only two phases
+            // after this one), into the set whose B fragments the compute
+            // phase before read; then the first PRE MFMAs of sub-step j, so
+            // that for part of every phase both waves of a SIMD issue MFMAs.
             constexpr int NMF = FM * FN;
             constexpr int PRE = PP_PRE < NMF ? PP_PRE : 0;
-            auto pre_mfma = [&](const Frag &cur) {
+            auto load_phase = [&](int j, Frag &cur) {
+                phase_loads(j);
+#pragma unroll
+                for (int r = 0; r < FM; ++r) read_one(j % SA, 0, 0, r, cur);
 #pragma unroll
                 for (int t = 0; t < PRE; ++t) {
                     mfma16x16x32<DT>(acc[t / FN][t % FN], cur.a[t / FN], cur.b[t % FN]);
@@ -960,34 +974,31 @@ gemm_fl_kernel(const uint16_t *__restrict__ A, const uint16_t *__restrict__ B,
                 }
             };
             // compute phase of sub-step j on `cur` (its MFMAs from PRE on),
-            // reading sub-step j + 1 into `nxt` (one read after every EV
-            // MFMAs; after the last sub-step these read stale ring contents
-            // that are never used)
+            // reading sub-step j + 1's B fragments into `nxt` (one read after
+            // every EV MFMAs, early enough that the last has landed when the
+            // phase ends; after the last sub-step these read stale ring
+            // contents that are never used)
             auto compute = [&](int j, auto par_c, Frag &cur, Frag &nxt) {
                 constexpr int PAR = decltype(par_c)::value;
-                constexpr int EV = (NMF - PRE) / NR > 0 ? (NMF - PRE) / NR : 1;
-                const int na = (j + 1) % SA, nb = ((j + 1) >> 1) % SB;
+                constexpr int EV = PP_BREAD_EVERY;
+                static_assert(EV >= 1 && FN * EV <= NMF - PRE, "B reads fit the compute phase");
+                const int nb = ((j + 1) >> 1) % SB;
 #pragma unroll
                 for (int t = PRE; t < NMF; ++t) {
                     mfma16x16x32<DT>(acc[t / FN][t % FN], cur.a[t / FN], cur.b[t % FN]);
                     const int u = t - PRE;
-                    if (u % EV == EV - 1 && u / EV < NR) read_one(na, nb, 1 - PAR, u / EV, nxt);
+                    if (u % EV == EV - 1 && u / EV < FN) read_one(0, nb, 1 - PAR, FM + u / EV, nxt);
                     __builtin_amdgcn_sched_barrier(0);
                 }
-                constexpr int DONE = (NMF - PRE) / EV < NR ? (NMF - PRE) / EV : NR;
-#pragma unroll
-                for (int r = DONE; r < NR; ++r) read_one(na, nb, 1 - PAR, r, nxt);
                 if (j + 2 < J) wait_for(std::integral_constant<int, PAR>{}, std::integral_constant<int, 2>{}, j);
                 __syncthreads();
             };
             for (int j = 0; j < J; j += 2) {
-                phase_loads(j);
-                pre_mfma(f0);
+                load_phase(j, f0);
                 __syncthreads();
                 compute(j, std::integral_constant<int, 0>{}, f0, f1);
                 if (j + 1 < J) {
-                    phase_loads(j + 1);
-                    pre_mfma(f1);
+                    load_phase(j + 1, f1);
                     __syncthreads();
                     compute(j + 1, std::integral_constant<int, 1>{}, f1, f0);
                 }
