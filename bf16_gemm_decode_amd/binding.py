@@ -72,6 +72,8 @@ SIGNATURES = {
     "migemm_hbm_read": (_I, [_P, ctypes.c_size_t, _P, _P]),
     "attention_decode_bf16": (_I, [_P, _P, _P, _P, _P, _P] + [_I] * 7 +
                               [ctypes.c_float, _I, _I, _P, ctypes.c_size_t, _P]),
+    "attention_decode_bf16_noalloc": (_I, [_P, _P, _P, _P, _P, _P] + [_I] * 7 +
+                                      [ctypes.c_float, _I, _I, _P]),
     "migemm_attention_segments": (_I, [_I, _I, _I, _I]),
     "migemm_attention_workspace_bytes": (ctypes.c_size_t, [_I, _I, _I, _I]),
     "migemm_hbm_read_sink_words": (_I, []),

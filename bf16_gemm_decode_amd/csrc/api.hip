@@ -4,6 +4,8 @@
 #include <stdint.h>
 #include <string.h>
 
+#include <mutex>
+
 #include "common.hpp"
 #include "kernels.hpp"
 #include "migemm.h"
@@ -539,12 +541,19 @@ size_t migemm_attention_workspace_bytes(int B, int Hq, int D, int num_segments)
     return attention_workspace_bytes(B, Hq, D, num_segments);
 }
 
-int attention_decode_bf16(const uint16_t *Q, const uint16_t *Kc, const uint16_t *Vc,
-                          const int32_t *block_table, const int32_t *seq_lens, uint16_t *Out,
-                          int B, int Hq, int Hkv, int D, int block_size, int max_blocks,
-                          int num_blocks, float scale, int max_seq_len, int num_segments,
-                          void *workspace, size_t workspace_bytes, void *stream)
+}  // extern "C"
+
+namespace {
+
+// attention_decode_bf16's checks of everything but the workspace, before any
+// HIP call.  On MIGEMM_OK with *run set, S is the segment count and need the
+// workspace bytes the call uses.
+int attention_plan(const uint16_t *Q, const uint16_t *Kc, const uint16_t *Vc,
+                   const int32_t *block_table, const int32_t *seq_lens, const uint16_t *Out,
+                   int B, int Hq, int Hkv, int D, int block_size, int max_blocks, int num_blocks,
+                   int max_seq_len, int num_segments, bool &run, int &S, size_t &need)
 {
+    run = false;
     if (B < 0 || Hq < 0 || Hkv < 0 || D < 0 || block_size < 0 || max_blocks < 0 ||
         num_blocks < 0 || max_seq_len < 0 || num_segments < 0)
         return MIGEMM_ERR_DIM;
@@ -559,25 +568,103 @@ int attention_decode_bf16(const uint16_t *Q, const uint16_t *Kc, const uint16_t 
     // steps of look-ahead) held in int
     if (B > 65535 || Hkv > 65535 || (int64_t)max_blocks * block_size > (1 << 30))
         return MIGEMM_ERR_SIZE;
-    if (!Q || !Kc || !Vc || !block_table || !seq_lens || !Out || !workspace) return MIGEMM_ERR_NULL;
-    if (((uintptr_t)Q | (uintptr_t)Kc | (uintptr_t)Vc | (uintptr_t)workspace) % 16 ||
+    if (!Q || !Kc || !Vc || !block_table || !seq_lens || !Out) return MIGEMM_ERR_NULL;
+    if (((uintptr_t)Q | (uintptr_t)Kc | (uintptr_t)Vc) % 16 ||
         ((uintptr_t)block_table | (uintptr_t)seq_lens) % 4 || (uintptr_t)Out % 2)
         return MIGEMM_ERR_ALIGN;
-    const int S = num_segments ? num_segments : migemm_attention_segments(B, Hq, Hkv, max_seq_len);
-    const size_t need = attention_workspace_bytes(B, Hq, D, S);
-    if (workspace_bytes < need) return MIGEMM_ERR_SIZE;
+    S = num_segments ? num_segments : migemm_attention_segments(B, Hq, Hkv, max_seq_len);
+    need = attention_workspace_bytes(B, Hq, D, S);
     const size_t qb = (size_t)B * Hq * D * 2;
     const size_t cb = (size_t)num_blocks * block_size * Hkv * D * 2;
     if (overlaps(Out, qb, Q, qb) || overlaps(Out, qb, Kc, cb) || overlaps(Out, qb, Vc, cb) ||
-        overlaps(Out, qb, workspace, need) || overlaps(workspace, need, Q, qb) ||
-        overlaps(workspace, need, Kc, cb) || overlaps(workspace, need, Vc, cb) ||
-        overlaps(workspace, need, block_table, (size_t)B * max_blocks * 4) ||
-        overlaps(workspace, need, seq_lens, (size_t)B * 4) ||
         overlaps(Out, qb, block_table, (size_t)B * max_blocks * 4) ||
         overlaps(Out, qb, seq_lens, (size_t)B * 4))
         return MIGEMM_ERR_OVERLAP;
+    run = true;
+    return MIGEMM_OK;
+}
+
+// The segment partials of attention_decode_bf16_noalloc: a file-scope device
+// array in place of a caller workspace.  In host code its name is only a
+// stand-in; the device address comes from hipGetSymbolAddress, looked up once
+// per device with that device current, and only that address is passed on.
+static __device__ __align__(256) unsigned char scratch[MIGEMM_NOALLOC_SCRATCH_BYTES];
+
+constexpr int kMaxDevices = 64;
+std::mutex g_scratch_mutex;
+void *g_scratch_ptr[kMaxDevices];
+
+// The current device's address of `scratch` (a HIP error code, or
+// MIGEMM_ERR_CONFIG past kMaxDevices devices).
+int scratch_address(void **ptr)
+{
+    int dev = 0;
+    hipError_t e = hipGetDevice(&dev);
+    if (e != hipSuccess) return (int)e;
+    if (dev < 0 || dev >= kMaxDevices) return MIGEMM_ERR_CONFIG;
+    std::lock_guard<std::mutex> lock(g_scratch_mutex);
+    if (!g_scratch_ptr[dev]) {
+        void *p = nullptr;
+        e = hipGetSymbolAddress(&p, HIP_SYMBOL(scratch));
+        if (e != hipSuccess) return (int)e;
+        if (!p) return (int)hipErrorInvalidSymbol;
+        g_scratch_ptr[dev] = p;
+    }
+    *ptr = g_scratch_ptr[dev];
+    return MIGEMM_OK;
+}
+
+}  // namespace
+
+extern "C" {
+
+int attention_decode_bf16(const uint16_t *Q, const uint16_t *Kc, const uint16_t *Vc,
+                          const int32_t *block_table, const int32_t *seq_lens, uint16_t *Out,
+                          int B, int Hq, int Hkv, int D, int block_size, int max_blocks,
+                          int num_blocks, float scale, int max_seq_len, int num_segments,
+                          void *workspace, size_t workspace_bytes, void *stream)
+{
+    bool run;
+    int S = 0;
+    size_t need = 0;
+    int rc = attention_plan(Q, Kc, Vc, block_table, seq_lens, Out, B, Hq, Hkv, D, block_size,
+                            max_blocks, num_blocks, max_seq_len, num_segments, run, S, need);
+    if (rc != MIGEMM_OK || !run) return rc;
+    if (!workspace) return MIGEMM_ERR_NULL;
+    if ((uintptr_t)workspace % 16) return MIGEMM_ERR_ALIGN;
+    if (workspace_bytes < need) return MIGEMM_ERR_SIZE;
+    const size_t qb = (size_t)B * Hq * D * 2;
+    const size_t cb = (size_t)num_blocks * block_size * Hkv * D * 2;
+    if (overlaps(Out, qb, workspace, need) || overlaps(workspace, need, Q, qb) ||
+        overlaps(workspace, need, Kc, cb) || overlaps(workspace, need, Vc, cb) ||
+        overlaps(workspace, need, block_table, (size_t)B * max_blocks * 4) ||
+        overlaps(workspace, need, seq_lens, (size_t)B * 4))
+        return MIGEMM_ERR_OVERLAP;
     AttentionLaunch A{Q, Kc, Vc, block_table, seq_lens, Out, B, Hq, Hkv, D, block_size,
                       max_blocks, num_blocks, scale, S, workspace};
+    return finish(attention_launch(A, (hipStream_t)stream), stream);
+}
+
+int attention_decode_bf16_noalloc(const uint16_t *Q, const uint16_t *Kc, const uint16_t *Vc,
+                                  const int32_t *block_table, const int32_t *seq_lens,
+                                  uint16_t *Out, int B, int Hq, int Hkv, int D, int block_size,
+                                  int max_blocks, int num_blocks, float scale, int max_seq_len,
+                                  int num_segments, void *stream)
+{
+    bool run;
+    int S = 0;
+    size_t need = 0;
+    int rc = attention_plan(Q, Kc, Vc, block_table, seq_lens, Out, B, Hq, Hkv, D, block_size,
+                            max_blocks, num_blocks, max_seq_len, num_segments, run, S, need);
+    if (rc != MIGEMM_OK || !run) return rc;
+    if (need > (size_t)MIGEMM_NOALLOC_SCRATCH_BYTES) return MIGEMM_ERR_SIZE;
+    void *ws = nullptr;
+    rc = scratch_address(&ws);
+    if (rc != MIGEMM_OK) return rc;
+    // every segment row of the partials is written before the merge reads
+    // it, so nothing left by an earlier call is read and nothing is cleared
+    AttentionLaunch A{Q, Kc, Vc, block_table, seq_lens, Out, B, Hq, Hkv, D, block_size,
+                      max_blocks, num_blocks, scale, S, ws};
     return finish(attention_launch(A, (hipStream_t)stream), stream);
 }
 

@@ -134,6 +134,27 @@ int attention_decode_bf16(const uint16_t *Q, const uint16_t *Kc, const uint16_t 
                           int num_segments, void *workspace, size_t workspace_bytes,
                           void *stream);
 
+/*
+ * attention_decode_bf16_noalloc -- attention_decode_bf16 for callers that
+ * cannot allocate device memory (code under HIP graph capture, tight
+ * serving loops, harnesses that forbid hipMalloc).  The same arguments
+ * without the workspace: the segment partials go to a device array the
+ * library holds on each GPU it runs on, MIGEMM_NOALLOC_SCRATCH_BYTES (8 MiB)
+ * each, until the process ends.  Returns MIGEMM_ERR_SIZE when
+ * migemm_attention_workspace_bytes(B, Hq, D, segments) exceeds it (checked
+ * on the host before any HIP call).  Allocates nothing: the array's address
+ * is looked up once per device, on the first call with that device current.
+ * All calls on one GPU share the array, so calls that run at the same time
+ * on one GPU (other streams, other host threads) race: the caller orders
+ * them.  Results equal attention_decode_bf16's for the same segment count.
+ */
+#define MIGEMM_NOALLOC_SCRATCH_BYTES (8 << 20)
+int attention_decode_bf16_noalloc(const uint16_t *Q, const uint16_t *Kc, const uint16_t *Vc,
+                                  const int32_t *block_table, const int32_t *seq_lens,
+                                  uint16_t *Out, int B, int Hq, int Hkv, int D, int block_size,
+                                  int max_blocks, int num_blocks, float scale, int max_seq_len,
+                                  int num_segments, void *stream);
+
 /* Segments the automatic choice uses (host only): the largest power of two
  * that keeps the segment workgroups (B * Hkv * ceil(Hq / Hkv / 4) per
  * segment) within one round of residency on 256 CUs (512) and at least

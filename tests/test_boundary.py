@@ -353,3 +353,26 @@ def test_gemv_route():
     assert binding.gemv_route(W, X, Y, 0, 8, 4) == (0, 0)
     assert binding.gemv_route(W, X, Y, 8, 8, -1)[0] == -1
     assert binding.gemv_route(W, X, W + 2, 8, 8, 1)[0] == -3               # Y over W
+
+
+def test_attention_noalloc_host_errors():
+    # the allocation-free attention entry: host-side checks before any HIP
+    # call (shape, nulls, alignment, and the scratch limit)
+    L = binding.lib()
+
+    def call(B=1, Hq=16, Hkv=4, D=256, S=16, Q=P, Out=P + 0x3200000, maxlen=1000):
+        return L.attention_decode_bf16_noalloc(Q, P + 0x1000000, P + 0x2000000, P + 0x3000000,
+                                               P + 0x3100000, Out, B, Hq, Hkv, D, 784, 2, 4, 0.0625,
+                                               maxlen, S, None)
+    assert call(B=0) == 0
+    assert call(Hq=-1) == -1
+    assert call(D=96) == -5
+    assert call(Q=None) == -2
+    assert call(Q=P + 8) == -4
+    assert call(Out=P + 8) == -3
+    # partials of 16 heads x 1024 segments x 258 FP32 = 16.9 MB > the 8 MiB array
+    assert L.migemm_attention_workspace_bytes(1, 16, 256, 1024) > (8 << 20)
+    assert call(S=1024) == -6
+    # 4 sequences x 16 heads x 128 segments x 258 FP32 = 8.45 MB, just past 8 MiB
+    assert L.migemm_attention_workspace_bytes(4, 16, 256, 128) == 8454144 > (8 << 20)
+    assert call(B=4, S=128) == -6
