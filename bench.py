@@ -108,7 +108,7 @@ def measured_traffic(sources, summary_file):
         return None
     if summ.get("kernel_sources") != sources or summ.get("kernel_sources_sha256") != source_digest(sources):
         return None
-    return summ.get("hbm_bytes_per_launch")
+    return summ.get("beyond_l2_bytes_per_launch")
 
 
 def measured_mfma_util(sources, summary_file, label):
@@ -128,26 +128,37 @@ def measured_mfma_util(sources, summary_file, label):
 
 
 def cpu_baseline(A, B, M, N, K, target_s):
-    """Oracle GFLOP rate on sampled entries of the GEMM, ~target_s seconds."""
+    """Oracle GFLOP rate on sampled entries of the GEMM, ~target_s seconds on
+    all the host's threads, then ~target_s / 4 seconds on one thread."""
     import numpy as np
     import oracle
     import synth
     cores = int(os.environ.get("OMP_NUM_THREADS", len(os.sched_getaffinity(0))))
     idx_all = synth.sample_indices(M, N, 1, count=1 << 21)
-    oracle.gemm_sampled(A, B, M, N, K, idx_all[:16], "f16")      # load, start threads
-    n = 512
-    t0 = time.perf_counter()
-    oracle.gemm_sampled(A, B, M, N, K, idx_all[:n], "f16")
-    dt = time.perf_counter() - t0
-    n = int(min(idx_all.size, max(n, n * target_s / max(dt, 1e-3))))
-    t0 = time.perf_counter()
-    r = oracle.gemm_sampled(A, B, M, N, K, idx_all[:n], "f16")
-    dt = time.perf_counter() - t0
-    assert r.macs == n * K
+
+    def timed(target, first):
+        oracle.gemm_sampled(A, B, M, N, K, idx_all[:16], "f16")      # load, start threads
+        n = first
+        t0 = time.perf_counter()
+        oracle.gemm_sampled(A, B, M, N, K, idx_all[:n], "f16")
+        dt = time.perf_counter() - t0
+        n = int(min(idx_all.size, max(n, n * target / max(dt, 1e-3))))
+        t0 = time.perf_counter()
+        r = oracle.gemm_sampled(A, B, M, N, K, idx_all[:n], "f16")
+        dt = time.perf_counter() - t0
+        assert r.macs == n * K
+        return n, dt
+
+    n, dt = timed(target_s, 512)
+    before = oracle.set_threads(1)
+    n1, dt1 = timed(target_s / 4, 16)
+    oracle.set_threads(before)
     return {"value": round(2.0 * n * K / dt / 1e12, 9), "unit": "TFLOP/s", "cores": cores,
             "kind": "oracle", "seconds": round(dt, 3),
             "sample": "%d sampled output entries of the 8192x8192x16384 FP16 GEMM "
-                      "(K = 16384 multiply-adds each, FP64 accumulation)" % n}
+                      "(K = 16384 multiply-adds each, FP64 accumulation)" % n,
+            "one_thread": {"value": round(2.0 * n1 * K / dt1 / 1e12, 9), "unit": "TFLOP/s",
+                           "seconds": round(dt1, 3), "sample": "%d sampled output entries" % n1}}
 
 
 def cpu_all():
@@ -222,6 +233,7 @@ def main():
 
     import synth
     from bf16_gemm_decode_amd import binding, roofline as rf
+    from bf16_gemm_decode_amd.gpu_monitor import GpuMonitor
     from bf16_gemm_decode_amd.profile_summary import ATTENTION_SOURCES, GEMM_SOURCES, GEMV_SOURCES
 
     torch.cuda.set_device(0)
@@ -283,6 +295,26 @@ def main():
                                    M, N, K, args.tile, args.group_m, args.xcd_remap)
     assert code == 0, code
     kernel = "gemm_fl_kernel" if plan["tile"] >= 7 else "gemm_kernel"
+
+    def gemm_clock(reps=10):
+        """The clock the headline GEMM runs at: `reps` back-to-back launches
+        through the library's measurement entry (the same kernel and plan;
+        wave 0 of every workgroup records its shader-clock and 100 MHz
+        real-time counts), one synchronisation at the end."""
+        out = torch.zeros((reps, plan["grid"], 2), dtype=torch.int64, device="cuda")
+        for r in range(reps):
+            assert L.migemm_gemm_clocked(binding.F16, dA.data_ptr(), dB.data_ptr(), dC.data_ptr(), M, N, K,
+                                         args.tile, args.group_m, args.xcd_remap, out[r].data_ptr(), h) == 0
+        stream.synchronize()
+        o = out.cpu().numpy()
+        ghz = [float(o[r, :, 0].sum()) / float(o[r, :, 1].sum()) * 0.1 for r in range(reps)]
+        return {"mean": round(sum(ghz) / reps, 3), "min": round(min(ghz), 3), "max": round(max(ghz), 3),
+                "method": "shader-clock / 100 MHz real-time counters read inside the GEMM kernel by wave 0 "
+                          "of every workgroup, over %d back-to-back launches after the timed region" % reps}
+
+    monitor = GpuMonitor(torch.cuda.current_device(), period_s=0.005)
+    monitor.start()
+    gpu_state = {}
     for i in range(args.warmup):
         assert gemm() == 0 and gemv(i) == 0
     stream.synchronize()
@@ -302,10 +334,14 @@ def main():
     stream.synchronize()
     torch.cuda.synchronize()
     wall = time.perf_counter() - t0
+    gpu_state["gemm_clock_ghz"] = gemm_clock()
+    gpu_state.update(monitor.stop())
 
     gemm_s = [e[0].elapsed_time(e[1]) / 1e3 for e in ev]
     gemv_s = [e[2].elapsed_time(e[3]) / 1e3 for e in ev]
     gemm_avg, gemv_step_avg = sum(gemm_s) / len(gemm_s), sum(gemv_s) / len(gemv_s)
+    gemm_sorted = sorted(gemm_s)
+    gemm_med, gemm_min = gemm_sorted[len(gemm_sorted) // 2], gemm_sorted[0]
 
     # The GEMV's launch duration: inside a step its events also hold the
     # dispatch gap (a few microseconds, a few percent of a ~50 us kernel), so
@@ -381,6 +417,10 @@ def main():
     del qC
 
     tflops = rf.gemm_flop(M, N, K) / gemm_avg / 1e12
+    clk = gpu_state["gemm_clock_ghz"]["mean"]
+    # the dense FP16 MFMA rate at the clock measured over the timed region:
+    # 256 CUs x 4096 FLOP per clock (the published 2.5 PFLOP/s is this at 2.4 GHz)
+    peak_at_clock = props.multi_processor_count * 4096 * clk * 1e9 / 1e12 if clk else None
     gemv_bytes = rf.gemv_bytes(GM, GK, gn)
     gemv_GBps = gemv_bytes / gemv_avg / 1e9
     peak = rf.MI355X["mfma_f16_tflops"]
@@ -414,7 +454,16 @@ def main():
                      "mfma_util_percent": measured_mfma_util(GEMM_SOURCES, GEMM_MFMA_SUMMARY,
                                                              "f16_tile%d" % plan["tile"]),
                      "kernel": "%s (2*M*N*K FLOP per launch)" % kernel,
-                     "avg_launch_ms": round(gemm_avg * 1e3, 4)},
+                     "avg_launch_ms": round(gemm_avg * 1e3, 4),
+                     "median_launch_ms": round(gemm_med * 1e3, 4),
+                     "min_launch_ms": round(gemm_min * 1e3, 4),
+                     "peak_note": "peak = MI355X published dense FP16/BF16 MFMA rate (2.5 PFLOP/s); "
+                                  "256 CUs x 4096 FLOP/clk x 2.4 GHz = 2516.6",
+                     "traffic_note": "FETCH_SIZE + WRITE_SIZE: bytes of requests leaving L2 "
+                                     "(to the MALL or HBM), scaled by a 1 GiB copy",
+                     "measured_clock_ghz": clk,
+                     "peak_at_measured_clock": round(peak_at_clock, 1) if peak_at_clock else None,
+                     "frac_at_measured_clock": round(tflops / peak_at_clock, 4) if peak_at_clock else None},
         "gemv": {"GBps": round(gemv_GBps, 1), "avg_launch_us": round(gemv_avg * 1e6, 2),
                  "launches_timed": nburst, "in_step_avg_us": round(gemv_step_avg * 1e6, 2),
                  "roofline": {"bound": "hbm", "achieved": round(gemv_GBps, 1), "peak": hbm,
@@ -436,6 +485,7 @@ def main():
         "gemm_8bit": {"shape": [M, N, K], "layout": "A k-major (gemm_tn_q_ex, automatic tile)",
                       "output": "BF16 of scale x sum", **q_rows},
         "device": {"name": props.name, "cus": props.multi_processor_count},
+        "gpu_state": gpu_state,
     }
     if not args.no_cpu_baseline:
         out["cpu_baseline"] = cpu_baseline(A, B, M, N, K, args.cpu_seconds)

@@ -77,6 +77,8 @@ SIGNATURES = {
     "migemm_attention_segments": (_I, [_I, _I, _I, _I]),
     "migemm_attention_workspace_bytes": (ctypes.c_size_t, [_I, _I, _I, _I]),
     "migemm_hbm_read_sink_words": (_I, []),
+    "migemm_clock_probe": (_I, [_P, _I, _I, _P]),
+    "migemm_gemm_clocked": (_I, [_I, _P, _P, _P, _I, _I, _I, _I, _I, _I, _P, _P]),
 }
 
 

@@ -212,6 +212,26 @@ int gemm_ex(int dtype, const uint16_t *A, const uint16_t *B, uint16_t *C, int M,
     return finish(gemm_launch(L, (hipStream_t)stream), stream);
 }
 
+int migemm_gemm_clocked(int dtype, const uint16_t *A, const uint16_t *B, uint16_t *C, int M, int N,
+                        int K, int tile, int group_m, int xcd_remap, uint64_t *clocks, void *stream)
+{
+    GemmLaunch L;
+    bool launch;
+    int rc = plan_gemm(dtype, A, B, C, M, N, K, tile, group_m, xcd_remap, L, launch);
+    if (rc != MIGEMM_OK || !launch) return rc;
+    // the record is written by the full-line kernels only
+    if (!((L.tile >= TILE_256x256_FL && L.tile <= TILE_128x128_SK) || L.tile == TILE_256x256_PP))
+        return MIGEMM_ERR_CONFIG;
+    if (!clocks) return MIGEMM_ERR_NULL;
+    if ((uintptr_t)clocks % 8) return MIGEMM_ERR_ALIGN;
+    const size_t cbytes = (size_t)M * N * 2, rbytes = (size_t)L.grid * 16;
+    if (overlaps(clocks, rbytes, A, (size_t)M * K * 2) || overlaps(clocks, rbytes, B, (size_t)K * N * 2) ||
+        overlaps(clocks, rbytes, C, cbytes))
+        return MIGEMM_ERR_OVERLAP;
+    L.clocks = clocks;
+    return finish(gemm_launch(L, (hipStream_t)stream), stream);
+}
+
 int gemm_f16(const uint16_t *A, const uint16_t *B, uint16_t *C, int M, int N, int K, void *stream)
 {
     return gemm_ex(DT_F16, A, B, C, M, N, K, TILE_AUTO, 0, 1, stream);
@@ -702,5 +722,15 @@ int migemm_hbm_read(const void *buf, size_t bytes, uint32_t *sink, void *stream)
 }
 
 int migemm_hbm_read_sink_words(void) { return hbm_read_sink_words(); }
+
+int migemm_clock_probe(uint64_t *out, int blocks, int iters, void *stream)
+{
+    if (blocks < 0 || iters < 0) return MIGEMM_ERR_DIM;
+    if (blocks == 0) return MIGEMM_OK;
+    if (blocks > 65535) return MIGEMM_ERR_SIZE;
+    if (!out) return MIGEMM_ERR_NULL;
+    if ((uintptr_t)out % 8) return MIGEMM_ERR_ALIGN;
+    return finish(clock_probe_launch(out, blocks, iters, (hipStream_t)stream), stream);
+}
 
 }  // extern "C"

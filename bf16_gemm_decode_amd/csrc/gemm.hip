@@ -570,6 +570,15 @@ gemm_fl_kernel(const uint16_t *__restrict__ A, const uint16_t *__restrict__ B,
     int pid_m, pid_n;
     tile_coord<int>((int)blockIdx.x, num_pid_m, num_pid_n, group_m, num_xcd, pid_m, pid_n);
     const int m0 = pid_m * BM, n0 = pid_n * BN;
+    // Measurement only (part is free when the k loop is not split): with
+    // part non-null, wave 0 of each workgroup records the shader-clock and
+    // 100 MHz real-time counts it ran for, as two 64-bit words per workgroup.
+    const bool clocked = !SPLIT && part != nullptr;
+    uint64_t clk_t0 = 0, clk_r0 = 0;
+    if (clocked) {
+        clk_t0 = __builtin_amdgcn_s_memtime();
+        clk_r0 = __builtin_amdgcn_s_memrealtime();
+    }
     const int lane = threadIdx.x & 63;
     const int wave = uniform(threadIdx.x >> 6);
     const int wm = wave % WGM, wn = wave / WGM;
@@ -1079,6 +1088,12 @@ gemm_fl_kernel(const uint16_t *__restrict__ A, const uint16_t *__restrict__ B,
             }
         }
     }
+    if (clocked && threadIdx.x == 0) {
+        const uint64_t t1 = __builtin_amdgcn_s_memtime(), r1 = __builtin_amdgcn_s_memrealtime();
+        uint64_t *rec = (uint64_t *)part + 2 * ((size_t)blockIdx.y * gridDim.x + blockIdx.x);
+        rec[0] = t1 - clk_t0;
+        rec[1] = r1 - clk_r0;
+    }
 }
 
 // OCC: waves per SIMD the kernel is compiled for (its register budget is
@@ -1109,7 +1124,7 @@ static hipError_t launch_fl(const GemmLaunch &L, hipStream_t stream)
     hipLaunchKernelGGL((gemm_fl_kernel<DT, AK, BM, BN, WGM, WGN, SA, SB, OC, false, PP, WIDE>),
                        dim3((unsigned)L.grid), block, 0, stream, L.A, L.B, L.C, L.M, L.N, L.K,
                        L.num_pid_m, L.num_pid_n, L.group_m, L.num_xcd, L.c_vec, L.scale, L.K & ~7,
-                       (float *)nullptr);
+                       (float *)L.clocks);
     return hipGetLastError();
 }
 

@@ -214,4 +214,27 @@ hipError_t hbm_read_launch(const void *buf, size_t bytes, uint32_t *sink, hipStr
     return hipGetLastError();
 }
 
+// Shader clock probe: each single-wave workgroup reads the shader-clock
+// counter (s_memtime) and the 100 MHz real-time counter (s_memrealtime)
+// around a dependent chain of `iters` FMAs and writes both elapsed counts;
+// their ratio is the clock the wave ran at.
+__global__ void __launch_bounds__(64) clock_probe_kernel(uint64_t *__restrict__ out, int iters)
+{
+    const uint64_t t0 = __builtin_amdgcn_s_memtime(), r0 = __builtin_amdgcn_s_memrealtime();
+    float x = (float)threadIdx.x;
+    for (int i = 0; i < iters; ++i) x = __builtin_fmaf(x, 0.999f, 1.0f);
+    const uint64_t t1 = __builtin_amdgcn_s_memtime(), r1 = __builtin_amdgcn_s_memrealtime();
+    if (threadIdx.x == 0) {
+        out[2 * blockIdx.x] = t1 - t0;
+        out[2 * blockIdx.x + 1] = r1 - r0;
+    }
+    if (x == -1.0f) out[0] = 0;   // keeps the chain (x stays positive)
+}
+
+hipError_t clock_probe_launch(uint64_t *out, int blocks, int iters, hipStream_t s)
+{
+    hipLaunchKernelGGL(clock_probe_kernel, dim3((unsigned)blocks), dim3(64), 0, s, out, iters);
+    return hipGetLastError();
+}
+
 }  // namespace migemm

@@ -101,6 +101,8 @@ struct GemmLaunch {
     int splits;                   // > 1: split-K over `splits` k slices of ks (full-line tiles)
     int ks;                       // slice length, a multiple of 64 (2-byte units)
     float *part;                  // split-K FP32 partials [splits][N][M]
+    uint64_t *clocks;             // measurement (full-line tiles, unsplit): per workgroup, shader
+                                  // clocks and 10 ns real-time ticks it ran for; nullptr = off
 };
 
 // Sum of split-K partials: C = round(sum_z part[z][n][m]) (gemm.hip).
@@ -168,5 +170,6 @@ hipError_t attention_launch(const AttentionLaunch &A, hipStream_t stream);
 
 hipError_t hbm_read_launch(const void *buf, size_t bytes, uint32_t *sink, hipStream_t stream);
 int hbm_read_sink_words();
+hipError_t clock_probe_launch(uint64_t *out, int blocks, int iters, hipStream_t stream);
 
 }  // namespace migemm

@@ -17,8 +17,8 @@ profiles/.
 The traffic mode averages FETCH_SIZE and WRITE_SIZE (KiB per dispatch) over
 the matching kernel's dispatches and scales each by what the same counter
 reads for the plain 1 GiB device copy of `bench.py --copy-calibration`
-(profiled with the same counter), so that hbm_bytes_per_launch is in true
-bytes.  It records a SHA-256 over the sources that decide what the kernel
+(profiled with the same counter), so that beyond_l2_bytes_per_launch (the
+requests that leave L2 for the MALL or HBM) is in true bytes.  It records a SHA-256 over the sources that decide what the kernel
 does (source_digest), so that a later change of them invalidates the figure.
 """
 import argparse
@@ -121,8 +121,10 @@ def traffic(args):
         out[counter.lower()] = {"kib_per_dispatch_raw": kib, "dispatches": len(vals),
                                 "copy_kib_raw": copy_kib, "scale_to_bytes": scale,
                                 "bytes_per_launch": kib * 1024.0 * scale}
-    out["hbm_bytes_per_launch"] = (out["fetch_size"]["bytes_per_launch"] +
-                                   out["write_size"]["bytes_per_launch"])
+    # FETCH_SIZE and WRITE_SIZE count the requests that leave L2 (served by
+    # the MALL or by HBM), not HBM transfers alone
+    out["beyond_l2_bytes_per_launch"] = (out["fetch_size"]["bytes_per_launch"] +
+                                         out["write_size"]["bytes_per_launch"])
     out["kernel_sources"] = args.source
     out["kernel_sources_sha256"] = source_digest(args.source)
     with open(args.out, "w") as o:

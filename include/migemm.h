@@ -375,6 +375,31 @@ int migemm_abi_version(void);
 int migemm_hbm_read(const void *buf, size_t bytes, uint32_t *sink, void *stream);
 int migemm_hbm_read_sink_words(void);
 
+/*
+ * Shader clock probe: `blocks` single-wave workgroups (up to 65535) each
+ * read the shader-clock counter and the 100 MHz real-time counter around a
+ * chain of `iters` dependent FMAs and write the two elapsed counts to
+ * out[2*b] and out[2*b + 1] (device, 8-byte aligned, 2 * blocks words).
+ * sum(out[2b]) / sum(out[2b+1]) * 100 MHz is the clock the GPU ran at; run
+ * right after a kernel on the same stream it gives the clock that kernel
+ * left the chip at.  Used to state measured rates against the measured
+ * clock as well as the nominal one.
+ */
+int migemm_clock_probe(uint64_t *out, int blocks, int iters, void *stream);
+
+/*
+ * gemm_ex that also records, for each workgroup, the shader-clock and
+ * 100 MHz real-time counts its wave 0 ran for: clocks[2*g] and
+ * clocks[2*g + 1] for workgroup g (device, 8-byte aligned, 2 * grid words,
+ * grid as migemm_gemm_plan_for reports).  sum(clocks[2g]) /
+ * sum(clocks[2g+1]) * 100 MHz is the clock the GEMM itself ran at (the
+ * chip lowers it under load within microseconds, so a probe after the
+ * kernel would not see it).  Full-line tiles only (MIGEMM_ERR_CONFIG
+ * otherwise); C is computed exactly as by gemm_ex.  For measurement.
+ */
+int migemm_gemm_clocked(int dtype, const uint16_t *A, const uint16_t *B, uint16_t *C, int M, int N,
+                        int K, int tile, int group_m, int xcd_remap, uint64_t *clocks, void *stream);
+
 #ifdef __cplusplus
 }
 #endif

@@ -66,6 +66,8 @@ def lib():
                                   ctypes.c_int, ctypes.c_int, ctypes.c_int]
         L.oracle_grouped_tile.restype = None
         L.oracle_grouped_tile.argtypes = [ctypes.c_int64] * 4 + [i64p, i64p]
+        L.oracle_set_threads.restype = ctypes.c_int
+        L.oracle_set_threads.argtypes = [ctypes.c_int]
         L.oracle_grouped_order.restype = None
         L.oracle_grouped_order.argtypes = [ctypes.c_int64] * 3 + [i64p, i64p]
         i32p = ctypes.POINTER(ctypes.c_int32)
@@ -282,6 +284,12 @@ def grouped_tile(pid, num_pid_m, num_pid_n, group_m):
     lib().oracle_grouped_tile(pid, num_pid_m, num_pid_n, group_m,
                               ctypes.byref(pm), ctypes.byref(pn))
     return pm.value, pn.value
+
+
+def set_threads(n):
+    """OpenMP threads for the oracle's loops from now on (results do not
+    depend on it); returns the previous count."""
+    return lib().oracle_set_threads(int(n))
 
 
 def grouped_order(num_pid_m, num_pid_n, group_m):

@@ -39,6 +39,7 @@
 #include <string.h>
 #include <stdlib.h>
 #include <fenv.h>
+#include <omp.h>
 
 #define ORACLE_FP16 0
 #define ORACLE_BF16 1
@@ -466,3 +467,15 @@ void oracle_attention_segmented(int fmt, const uint16_t *Q, const uint16_t *Kc, 
 }
 
 int oracle_abi_version(void) { return 3; }
+
+/* ---- threads ------------------------------------------------------------- */
+
+/* Number of OpenMP threads the oracle's loops use from now on (n >= 1); the
+ * result of every function is the same for any count, only its time
+ * changes.  Returns the count in force before the call. */
+int oracle_set_threads(int n)
+{
+    const int before = omp_get_max_threads();
+    if (n >= 1) omp_set_num_threads(n);
+    return before;
+}

@@ -49,7 +49,7 @@ def test_traffic_scales_by_the_copy_reading(tmp_path):
     assert t["fetch_size"]["dispatches"] == 2
     assert t["fetch_size"]["bytes_per_launch"] == pytest.approx(2000.0 * 1024 * 2.0)
     assert t["write_size"]["bytes_per_launch"] == pytest.approx(100.0 * 1024)
-    assert t["hbm_bytes_per_launch"] == pytest.approx(2000.0 * 2048 + 100.0 * 1024)
+    assert t["beyond_l2_bytes_per_launch"] == pytest.approx(2000.0 * 2048 + 100.0 * 1024)
     assert t["kernel_sources_sha256"] == ps.source_digest(["gemm.hip", "common.hpp"])
 
 
@@ -99,7 +99,7 @@ def test_bench_reports_counters_only_for_unchanged_sources(tmp_path, monkeypatch
     srcs = ["gemm.hip", "common.hpp"]
     prof = tmp_path / "profiles"
     prof.mkdir()
-    good = {"kernel_sources": srcs, "kernel_sources_sha256": ps.source_digest(srcs), "hbm_bytes_per_launch": 7.0,
+    good = {"kernel_sources": srcs, "kernel_sources_sha256": ps.source_digest(srcs), "beyond_l2_bytes_per_launch": 7.0,
             "kernels": {"k": {"mfma_util_percent": {"mean": 12.345}}}}
     stale = dict(good, kernel_sources_sha256="0" * 64)
     (prof / "good.json").write_text(json.dumps(good))
