@@ -151,19 +151,21 @@ int plan_gemm(int dtype, const uint16_t *A, const uint16_t *B, const uint16_t *C
         // rows, the few-token kernels
         if (!fl) return MIGEMM_ERR_ALIGN;
         if (tile == TILE_AUTO) {
-            tile = wide && N <= kSkinnyAutoMax ? TILE_SKINNY
-                   : wide && N <= kBatchAutoMax ? TILE_BATCH
-                                                : auto_tile();
+            tile = wide && batch_rows_auto(M, N) ? TILE_BATCH_ROWS
+                   : wide && N <= kSkinnyAutoMax ? TILE_SKINNY
+                   : wide && N <= kBatchAutoMax  ? TILE_BATCH
+                                                 : auto_tile();
         } else if ((tile < TILE_256x256_FL) || tile == TILE_256x256_PP ||
                    (tile == TILE_SKINNY && N > kSkinnyMaxTokens) ||
-                   (tile == TILE_BATCH && N > kBatchMaxTokens)) {
+                   (tile == TILE_BATCH && N > kBatchMaxTokens) ||
+                   (tile == TILE_BATCH_ROWS && N > kBatchRowsMaxTokens)) {
             return MIGEMM_ERR_CONFIG;
         } else if (!wide && !is_fl(tile)) {
             return MIGEMM_ERR_ALIGN;
         }
     } else if (tile == TILE_AUTO) {
         tile = auto_tile();
-    } else if (tile == TILE_SKINNY || tile == TILE_BATCH) {
+    } else if (is_decode_tile(tile)) {
         return MIGEMM_ERR_CONFIG;   // only with a k-major A (gemm_tn_ex)
     } else if (tile != TILE_128x128 && !(wide || (fl && is_fl(tile)))) {
         return MIGEMM_ERR_CONFIG;   // the other tiles load 16-byte (full-line: 4-byte aligned) rows
@@ -174,6 +176,10 @@ int plan_gemm(int dtype, const uint16_t *A, const uint16_t *B, const uint16_t *C
     if (tile == TILE_BATCH) {
         bm = batch_tile_m(N);
         bn = batch_tile_n(N);
+    }
+    if (tile == TILE_BATCH_ROWS) {
+        bm = batch_rows_per_workgroup(M);
+        bn = batch_rows_tile_n(N);
     }
     const int64_t pm = cdiv(M, bm), pn = cdiv(N, bn);
     if (pm * pn > 0x7fffffff) return MIGEMM_ERR_SIZE;
@@ -186,6 +192,17 @@ int plan_gemm(int dtype, const uint16_t *A, const uint16_t *B, const uint16_t *C
     L.grid = pm * pn;
     launch = (M > 0 && N > 0);
     return MIGEMM_OK;
+}
+
+// Y = X W^T on one of the decode kernels: W = At, X = B, Y = C (all
+// row-major), the product gemm_tn computes
+hipError_t decode_launch(int tile, int dtype, const uint16_t *At, const uint16_t *B, uint16_t *C,
+                         int M, int N, int K, int c_vec, hipStream_t stream)
+{
+    SkinnyLaunch S{dtype, At, B, C, M, K, N, c_vec};
+    return tile == TILE_SKINNY ? skinny_launch(S, stream)
+           : tile == TILE_BATCH ? batch_launch(S, stream)
+                                : batch_rows_launch(S, stream);
 }
 
 int finish(hipError_t e, void *stream)
@@ -250,13 +267,10 @@ int gemm_tn_ex(int dtype, const uint16_t *At, const uint16_t *B, uint16_t *C, in
     bool launch;
     int rc = plan_gemm(dtype, At, B, C, M, N, K, tile, group_m, xcd_remap, L, launch, true);
     if (rc != MIGEMM_OK || !launch) return rc;
-    if (L.tile == TILE_SKINNY || L.tile == TILE_BATCH) {
+    if (is_decode_tile(L.tile))
         // C(m,n) = sum_k At[k + m*K] B[k + n*K] is Y = X W^T with W = At,
-        // X = B, Y = C, all row-major: the skinny and batch kernels' contract
-        SkinnyLaunch S{dtype, At, B, C, M, K, N, L.c_vec};
-        return finish((L.tile == TILE_SKINNY ? skinny_launch : batch_launch)(S, (hipStream_t)stream),
-                      stream);
-    }
+        // X = B, Y = C, all row-major: the decode kernels' contract
+        return finish(decode_launch(L.tile, dtype, At, B, C, M, N, K, L.c_vec, (hipStream_t)stream), stream);
     return finish(gemm_launch(L, (hipStream_t)stream), stream);
 }
 
@@ -341,11 +355,8 @@ int gemm_splitk_ex(int dtype, int a_kmajor, const uint16_t *A, const uint16_t *B
             e = splitk_reduce_launch(dtype, L.part, C, (int64_t)M * N, S_eff, (hipStream_t)stream);
         return finish(e, stream);
     }
-    if (L.tile == TILE_SKINNY || L.tile == TILE_BATCH) {
-        SkinnyLaunch Sk{dtype, A, B, C, M, K, N, L.c_vec};
-        return finish((L.tile == TILE_SKINNY ? skinny_launch : batch_launch)(Sk, (hipStream_t)stream),
-                      stream);
-    }
+    if (is_decode_tile(L.tile))
+        return finish(decode_launch(L.tile, dtype, A, B, C, M, N, K, L.c_vec, (hipStream_t)stream), stream);
     return finish(gemm_launch(L, (hipStream_t)stream), stream);
 }
 
@@ -415,6 +426,21 @@ static int plan_for(int dtype, const uint16_t *A, const uint16_t *B, const uint1
         plan->a_kmajor = 1;
         return rc;
     }
+    if (L.tile == TILE_BATCH_ROWS) {
+        plan->tile_m = batch_rows_per_workgroup(M);   // rows per workgroup (9 waves of 16)
+        plan->tile_n = batch_rows_tile_n(N);
+        plan->tile_k = 64;
+        plan->waves = 9;
+        plan->group_m = 1;
+        plan->xcd_remap = 0;
+        plan->vec_a = L.vec_a;
+        plan->vec_b = L.vec_b;
+        plan->grid = launch ? L.grid : 0;
+        plan->lds_bytes = batch_rows_lds_bytes(N);
+        plan->tile = L.tile;
+        plan->a_kmajor = 1;
+        return rc;
+    }
     if (L.tile == TILE_BATCH) {
         plan->tile_m = batch_tile_m(N);         // waves x 16 rows
         plan->tile_n = batch_tile_n(N);
@@ -475,13 +501,16 @@ static int plan_gemv(const uint16_t *W, const uint16_t *X, const uint16_t *Y, in
     if (overlaps(Y, ybytes, W, wbytes) || overlaps(Y, ybytes, X, xbytes)) return MIGEMM_ERR_OVERLAP;
     if (M == 0 || n == 0) return MIGEMM_OK;
     const bool vec = (K % 8 == 0 && (uintptr_t)W % 16 == 0 && (uintptr_t)X % 16 == 0);
-    // Y = X W^T is gemm_tn with At = W, B = X, C = Y (all row-major): up to
+    // Y = X W^T is gemm_tn with At = W, B = X, C = Y (all row-major): the
+    // row-balanced kernel where batch_rows_auto says so, else up to
     // kSkinnyAutoMax tokens on the 4x4x4 MFMA kernel, up to kBatchAutoMax on
     // the 16x16x32 batch kernel, more on the full-line 256x128 tile within
     // the GEMM's own size limits; everything else on the vector kernel
     const bool gemm_fits = M <= MIGEMM_MAX_MN && K <= MIGEMM_MAX_K;
     route = 1;
-    if (rows_per_block == 0 && vec && n >= kSkinnyMinTokens)
+    if (rows_per_block == 0 && vec && batch_rows_auto(M, n))
+        route = TILE_BATCH_ROWS;
+    else if (rows_per_block == 0 && vec && n >= kSkinnyMinTokens)
         route = n <= kSkinnyAutoMax ? TILE_SKINNY
                 : n <= kBatchAutoMax ? TILE_BATCH
                 : gemm_fits ? TILE_256x128_FL : 1;
@@ -505,11 +534,10 @@ int gemv_bf16_ex(const uint16_t *W, const uint16_t *X, uint16_t *Y, int M, int K
     if (rc != MIGEMM_OK || route == 0) return rc;
     if (route == TILE_256x128_FL)
         return gemm_tn_ex(DT_BF16, W, X, Y, M, n, K, TILE_256x128_FL, 0, 1, stream);
-    if (route == TILE_SKINNY || route == TILE_BATCH) {
-        SkinnyLaunch S{DT_BF16, W, X, Y, M, K, n, (M % 4 == 0 && (uintptr_t)Y % 8 == 0) ? 1 : 0};
-        return finish((route == TILE_BATCH ? batch_launch : skinny_launch)(S, (hipStream_t)stream),
+    if (is_decode_tile(route))
+        return finish(decode_launch(route, DT_BF16, W, X, Y, M, n, K,
+                                    (M % 4 == 0 && (uintptr_t)Y % 8 == 0) ? 1 : 0, (hipStream_t)stream),
                       stream);
-    }
     const bool vec = (K % 8 == 0 && (uintptr_t)W % 16 == 0 && (uintptr_t)X % 16 == 0);
 
     GemvLaunch L{};

@@ -25,6 +25,7 @@ enum GemmTile {
     TILE_BATCH = 15,            // 9..128 columns: W into 16x16x32 MFMA registers, X in LDS (batch.hip)
     TILE_256x256_PP = 16,       // as 10, m-major A, ping-pong: the two waves of a SIMD alternate MFMA and memory phases
     TILE_256x128_F8W = 17,      // FP8 only, k-major A: 256x128, 8 waves of 64x64, whole 64-unit steps on the 16x16x128 MFMA
+    TILE_BATCH_ROWS = 18,       // up to 256 columns: W's rows spread evenly, 9 waves of 16 rows per workgroup (batch.hip)
     TILE_COUNT
 };
 
@@ -54,6 +55,7 @@ constexpr TileShape kTileShapes[TILE_COUNT] = {
     {64, 128, 128, 0, 4, 0},
     {256, 256, 32, 4, 8, 3},
     {256, 128, 32, 3, 8, 3},
+    {144, 256, 64, 0, 9, 0},
 };
 
 // The full-line tiles with A k-major: stages = A ring stages of 64 k.
@@ -76,6 +78,7 @@ constexpr TileShape kTileShapesKmajorA[TILE_COUNT] = {
     {64, 128, 128, 0, 4, 0},
     {0, 0, 0, 0, 0, 0},
     {256, 128, 32, 3, 8, 3},
+    {144, 256, 64, 0, 9, 0},
 };
 
 constexpr int tile_lds_bytes(const TileShape &t, bool a_kmajor = false)
@@ -144,6 +147,31 @@ struct SkinnyLaunch {
 
 hipError_t skinny_launch(const SkinnyLaunch &L, hipStream_t stream);
 hipError_t batch_launch(const SkinnyLaunch &L, hipStream_t stream);
+// Row-balanced batch kernel (batch.hip): W's rows spread evenly over the
+// workgroups, 9 waves of 16 rows each, up to kBatchRowsMaxTokens tokens.
+constexpr int kBatchRowsMaxTokens = 256;
+// Automatic choice for 2 .. 128 tokens (measured on W 34816 x 5120, 16384 x
+// 4096 and 4096 x 4096): the row-balanced kernel once its workgroups hold
+// 64 rows or more (M >= 16384; 54 us against 58-65 us for 2-16 tokens and 64
+// against 92 us for 64 tokens on 34816 x 5120), and from 33 tokens on for any
+// M (4096 x 4096, 64 tokens: 20 against 28 us).  Above 128 tokens the GEMM's
+// tiles do as well or better.
+constexpr int kBatchRowsAutoMax = 128;
+constexpr int kBatchRowsAutoMinM = 16384;
+constexpr int kBatchRowsAutoAnyM = 33;
+constexpr bool batch_rows_auto(int M, int n)
+{
+    return n >= 2 && n <= kBatchRowsAutoMax && (M >= kBatchRowsAutoMinM || n >= kBatchRowsAutoAnyM);
+}
+hipError_t batch_rows_launch(const SkinnyLaunch &L, hipStream_t stream);
+int batch_rows_per_workgroup(int M);
+// token columns of one row-balanced workgroup (16, 32, 64, 128, 256) and its
+// LDS: two staged 64-k chunks of X (token rows of 144 bytes) and the 9
+// waves' 2 KB areas that re-lay W out
+constexpr int batch_rows_tile_n(int n) { return n <= 16 ? 16 : n <= 32 ? 32 : n <= 64 ? 64 : n <= 128 ? 128 : 256; }
+constexpr int batch_rows_lds_bytes(int n) { return 2 * batch_rows_tile_n(n) * 144 + 9 * 2048; }
+// the kernels above that take Y = X W^T directly (gemm_tn with At = W, B = X)
+constexpr bool is_decode_tile(int t) { return t == TILE_SKINNY || t == TILE_BATCH || t == TILE_BATCH_ROWS; }
 // token columns of one batch-kernel workgroup for n tokens (16, 32, 64, 128)
 constexpr int batch_tile_n(int n) { return n <= 16 ? 16 : n <= 32 ? 32 : n <= 64 ? 64 : 128; }
 // its waves (16 rows of W each): 2 for one 16-token block (finer workgroups

@@ -81,16 +81,18 @@ int gemm_bf16(const uint16_t *A, const uint16_t *B, uint16_t *C,
  *
  * W and X are read only.  n == 0 or M == 0 returns 0 without a launch;
  * K == 0 writes +0.0 to Y.  Errors as for the GEMM (Y must not overlap W, X).
- * n may be any positive value.  n <= 2 (or K not a multiple of 8, or W, X
- * not 16-byte aligned) runs the row-blocked vector kernel; from 3 tokens on,
- * with 16-byte rows, the multiply-adds run on MFMA: up to 4 tokens on the
- * 4x4x4 MFMA with W streamed straight into operand registers, up to 64 on
- * the 16x16x32 MFMA with W read as whole cache lines and the token block of
- * X staged in LDS (tile 15 below), beyond that as gemm_tn_bf16 on the
- * 256x128 full-line tile while M and K are within the GEMM's limits
- * (MIGEMM_MAX_MN, MIGEMM_MAX_K; larger problems take the vector kernel).
- * gemv_bf16_ex with a non-zero rows_per_block always runs the vector
- * kernel.  migemm_gemv_plan_for reports the choice.
+ * n may be any positive value.  One token (or K not a multiple of 8, or W,
+ * X not 16-byte aligned) runs the row-blocked vector kernel.  With 16-byte
+ * rows the multiply-adds of 2 .. 128 tokens run on the row-balanced 16x16x32
+ * MFMA kernel (tile 18 below: W's rows cut evenly over the CUs) when M >=
+ * 16384, or from 33 tokens on for any M; otherwise 2 tokens take the vector
+ * kernel, 3 or 4 the 4x4x4 MFMA with W streamed straight into operand
+ * registers, up to 64 the 16x16x32 MFMA with W read as whole cache lines and
+ * the token block of X staged in LDS (tile 15 below), and beyond that
+ * gemm_tn_bf16 on the 256x128 full-line tile while M and K are within the
+ * GEMM's limits (MIGEMM_MAX_MN, MIGEMM_MAX_K; larger problems take the
+ * vector kernel).  gemv_bf16_ex with a non-zero rows_per_block always runs
+ * the vector kernel.  migemm_gemv_plan_for reports the choice.
  */
 int gemv_bf16(const uint16_t *W, const uint16_t *X, uint16_t *Y,
               int M, int K, int n, void *stream);
@@ -246,7 +248,11 @@ size_t migemm_splitk_workspace_bytes(int M, int N, int splits);
  *            shape, rings and layouts with the ping-pong schedule (the two
  *            waves of each SIMD alternate a load phase and an MFMA phase;
  *            gemm_ex only, not split-K); 17 = the FP8 double-rate tile
- *            (gemm_tn_q_ex only).
+ *            (gemm_tn_q_ex only); 18 = the row-balanced batch kernel
+ *            (gemm_tn_* only, N <= 256: W's rows spread evenly over the
+ *            workgroups, about M / 256 each rounded up to a multiple of 8 and
+ *            at most 144, 9 waves of 16 rows, 16..256 columns, K in steps of
+ *            64, A read as whole lines through LDS, B staged in LDS).
  *            All step K by 32.  Tiles 1, 2, 4, 5, 6 need 16-byte rows (M and
  *            K multiples of 8, A and B 16-byte aligned); the full-line tiles
  *            7 .. 13 and 16 need 4-byte rows (M and K even, A and B 4-byte
@@ -271,13 +277,15 @@ int gemm_ex(int dtype, const uint16_t *A, const uint16_t *B, uint16_t *C,
  * DCU decode page's Y = X W^T (section 6.1) for a batch of N token rows,
  * with Y row-major [N, M] -- the GEMV's own layout.  Same argument checks,
  * ownership and completion rules as gemm_f16 / gemm_bf16.  Runs on the
- * full-line tiles only: tile 0 (automatic: 14 for N <= 4, 15 for
- * N <= 64, else the least estimated time among 10, 9 and 13) or 7 .. 15
- * (A takes B's 64-k ring layout; MIGEMM_ERR_CONFIG for other tiles, 16 and
- * 17 included, and
- * for 14 with N > 8 or 15 with N > 128).  K even and At, B 4-byte aligned
- * (4-byte rows) for tiles 7 .. 13, K a multiple of 8 and At, B 16-byte
- * aligned for 14 and 15 (which tile 0 then uses); else MIGEMM_ERR_ALIGN.
+ * full-line and decode tiles only: tile 0 (automatic, with 16-byte rows:
+ * 18 for 2 <= N <= 128 when M >= 16384 or N >= 33, else 14 for N <= 4, 15
+ * for N <= 64; beyond that, or with 4-byte rows, the least estimated time
+ * among 10, 9 and 13) or 7 .. 15 and 18 (A takes B's 64-k ring layout;
+ * MIGEMM_ERR_CONFIG for other tiles, 16 and 17 included, and for 14 with
+ * N > 8, 15 with N > 128 or 18 with N > 256).  K even and At, B 4-byte
+ * aligned (4-byte rows) for tiles 7 .. 13, K a multiple of 8 and At, B
+ * 16-byte aligned for 14, 15 and 18 (which tile 0 then uses); else
+ * MIGEMM_ERR_ALIGN.
  */
 int gemm_tn_f16(const uint16_t *At, const uint16_t *B, uint16_t *C,
                 int M, int N, int K, void *stream);
@@ -348,7 +356,8 @@ int migemm_gemm_tn_plan_for(int dtype, const uint16_t *At, const uint16_t *B,
 /* Which kernel gemv_bf16_ex would run for these arguments (pointers are
  * inspected for alignment only, never dereferenced): writes to *route 0 (no
  * launch: M or n is 0), 1 (the row-blocked vector kernel), 14 (the 4x4x4
- * MFMA kernel), 15 (the batch kernel) or 9 (gemm_tn on the 256x128
+ * MFMA kernel), 15 (the batch kernel), 18 (the row-balanced batch kernel)
+ * or 9 (gemm_tn on the 256x128
  * full-line tile; only while M <= MIGEMM_MAX_MN and K <= MIGEMM_MAX_K,
  * larger problems stay on the vector kernel), and returns the code
  * gemv_bf16_ex would return for the argument checks. */

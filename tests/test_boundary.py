@@ -110,9 +110,9 @@ def test_tn_plan_and_errors():
     code, p = binding.gemm_plan(1, P, P + 2 ** 30, P + 2 ** 31, 34816, 8, 5120, 14, a_kmajor=True)
     assert code == 0 and (p["tile"], p["tile_m"], p["tile_n"], p["waves"], p["grid"]) == (14, 32, 8, 4, 1088)
     assert binding.gemm_plan(1, P, P + 2 ** 30, P + 2 ** 31, 34816, 5, 5120, 14, a_kmajor=True)[1]["tile_n"] == 8
-    code, p = binding.gemm_plan(1, P, P + 2 ** 30, P + 2 ** 31, 34816, 4, 5120, a_kmajor=True)
-    assert code == 0 and (p["tile"], p["tile_n"]) == (14, 4)          # automatic up to 4 columns
-    assert binding.gemm_plan(1, P, P + 2 ** 30, P + 2 ** 31, 34816, 5, 5120, a_kmajor=True)[1]["tile"] == 15
+    code, p = binding.gemm_plan(1, P, P + 2 ** 30, P + 2 ** 31, 4096, 4, 5120, a_kmajor=True)
+    assert code == 0 and (p["tile"], p["tile_n"]) == (14, 4)          # automatic up to 4 columns (M < 16384)
+    assert binding.gemm_plan(1, P, P + 2 ** 30, P + 2 ** 31, 4096, 5, 5120, a_kmajor=True)[1]["tile"] == 15
     assert L.gemm_tn_ex(0, P, P + 0x100000, P + 0x200000, 64, 9, 64, 14, 0, 1, None) == -5
     assert L.gemm_ex(0, P, P + 0x100000, P + 0x200000, 64, 16, 64, 14, 0, 1, None) == -5
     # the batch tile: 9 .. 128 columns, token blocks of 16 .. 128; 2 waves
@@ -122,8 +122,24 @@ def test_tn_plan_and_errors():
         w = 2 if tn == 16 else 4
         assert code == 0 and (p["tile"], p["tile_m"], p["tile_n"], p["tile_k"], p["waves"]) == (15, 16 * w, tn, 128, w)
         assert p["grid"] == 34816 // (16 * w) and p["lds_bytes"] == 2 * tn * 272 + w * 4096
-    assert binding.gemm_plan(1, P, P + 2 ** 30, P + 2 ** 31, 34816, 64, 5120, a_kmajor=True)[1]["tile"] == 15
-    assert binding.gemm_plan(1, P, P + 2 ** 30, P + 2 ** 31, 34816, 65, 5120, a_kmajor=True)[1]["tile"] == 9
+    assert binding.gemm_plan(1, P, P + 2 ** 30, P + 2 ** 31, 4096, 32, 5120, a_kmajor=True)[1]["tile"] == 15
+    assert binding.gemm_plan(1, P, P + 2 ** 30, P + 2 ** 31, 34816, 129, 5120, a_kmajor=True)[1]["tile"] == 10
+    # the row-balanced tile: W's rows cut into 256 equal parts, rounded up to
+    # a multiple of 8 and capped at 144 (9 waves of 16); token blocks of
+    # 16 .. 256; automatic for 2 .. 128 columns once M >= 16384, and from 33
+    # columns for any M
+    for M, R in ((34816, 136), (16384, 64), (2051, 16), (100, 8), (36864, 144), (40000, 144)):
+        for n, tn in ((1, 16), (17, 32), (64, 64), (65, 128), (129, 256), (256, 256)):
+            code, p = binding.gemm_plan(1, P, P + 2 ** 30, P + 2 ** 31, M, n, 5120, 18, a_kmajor=True)
+            assert code == 0 and (p["tile"], p["tile_m"], p["tile_n"], p["tile_k"], p["waves"]) == (18, R, tn, 64, 9)
+            assert p["grid"] == -(-M // R) and p["lds_bytes"] == 2 * tn * 144 + 9 * 2048
+    for M, n, want in ((34816, 1, 14), (34816, 2, 18), (34816, 4, 18), (34816, 128, 18), (34816, 129, 10),
+                       (16384, 2, 18), (16383, 2, 14), (4096, 32, 15), (4096, 33, 18), (4096, 128, 18),
+                       (64, 33, 18)):
+        code, p = binding.gemm_plan(1, P, P + 2 ** 30, P + 2 ** 31, M, n, 5120, a_kmajor=True)
+        assert code == 0 and p["tile"] == want, (M, n, p["tile"])
+    assert L.gemm_tn_ex(0, P, P + 0x100000, P + 0x200000, 64, 257, 64, 18, 0, 1, None) == -5
+    assert L.gemm_ex(0, P, P + 0x100000, P + 0x200000, 64, 16, 64, 18, 0, 1, None) == -5
     assert L.gemm_tn_ex(0, P, P + 0x100000, P + 0x200000, 64, 129, 64, 15, 0, 1, None) == -5
     assert L.gemm_ex(0, P, P + 0x100000, P + 0x200000, 64, 16, 64, 15, 0, 1, None) == -5
     # only the full-line tiles take a k-major A
@@ -343,13 +359,18 @@ def test_gemv_route():
     # rows_per_block keeps the vector kernel; beyond the GEMM's size limits
     # many tokens stay on the vector kernel instead of failing
     W, X, Y = P, P + (1 << 36), P + (1 << 37)
-    for n, want in ((1, 1), (2, 1), (3, 14), (4, 14), (5, 15), (64, 15), (65, 9), (1000, 9)):
+    for n, want in ((1, 1), (2, 18), (3, 18), (4, 18), (5, 18), (64, 18), (128, 18), (129, 9), (1000, 9)):
         assert binding.gemv_route(W, X, Y, 34816, 5120, n) == (0, want), n
+    for n, want in ((1, 1), (2, 1), (3, 14), (4, 14), (5, 15), (32, 15), (33, 18), (128, 18), (129, 9)):
+        assert binding.gemv_route(W, X, Y, 4096, 4096, n) == (0, want), n
+    assert binding.gemv_route(W, X, Y, 16384, 4096, 2) == (0, 18)
+    assert binding.gemv_route(W, X, Y, 16376, 4096, 2) == (0, 1)
     assert binding.gemv_route(W, X, Y, 34816, 5120, 16, rows_per_block=8) == (0, 1)
     assert binding.gemv_route(W, X, Y, 34816, 5122, 16) == (0, 1)          # K % 8: no MFMA route
-    assert binding.gemv_route(W, X, Y, (1 << 23) + 64, 8, 65) == (0, 1)     # M past the GEMM limit
-    assert binding.gemv_route(W, X, Y, 64, (1 << 21) + 8, 65) == (0, 1)     # K past the GEMM limit
-    assert binding.gemv_route(W, X, Y, (1 << 23) + 64, 8, 64) == (0, 15)
+    assert binding.gemv_route(W, X, Y, (1 << 23) + 64, 8, 129) == (0, 1)    # M past the GEMM limit
+    assert binding.gemv_route(W, X, Y, 64, (1 << 21) + 8, 129) == (0, 1)    # K past the GEMM limit
+    assert binding.gemv_route(W, X, Y, (1 << 23) + 64, 8, 128) == (0, 18)
+    assert binding.gemv_route(W, X, Y, 100, 8, 64) == (0, 18)
     assert binding.gemv_route(W, X, Y, 0, 8, 4) == (0, 0)
     assert binding.gemv_route(W, X, Y, 8, 8, -1)[0] == -1
     assert binding.gemv_route(W, X, W + 2, 8, 8, 1)[0] == -3               # Y over W

@@ -140,9 +140,17 @@ def _sampled_case(name, extra_strips=False):
     rep = assert_parity(got[idx], ref, fmt, name + " samples")
     print(name, "samples", idx.size, "max err/bound", rep["max_ratio"])
     if extra_strips:
-        # every element of the last partial row block and column block
-        m_last = np.arange(M - M % 128 if M % 128 else M - 128, M)
-        n_last = np.arange(N - N % 128 if N % 128 else N - 128, N)
+        # every element of the last partial row block and column block of
+        # the tile the automatic plan launches (256 x 256 here: 136 rows and
+        # 184 columns at 5000 x 3000)
+        from bf16_gemm_decode_amd import binding
+        code, plan = binding.gemm_plan(binding.F16 if fmt == "f16" else binding.BF16, 1 << 20, 1 << 21,
+                                       1 << 40, M, N, K)
+        assert code == 0, code
+        tm, tn = plan["tile_m"], plan["tile_n"]
+        m_last = np.arange(M - (M % tm or tm), M)
+        n_last = np.arange(N - (N % tn or tn), N)
+        print(name, "tile", plan["tile"], "last blocks", m_last.size, "rows,", n_last.size, "columns", flush=True)
         rows = (m_last[:, None] + np.arange(N)[None, :] * M).ravel()
         cols = (np.arange(M)[:, None] + n_last[None, :] * M).ravel()
         strip = np.unique(np.concatenate([rows, cols]))

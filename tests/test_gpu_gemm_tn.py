@@ -2,7 +2,8 @@
 the C ABI against the CPU oracle, which takes the same matrix column-major:
 every element at small sizes, K tails inside a 64-k stage, ragged M and N,
 bit-identical agreement with gemm_ex on the same tile (same MFMA order), and
-the DCU page's Y = X W^T in its own row-major layout for a batch of tokens."""
+the DCU page's Y = X W^T in its own row-major layout for a batch of tokens,
+and the decode tiles (14, 15, 18) at their token blocks and ragged edges."""
 import numpy as np
 import pytest
 
@@ -146,6 +147,34 @@ def test_batch_matches_exact_integers():
         want = oracle.gemm(kmajor_to_colmajor(At, M, K), B, M, N, K, fmt).bits
         got, _, _ = gemm_tn_gpu(At, B, M, N, K, fmt, tile=15)
         assert np.array_equal(got, want), fmt
+
+
+@pytest.mark.parametrize("fmt", FMTS)
+def test_batch_rows_tile_token_blocks_and_ragged_edges(fmt):
+    # tile 18 (W's rows cut evenly over the workgroups, R = ceil(M / 256)
+    # rounded up to 8 and capped at 144, 9 waves of 16 rows; 64-wide k
+    # chunks, 2 to 8 in flight and the chunk count padded to that): every
+    # token-block width (16 .. 256) with ragged token counts, workgroups of 8
+    # rows (one wave, half live), of a few waves and of all 9, more than one
+    # workgroup per CU (M > 36864), ragged last workgroups, K tails inside a
+    # chunk, K shorter than one chunk
+    for (M, N, K) in [(100, 2, 64), (37, 17, 40), (2051, 33, 520), (300, 64, 264), (20000, 65, 136),
+                      (36000, 128, 72), (40000, 129, 64), (1000, 256, 200), (9, 200, 5120),
+                      (2051, 1, 5120), (130, 255, 1160), (16400, 16, 8), (36871, 3, 584)]:
+        print("case batch rows", M, N, K, fmt, flush=True)
+        _tn_case(M, N, K, fmt, seed=3000 + M + N + K, tile=18)
+
+
+def test_batch_rows_matches_exact_integers():
+    rng = np.random.default_rng(31)
+    for M, N, K in ((520, 77, 1032), (4100, 250, 200), (33000, 8, 648)):
+        for fmt in FMTS:
+            print("case batch rows exact", M, N, K, fmt, flush=True)
+            At = synth.to_bits(synth.small_ints(rng, M * K, -3, 3), fmt)
+            B = synth.to_bits(synth.small_ints(rng, K * N, -3, 3), fmt)
+            want = oracle.gemm(kmajor_to_colmajor(At, M, K), B, M, N, K, fmt).bits
+            got, _, _ = gemm_tn_gpu(At, B, M, N, K, fmt, tile=18)
+            assert np.array_equal(got, want), (M, N, K, fmt)
 
 
 def test_tn_is_the_decode_product_for_a_token_batch():

@@ -1,7 +1,8 @@
 """GPU parity of gemv_bf16 (through the C ABI) against the CPU oracle:
-every element of the 34816 x 5120 decode shape at n = 1, 4, 16, ragged
-shapes and token counts, the one-hot exact case, agreement with the GEMM
-at n = 1, and bit-identical results across rows_per_block."""
+every element of the 34816 x 5120 decode shape at n = 1, 4, 16, sampled rows
+(all tokens) at n = 2, 64, 128, ragged shapes and token counts on every
+automatic route, the one-hot exact case, agreement with the GEMM at n = 1,
+and bit-identical results across rows_per_block."""
 import numpy as np
 import pytest
 
@@ -29,12 +30,18 @@ def test_small_shapes():
 
 
 def test_ragged_shapes_and_token_counts():
-    # n <= 2 the vector kernel, 3..8 the 4x4x4 MFMA kernel, more the
-    # full-line GEMM tile (K a multiple of 8); K % 8 != 0 always the vector one
+    # with K a multiple of 8 and M < 16384: 1 and 2 tokens the vector
+    # kernel, 3 and 4 the 4x4x4 MFMA kernel, 5..32 the batch kernel, 33..128
+    # the row-balanced kernel, more the full-line GEMM tile; K % 8 != 0
+    # always the vector kernel (gemv_route reports each choice)
+    from bf16_gemm_decode_amd import binding
+    seen = set()
     for (M, K) in [(7, 13), (100, 512), (129, 1031), (1000, 5120), (77, 5128), (31, 4096)]:
-        for n in (1, 2, 3, 4, 5, 8, 9, 16, 17, 33):
+        for n in (1, 2, 3, 4, 5, 8, 9, 16, 17, 33, 130):
+            seen.add(binding.gemv_route(1 << 20, 1 << 30, 1 << 40, M, K, n)[1])
             print("case", M, K, n, flush=True)
             _case(M, K, n, seed=M * 7 + K + n)
+    assert seen == {1, 9, 14, 15, 18}, seen
 
 
 @pytest.mark.parametrize("n", [1, 4, 16])
@@ -42,6 +49,27 @@ def test_decode_shape_full(n):
     w = synth.WORKLOADS["gemv_34816x5120_bf16"]
     print("case decode n", n, flush=True)
     _, rep = _case(w["M"], w["K"], n, seed=w["seed"])
+    print("n", n, "max err/bound", rep["max_ratio"])
+
+
+@pytest.mark.parametrize("n", [2, 64, 128])
+def test_decode_shape_sampled_rows(n):
+    # the row-balanced kernel's decode shape (136 rows per workgroup) at more
+    # tokens than the full oracle finishes quickly: 512 random rows, the rows
+    # around the first workgroup boundaries and the last workgroup, every
+    # token, against the oracle GEMV of those rows
+    from bf16_gemm_decode_amd import binding
+    w = synth.WORKLOADS["gemv_34816x5120_bf16"]
+    M, K = w["M"], w["K"]
+    assert binding.gemv_route(1 << 20, 1 << 30, 1 << 40, M, K, n)[1] == 18
+    W, X = synth.gemv_operands(M, K, n, seed=w["seed"])
+    got, guards, unchanged = gemv_gpu(W, X, M, K, n)
+    assert guards and unchanged
+    rows = np.unique(np.concatenate([np.random.default_rng(n).choice(M, 512, replace=False),
+                                     np.arange(120, 152), np.arange(264, 280), np.arange(M - 144, M)]))
+    ref = oracle.gemv(W.reshape(M, K)[rows].ravel(), X, rows.size, K, n)
+    print("case decode sampled n", n, "rows", rows.size, flush=True)
+    rep = assert_parity(got.reshape(n, M)[:, rows].ravel(), ref, "bf16", "decode sampled n=%d" % n)
     print("n", n, "max err/bound", rep["max_ratio"])
 
 
@@ -60,9 +88,10 @@ def test_rows_per_block_bit_identical(n):
 
 
 def test_every_route_against_the_vector_kernel():
-    # the automatic routes (4x4x4 MFMA for 3..8 tokens, the batch kernel for
-    # 9..128, the GEMM tile beyond) and the vector kernel
-    # (rows_per_block given) both meet the oracle's bound at the decode width
+    # the automatic routes at M = 2051 (the 4x4x4 MFMA kernel for 3 and 4
+    # tokens, the batch kernel for 5..32, the row-balanced kernel for
+    # 33..128, the GEMM tile beyond) and the vector kernel (rows_per_block
+    # given) both meet the oracle's bound at the decode width
     M, K = 2051, 5120
     for n in (3, 6, 8, 12, 40, 100, 129):
         print("case route n", n, flush=True)
