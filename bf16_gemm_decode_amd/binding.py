@@ -145,7 +145,7 @@ def gemm_plan(dtype, A, B, C, M, N, K, tile=0, group_m=0, xcd_remap=1, a_kmajor=
 def gemv_route(W, X, Y, M, K, n, rows_per_block=0):
     """(code, route) of gemv_bf16_ex's checks and kernel choice: route 0 no
     launch, 1 vector kernel, 14 4x4x4 MFMA kernel, 15 batch kernel, 18
-    row-balanced batch kernel, 9 gemm_tn."""
+    row-balanced batch kernel, 19 wide row-balanced kernel, 9 gemm_tn."""
     r = _I()
     code = lib().migemm_gemv_plan_for(W, X, Y, M, K, n, rows_per_block, ctypes.byref(r))
     return code, r.value

@@ -151,14 +151,16 @@ int plan_gemm(int dtype, const uint16_t *A, const uint16_t *B, const uint16_t *C
         // rows, the few-token kernels
         if (!fl) return MIGEMM_ERR_ALIGN;
         if (tile == TILE_AUTO) {
-            tile = wide && batch_rows_auto(M, N) ? TILE_BATCH_ROWS
+            tile = wide && batch_wide_auto(M, N) ? TILE_BATCH_WIDE
+                   : wide && batch_rows_auto(M, N) ? TILE_BATCH_ROWS
                    : wide && N <= kSkinnyAutoMax ? TILE_SKINNY
                    : wide && N <= kBatchAutoMax  ? TILE_BATCH
                                                  : auto_tile();
         } else if ((tile < TILE_256x256_FL) || tile == TILE_256x256_PP ||
                    (tile == TILE_SKINNY && N > kSkinnyMaxTokens) ||
                    (tile == TILE_BATCH && N > kBatchMaxTokens) ||
-                   (tile == TILE_BATCH_ROWS && N > kBatchRowsMaxTokens)) {
+                   (tile == TILE_BATCH_ROWS && N > kBatchRowsMaxTokens) ||
+                   (tile == TILE_BATCH_WIDE && N > kBatchWideMaxTokens)) {
             return MIGEMM_ERR_CONFIG;
         } else if (!wide && !is_fl(tile)) {
             return MIGEMM_ERR_ALIGN;
@@ -181,6 +183,10 @@ int plan_gemm(int dtype, const uint16_t *A, const uint16_t *B, const uint16_t *C
         bm = batch_rows_per_workgroup(M);
         bn = batch_rows_tile_n(N);
     }
+    if (tile == TILE_BATCH_WIDE) {
+        bm = batch_rows_per_workgroup(M);
+        bn = batch_wide_tile_n(N);
+    }
     const int64_t pm = cdiv(M, bm), pn = cdiv(N, bn);
     if (pm * pn > 0x7fffffff) return MIGEMM_ERR_SIZE;
     L.num_pid_m = (int)(pm ? pm : 1);
@@ -200,9 +206,10 @@ hipError_t decode_launch(int tile, int dtype, const uint16_t *At, const uint16_t
                          int M, int N, int K, int c_vec, hipStream_t stream)
 {
     SkinnyLaunch S{dtype, At, B, C, M, K, N, c_vec};
-    return tile == TILE_SKINNY ? skinny_launch(S, stream)
-           : tile == TILE_BATCH ? batch_launch(S, stream)
-                                : batch_rows_launch(S, stream);
+    return tile == TILE_SKINNY       ? skinny_launch(S, stream)
+           : tile == TILE_BATCH      ? batch_launch(S, stream)
+           : tile == TILE_BATCH_ROWS ? batch_rows_launch(S, stream)
+                                     : batch_wide_launch(S, stream);
 }
 
 int finish(hipError_t e, void *stream)
@@ -426,17 +433,18 @@ static int plan_for(int dtype, const uint16_t *A, const uint16_t *B, const uint1
         plan->a_kmajor = 1;
         return rc;
     }
-    if (L.tile == TILE_BATCH_ROWS) {
-        plan->tile_m = batch_rows_per_workgroup(M);   // rows per workgroup (9 waves of 16)
-        plan->tile_n = batch_rows_tile_n(N);
+    if (L.tile == TILE_BATCH_ROWS || L.tile == TILE_BATCH_WIDE) {
+        const bool wide = L.tile == TILE_BATCH_WIDE;
+        plan->tile_m = batch_rows_per_workgroup(M);   // rows per workgroup
+        plan->tile_n = wide ? batch_wide_tile_n(N) : batch_rows_tile_n(N);
         plan->tile_k = 64;
-        plan->waves = 9;
+        plan->waves = wide ? 8 : 9;
         plan->group_m = 1;
         plan->xcd_remap = 0;
         plan->vec_a = L.vec_a;
         plan->vec_b = L.vec_b;
         plan->grid = launch ? L.grid : 0;
-        plan->lds_bytes = batch_rows_lds_bytes(N);
+        plan->lds_bytes = wide ? batch_wide_lds_bytes(N) : batch_rows_lds_bytes(N);
         plan->tile = L.tile;
         plan->a_kmajor = 1;
         return rc;
@@ -502,13 +510,16 @@ static int plan_gemv(const uint16_t *W, const uint16_t *X, const uint16_t *Y, in
     if (M == 0 || n == 0) return MIGEMM_OK;
     const bool vec = (K % 8 == 0 && (uintptr_t)W % 16 == 0 && (uintptr_t)X % 16 == 0);
     // Y = X W^T is gemm_tn with At = W, B = X, C = Y (all row-major): the
-    // row-balanced kernel where batch_rows_auto says so, else up to
+    // wide row-balanced kernel where batch_wide_auto says so, the
+    // row-balanced kernel where batch_rows_auto does, else up to
     // kSkinnyAutoMax tokens on the 4x4x4 MFMA kernel, up to kBatchAutoMax on
     // the 16x16x32 batch kernel, more on the full-line 256x128 tile within
     // the GEMM's own size limits; everything else on the vector kernel
     const bool gemm_fits = M <= MIGEMM_MAX_MN && K <= MIGEMM_MAX_K;
     route = 1;
-    if (rows_per_block == 0 && vec && batch_rows_auto(M, n))
+    if (rows_per_block == 0 && vec && batch_wide_auto(M, n))
+        route = TILE_BATCH_WIDE;
+    else if (rows_per_block == 0 && vec && batch_rows_auto(M, n))
         route = TILE_BATCH_ROWS;
     else if (rows_per_block == 0 && vec && n >= kSkinnyMinTokens)
         route = n <= kSkinnyAutoMax ? TILE_SKINNY

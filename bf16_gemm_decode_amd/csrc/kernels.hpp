@@ -26,6 +26,7 @@ enum GemmTile {
     TILE_256x256_PP = 16,       // as 10, m-major A, ping-pong: the two waves of a SIMD alternate MFMA and memory phases
     TILE_256x128_F8W = 17,      // FP8 only, k-major A: 256x128, 8 waves of 64x64, whole 64-unit steps on the 16x16x128 MFMA
     TILE_BATCH_ROWS = 18,       // up to 256 columns: W's rows spread evenly, 9 waves of 16 rows per workgroup (batch.hip)
+    TILE_BATCH_WIDE = 19,       // up to 256 columns: W's rows spread evenly, 8 waves of 5 or 4 row tiles x a quarter of the columns (wide.hip)
     TILE_COUNT
 };
 
@@ -56,6 +57,7 @@ constexpr TileShape kTileShapes[TILE_COUNT] = {
     {256, 256, 32, 4, 8, 3},
     {256, 128, 32, 3, 8, 3},
     {144, 256, 64, 0, 9, 0},
+    {144, 256, 64, 0, 8, 0},
 };
 
 // The full-line tiles with A k-major: stages = A ring stages of 64 k.
@@ -79,6 +81,7 @@ constexpr TileShape kTileShapesKmajorA[TILE_COUNT] = {
     {0, 0, 0, 0, 0, 0},
     {256, 128, 32, 3, 8, 3},
     {144, 256, 64, 0, 9, 0},
+    {144, 256, 64, 0, 8, 0},
 };
 
 constexpr int tile_lds_bytes(const TileShape &t, bool a_kmajor = false)
@@ -170,8 +173,31 @@ int batch_rows_per_workgroup(int M);
 // waves' 2 KB areas that re-lay W out
 constexpr int batch_rows_tile_n(int n) { return n <= 16 ? 16 : n <= 32 ? 32 : n <= 64 ? 64 : n <= 128 ? 128 : 256; }
 constexpr int batch_rows_lds_bytes(int n) { return 2 * batch_rows_tile_n(n) * 144 + 9 * 2048; }
+// Row-balanced wide kernel (wide.hip): the same rows per workgroup, 8 waves
+// in two row groups (5 and 4 tiles of 16) times four column groups, both
+// operands staged in LDS by direct loads; 128- or 256-column blocks.
+constexpr int kBatchWideMaxTokens = 256;
+hipError_t batch_wide_launch(const SkinnyLaunch &L, hipStream_t stream);
+constexpr int batch_wide_tile_n(int n) { return n <= 128 ? 128 : 256; }
+// Automatic choice for 65 .. 256 tokens once the workgroups hold more than
+// 120 rows (M > 30720): on W 34816 x 5120, 73 us for 128 tokens (the
+// row-balanced kernel 113-122 us, the GEMM's 256x128 tile 115 us) and
+// 118-136 us for 256 (the GEMM tiles 158-203 us).  With fewer rows its
+// fixed 9 row tiles waste work (16384 x 4096, 128 tokens: 47 us against 40
+// for the row-balanced kernel).
+constexpr int kBatchWideAutoMinM = 30721;
+constexpr bool batch_wide_auto(int M, int n) { return n >= 65 && n <= kBatchWideMaxTokens && M >= kBatchWideAutoMinM; }
+// its LDS: 4 ring stages of 9 + 8 tiles of 2 KiB (128 columns) or 3 of
+// 9 + 16, and a 1 KiB sink
+constexpr int batch_wide_lds_bytes(int n)
+{
+    return n <= 128 ? 4 * (9 + 8) * 2048 + 1024 : 3 * (9 + 16) * 2048 + 1024;
+}
 // the kernels above that take Y = X W^T directly (gemm_tn with At = W, B = X)
-constexpr bool is_decode_tile(int t) { return t == TILE_SKINNY || t == TILE_BATCH || t == TILE_BATCH_ROWS; }
+constexpr bool is_decode_tile(int t)
+{
+    return t == TILE_SKINNY || t == TILE_BATCH || t == TILE_BATCH_ROWS || t == TILE_BATCH_WIDE;
+}
 // token columns of one batch-kernel workgroup for n tokens (16, 32, 64, 128)
 constexpr int batch_tile_n(int n) { return n <= 16 ? 16 : n <= 32 ? 32 : n <= 64 ? 64 : 128; }
 // its waves (16 rows of W each): 2 for one 16-token block (finer workgroups

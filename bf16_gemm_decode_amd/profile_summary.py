@@ -31,8 +31,8 @@ import sys
 
 CSRC = os.path.join(os.path.dirname(os.path.abspath(__file__)), "csrc")
 # the sources whose change invalidates a kernel's recorded counters
-GEMM_SOURCES = ["gemm.hip", "api.hip", "kernels.hpp", "tile_map.hpp", "common.hpp"]
-GEMV_SOURCES = ["gemv.hip", "skinny.hip", "batch.hip", "api.hip", "kernels.hpp", "common.hpp"]
+GEMM_SOURCES = ["gemm.hip", "api.hip", "kernels.hpp", "tile_map.hpp", "common.hpp", "dma.hpp"]
+GEMV_SOURCES = ["gemv.hip", "skinny.hip", "batch.hip", "wide.hip", "api.hip", "kernels.hpp", "common.hpp", "dma.hpp"]
 ATTENTION_SOURCES = ["attention.hip", "api.hip", "kernels.hpp", "common.hpp"]
 
 

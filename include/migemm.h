@@ -83,9 +83,11 @@ int gemm_bf16(const uint16_t *A, const uint16_t *B, uint16_t *C,
  * K == 0 writes +0.0 to Y.  Errors as for the GEMM (Y must not overlap W, X).
  * n may be any positive value.  One token (or K not a multiple of 8, or W,
  * X not 16-byte aligned) runs the row-blocked vector kernel.  With 16-byte
- * rows the multiply-adds of 2 .. 128 tokens run on the row-balanced 16x16x32
- * MFMA kernel (tile 18 below: W's rows cut evenly over the CUs) when M >=
- * 16384, or from 33 tokens on for any M; otherwise 2 tokens take the vector
+ * rows, 65 .. 256 tokens with M > 30720 run on the wide row-balanced
+ * 16x16x32 MFMA kernel (tile 19 below: W's rows cut evenly over the CUs,
+ * each workgroup's rows reused from registers across its tokens); 2 .. 128
+ * tokens otherwise on the row-balanced kernel (tile 18) when M >= 16384,
+ * or from 33 tokens on for any M; otherwise 2 tokens take the vector
  * kernel, 3 or 4 the 4x4x4 MFMA with W streamed straight into operand
  * registers, up to 64 the 16x16x32 MFMA with W read as whole cache lines and
  * the token block of X staged in LDS (tile 15 below), and beyond that
@@ -252,7 +254,12 @@ size_t migemm_splitk_workspace_bytes(int M, int N, int splits);
  *            (gemm_tn_* only, N <= 256: W's rows spread evenly over the
  *            workgroups, about M / 256 each rounded up to a multiple of 8 and
  *            at most 144, 9 waves of 16 rows, 16..256 columns, K in steps of
- *            64, A read as whole lines through LDS, B staged in LDS).
+ *            64, A read as whole lines through LDS, B staged in LDS); 19 =
+ *            the wide row-balanced kernel (gemm_tn_* only, N <= 256: the
+ *            same rows per workgroup, 8 waves in two row groups of 5 and 4
+ *            row tiles of 16 times four column groups, 128- or 256-column
+ *            blocks, K in steps of 64, A and B both staged in LDS by direct
+ *            loads).
  *            All step K by 32.  Tiles 1, 2, 4, 5, 6 need 16-byte rows (M and
  *            K multiples of 8, A and B 16-byte aligned); the full-line tiles
  *            7 .. 13 and 16 need 4-byte rows (M and K even, A and B 4-byte
@@ -278,14 +285,14 @@ int gemm_ex(int dtype, const uint16_t *A, const uint16_t *B, uint16_t *C,
  * with Y row-major [N, M] -- the GEMV's own layout.  Same argument checks,
  * ownership and completion rules as gemm_f16 / gemm_bf16.  Runs on the
  * full-line and decode tiles only: tile 0 (automatic, with 16-byte rows:
- * 18 for 2 <= N <= 128 when M >= 16384 or N >= 33, else 14 for N <= 4, 15
- * for N <= 64; beyond that, or with 4-byte rows, the least estimated time
- * among 10, 9 and 13) or 7 .. 15 and 18 (A takes B's 64-k ring layout;
- * MIGEMM_ERR_CONFIG for other tiles, 16 and 17 included, and for 14 with
- * N > 8, 15 with N > 128 or 18 with N > 256).  K even and At, B 4-byte
- * aligned (4-byte rows) for tiles 7 .. 13, K a multiple of 8 and At, B
- * 16-byte aligned for 14, 15 and 18 (which tile 0 then uses); else
- * MIGEMM_ERR_ALIGN.
+ * 19 for 65 <= N <= 256 when M > 30720, else 18 for 2 <= N <= 128 when
+ * M >= 16384 or N >= 33, else 14 for N <= 4, 15 for N <= 64; beyond that,
+ * or with 4-byte rows, the least estimated time among 10, 9 and 13) or
+ * 7 .. 15, 18 and 19 (A takes B's 64-k ring layout; MIGEMM_ERR_CONFIG for
+ * other tiles, 16 and 17 included, and for 14 with N > 8, 15 with N > 128
+ * or 18 and 19 with N > 256).  K even and At, B 4-byte aligned (4-byte
+ * rows) for tiles 7 .. 13, K a multiple of 8 and At, B 16-byte aligned for
+ * 14, 15, 18 and 19 (which tile 0 then uses); else MIGEMM_ERR_ALIGN.
  */
 int gemm_tn_f16(const uint16_t *At, const uint16_t *B, uint16_t *C,
                 int M, int N, int K, void *stream);
@@ -356,8 +363,8 @@ int migemm_gemm_tn_plan_for(int dtype, const uint16_t *At, const uint16_t *B,
 /* Which kernel gemv_bf16_ex would run for these arguments (pointers are
  * inspected for alignment only, never dereferenced): writes to *route 0 (no
  * launch: M or n is 0), 1 (the row-blocked vector kernel), 14 (the 4x4x4
- * MFMA kernel), 15 (the batch kernel), 18 (the row-balanced batch kernel)
- * or 9 (gemm_tn on the 256x128
+ * MFMA kernel), 15 (the batch kernel), 18 (the row-balanced batch kernel),
+ * 19 (the wide row-balanced kernel) or 9 (gemm_tn on the 256x128
  * full-line tile; only while M <= MIGEMM_MAX_MN and K <= MIGEMM_MAX_K,
  * larger problems stay on the vector kernel), and returns the code
  * gemv_bf16_ex would return for the argument checks. */

@@ -100,7 +100,9 @@ def test_tn_plan_and_errors():
     code, p = binding.gemm_plan(0, P, P + 2 ** 30, P + 2 ** 31, 8192, 8192, 16384, a_kmajor=True)
     assert code == 0 and (p["tile_m"], p["tile_n"], p["vec_a"], p["vec_b"]) == (256, 256, 8, 8)
     assert p["lds_bytes"] == 2 * 64 * 256 * 2 + 3 * 64 * 256 * 2 and p["waves"] == 8
-    code, p = binding.gemm_plan(1, P, P + 2 ** 30, P + 2 ** 31, 34816, 200, 5120, a_kmajor=True)
+    # (K % 8 != 0: 4-byte rows, so the decode tiles are out and the GEMM's
+    # estimate decides)
+    code, p = binding.gemm_plan(1, P, P + 2 ** 30, P + 2 ** 31, 34816, 200, 5122, a_kmajor=True)
     assert code == 0 and (p["tile_m"], p["tile_n"]) == (256, 256) and p["grid"] == 136   # one round
     code, p = binding.gemm_plan(1, P, P + 2 ** 30, P + 2 ** 31, 2816, 2816, 4096, a_kmajor=True)
     assert code == 0 and (p["tile_m"], p["tile_n"]) == (256, 128) and p["grid"] == 242   # one round
@@ -123,7 +125,7 @@ def test_tn_plan_and_errors():
         assert code == 0 and (p["tile"], p["tile_m"], p["tile_n"], p["tile_k"], p["waves"]) == (15, 16 * w, tn, 128, w)
         assert p["grid"] == 34816 // (16 * w) and p["lds_bytes"] == 2 * tn * 272 + w * 4096
     assert binding.gemm_plan(1, P, P + 2 ** 30, P + 2 ** 31, 4096, 32, 5120, a_kmajor=True)[1]["tile"] == 15
-    assert binding.gemm_plan(1, P, P + 2 ** 30, P + 2 ** 31, 34816, 129, 5120, a_kmajor=True)[1]["tile"] == 10
+    assert binding.gemm_plan(1, P, P + 2 ** 30, P + 2 ** 31, 34816, 257, 5120, a_kmajor=True)[1]["tile"] == 9
     # the row-balanced tile: W's rows cut into 256 equal parts, rounded up to
     # a multiple of 8 and capped at 144 (9 waves of 16); token blocks of
     # 16 .. 256; automatic for 2 .. 128 columns once M >= 16384, and from 33
@@ -133,9 +135,20 @@ def test_tn_plan_and_errors():
             code, p = binding.gemm_plan(1, P, P + 2 ** 30, P + 2 ** 31, M, n, 5120, 18, a_kmajor=True)
             assert code == 0 and (p["tile"], p["tile_m"], p["tile_n"], p["tile_k"], p["waves"]) == (18, R, tn, 64, 9)
             assert p["grid"] == -(-M // R) and p["lds_bytes"] == 2 * tn * 144 + 9 * 2048
-    for M, n, want in ((34816, 1, 14), (34816, 2, 18), (34816, 4, 18), (34816, 128, 18), (34816, 129, 10),
-                       (16384, 2, 18), (16383, 2, 14), (4096, 32, 15), (4096, 33, 18), (4096, 128, 18),
-                       (64, 33, 18)):
+    # the wide row-balanced tile: the same rows per workgroup, 8 waves,
+    # 128- or 256-column blocks; automatic for 65 .. 256 columns once M > 30720
+    for M, R in ((34816, 136), (30721, 128), (16384, 64), (100, 8), (40000, 144)):
+        for n, tn, lds in ((1, 128, 4 * 17 * 2048 + 1024), (128, 128, 4 * 17 * 2048 + 1024),
+                           (129, 256, 3 * 25 * 2048 + 1024), (256, 256, 3 * 25 * 2048 + 1024)):
+            code, p = binding.gemm_plan(1, P, P + 2 ** 30, P + 2 ** 31, M, n, 5120, 19, a_kmajor=True)
+            assert code == 0 and (p["tile"], p["tile_m"], p["tile_n"], p["tile_k"], p["waves"]) == (19, R, tn, 64, 8)
+            assert p["grid"] == -(-M // R) and p["lds_bytes"] == lds <= 160 * 1024
+    assert L.gemm_tn_ex(0, P, P + 0x100000, P + 0x200000, 64, 257, 64, 19, 0, 1, None) == -5
+    assert L.gemm_ex(0, P, P + 0x100000, P + 0x200000, 64, 16, 64, 19, 0, 1, None) == -5
+    for M, n, want in ((34816, 1, 14), (34816, 2, 18), (34816, 4, 18), (34816, 64, 18), (34816, 65, 19),
+                       (34816, 128, 19), (34816, 256, 19), (34816, 257, 9), (30721, 65, 19), (30720, 65, 18),
+                       (30720, 129, 9), (16384, 2, 18), (16383, 2, 14), (4096, 32, 15), (4096, 33, 18),
+                       (4096, 128, 18), (64, 33, 18)):
         code, p = binding.gemm_plan(1, P, P + 2 ** 30, P + 2 ** 31, M, n, 5120, a_kmajor=True)
         assert code == 0 and p["tile"] == want, (M, n, p["tile"])
     assert L.gemm_tn_ex(0, P, P + 0x100000, P + 0x200000, 64, 257, 64, 18, 0, 1, None) == -5
@@ -359,7 +372,8 @@ def test_gemv_route():
     # rows_per_block keeps the vector kernel; beyond the GEMM's size limits
     # many tokens stay on the vector kernel instead of failing
     W, X, Y = P, P + (1 << 36), P + (1 << 37)
-    for n, want in ((1, 1), (2, 18), (3, 18), (4, 18), (5, 18), (64, 18), (128, 18), (129, 9), (1000, 9)):
+    for n, want in ((1, 1), (2, 18), (3, 18), (4, 18), (5, 18), (64, 18), (65, 19), (128, 19), (256, 19),
+                    (257, 9), (1000, 9)):
         assert binding.gemv_route(W, X, Y, 34816, 5120, n) == (0, want), n
     for n, want in ((1, 1), (2, 1), (3, 14), (4, 14), (5, 15), (32, 15), (33, 18), (128, 18), (129, 9)):
         assert binding.gemv_route(W, X, Y, 4096, 4096, n) == (0, want), n
@@ -367,9 +381,10 @@ def test_gemv_route():
     assert binding.gemv_route(W, X, Y, 16376, 4096, 2) == (0, 1)
     assert binding.gemv_route(W, X, Y, 34816, 5120, 16, rows_per_block=8) == (0, 1)
     assert binding.gemv_route(W, X, Y, 34816, 5122, 16) == (0, 1)          # K % 8: no MFMA route
-    assert binding.gemv_route(W, X, Y, (1 << 23) + 64, 8, 129) == (0, 1)    # M past the GEMM limit
+    assert binding.gemv_route(W, X, Y, (1 << 23) + 64, 8, 257) == (0, 1)    # M past the GEMM limit
+    assert binding.gemv_route(W, X, Y, (1 << 23) + 64, 8, 129) == (0, 19)
     assert binding.gemv_route(W, X, Y, 64, (1 << 21) + 8, 129) == (0, 1)    # K past the GEMM limit
-    assert binding.gemv_route(W, X, Y, (1 << 23) + 64, 8, 128) == (0, 18)
+    assert binding.gemv_route(W, X, Y, (1 << 23) + 64, 8, 64) == (0, 18)
     assert binding.gemv_route(W, X, Y, 100, 8, 64) == (0, 18)
     assert binding.gemv_route(W, X, Y, 0, 8, 4) == (0, 0)
     assert binding.gemv_route(W, X, Y, 8, 8, -1)[0] == -1

@@ -3,7 +3,7 @@ the C ABI against the CPU oracle, which takes the same matrix column-major:
 every element at small sizes, K tails inside a 64-k stage, ragged M and N,
 bit-identical agreement with gemm_ex on the same tile (same MFMA order), and
 the DCU page's Y = X W^T in its own row-major layout for a batch of tokens,
-and the decode tiles (14, 15, 18) at their token blocks and ragged edges."""
+and the decode tiles (14, 15, 18, 19) at their token blocks and ragged edges."""
 import numpy as np
 import pytest
 
@@ -175,6 +175,44 @@ def test_batch_rows_matches_exact_integers():
             want = oracle.gemm(kmajor_to_colmajor(At, M, K), B, M, N, K, fmt).bits
             got, _, _ = gemm_tn_gpu(At, B, M, N, K, fmt, tile=18)
             assert np.array_equal(got, want), (M, N, K, fmt)
+
+
+@pytest.mark.parametrize("fmt", FMTS)
+def test_batch_wide_tile_token_blocks_and_ragged_edges(fmt):
+    # tile 19 (the same rows per workgroup as tile 18; 8 waves in row groups
+    # of 5 and 4 tiles times four token groups; 64-wide k chunks loaded
+    # straight into a 4-stage (128 tokens) or 3-stage (256 tokens) LDS ring):
+    # both token blocks with ragged token counts, workgroups of 8 rows (most
+    # row tiles empty), of a few tiles and of all 9, more than one workgroup
+    # per CU (M > 36864), ragged last workgroups, K tails inside a chunk, K
+    # shorter than one chunk and shorter than the ring
+    for (M, N, K) in [(100, 65, 64), (37, 1, 40), (2051, 128, 520), (300, 129, 264), (20000, 200, 136),
+                      (36000, 256, 72), (40000, 100, 64), (9, 256, 5120), (130, 255, 1160),
+                      (16400, 16, 8), (36871, 250, 584), (34816, 130, 128)]:
+        print("case batch wide", M, N, K, fmt, flush=True)
+        _tn_case(M, N, K, fmt, seed=4000 + M + N + K, tile=19)
+
+
+def test_batch_wide_matches_exact_integers():
+    rng = np.random.default_rng(37)
+    for M, N, K in ((520, 77, 1032), (4100, 250, 200), (33000, 130, 648)):
+        for fmt in FMTS:
+            print("case batch wide exact", M, N, K, fmt, flush=True)
+            At = synth.to_bits(synth.small_ints(rng, M * K, -3, 3), fmt)
+            B = synth.to_bits(synth.small_ints(rng, K * N, -3, 3), fmt)
+            want = oracle.gemm(kmajor_to_colmajor(At, M, K), B, M, N, K, fmt).bits
+            got, _, _ = gemm_tn_gpu(At, B, M, N, K, fmt, tile=19)
+            assert np.array_equal(got, want), (M, N, K, fmt)
+
+
+def test_row_balanced_tiles_agree_bit_for_bit():
+    # tiles 18 and 19 add the same 32-k MFMA steps in the same order into
+    # FP32, so their outputs agree bit for bit
+    M, N, K = 34816, 200, 1024
+    At, B = synth.gemm_operands(M, N, K, "bf16", ("normal", 0.02, 1.0), 77)
+    g18, _, _ = gemm_tn_gpu(At, B, M, N, K, "bf16", tile=18)
+    g19, _, _ = gemm_tn_gpu(At, B, M, N, K, "bf16", tile=19)
+    assert np.array_equal(g18, g19)
 
 
 def test_tn_is_the_decode_product_for_a_token_batch():

@@ -1,6 +1,6 @@
 """GPU parity of gemv_bf16 (through the C ABI) against the CPU oracle:
 every element of the 34816 x 5120 decode shape at n = 1, 4, 16, sampled rows
-(all tokens) at n = 2, 64, 128, ragged shapes and token counts on every
+(all tokens) at n = 2, 64, 128, 256, ragged shapes and token counts on every
 automatic route, the one-hot exact case, agreement with the GEMM at n = 1,
 and bit-identical results across rows_per_block."""
 import numpy as np
@@ -52,16 +52,16 @@ def test_decode_shape_full(n):
     print("n", n, "max err/bound", rep["max_ratio"])
 
 
-@pytest.mark.parametrize("n", [2, 64, 128])
-def test_decode_shape_sampled_rows(n):
-    # the row-balanced kernel's decode shape (136 rows per workgroup) at more
+@pytest.mark.parametrize("n,route", [(2, 18), (64, 18), (128, 19), (256, 19)])
+def test_decode_shape_sampled_rows(n, route):
+    # the row-balanced kernels' decode shape (136 rows per workgroup) at more
     # tokens than the full oracle finishes quickly: 512 random rows, the rows
     # around the first workgroup boundaries and the last workgroup, every
     # token, against the oracle GEMV of those rows
     from bf16_gemm_decode_amd import binding
     w = synth.WORKLOADS["gemv_34816x5120_bf16"]
     M, K = w["M"], w["K"]
-    assert binding.gemv_route(1 << 20, 1 << 30, 1 << 40, M, K, n)[1] == 18
+    assert binding.gemv_route(1 << 20, 1 << 30, 1 << 40, M, K, n)[1] == route
     W, X = synth.gemv_operands(M, K, n, seed=w["seed"])
     got, guards, unchanged = gemv_gpu(W, X, M, K, n)
     assert guards and unchanged
