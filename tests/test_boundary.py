@@ -108,6 +108,14 @@ def test_tn_plan_and_errors():
     assert code == 0 and (p["tile_m"], p["tile_n"]) == (256, 128) and p["grid"] == 242   # one round
     code, p = binding.gemm_plan(1, P, P + 2 ** 30, P + 2 ** 31, 2048, 2048, 4096, a_kmajor=True)
     assert code == 0 and (p["tile"], p["grid"]) == (13, 256)
+    # fewer than 128 tiles of 128x128: the 64-row tiles (64x64 once they
+    # fill half the chip), both layouts
+    for kmaj in (False, True):
+        for (M, N, K), (tile, grid) in (((512, 512, 512), (11, 128)), ((768, 768, 768), (12, 144)),
+                                       ((1024, 1024, 1024), (12, 256)), ((1152, 1408, 256), (12, 396)),
+                                       ((1536, 1536, 256), (13 if kmaj else 3, 144))):
+            code, p = binding.gemm_plan(0, P, P + 2 ** 30, P + 2 ** 31, M, N, K, a_kmajor=kmaj)
+            assert code == 0 and (p["tile"], p["grid"]) == (tile, grid), (M, N, K, kmaj, p)
     # the skinny tile: few columns only, and only with a k-major A
     code, p = binding.gemm_plan(1, P, P + 2 ** 30, P + 2 ** 31, 34816, 8, 5120, 14, a_kmajor=True)
     assert code == 0 and (p["tile"], p["tile_m"], p["tile_n"], p["waves"], p["grid"]) == (14, 32, 8, 4, 1088)
@@ -165,7 +173,7 @@ def test_tn_plan_and_errors():
     code, p = binding.gemm_plan(0, P, P + 2 ** 20, P + 2 ** 21, 64, 64, 60, 7, a_kmajor=True)
     assert code == 0 and p["tile"] == 7 and (p["vec_a"], p["vec_b"]) == (2, 2)
     assert binding.gemm_plan(0, P, P + 2 ** 20, P + 2 ** 21, 64, 8, 60, 14, a_kmajor=True)[0] == -4
-    assert binding.gemm_plan(0, P, P + 2 ** 20, P + 2 ** 21, 64, 64, 60, 0, a_kmajor=True)[1]["tile"] == 13
+    assert binding.gemm_plan(0, P, P + 2 ** 20, P + 2 ** 21, 64, 64, 60, 0, a_kmajor=True)[1]["tile"] == 11     # few tiles: the 64x32 tile
     # the shared checks
     assert L.gemm_tn_f16(P, P + 0x100000, P + 0x200000, -1, 64, 64, None) == -1
     assert L.gemm_tn_bf16(None, P + 0x100000, P + 0x200000, 64, 64, 64, None) == -2
