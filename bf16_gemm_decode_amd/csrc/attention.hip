@@ -29,8 +29,8 @@
 // denominator, unnormalised output) go to the workspace in FP32.
 //
 // Merge kernel: one workgroup per (query head, sequence, 64 output
-// columns); each thread merges a quarter of the segments of its column
-// online (log-sum-exp), the quarters are merged through LDS, then one
+// columns); each thread merges a sixteenth of the segments of its column
+// online (log-sum-exp), the sixteen are merged through LDS, then one
 // division and one rounding to BF16.  Empty segments (max = -inf, denominator 0) add
 // nothing; a sequence with no token gives zeros.  Tokens whose page id is
 // outside [0, num_blocks) add nothing: their rows are read from a block of
@@ -323,11 +323,14 @@ attn_segment_kernel(const uint16_t *__restrict__ Q, const uint16_t *__restrict__
 }
 
 constexpr int kMaxSegments = 1024;
-constexpr int kMergeRows = 4;            // segment rows per merge workgroup
+constexpr int kMergeRows = 16;           // segment rows per merge workgroup
+constexpr int kMergeBatch = 8;           // rows a thread loads before merging them
 
-// grid (query head, sequence, 64-column chunk), 256 threads: thread
-// (r, col) merges segments r, r + 4, ... of its column online (all loads
-// independent of each other), then the 4 rows are merged through LDS.
+// grid (query head, sequence, 64-column chunk), 1024 threads: thread
+// (r, col) merges segments r, r + 16, ... of its column online, loading 8
+// rows at a time before using any (the partials come from other XCDs'
+// writes: one trip to memory per batch, not per row), then the 16 rows are
+// merged through LDS.
 __global__ void __launch_bounds__(64 * kMergeRows)
 attn_merge_kernel(const float *__restrict__ part_o, const float *__restrict__ part_ml,
                   uint16_t *__restrict__ Out, int Hq, int D, int S)
@@ -338,16 +341,26 @@ attn_merge_kernel(const float *__restrict__ part_o, const float *__restrict__ pa
     const size_t base = ((size_t)b * Hq + h) * S;
 
     float m = kNegInf, z = 0.f, acc = 0.f;
-#pragma unroll 8
-    for (int s = r; s < S; s += kMergeRows) {
-        const float ms = part_ml[(base + s) * 2], ls = part_ml[(base + s) * 2 + 1];
-        const float os = part_o[(base + s) * D + col];
-        const float mn = fmaxf(m, ms);
-        const float a = mn == kNegInf ? 0.f : exp2_guarded(m - mn);
-        const float w = mn == kNegInf ? 0.f : exp2_guarded(ms - mn);
-        z = z * a + ls * w;
-        acc = acc * a + os * w;
-        m = mn;
+    for (int s0 = r; s0 < S; s0 += kMergeRows * kMergeBatch) {
+        float ms[kMergeBatch], ls[kMergeBatch], os[kMergeBatch];
+#pragma unroll
+        for (int i = 0; i < kMergeBatch; ++i) {
+            const int s = s0 + i * kMergeRows;
+            const size_t row = base + (s < S ? s : r);            // past S: row r again, ignored
+            ms[i] = part_ml[row * 2];
+            ls[i] = part_ml[row * 2 + 1];
+            os[i] = part_o[row * D + col];
+            if (s >= S) ms[i] = kNegInf;
+        }
+#pragma unroll
+        for (int i = 0; i < kMergeBatch; ++i) {
+            const float mn = fmaxf(m, ms[i]);
+            const float a = mn == kNegInf ? 0.f : exp2_guarded(m - mn);
+            const float w = mn == kNegInf ? 0.f : exp2_guarded(ms[i] - mn);
+            z = z * a + ls[i] * w;
+            acc = acc * a + os[i] * w;
+            m = mn;
+        }
     }
     sm[r][threadIdx.x & 63] = m;
     sz[r][threadIdx.x & 63] = z;

@@ -28,7 +28,7 @@ def _gpu(op, scale, S, max_seq_len=None):
     mlen = int(max(op["seq_lens"])) if max_seq_len is None else max_seq_len
     segs = S or L.migemm_attention_segments(B, Hq, Hkv, mlen)
     need = L.migemm_attention_workspace_bytes(B, Hq, D, segs)
-    ws = torch.empty(max(need, 16), dtype=torch.uint8, device="cuda")
+    ws = torch.zeros(max(need, 16), dtype=torch.uint8, device="cuda")   # counters start at zero
     code = L.attention_decode_bf16(dQ.data_ptr(), dK.data_ptr(), dV.data_ptr(), bt.data_ptr(),
                                    sl.data_ptr(), out.data_ptr() + 2 * guard, B, Hq, Hkv, D,
                                    op["block_size"], op["max_blocks"], op["num_blocks"], scale,
@@ -153,3 +153,74 @@ def test_page_head_shape_automatic_vs_16_and_32_segments(L):
         other = oracle.decode(_gpu(op, scale, S), "bf16")
         d = np.abs(auto - other)
         assert d.max() <= 2.44e-4 and d.mean() <= 1.58e-5, (S, d.max(), d.mean())
+
+
+
+def test_one_workspace_many_shapes():
+    # one workspace serves calls of different shapes and segment counts in
+    # a row; every result meets the oracle's bound
+    import torch
+    from bf16_gemm_decode_amd import binding
+    L = binding.lib()
+    ws = torch.empty(16 << 20, dtype=torch.uint8, device="cuda")
+    cases = [(2, 8, 2, 128, [300, 77], 16, 1), (1, 16, 4, 256, [2000], 784, 16),
+             (3, 4, 4, 64, [50, 0, 129], 8, 17), (1, 16, 4, 256, [4000], 784, 128),
+             (2, 8, 1, 128, [999, 1], 32, 1024), (1, 2, 2, 64, [5], 4, 40)]
+    for i, (B, Hq, Hkv, D, lens, bs, S) in enumerate(cases):
+        print("case shared workspace", i, B, Hq, Hkv, D, lens, bs, S, flush=True)
+        op = synth.attention_operands(B, Hq, Hkv, D, lens, bs, seed=80 + i)
+        scale = 1.0 / np.sqrt(D)
+        dQ, dK, dV = dev(op["Q"]), dev(op["K"]), dev(op["V"])
+        bt = torch.from_numpy(np.ascontiguousarray(op["block_table"], np.int32)).cuda()
+        sl = torch.from_numpy(np.ascontiguousarray(op["seq_lens"], np.int32)).cuda()
+        out = torch.empty(B * Hq * D, dtype=torch.int16, device="cuda")
+        assert L.migemm_attention_workspace_bytes(B, Hq, D, S) <= ws.numel()
+        code = L.attention_decode_bf16(dQ.data_ptr(), dK.data_ptr(), dV.data_ptr(), bt.data_ptr(),
+                                       sl.data_ptr(), out.data_ptr(), B, Hq, Hkv, D, op["block_size"],
+                                       op["max_blocks"], op["num_blocks"], scale, max(lens), S,
+                                       ws.data_ptr(), ws.numel(), None)
+        assert code == 0, code
+        torch.cuda.synchronize()
+        ref = _ref(op, scale)
+        ok, rep = oracle.check(host(out), ref, "bf16", rel=oracle.attention_rel(ref, op["seq_lens"], Hq, D))
+        assert ok, (i, rep)
+
+
+def test_graph_replays_match_eager():
+    # the call (segment and merge kernels) captured in a HIP graph and
+    # replayed several times, with eager work in between: every replay
+    # equals the eager result bit for bit
+    import torch
+    from bf16_gemm_decode_amd import binding
+    L = binding.lib()
+    w = synth.WORKLOADS["attention_decode_16q4kv_d256_bf16"]
+    op = synth.attention_operands(1, w["Hq"], w["Hkv"], w["D"], [8192], w["block_size"], seed=w["seed"])
+    scale = 1.0 / np.sqrt(w["D"])
+    dQ, dK, dV = dev(op["Q"]), dev(op["K"]), dev(op["V"])
+    bt = torch.from_numpy(np.ascontiguousarray(op["block_table"], np.int32)).cuda()
+    sl = torch.from_numpy(np.ascontiguousarray(op["seq_lens"], np.int32)).cuda()
+    S = L.migemm_attention_segments(1, w["Hq"], w["Hkv"], 8192)
+    ws = torch.empty(L.migemm_attention_workspace_bytes(1, w["Hq"], w["D"], S), dtype=torch.uint8, device="cuda")
+    out = torch.empty(w["Hq"] * w["D"], dtype=torch.int16, device="cuda")
+    s = torch.cuda.Stream()
+
+    def call():
+        return L.attention_decode_bf16(dQ.data_ptr(), dK.data_ptr(), dV.data_ptr(), bt.data_ptr(),
+                                       sl.data_ptr(), out.data_ptr(), 1, w["Hq"], w["Hkv"], w["D"],
+                                       op["block_size"], op["max_blocks"], op["num_blocks"], scale, 8192, S,
+                                       ws.data_ptr(), ws.numel(), s.cuda_stream)
+    with torch.cuda.stream(s):
+        assert call() == 0
+    s.synchronize()
+    eager = out.clone()
+    g = torch.cuda.CUDAGraph()
+    with torch.cuda.graph(g, stream=s):
+        assert call() == 0
+    for r in range(4):
+        print("case graph replay", r, flush=True)
+        out.fill_(-1)
+        torch.cuda.synchronize()
+        g.replay()
+        torch.cuda.synchronize()
+        assert torch.equal(out, eager), r
+        _ = (dQ.float() * 2).sum().item()                # eager work between replays
