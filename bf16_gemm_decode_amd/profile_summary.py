@@ -9,6 +9,9 @@ profiles/.
                      --source <files...> --out <out.json> --commands "<cmd>" ...
   sweep-mfma:    python -m bf16_gemm_decode_amd.profile_summary sweep-mfma \
                      --util-csv <csv> --sweep-json <sweep stdout> --out <out.md> --command "<cmd>"
+  counters:      python -m bf16_gemm_decode_amd.profile_summary counters \
+                     --csv <counter_collection.csv> ... --kernel label=<substring> ... \
+                     --source <files...> --out <out.json> --commands "<cmd>" ...
   traffic:       python -m bf16_gemm_decode_amd.profile_summary traffic \
                      --fetch <csv> --fetch-cal <csv> --write <csv> --write-cal <csv> \
                      --kernel <name substring> --source <source files...> \
@@ -132,6 +135,39 @@ def traffic(args):
     print(json.dumps(out, indent=1))
 
 
+def counters(args):
+    """Every counter of the given --pmc runs, per kernel label: mean, min and
+    max over the matching dispatches, with their average duration."""
+    out = {"commands": args.commands, "kernels": {}}
+    rows = [r for path in args.csv for r in _rows(path)]
+    for spec in args.kernel:
+        label, substr = spec.split("=", 1)
+        per = collections.defaultdict(dict)     # counter -> {(file row set, dispatch): value}
+        dur = {}
+        for r in rows:
+            if substr not in r["Kernel_Name"]:
+                continue
+            key = (r["Counter_Name"], r["Dispatch_Id"], r["Kernel_Name"])
+            per[r["Counter_Name"]][key] = float(r["Counter_Value"])
+            dur[(r["Dispatch_Id"], r["Kernel_Name"], r["Counter_Name"])] = \
+                int(r["End_Timestamp"]) - int(r["Start_Timestamp"])
+        if not per:
+            sys.exit("no counter rows for kernel %r" % substr)
+        k = {"kernel_name_contains": substr, "counters": {}}
+        for name, vals in sorted(per.items()):
+            v = list(vals.values())
+            k["counters"][name] = {"mean": sum(v) / len(v), "min": min(v), "max": max(v),
+                                   "dispatches": len(v)}
+        d = list(dur.values())
+        k["avg_duration_ns"] = sum(d) / len(d)
+        out["kernels"][label] = k
+    out["kernel_sources"] = args.source
+    out["kernel_sources_sha256"] = source_digest(args.source)
+    with open(args.out, "w") as o:
+        json.dump(out, o, indent=1)
+    print(json.dumps(out, indent=1))
+
+
 def _per_dispatch(path, counter, substr):
     """{dispatch id: (value, duration in ns)} of one counter for the
     dispatches whose kernel name contains substr (rocprofv3's CSV holds one
@@ -245,6 +281,12 @@ def main(argv=None):
     m.add_argument("--source", nargs="+", required=True)
     m.add_argument("--out", required=True)
     m.add_argument("--commands", nargs="+", required=True)
+    c = sub.add_parser("counters")
+    c.add_argument("--csv", nargs="+", required=True, help="counter_collection CSVs of --pmc runs")
+    c.add_argument("--kernel", nargs="+", required=True, help="label=<kernel name substring>")
+    c.add_argument("--source", nargs="+", required=True)
+    c.add_argument("--out", required=True)
+    c.add_argument("--commands", nargs="+", required=True)
     w = sub.add_parser("sweep-mfma")
     w.add_argument("--util-csv", required=True)
     w.add_argument("--sweep-json", required=True, help="stdout of the profiled sweep.py run")
@@ -253,7 +295,8 @@ def main(argv=None):
     w.add_argument("--out", required=True)
     w.add_argument("--command", required=True)
     a = p.parse_args(argv)
-    {"stats": stats, "traffic": traffic, "mfma": mfma, "sweep-mfma": sweep_mfma}[a.mode](a)
+    {"stats": stats, "traffic": traffic, "mfma": mfma, "sweep-mfma": sweep_mfma,
+     "counters": counters}[a.mode](a)
 
 
 if __name__ == "__main__":

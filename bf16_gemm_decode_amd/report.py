@@ -165,6 +165,20 @@ def main(argv=None):
                  "frac_of_probe": round(gb / probe, 4)}
             rows.append(r)
             print(json.dumps(r), flush=True)
+    # the DCU page's section 6.2 knob: output rows of W per workgroup of the
+    # vector kernel, one token
+    _, X1 = synth.gemv_operands(M, K, 1, seed=wv["seed"]) if wv else (None, None)
+    dX1 = _dev(torch, X1) if wv else None
+    dY1 = torch.empty(M, dtype=torch.int16, device="cuda") if wv else None
+    for rpb in ((2, 4, 8, 16, 32) if wv else ()):
+        med, mn = _timer(torch, s, lambda i: L.gemv_bf16_ex(copies[i % 4].data_ptr(), dX1.data_ptr(),
+                                                             dY1.data_ptr(), M, K, 1, rpb, h), 40, a.rounds)
+        gb = rf.gemv_bytes(M, K, 1) / med / 1e9
+        r = {"workload": "gemv_34816x5120_bf16: rows_per_block sweep (vector kernel)", "n": 1,
+             "rows_per_block": rpb, "median_us": round(med * 1e6, 2), "min_us": round(mn * 1e6, 2),
+             "GBps": round(gb, 1), "util": round(gb / hbm, 4), "frac_of_probe": round(gb / probe, 4)}
+        rows.append(r)
+        print(json.dumps(r), flush=True)
     for n in ((4, 8, 16, 32, 64, 128, 256) if wv else ()):
         _, X = synth.gemv_operands(M, K, n, seed=wv["seed"])
         dX = _dev(torch, X)
@@ -325,6 +339,7 @@ def main(argv=None):
             f.write("|---|---|---|---|---|---|---|---|---|---|---|\n")
             for r in rows:
                 shape = ("%dx%dx%d" % (r["M"], r["N"], r["K"]) if "M" in r else
+                         "n=%d rows_per_block=%d" % (r["n"], r["rows_per_block"]) if "rows_per_block" in r else
                          "n=%d" % r["n"] if "n" in r else
                          "B=%d L=%d S=%d" % (r["B"], r["L"], r["segments"]) if "L" in r else "")
                 tile = ("%d (%s)" % (r["tile"], "x".join(str(v) for v in r["tile_mnk"]))

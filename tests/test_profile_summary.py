@@ -53,6 +53,25 @@ def test_traffic_scales_by_the_copy_reading(tmp_path):
     assert t["kernel_sources_sha256"] == ps.source_digest(["gemm.hip", "common.hpp"])
 
 
+def test_counters_per_kernel_label(tmp_path):
+    a = _write_csv(tmp_path / "a.csv", _counter_rows("TA_BUSY_avr", [
+        (1, "batch_rows_kernel<1, 1>", 10.0), (2, "attn_segment_kernel<256, 4>", 4.0),
+        (3, "batch_rows_kernel<1, 1>", 30.0)]))
+    b = _write_csv(tmp_path / "b.csv", _counter_rows("MemUnitStalled", [(1, "batch_rows_kernel<1, 1>", 2.0)]))
+    out = tmp_path / "c.json"
+    ps.main(["counters", "--csv", a, b, "--kernel", "rows=batch_rows_kernel", "attn=attn_segment",
+             "--source", "batch.hip", "--out", str(out), "--commands", "c"])
+    c = json.load(open(out))
+    rows = c["kernels"]["rows"]["counters"]
+    assert rows["TA_BUSY_avr"] == {"mean": 20.0, "min": 10.0, "max": 30.0, "dispatches": 2}
+    assert rows["MemUnitStalled"]["mean"] == 2.0
+    assert c["kernels"]["attn"]["counters"]["TA_BUSY_avr"]["dispatches"] == 1
+    assert c["kernels"]["rows"]["avg_duration_ns"] == 500
+    with pytest.raises(SystemExit):
+        ps.main(["counters", "--csv", a, "--kernel", "x=no_such_kernel", "--source", "batch.hip",
+                 "--out", str(out), "--commands", "c"])
+
+
 def test_timed_region_and_bench_line(tmp_path):
     stats = _write_csv(tmp_path / "s.csv", [{"Name": "gemm_fl_kernel<0, y>", "Calls": 5, "AverageNs": 1.0}])
     # dispatches of the GEMM: two warm-ups of 3000 ns, then 1000, 1100, 1200
