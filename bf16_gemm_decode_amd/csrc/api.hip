@@ -125,12 +125,15 @@ int plan_gemm(int dtype, const uint16_t *A, const uint16_t *B, const uint16_t *C
     auto auto_tile = [&]() {
         const int64_t t256 = cdiv(M, 256) * cdiv(N, 256), t2 = cdiv(M, 256) * cdiv(N, 128),
                       t128 = cdiv(M, 128) * cdiv(N, 128);
-        // Fewer than 128 tiles of 128x128: the time per k step (barrier and
-        // load latency, not the MFMAs) decides, so the most workgroups win:
-        // 64x64 when they fill half the chip, else 64x32 (FP16, measured:
-        // 512^3 8.0 us on 64x32 against 11.0 on 128x128, 768^3 11.9 on 64x64
-        // against 14.4, 1024^3 15.2 against 17.7).
-        if (fl && t128 < 128)
+        // Fewer than 128 tiles of 128x128 and a short K: the time per k
+        // step (barrier and load latency, not the MFMAs) decides, so the
+        // most workgroups win: 64x64 when they fill half the chip, else
+        // 64x32 (FP16, measured: 512^3 8.0 us on 64x32 against 11.0 on
+        // 128x128, 768^3 11.9 on 64x64 against 14.4, 1024^3 15.2 against
+        // 17.7, 512x512x2048 23.1 against 29.7).  Over a long K the
+        // 128x128 tile's throughput per CU wins again (512x512x131072: 1586
+        // us against 1831 on 64x32).
+        if (fl && t128 < 128 && K <= 8192)
             return cdiv(M, 64) * cdiv(N, 64) >= 128 ? (int)TILE_64x64_SK : (int)TILE_64x32_SK;
         int best = TILE_128x128;
         int64_t cost = INT64_MAX;

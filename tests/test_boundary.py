@@ -113,7 +113,8 @@ def test_tn_plan_and_errors():
     for kmaj in (False, True):
         for (M, N, K), (tile, grid) in (((512, 512, 512), (11, 128)), ((768, 768, 768), (12, 144)),
                                        ((1024, 1024, 1024), (12, 256)), ((1152, 1408, 256), (12, 396)),
-                                       ((1536, 1536, 256), (13 if kmaj else 3, 144))):
+                                       ((1536, 1536, 256), (13 if kmaj else 3, 144)),
+                                       ((512, 512, 131072), (13 if kmaj else 3, 16))):
             code, p = binding.gemm_plan(0, P, P + 2 ** 30, P + 2 ** 31, M, N, K, a_kmajor=kmaj)
             assert code == 0 and (p["tile"], p["grid"]) == (tile, grid), (M, N, K, kmaj, p)
     # the skinny tile: few columns only, and only with a k-major A
