@@ -13,14 +13,18 @@
 //    kernel (R = ceil(M / 256) rounded up to 8, at most 144: 136 rows of
 //    34816), so every CU streams the same share of W once.
 //  * A workgroup is 8 waves, two per SIMD, in two row groups (waves 0-3 the
-//    first 5 row tiles of 16, waves 4-7 the other 4) and four token groups
+//    first 7 row tiles of 16, waves 4-7 the other 2) and four token groups
 //    (TW = NT/4 tiles of 16 each); the two waves of a SIMD are one of each
-//    row group, so every SIMD multiplies all 9 row tiles.  Per 32-k step a
-//    wave reads its 5 (4) A operands and TW B operands from LDS for 5 TW
-//    (4 TW) MFMAs: 136 KiB of LDS reads per 64-k chunk at 256 tokens,
-//    against 288 KiB when every wave reads one operand per MFMA (one wave
-//    per 16 rows, every token).  The accumulators stay in AGPRs over all
-//    of K.
+//    row group, so every SIMD multiplies all 9 row tiles.  Waves 4-7 also
+//    issue every load of the ring: a load waits at issue while the memory
+//    pipe is backed up, and that stall then holds up only the wave with the
+//    smaller share of MFMAs while the other keeps the SIMD's matrix core
+//    busy (measured 99-109 against 111-127 us at 256 tokens with 5 + 4 row
+//    tiles and every wave loading).  Per 32-k step a wave reads its 7 (2) A
+//    operands and TW B operands from LDS for 7 TW (2 TW) MFMAs: 144 KiB of
+//    LDS reads per 64-k chunk at 256 tokens, against 288 KiB when every
+//    wave reads one operand per MFMA (one wave per 16 rows, every token).
+//    The accumulators stay in AGPRs over all of K.
 //  * K goes in chunks of 64 (one 128-byte line per row).  Both W's rows and
 //    X's token rows reach LDS by direct buffer loads (buffer_load ... lds),
 //    each instruction one 1 KiB half of a 16-row tile: 8 whole 128-byte
@@ -29,9 +33,9 @@
 //    in the order the operand reads want (below).  W's loads carry the
 //    non-temporal hint (each line is read once), which leaves L2 to the
 //    token rows every workgroup re-reads.  The 2 * (RT + NT) loads of a
-//    chunk go round-robin over the waves, padded to a multiple of 8 with
-//    loads of nothing, so every wave issues the same count and one counter
-//    wait plus one barrier per chunk order the ring.
+//    chunk go round-robin over the four loading waves, padded to a multiple
+//    of 4 with loads of nothing, so every loading wave issues the same count
+//    and one counter wait plus one barrier per chunk order the ring.
 //  * ST ring stages.  The wait and barrier for chunk c + 1 sit between the
 //    two 32-k steps of chunk c; the barrier also closes every wave's reads
 //    of chunk c, so chunk c + ST is loaded into that stage right after it.
@@ -65,7 +69,8 @@ namespace {
 
 constexpr int kWideWaves = 8;
 constexpr int kWideRT = 9;             // row tiles per workgroup (144 rows at most)
-constexpr int kWideRT0 = 5;            // row tiles of waves 0-3; waves 4-7 take the other 4
+constexpr int kWideRT0 = 7;            // row tiles of waves 0-3; waves 4-7 take the other 2
+constexpr int kWideLoaders = 4;        // waves 4-7 issue the ring's loads
 constexpr int kWideKC = 64;            // k per chunk
 constexpr int kTileBytes = 16 * kWideKC * 2;
 
@@ -98,14 +103,16 @@ __device__ inline int tile_slot(int r, int p)
 
 }  // namespace
 
-template <int DT, int NT, int ST>
+template <int DT, int NT, int ST, int RT0, int LW>
 __global__ void __launch_bounds__(64 * kWideWaves)
 batch_wide_kernel(const uint16_t *__restrict__ W, const uint16_t *__restrict__ X,
                   uint16_t *__restrict__ Y, int M, int K, int n, int R, int y_vec)
 {
     constexpr int TW = NT / 4;                            // token tiles per wave
     constexpr int NLOAD = 2 * (kWideRT + NT);             // 1 KiB loads per chunk
-    constexpr int Q = (NLOAD + kWideWaves - 1) / kWideWaves;   // per wave, padded
+    constexpr int Q = (NLOAD + LW - 1) / LW;              // per loading wave, padded
+    static_assert(LW == 4 || LW == 8, "loads by all waves or by waves 4-7");
+    static_assert(RT0 >= 1 && RT0 < kWideRT, "two row groups");
     constexpr int STAGE = (kWideRT + NT) * kTileBytes;
     constexpr int B_OFF = kWideRT * kTileBytes;           // B tiles after the A tiles
     static_assert(NT % 4 == 0 && ST >= 3, "token tiles per wave, ring depth");
@@ -134,7 +141,7 @@ batch_wide_kernel(const uint16_t *__restrict__ W, const uint16_t *__restrict__ X
     int pk[Q];
 #pragma unroll
     for (int i = 0; i < Q; ++i) {
-        const int id = wave + kWideWaves * i;             // load id within the chunk
+        const int id = (wave - (kWideWaves - LW)) + LW * i;  // load id within the chunk
         const int tile = (id >> 1) < kWideRT ? (id >> 1) : (id >> 1) - kWideRT;
         const int b = id & 1;
         const int q = (lane >> 3) ^ b;                    // tile row 8b + q
@@ -144,10 +151,11 @@ batch_wide_kernel(const uint16_t *__restrict__ W, const uint16_t *__restrict__ X
         if (id >= NLOAD) pk[i] = K;                       // padding: never in range
     }
     auto issue = [&](int c) {
+        if (wave < kWideWaves - LW) return;               // not a loading wave
         const uint32_t base = lds0 + (uint32_t)((c % ST) * STAGE);
 #pragma unroll
         for (int i = 0; i < Q; ++i) {
-            const int id = wave + kWideWaves * i;         // wave-uniform
+            const int id = (wave - (kWideWaves - LW)) + LW * i;  // wave-uniform
             const bool is_a = (id >> 1) < kWideRT;
             const uint32_t dst = id >= NLOAD ? lds0 + ST * STAGE
                                  : base + (is_a ? 0 : B_OFF) +
@@ -244,19 +252,19 @@ batch_wide_kernel(const uint16_t *__restrict__ W, const uint16_t *__restrict__ X
     };
     // waves w and w + 4 share a SIMD: one of each row group on every SIMD
     if (wave < 4)
-        run(std::integral_constant<int, 0>{}, std::integral_constant<int, kWideRT0>{});
+        run(std::integral_constant<int, 0>{}, std::integral_constant<int, RT0>{});
     else
-        run(std::integral_constant<int, kWideRT0>{}, std::integral_constant<int, kWideRT - kWideRT0>{});
+        run(std::integral_constant<int, RT0>{}, std::integral_constant<int, kWideRT - RT0>{});
 }
 
 namespace {
 
-template <int DT, int NT, int ST>
+template <int DT, int NT, int ST, int RT0 = kWideRT0, int LW = kWideLoaders>
 hipError_t launch_wide(const SkinnyLaunch &L, hipStream_t s)
 {
     const int R = batch_rows_per_workgroup(L.M);
     const dim3 grid((unsigned)((L.M + R - 1) / R), (unsigned)((L.n + NT * 16 - 1) / (NT * 16)));
-    hipLaunchKernelGGL((batch_wide_kernel<DT, NT, ST>), grid, dim3(64 * kWideWaves), 0, s, L.W, L.X, L.Y,
+    hipLaunchKernelGGL((batch_wide_kernel<DT, NT, ST, RT0, LW>), grid, dim3(64 * kWideWaves), 0, s, L.W, L.X, L.Y,
                        L.M, L.K, L.n, R, L.y_vec && R % 4 == 0);
     return hipGetLastError();
 }
