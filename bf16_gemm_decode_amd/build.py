@@ -15,7 +15,7 @@ CSRC = os.path.join(PKG, "csrc")
 INCLUDE = os.path.join(ROOT, "include")
 BUILD = os.path.join(PKG, "_build")
 LIB = os.path.join(PKG, "libmigemm.so")
-SOURCES = ["api.hip", "gemm.hip", "gemv.hip", "skinny.hip", "batch.hip", "wide.hip", "attention.hip"]
+SOURCES = ["api.hip", "gemm.hip", "gemv.hip", "skinny.hip", "batch.hip", "wide.hip", "small.hip", "attention.hip"]
 ARCH = "gfx950"
 FLAGS = ["-O3", "-std=c++17", "-fPIC", f"--offload-arch={ARCH}",
          "-Xclang", "-target-feature", "-Xclang", "-packed-fp32-ops",

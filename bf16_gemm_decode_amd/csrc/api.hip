@@ -108,6 +108,12 @@ int plan_gemm(int dtype, const uint16_t *A, const uint16_t *B, const uint16_t *C
     const bool wide = (L.vec_a == 8 && L.vec_b == 8);
     const bool fl = (L.vec_a >= 2 && L.vec_b >= 2);
     auto is_fl = [](int t) { return (t >= TILE_256x256_FL && t <= TILE_128x128_SK) || t == TILE_256x256_PP; };
+    // the small-problem kernel: 16-byte rows of B (and of a k-major A); an
+    // m-major A is read 2 bytes at a time; its grid's second dimension is
+    // the 32-column blocks
+    const bool small_ok = !q8 && L.vec_b == 8 && (!a_kmajor || L.vec_a == 8) && cdiv(N, 32) <= 65535;
+    if (tile == TILE_SMALL && !small_ok) return q8 ? MIGEMM_ERR_CONFIG : cdiv(N, 32) > 65535 ? MIGEMM_ERR_SIZE
+                                                                                           : MIGEMM_ERR_ALIGN;
     if (tile == TILE_AUTO && group_m == 0 && !q8) {
         const ShapeConfig *c = find_shape(dtype, a_kmajor, M, N, K);
         if (c && (wide || c->tile == TILE_128x128 || (fl && is_fl(c->tile)))) {
@@ -125,6 +131,7 @@ int plan_gemm(int dtype, const uint16_t *A, const uint16_t *B, const uint16_t *C
     auto auto_tile = [&]() {
         const int64_t t256 = cdiv(M, 256) * cdiv(N, 256), t2 = cdiv(M, 256) * cdiv(N, 128),
                       t128 = cdiv(M, 128) * cdiv(N, 128);
+        if (small_ok && cdiv(M, 32) * cdiv(N, 32) <= kSmallMaxTiles) return (int)TILE_SMALL;
         // Fewer than 128 tiles of 128x128 and a short K: the time per k
         // step (barrier and load latency, not the MFMAs) decides, so the
         // most workgroups win: 64x64 when they fill half the chip, else
@@ -179,7 +186,7 @@ int plan_gemm(int dtype, const uint16_t *A, const uint16_t *B, const uint16_t *C
         tile = auto_tile();
     } else if (is_decode_tile(tile)) {
         return MIGEMM_ERR_CONFIG;   // only with a k-major A (gemm_tn_ex)
-    } else if (tile != TILE_128x128 && !(wide || (fl && is_fl(tile)))) {
+    } else if (tile != TILE_128x128 && tile != TILE_SMALL && !(wide || (fl && is_fl(tile)))) {
         return MIGEMM_ERR_CONFIG;   // the other tiles load 16-byte (full-line: 4-byte aligned) rows
     }
     L.tile = tile;
@@ -222,6 +229,12 @@ hipError_t decode_launch(int tile, int dtype, const uint16_t *At, const uint16_t
                                      : batch_wide_launch(S, stream);
 }
 
+// gemm_launch, or the small-problem kernel for its tile
+hipError_t launch_gemm_or_small(const GemmLaunch &L, hipStream_t stream)
+{
+    return L.tile == TILE_SMALL ? small_launch(L, stream) : gemm_launch(L, stream);
+}
+
 int finish(hipError_t e, void *stream)
 {
     if (e != hipSuccess) return (int)e;
@@ -243,7 +256,7 @@ int gemm_ex(int dtype, const uint16_t *A, const uint16_t *B, uint16_t *C, int M,
     bool launch;
     int rc = plan_gemm(dtype, A, B, C, M, N, K, tile, group_m, xcd_remap, L, launch);
     if (rc != MIGEMM_OK || !launch) return rc;
-    return finish(gemm_launch(L, (hipStream_t)stream), stream);
+    return finish(launch_gemm_or_small(L, (hipStream_t)stream), stream);
 }
 
 int migemm_gemm_clocked(int dtype, const uint16_t *A, const uint16_t *B, uint16_t *C, int M, int N,
@@ -288,7 +301,7 @@ int gemm_tn_ex(int dtype, const uint16_t *At, const uint16_t *B, uint16_t *C, in
         // C(m,n) = sum_k At[k + m*K] B[k + n*K] is Y = X W^T with W = At,
         // X = B, Y = C, all row-major: the decode kernels' contract
         return finish(decode_launch(L.tile, dtype, At, B, C, M, N, K, L.c_vec, (hipStream_t)stream), stream);
-    return finish(gemm_launch(L, (hipStream_t)stream), stream);
+    return finish(launch_gemm_or_small(L, (hipStream_t)stream), stream);
 }
 
 // The automatic split: the 256x256 tile (10) with the smallest power-of-two
@@ -374,7 +387,7 @@ int gemm_splitk_ex(int dtype, int a_kmajor, const uint16_t *A, const uint16_t *B
     }
     if (is_decode_tile(L.tile))
         return finish(decode_launch(L.tile, dtype, A, B, C, M, N, K, L.c_vec, (hipStream_t)stream), stream);
-    return finish(gemm_launch(L, (hipStream_t)stream), stream);
+    return finish(launch_gemm_or_small(L, (hipStream_t)stream), stream);
 }
 
 int gemm_tn_q_ex(int qtype, const void *At, const void *B, uint16_t *C, int M, int N, int K,
@@ -441,6 +454,21 @@ static int plan_for(int dtype, const uint16_t *A, const uint16_t *B, const uint1
         plan->lds_bytes = 0;
         plan->tile = L.tile;
         plan->a_kmajor = 1;
+        return rc;
+    }
+    if (L.tile == TILE_SMALL) {
+        plan->tile_m = 32;
+        plan->tile_n = 32;
+        plan->tile_k = 32;
+        plan->waves = 4;                        // splitting K between them
+        plan->group_m = 1;
+        plan->xcd_remap = 0;
+        plan->vec_a = L.vec_a;
+        plan->vec_b = L.vec_b;
+        plan->grid = launch ? L.grid : 0;
+        plan->lds_bytes = kSmallLdsBytes;
+        plan->tile = L.tile;
+        plan->a_kmajor = a_kmajor ? 1 : 0;
         return rc;
     }
     if (L.tile == TILE_BATCH_ROWS || L.tile == TILE_BATCH_WIDE) {

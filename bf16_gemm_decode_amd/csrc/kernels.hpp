@@ -26,7 +26,8 @@ enum GemmTile {
     TILE_256x256_PP = 16,       // as 10, m-major A, ping-pong: the two waves of a SIMD alternate MFMA and memory phases
     TILE_256x128_F8W = 17,      // FP8 only, k-major A: 256x128, 8 waves of 64x64, whole 64-unit steps on the 16x16x128 MFMA
     TILE_BATCH_ROWS = 18,       // up to 256 columns: W's rows spread evenly, 9 waves of 16 rows per workgroup (batch.hip)
-    TILE_BATCH_WIDE = 19,       // up to 256 columns: W's rows spread evenly, 8 waves of 5 or 4 row tiles x a quarter of the columns (wide.hip)
+    TILE_BATCH_WIDE = 19,       // up to 256 columns: W's rows spread evenly, 8 waves of 7 or 2 row tiles x a quarter of the columns (wide.hip)
+    TILE_SMALL = 20,            // few output tiles: 32x32 per workgroup, 4 waves splitting K, no LDS staging (small.hip)
     TILE_COUNT
 };
 
@@ -58,6 +59,7 @@ constexpr TileShape kTileShapes[TILE_COUNT] = {
     {256, 128, 32, 3, 8, 3},
     {144, 256, 64, 0, 9, 0},
     {144, 256, 64, 0, 8, 0},
+    {32, 32, 32, 0, 4, 0},
 };
 
 // The full-line tiles with A k-major: stages = A ring stages of 64 k.
@@ -82,6 +84,7 @@ constexpr TileShape kTileShapesKmajorA[TILE_COUNT] = {
     {256, 128, 32, 3, 8, 3},
     {144, 256, 64, 0, 9, 0},
     {144, 256, 64, 0, 8, 0},
+    {32, 32, 32, 0, 4, 0},
 };
 
 constexpr int tile_lds_bytes(const TileShape &t, bool a_kmajor = false)
@@ -116,6 +119,14 @@ hipError_t splitk_reduce_launch(int dtype, const float *part, uint16_t *C, int64
                                 int splits, hipStream_t stream);
 
 hipError_t gemm_launch(const GemmLaunch &L, hipStream_t stream);
+// The small-problem kernel (small.hip): automatic while the 32x32 output
+// tiles number at most kSmallMaxTiles (measured, FP16: 512^3 4.2 us against
+// 7.9 on the 64x32 tile, 512x512x4096 21.5 against 54.6, 2048x256x512 6.2
+// against 8.2, 768^3 (576 tiles) 10.3 against 12.0 on 64x64; at 1024 tiles
+// (1024^3) it loses, 17.1 against 15.3).
+constexpr int kSmallMaxTiles = 768;
+constexpr int kSmallLdsBytes = 4 * 4 * 64 * 16;
+hipError_t small_launch(const GemmLaunch &L, hipStream_t stream);
 
 struct GemvLaunch {
     const uint16_t *W, *X;

@@ -230,9 +230,11 @@ size_t migemm_splitk_workspace_bytes(int M, int N, int splits);
  * the caller instead of chosen by the library:
  *   tile:    0 = automatic (with group_m 0: first an exact-shape table of
  *            measured configurations -- the headline FP16 GEMM, the prefill
- *            GEMM in both layouts, the ragged BF16 GEMM -- then the least
- *            estimated time over rounds of workgroups on the 256 CUs among
- *            tiles 16, 2 (9 without 16-byte rows) and 3); 1 = 256x256 (4 waves as 2x2, 4 LDS stages);
+ *            GEMM in both layouts, the ragged BF16 GEMM -- then tile 20 when
+ *            its 32x32 tiles number at most 768 and B has 16-byte rows, then
+ *            tile 12 or 11 below 128 tiles of 128x128 and K <= 8192, else the
+ *            least estimated time over rounds of workgroups on the 256 CUs
+ *            among tiles 16, 2 (9 without 16-byte rows) and 3); 1 = 256x256 (4 waves as 2x2, 4 LDS stages);
  *            2 = 256x128 (5 stages); 3 = 128x128 (4 stages, two workgroups
  *            per CU); 4 = tile 1 with 5 stages; 5 = 256x256 with the 4 waves
  *            stacked along M; 6 = tile 1 with 3 stages; 7 = 256x256, waves
@@ -256,10 +258,15 @@ size_t migemm_splitk_workspace_bytes(int M, int N, int splits);
  *            at most 144, 9 waves of 16 rows, 16..256 columns, K in steps of
  *            64, A read as whole lines through LDS, B staged in LDS); 19 =
  *            the wide row-balanced kernel (gemm_tn_* only, N <= 256: the
- *            same rows per workgroup, 8 waves in two row groups of 5 and 4
+ *            same rows per workgroup, 8 waves in two row groups of 7 and 2
  *            row tiles of 16 times four column groups, 128- or 256-column
  *            blocks, K in steps of 64, A and B both staged in LDS by direct
- *            loads).
+ *            loads); 20 = small problems: a 32x32 tile per workgroup whose 4
+ *            waves split K, operands read straight into MFMA registers, the
+ *            partial tiles summed in LDS (both layouts; B, and a k-major A,
+ *            with 16-byte rows, else MIGEMM_ERR_ALIGN; an m-major A of any M;
+ *            at most 65535 32-column blocks, else MIGEMM_ERR_SIZE; not for
+ *            8-bit types or split-K).
  *            All step K by 32.  Tiles 1, 2, 4, 5, 6 need 16-byte rows (M and
  *            K multiples of 8, A and B 16-byte aligned); the full-line tiles
  *            7 .. 13 and 16 need 4-byte rows (M and K even, A and B 4-byte

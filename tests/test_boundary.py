@@ -108,15 +108,32 @@ def test_tn_plan_and_errors():
     assert code == 0 and (p["tile_m"], p["tile_n"]) == (256, 128) and p["grid"] == 242   # one round
     code, p = binding.gemm_plan(1, P, P + 2 ** 30, P + 2 ** 31, 2048, 2048, 4096, a_kmajor=True)
     assert code == 0 and (p["tile"], p["grid"]) == (13, 256)
-    # fewer than 128 tiles of 128x128: the 64-row tiles (64x64 once they
-    # fill half the chip), both layouts
+    # at most 512 tiles of 32x32 (16-byte rows of B, and of a k-major A):
+    # the small-problem kernel; fewer than 128 tiles of 128x128: the 64-row
+    # tiles (64x64 once they fill half the chip), both layouts
     for kmaj in (False, True):
-        for (M, N, K), (tile, grid) in (((512, 512, 512), (11, 128)), ((768, 768, 768), (12, 144)),
-                                       ((1024, 1024, 1024), (12, 256)), ((1152, 1408, 256), (12, 396)),
+        for (M, N, K), (tile, grid) in (((512, 512, 512), (20, 256)), ((1024, 512, 4096), (20, 512)),
+                                       ((768, 768, 768), (20, 576)), ((1024, 768, 64), (20, 768)),
+                                       ((1056, 768, 64), (12, 204)), ((1024, 1024, 1024), (12, 256)),
+                                       ((1152, 1408, 256), (12, 396)),
                                        ((1536, 1536, 256), (13 if kmaj else 3, 144)),
-                                       ((512, 512, 131072), (13 if kmaj else 3, 16))):
+                                       ((512, 512, 131072), (20, 256))):
             code, p = binding.gemm_plan(0, P, P + 2 ** 30, P + 2 ** 31, M, N, K, a_kmajor=kmaj)
             assert code == 0 and (p["tile"], p["grid"]) == (tile, grid), (M, N, K, kmaj, p)
+    # the small kernel's plan, and where it is not offered: B without 16-byte
+    # rows (K % 8), a k-major A without them, 8-bit types, more than 65535
+    # column blocks; an m-major A may have any M
+    code, p = binding.gemm_plan(1, P, P + 2 ** 30, P + 2 ** 31, 513, 511, 520)
+    assert code == 0 and (p["tile"], p["tile_m"], p["tile_n"], p["tile_k"], p["waves"], p["grid"], p["lds_bytes"]) == \
+        (20, 32, 32, 32, 4, 17 * 16, 16384)
+    assert binding.gemm_plan(1, P, P + 2 ** 30, P + 2 ** 31, 512, 512, 516)[1]["tile"] != 20
+    assert binding.gemm_plan(1, P + 2, P + 2 ** 30, P + 2 ** 31, 512, 512, 520, a_kmajor=True)[1]["tile"] != 20
+    assert binding.gemm_plan(1, P, P + 2 ** 30, P + 2 ** 31, 512, 512, 516, 20)[0] == -4
+    assert binding.gemm_plan(1, P + 2, P + 2 ** 30, P + 2 ** 31, 512, 512, 520, 20, a_kmajor=True)[0] == -4
+    assert binding.gemm_plan(1, P, P + 2 ** 30, P + 2 ** 31, 64, (65536 * 32) + 1, 64, 20)[0] == -6
+    assert binding.gemm_plan(2, P, P + 2 ** 30, P + 2 ** 31, 512, 512, 512, 20, a_kmajor=True)[0] == -5
+    code, p = binding.gemm_plan(1, P, P + 2 ** 30, P + 2 ** 31, 8192, 8192, 512, 20)
+    assert code == 0 and p["grid"] == 256 * 256                   # explicit: any tile count
     # the skinny tile: few columns only, and only with a k-major A
     code, p = binding.gemm_plan(1, P, P + 2 ** 30, P + 2 ** 31, 34816, 8, 5120, 14, a_kmajor=True)
     assert code == 0 and (p["tile"], p["tile_m"], p["tile_n"], p["waves"], p["grid"]) == (14, 32, 8, 4, 1088)

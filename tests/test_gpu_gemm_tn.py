@@ -14,7 +14,7 @@ from helpers import assert_parity, gemm_gpu, gemm_tn_gpu, gemv_gpu, kmajor_to_co
 pytestmark = pytest.mark.gpu
 
 FMTS = ["f16", "bf16"]
-TN_TILES = [0, 7, 8, 9, 10, 11, 12, 13]
+TN_TILES = [0, 7, 8, 9, 10, 11, 12, 13, 20]
 
 
 def _tn_case(M, N, K, fmt, seed, tile=0, dist=("normal", 1.0, 1.0)):
@@ -35,7 +35,7 @@ def test_tn_each_tile_ragged(tile, fmt):
     _tn_case(520, 600, 200, fmt, seed=800 + tile, tile=tile)
 
 
-@pytest.mark.parametrize("tile", [7, 9, 10, 11, 12, 13])
+@pytest.mark.parametrize("tile", [7, 9, 10, 11, 12, 13, 20])
 def test_tn_short_and_ragged_k(tile):
     for i, K in enumerate([8, 32, 40, 64, 72, 96, 136, 264, 520]):
         fmt = FMTS[i % 2]
@@ -83,7 +83,7 @@ def test_tn_matches_column_major_path_bit_for_bit():
     for fmt in FMTS:
         At, B = synth.gemm_operands(M, N, K, fmt, ("uniform", 1.0, 1.0), seed=31)
         A = kmajor_to_colmajor(At, M, K)
-        for tile in (7, 8, 10, 11, 12, 13):
+        for tile in (7, 8, 10, 11, 12, 13, 20):
             print("case bitwise tile", tile, fmt, flush=True)
             tn, _, _ = gemm_tn_gpu(At, B, M, N, K, fmt, tile=tile)
             cm, _, _ = gemm_gpu(A, B, M, N, K, fmt, tile=tile)
