@@ -10,7 +10,7 @@ Printed: one JSON line.  `value` is the GEMM's TFLOP/s (2*M*N*K per launch over
 the average launch time measured with HIP events on the launch stream); the
 GEMV's HBM GB/s is reported beside it with its own roofline, against both the
 8 TB/s nominal peak and the read bandwidth measured here by the streaming-read
-probe; its launch duration comes from a burst of back-to-back launches on the
+probe (over 4 GiB, and over W's 356.5 MB, where the launch ramp weighs more); its launch duration comes from a burst of back-to-back launches on the
 same stream (inside a step the events also hold the dispatch gap, reported as
 in_step_avg_us).  `cpu_baseline` times the CPU oracle on a bounded sample of the same
 GEMM (sampled output entries), scaled to TFLOP/s.
@@ -75,23 +75,33 @@ def dev(bits):
     return torch.from_numpy(np.ascontiguousarray(bits).view(np.int16)).cuda()
 
 
-def hbm_probe(binding, torch, stream, nbytes=4 << 30, reps=20):
-    """Median achievable read bandwidth (GB/s) of the streaming-read probe."""
-    buf = torch.empty(nbytes // 4, dtype=torch.int32, device="cuda")
+def hbm_probe(binding, torch, stream, nbytes=4 << 30, copies=1, burst=4, rounds=7):
+    """Achievable read bandwidth (GB/s) of the streaming-read probe, timed like
+    the GEMV: bursts of back-to-back launches between two events on the
+    launch stream (median per-launch time over the rounds); launch i reads
+    copy i % copies of an nbytes region."""
+    buf = torch.empty(nbytes * copies // 4, dtype=torch.int32, device="cuda")
     buf.fill_(7)
     sink = torch.zeros(binding.hbm_read_sink_words(), dtype=torch.int32, device="cuda")
+    h = stream.cuda_stream
+
+    def launch(i):
+        code = binding.lib().migemm_hbm_read(buf.data_ptr() + (i % copies) * nbytes, nbytes,
+                                             sink.data_ptr(), h)
+        assert code == 0, code
+
     ts = []
     with torch.cuda.stream(stream):
-        for i in range(reps + 3):
+        for i in range(2):
+            launch(i)
+        for _ in range(rounds):
             e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
             e0.record(stream)
-            code = binding.lib().migemm_hbm_read(buf.data_ptr(), nbytes, sink.data_ptr(),
-                                                 stream.cuda_stream)
+            for i in range(burst):
+                launch(i)
             e1.record(stream)
-            assert code == 0, code
             stream.synchronize()
-            if i >= 3:
-                ts.append(e0.elapsed_time(e1) / 1e3)
+            ts.append(e0.elapsed_time(e1) / 1e3 / burst)
     ts.sort()
     del buf
     return nbytes / ts[len(ts) // 2] / 1e9
@@ -279,6 +289,7 @@ def main():
     torch.cuda.synchronize()
 
     probe_GBps = hbm_probe(binding, torch, stream)
+    probe_w_GBps = hbm_probe(binding, torch, stream, nbytes=GM * GK * 2, copies=4, burst=20)   # W's size
 
     L = binding.lib()
     h = stream.cuda_stream
@@ -471,7 +482,9 @@ def main():
                               "traffic": measured_traffic(GEMV_SOURCES, "gemv_34816x5120_bf16_n1_traffic.json"),
                               "algorithmic_bytes": int(gemv_bytes)},
                  "probe_read_GBps": round(probe_GBps, 1),
-                 "frac_of_probe": round(gemv_GBps / probe_GBps, 4)},
+                 "frac_of_probe": round(gemv_GBps / probe_GBps, 4),
+                 "probe_read_GBps_at_w_size": round(probe_w_GBps, 1),
+                 "frac_of_probe_at_w_size": round(gemv_GBps / probe_w_GBps, 4)},
         "attention": {"workload": "%s, 1 sequence of %d tokens" % (ATT_CFG, ATT_LEN),
                       "segments": segs, "avg_call_us": round(att_avg * 1e6, 2),
                       "calls_timed": natt, "kernels": "attn_segment_kernel + attn_merge_kernel",

@@ -174,12 +174,15 @@ hipError_t gemv_launch(const GemvLaunch &L, hipStream_t s)
 
 // ---- streaming-read probe ------------------------------------------------
 
-constexpr int kProbeWaves = 8192;        // one-wave workgroups, 32 per CU
+constexpr int kProbeWaves = 768;         // one-wave workgroups, 3 per CU
 constexpr int kProbeChunk = 8 * 64;      // 16-byte words per wave per step (8 KiB)
 
 // Wave w reads the 8 KiB chunks w, w + kProbeWaves, ...: each lane keeps
 // eight 16-byte non-temporal loads in flight, a wave's loads of one chunk
-// cover it contiguously.  The words past the last whole chunk are read
+// cover it contiguously.  The grid size was swept (512 .. 8192 waves, 4 or
+// 16 loads per lane): 3 waves per CU (6 MiB in flight over the chip) read
+// fastest at 4 GiB and at 356 MB; more waves keep more requests in flight
+// and read a few percent slower, fewer cannot cover the latency.  The words past the last whole chunk are read
 // grid-stride.  sink[w] receives the XOR of every 32-bit word wave w read,
 // so the XOR of all sink words equals the XOR of the buffer.
 __global__ void __launch_bounds__(64) hbm_read_kernel(const u32x4 *__restrict__ buf, size_t n16,

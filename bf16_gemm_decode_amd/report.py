@@ -146,10 +146,18 @@ def main(argv=None):
     pmed, pmin = _timer(torch, s, lambda i: L.migemm_hbm_read(probe_buf.data_ptr(), 4 << 30,
                                                                sink.data_ptr(), h), 5, a.rounds)
     probe = (4 << 30) / pmed / 1e9
-    del probe_buf
     rows.append({"workload": "hbm_read probe (4 GiB)", "median_us": round(pmed * 1e6, 1),
                  "GBps": round(probe, 1), "util": round(probe / hbm, 4)})
     print(json.dumps(rows[-1]), flush=True)
+    if wv:
+        wb = M * K * 2          # one copy of W; launches rotate over 4 disjoint regions like the GEMV
+        wmed, wmin = _timer(torch, s, lambda i: L.migemm_hbm_read(probe_buf.data_ptr() + (i % 4) * wb, wb,
+                                                                   sink.data_ptr(), h), 5, a.rounds)
+        rows.append({"workload": "hbm_read probe (W's %.1f MB)" % (wb / 1e6), "median_us": round(wmed * 1e6, 1),
+                     "min_us": round(wmin * 1e6, 1), "GBps": round(wb / wmed / 1e9, 1),
+                     "util": round(wb / wmed / 1e9 / hbm, 4)})
+        print(json.dumps(rows[-1]), flush=True)
+    del probe_buf
     for n in ((1, 2, 3, 4, 8, 16) if wv else ()):
         _, X = synth.gemv_operands(M, K, n, seed=wv["seed"])
         dX = _dev(torch, X)

@@ -388,8 +388,9 @@ int migemm_abi_version(void);
 
 /*
  * Streaming-read bandwidth probe: reads `bytes` bytes from device buffer
- * `buf` once (each wave reads contiguous 8 KiB chunks with eight 16-byte
- * non-temporal loads per lane in flight) and writes one 32-bit XOR
+ * `buf` once (768 one-wave workgroups, 3 per CU; each wave reads contiguous
+ * 8 KiB chunks with eight 16-byte non-temporal loads per lane in flight,
+ * the grid size that read fastest when swept) and writes one 32-bit XOR
  * checksum per wave to `sink` (device, migemm_hbm_read_sink_words() words;
  * the XOR of all of them is the XOR of the buffer's 32-bit words).
  * `bytes` must be a multiple of 16 and `buf` 16-byte aligned.  Used to
