@@ -460,13 +460,13 @@ static int plan_for(int dtype, const uint16_t *A, const uint16_t *B, const uint1
         plan->tile_m = 32;
         plan->tile_n = 32;
         plan->tile_k = 32;
-        plan->waves = 4;                        // splitting K between them
+        plan->waves = small_waves(cdiv(M, 32) * cdiv(N, 32), K);   // splitting K between them
         plan->group_m = 1;
         plan->xcd_remap = 0;
         plan->vec_a = L.vec_a;
         plan->vec_b = L.vec_b;
         plan->grid = launch ? L.grid : 0;
-        plan->lds_bytes = kSmallLdsBytes;
+        plan->lds_bytes = small_lds_bytes(cdiv(M, 32) * cdiv(N, 32), K);
         plan->tile = L.tile;
         plan->a_kmajor = a_kmajor ? 1 : 0;
         return rc;

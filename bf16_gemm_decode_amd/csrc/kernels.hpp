@@ -125,7 +125,12 @@ hipError_t gemm_launch(const GemmLaunch &L, hipStream_t stream);
 // against 8.2, 768^3 (576 tiles) 10.3 against 12.0 on 64x64; at 1024 tiles
 // (1024^3) it loses, 17.1 against 15.3).
 constexpr int kSmallMaxTiles = 768;
-constexpr int kSmallLdsBytes = 4 * 4 * 64 * 16;
+// Waves per tile, splitting K: 8 for at most 256 tiles with K >= 1024, else 4
+// (measured, FP16: 512x512xK 5.9 / 9.4 / 19.0 / 66.7 us at K = 1024 / 2048 /
+// 4096 / 16384 against 6.3 / 10.2 / 21.7 / 79.8 with 4; 16 waves no better;
+// with more tiles the extra waves only wait: 768x768x4096 47.5 against 45.2).
+constexpr int small_waves(int64_t tiles, int K) { return tiles <= 256 && K >= 1024 ? 8 : 4; }
+constexpr int small_lds_bytes(int64_t tiles, int K) { return small_waves(tiles, K) * 4 * 64 * 16; }
 hipError_t small_launch(const GemmLaunch &L, hipStream_t stream);
 
 struct GemvLaunch {

@@ -8,17 +8,18 @@
 //
 // At these sizes the tiled kernels wait on one chain per k step (a barrier,
 // the operand reads, the MFMAs) over all of K, with most CUs idle.  Here a
-// workgroup of 4 waves owns one 32x32 tile of C and the waves split K
-// between them (wave w takes the 32-k steps w, w + 4, ...), so each wave
-// walks a quarter of the steps:
+// workgroup of NW waves (4, or 8 when K is long) owns one 32x32 tile of
+// C and the waves split K between them (wave w takes the 32-k steps w,
+// w + NW, ...), so each wave walks 1/NW of the steps:
 //  * no LDS staging: a wave loads its operands straight into the 16x16x32
 //    MFMA layout (lane (g, r): row or column r of a 16-wide block, k 8g ..
 //    8g+7 of the step).  B's column and a k-major A's row are 16 contiguous
 //    bytes; an m-major A gives each lane 8 values one row of A apart (2-byte
 //    loads, 16 lanes reading 32 contiguous bytes per k);
 //  * two steps' loads in flight per wave before their MFMAs;
-//  * the 4 waves' 32x32 FP32 partials meet in LDS (16 KiB), one thread sums
-//    the four of each output element and rounds it once to FP16/BF16.
+//  * the NW waves' 32x32 FP32 partials meet in LDS (4 KiB per wave), one
+//    thread sums the NW of each output element and rounds it once to
+//    FP16/BF16.
 // Elements past M, N or K read as zero (from a zero block) and are never
 // stored.  B (and a k-major A) must have 16-byte rows: K a multiple of 8 and
 // 16-byte aligned base pointers; an m-major A may have any M.
@@ -29,7 +30,6 @@ namespace migemm {
 
 namespace {
 
-constexpr int kSmallWaves = 4;
 constexpr int kSmallSteps = 2;            // 32-k steps a wave loads before multiplying
 
 // 16 zero bytes in device memory: masked lanes load from here.
@@ -51,12 +51,13 @@ __device__ inline void small_mfma(f32x4 &acc, u32x4 a, u32x4 b)
 
 }  // namespace
 
-template <int DT, bool AK>
-__global__ void __launch_bounds__(64 * kSmallWaves)
+template <int DT, bool AK, int NW>
+__global__ void __launch_bounds__(64 * NW)
 small_gemm_kernel(const uint16_t *__restrict__ A, const uint16_t *__restrict__ B,
                   uint16_t *__restrict__ C, int M, int N, int K)
 {
-    __shared__ f32x4 part[kSmallWaves][4][64];
+    static_assert(NW == 4 || NW == 8, "waves per tile");
+    __shared__ f32x4 part[NW][4][64];
     const int lane = threadIdx.x & 63, w = threadIdx.x >> 6;
     const int g = lane >> 4, r16 = lane & 15;
     const int m0 = blockIdx.x * 32, n0 = blockIdx.y * 32;
@@ -68,11 +69,11 @@ small_gemm_kernel(const uint16_t *__restrict__ A, const uint16_t *__restrict__ B
 #pragma unroll
         for (int j = 0; j < 2; ++j) acc[i][j] = f32x4{0.f, 0.f, 0.f, 0.f};
 
-    for (int s0 = w; s0 < steps; s0 += kSmallWaves * kSmallSteps) {
+    for (int s0 = w; s0 < steps; s0 += NW * kSmallSteps) {
         u32x4 a[kSmallSteps][2], b[kSmallSteps][2];
 #pragma unroll
         for (int q = 0; q < kSmallSteps; ++q) {
-            const int s = s0 + kSmallWaves * q;
+            const int s = s0 + NW * q;
             const int k0 = 32 * s + 8 * g;                     // this lane's 8 k of step s
             const bool kin = s < steps && k0 < K;              // K % 8 == 0: all 8 in or out
 #pragma unroll
@@ -109,11 +110,12 @@ small_gemm_kernel(const uint16_t *__restrict__ A, const uint16_t *__restrict__ B
 #pragma unroll
         for (int j = 0; j < 2; ++j) part[w][2 * i + j][lane] = acc[i][j];
     __syncthreads();
-    // thread (w, lane) sums block w's lane over the 4 waves: rows 4g .. 4g+3
-    // of the block, column r16
+    // thread (w, lane), w < 4, sums block w's lane over the NW waves: rows
+    // 4g .. 4g+3 of the block, column r16
+    if (w >= 4) return;
     f32x4 t = part[0][w][lane];
 #pragma unroll
-    for (int v = 1; v < kSmallWaves; ++v) {
+    for (int v = 1; v < NW; ++v) {
         const f32x4 u = part[v][w][lane];
         t = f32x4{t[0] + u[0], t[1] + u[1], t[2] + u[2], t[3] + u[3]};
     }
@@ -126,17 +128,24 @@ small_gemm_kernel(const uint16_t *__restrict__ A, const uint16_t *__restrict__ B
     }
 }
 
-template <int DT>
-static hipError_t small_launch_dt(const GemmLaunch &L, hipStream_t s)
+template <int DT, int NW>
+static hipError_t small_launch_nw(const GemmLaunch &L, hipStream_t s)
 {
     const dim3 grid((unsigned)((L.M + 31) / 32), (unsigned)((L.N + 31) / 32));
     if (L.a_kmajor)
-        hipLaunchKernelGGL((small_gemm_kernel<DT, true>), grid, dim3(64 * kSmallWaves), 0, s, L.A, L.B, L.C,
+        hipLaunchKernelGGL((small_gemm_kernel<DT, true, NW>), grid, dim3(64 * NW), 0, s, L.A, L.B, L.C,
                            L.M, L.N, L.K);
     else
-        hipLaunchKernelGGL((small_gemm_kernel<DT, false>), grid, dim3(64 * kSmallWaves), 0, s, L.A, L.B, L.C,
+        hipLaunchKernelGGL((small_gemm_kernel<DT, false, NW>), grid, dim3(64 * NW), 0, s, L.A, L.B, L.C,
                            L.M, L.N, L.K);
     return hipGetLastError();
+}
+
+template <int DT>
+static hipError_t small_launch_dt(const GemmLaunch &L, hipStream_t s)
+{
+    const int64_t tiles = (int64_t)((L.M + 31) / 32) * ((L.N + 31) / 32);
+    return small_waves(tiles, L.K) == 8 ? small_launch_nw<DT, 8>(L, s) : small_launch_nw<DT, 4>(L, s);
 }
 
 hipError_t small_launch(const GemmLaunch &L, hipStream_t s)

@@ -262,7 +262,8 @@ size_t migemm_splitk_workspace_bytes(int M, int N, int splits);
  *            row tiles of 16 times four column groups, 128- or 256-column
  *            blocks, K in steps of 64, A and B both staged in LDS by direct
  *            loads); 20 = small problems: a 32x32 tile per workgroup whose 4
- *            waves split K, operands read straight into MFMA registers, the
+ *            waves (8 for at most 256 tiles with K >= 1024) split K,
+ *            operands read straight into MFMA registers, the
  *            partial tiles summed in LDS (both layouts; B, and a k-major A,
  *            with 16-byte rows, else MIGEMM_ERR_ALIGN; an m-major A of any M;
  *            at most 65535 32-column blocks, else MIGEMM_ERR_SIZE; not for

@@ -126,6 +126,11 @@ def test_tn_plan_and_errors():
     code, p = binding.gemm_plan(1, P, P + 2 ** 30, P + 2 ** 31, 513, 511, 520)
     assert code == 0 and (p["tile"], p["tile_m"], p["tile_n"], p["tile_k"], p["waves"], p["grid"], p["lds_bytes"]) == \
         (20, 32, 32, 32, 4, 17 * 16, 16384)
+    # 8 waves once there are at most 256 tiles and K >= 1024
+    for (M, N, K), waves in (((512, 512, 1016), 4), ((512, 512, 1024), 8), ((544, 512, 1024), 4),
+                             ((256, 256, 32768), 8), ((768, 768, 4096), 4)):
+        code, p = binding.gemm_plan(1, P, P + 2 ** 30, P + 2 ** 31, M, N, K)
+        assert code == 0 and (p["tile"], p["waves"], p["lds_bytes"]) == (20, waves, waves * 4096), (M, N, K, p)
     assert binding.gemm_plan(1, P, P + 2 ** 30, P + 2 ** 31, 512, 512, 516)[1]["tile"] != 20
     assert binding.gemm_plan(1, P + 2, P + 2 ** 30, P + 2 ** 31, 512, 512, 520, a_kmajor=True)[1]["tile"] != 20
     assert binding.gemm_plan(1, P, P + 2 ** 30, P + 2 ** 31, 512, 512, 516, 20)[0] == -4

@@ -91,12 +91,14 @@ def test_full_line_tiles_4byte_rows(tile):
 
 
 def test_small_tile_shapes_and_k():
-    # tile 20 (32x32 per workgroup, K split over 4 waves, operands straight
-    # from memory, partials summed in LDS): any M for an m-major A (2-byte
-    # loads), ragged N, K from one 8-element piece to several thousand with
-    # tails inside a 32-k step, more k steps than waves and fewer
+    # tile 20 (32x32 per workgroup, K split over 4 waves, or 8 for at most
+    # 256 tiles with K >= 1024; operands straight from memory, partials
+    # summed in LDS): any M for an m-major A (2-byte loads), ragged N, K from
+    # one 8-element piece to several thousand with tails inside a 32-k step,
+    # more k steps than waves and fewer
     for i, (M, N, K) in enumerate([(513, 511, 520), (1, 1, 8), (33, 17, 40), (100, 70, 200), (31, 129, 4104),
-                                   (512, 512, 512), (7, 300, 72), (250, 5, 2048)]):
+                                   (512, 512, 512), (7, 300, 72), (250, 5, 2048), (64, 64, 1032),
+                                   (300, 200, 1024)]):
         for fmt in FMTS:
             print("case small tile", (M, N, K), fmt, flush=True)
             _full_case(M, N, K, fmt, seed=1500 + i, tile=20)
