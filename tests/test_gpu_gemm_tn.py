@@ -35,6 +35,16 @@ def test_tn_each_tile_ragged(tile, fmt):
     _tn_case(520, 600, 200, fmt, seed=800 + tile, tile=tile)
 
 
+@pytest.mark.parametrize("fmt", FMTS)
+def test_tn_small_tile_eight_waves(fmt):
+    # tile 20 with a k-major A where K is split over 8 waves (at most 256
+    # output tiles and K >= 1024): K tails inside a 32-k step, more steps than
+    # waves, ragged M and N
+    for i, (M, N, K) in enumerate([(300, 200, 1032), (64, 64, 4104), (31, 129, 2048), (513, 40, 1024)]):
+        print("case tn small tile 8 waves", (M, N, K), fmt, flush=True)
+        _tn_case(M, N, K, fmt, seed=1700 + i, tile=20)
+
+
 @pytest.mark.parametrize("tile", [7, 9, 10, 11, 12, 13, 20])
 def test_tn_short_and_ragged_k(tile):
     for i, K in enumerate([8, 32, 40, 64, 72, 96, 136, 264, 520]):
