@@ -19,9 +19,10 @@
 // caches serve).  A K or V row of D BF16 values is D/8 lanes x 16 bytes, so
 // one wave load reads 64/(D/8) whole rows (2 rows of 512 B at D = 256): full
 // cache lines.  The 4 waves split the segment's tokens and walk them in
-// steps of 16 tokens, double-buffered in registers (the next step's rows
-// in flight while one is computed, the page ids of the step after that on
-// their way; each lane reads the block-table entry of its own row).  Per
+// steps of 16 tokens, double-buffered in registers: the next step's K rows
+// are requested before a step and its V rows half way through it (before
+// prob V), the page ids of the step after that on their way (each lane
+// reads the block-table entry of its own row).  Per
 // step, q K^T is one 16-token x 16-head tile on the matrix cores, the
 // online softmax runs once per (token, head), and prob V runs on the vector
 // ALUs; the details are at the kernel.  At the end the token slots of a
@@ -177,8 +178,9 @@ attn_segment_kernel(const uint16_t *__restrict__ Q, const uint16_t *__restrict__
             pg[u] = t + TPI * u + slot < w1 ? v : -1;
         }
     };
-    // K and V loads of a step (non-temporal); masked rows read zeros
-    auto issue = [&](int t, const int (&pg)[U], u32x4 (&kr)[U], u32x4 (&vr)[U], bool (&ok)[U]) {
+    // K loads of a step (non-temporal), keeping each row's validity and
+    // offset for the V loads; masked rows read zeros
+    auto issue_k = [&](int t, const int (&pg)[U], u32x4 (&kr)[U], bool (&ok)[U], size_t (&of)[U]) {
         const int pf = t / block_size;
         const int r0 = t - pf * block_size;
 #pragma unroll
@@ -189,13 +191,20 @@ attn_segment_kernel(const uint16_t *__restrict__ Q, const uint16_t *__restrict__
             if (in < 0) in += block_size;
             else if (in >= block_size) in -= block_size;
             ok[u] = pg[u] >= 0 && pg[u] < num_blocks;
-            const size_t off = ((size_t)pg[u] * block_size + in) * row_stride + lane_off;
-            kr[u] = __builtin_nontemporal_load((attn_gptr16)(ok[u] ? Kc + off : kAttnZeros));
-            vr[u] = __builtin_nontemporal_load((attn_gptr16)(ok[u] ? Vc + off : kAttnZeros));
+            of[u] = ((size_t)pg[u] * block_size + in) * row_stride + lane_off;
+            kr[u] = __builtin_nontemporal_load((attn_gptr16)(ok[u] ? Kc + of[u] : kAttnZeros));
         }
     };
+    auto issue_v = [&](u32x4 (&vr)[U], const bool (&ok)[U], const size_t (&of)[U]) {
+#pragma unroll
+        for (int u = 0; u < U; ++u)
+            vr[u] = __builtin_nontemporal_load((attn_gptr16)(ok[u] ? Vc + of[u] : kAttnZeros));
+    };
 
-    auto step = [&](const u32x4 (&kr)[U], const u32x4 (&vr)[U], const bool (&ok)[U]) {
+    // `mid` runs between the softmax and prob x V: it requests the next
+    // step's V rows, so about one and a half steps of K and V are in flight
+    // (measured: faster than two whole steps, and than one)
+    auto step = [&](const u32x4 (&kr)[U], const u32x4 (&vr)[U], const bool (&ok)[U], auto &&mid) {
         // K rows into the tile, token validity beside them
 #pragma unroll
         for (int u = 0; u < U; ++u) {
@@ -239,6 +248,7 @@ attn_segment_kernel(const uint16_t *__restrict__ Q, const uint16_t *__restrict__
             if (g == 0) ct[wave][r16] = corr;
         }
         __builtin_amdgcn_s_waitcnt(0xc07f);
+        mid();
         // prob x V for this lane's tokens
         const f32x4 cr = *(const f32x4 *)ct[wave];
 #pragma unroll
@@ -261,24 +271,26 @@ attn_segment_kernel(const uint16_t *__restrict__ Q, const uint16_t *__restrict__
         }
     };
 
-    // two register buffers: while one step is computed the next one's K and
-    // V are in flight; each step's page ids are requested before the loads
-    // issued alongside them
+    // two register buffers: while one step is computed the next one's K is
+    // in flight and its V is requested half way; each step's page ids are
+    // requested two steps ahead
     u32x4 ka[U], va[U], kb2[U], vb2[U];
     bool oka[U], okb[U];
+    size_t oa[U], ob[U];
     int pa[U], pb[U];
     page_ids(w0, pa);
     page_ids(w0 + T, pb);
-    issue(w0, pa, ka, va, oka);
+    issue_k(w0, pa, ka, oka, oa);
+    issue_v(va, oka, oa);
     store_q();
     for (int t0 = w0; t0 < w1; t0 += 2 * T) {
         page_ids(t0 + 2 * T, pa);
-        issue(t0 + T, pb, kb2, vb2, okb);
-        step(ka, va, oka);
+        issue_k(t0 + T, pb, kb2, okb, ob);
+        step(ka, va, oka, [&] { issue_v(vb2, okb, ob); });
         if (t0 + T >= w1) break;
         page_ids(t0 + 3 * T, pb);
-        issue(t0 + 2 * T, pa, ka, va, oka);
-        step(kb2, vb2, okb);
+        issue_k(t0 + 2 * T, pa, ka, oka, oa);
+        step(kb2, vb2, okb, [&] { issue_v(va, oka, oa); });
     }
 
     // the token slots of a wave share the running max: add their outputs
