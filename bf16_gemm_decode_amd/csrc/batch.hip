@@ -381,18 +381,32 @@ int batch_rows_per_workgroup(int M)
     return R < 8 ? 8 : (R > 16 * kRowWaves ? 16 * kRowWaves : R);
 }
 
-template <int DT, int NTT>
-static hipError_t launch_rows_ntt(const SkinnyLaunch &L, hipStream_t s)
+template <int DT, int NTT, int U>
+static hipError_t launch_rows_ntt_u(const SkinnyLaunch &L, int R, hipStream_t s)
 {
-    // W chunks in flight; X staged one chunk ahead for 256 tokens (the
-    // second staging set would not fit the 168 registers of 9 waves)
-    constexpr int U = NTT >= 16 ? 2 : NTT >= 4 ? 4 : 8;
+    // X staged one chunk ahead for 256 tokens (the second staging set would
+    // not fit the 168 registers of 9 waves)
     constexpr int XD = NTT >= 16 ? 1 : 2;
-    const int R = batch_rows_per_workgroup(L.M);
     const dim3 grid((unsigned)((L.M + R - 1) / R), (unsigned)((L.n + NTT * 16 - 1) / (NTT * 16)));
     hipLaunchKernelGGL((batch_rows_kernel<DT, NTT, U, XD>), grid, dim3(64 * kRowWaves), 0, s, L.W, L.X, L.Y, L.M,
                        L.K, L.n, R, L.y_vec && R % 4 == 0);
     return hipGetLastError();
+}
+
+template <int DT, int NTT>
+static hipError_t launch_rows_ntt(const SkinnyLaunch &L, hipStream_t s)
+{
+    // W chunks in flight per wave: 2 for 256 tokens, else 4 -- measured 1-4%
+    // faster than 8 from 64 to 136 rows per workgroup (4 to 9 waves with
+    // rows; 2 chunks lose 7-35%) -- and 8 when a workgroup has fewer rows,
+    // whose few waves carry all of the CU's loads
+    const int R = batch_rows_per_workgroup(L.M);
+    if constexpr (NTT >= 16)
+        return launch_rows_ntt_u<DT, NTT, 2>(L, R, s);
+    else if constexpr (NTT >= 4)
+        return launch_rows_ntt_u<DT, NTT, 4>(L, R, s);
+    else
+        return R >= 64 ? launch_rows_ntt_u<DT, NTT, 4>(L, R, s) : launch_rows_ntt_u<DT, NTT, 8>(L, R, s);
 }
 
 template <int DT>
