@@ -58,6 +58,9 @@ def parse():
     p.add_argument("--rows-per-block", type=int, default=0)
     p.add_argument("--gemv-n", type=int, default=1)
     p.add_argument("--no-cpu-baseline", action="store_true")
+    p.add_argument("--monitor-s", type=float, default=2.0,
+                   help="seconds of the headline GEMM, back to back after the timed region, over which the "
+                        "firmware metrics table (clocks, power, temperatures) is sampled; 0 = none")
     p.add_argument("--cpu-seconds", type=float, default=12.0,
                    help="target CPU time of the oracle sample")
     p.add_argument("--cpu-all", action="store_true",
@@ -324,7 +327,6 @@ def main():
                           "of every workgroup, over %d back-to-back launches after the timed region" % reps}
 
     monitor = GpuMonitor(torch.cuda.current_device(), period_s=0.005)
-    monitor.start()
     gpu_state = {}
     for i in range(args.warmup):
         assert gemm() == 0 and gemv(i) == 0
@@ -346,11 +348,24 @@ def main():
     torch.cuda.synchronize()
     wall = time.perf_counter() - t0
     gpu_state["gemm_clock_ghz"] = gemm_clock()
-    gpu_state.update(monitor.stop())
 
     gemm_s = [e[0].elapsed_time(e[1]) / 1e3 for e in ev]
     gemv_s = [e[2].elapsed_time(e[3]) / 1e3 for e in ev]
     gemm_avg, gemv_step_avg = sum(gemm_s) / len(gemm_s), sum(gemv_s) / len(gemv_s)
+
+    # The firmware metrics table refreshes too slowly to be read inside the
+    # timed region (tens of milliseconds): it is sampled over a burst of the
+    # same GEMM right after it instead, long enough for several refreshes.
+    if args.monitor_s > 0:
+        n_mon = max(1, int(round(args.monitor_s / gemm_avg)))
+        monitor.start()
+        with torch.cuda.stream(stream):
+            for _ in range(n_mon):
+                assert gemm() == 0
+        stream.synchronize()
+        gpu_state.update(monitor.stop())
+        gpu_state["window"] = ("%d back-to-back launches of the headline GEMM (%.2f s) right after the timed "
+                               "region" % (n_mon, n_mon * gemm_avg))
     gemm_sorted = sorted(gemm_s)
     gemm_med, gemm_min = gemm_sorted[len(gemm_sorted) // 2], gemm_sorted[0]
 

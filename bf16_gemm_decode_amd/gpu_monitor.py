@@ -91,17 +91,28 @@ class GpuMonitor:
         s = self.samples
         out = {"source": "amdsmi GPU metrics table, sampled every %.0f ms" % (self.period * 1e3),
                "samples": len(s),
-               # the firmware refreshes the table at its own pace: the number
-               # of distinct table time stamps among the samples
+               # the firmware refreshes the table at its own pace (about once
+               # a second on MI355X): the number of distinct table time
+               # stamps among the samples
                "distinct_readings": len({x["stamp"] for x in s}) if s else 0,
                "window_s": round(s[-1]["t"] - s[0]["t"], 3) if len(s) > 1 else 0.0}
         if self.error:
             out["error"] = self.error
         if not s:
             return out
+        # The reading in place when the window opened describes the time
+        # before it: use only readings refreshed inside the window, each once.
+        fresh = {}
+        for x in s:
+            if x["stamp"] != s[0]["stamp"]:
+                fresh.setdefault(x["stamp"], x)
+        out["readings_used"] = len(fresh) if fresh else 1
+        if not fresh:
+            out["note"] = "no refresh of the table inside the window: the one reading predates it"
+        r = list(fresh.values()) if fresh else s[:1]
 
         def stat(key, scale=1.0):
-            v = [x[key] for x in s if x[key] is not None]
+            v = [x[key] for x in r if x[key] is not None]
             if not v:
                 return None
             return {"mean": round(sum(v) / len(v) * scale, 3), "min": round(min(v) * scale, 3),
