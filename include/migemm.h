@@ -173,8 +173,8 @@ size_t migemm_attention_workspace_bytes(int B, int Hq, int D, int num_segments);
  *                                                  B(k,n) = B[k + n*K],
  * i.e. A row-major M x K and B given as its N columns of K contiguous
  * elements (with At = W [M, K] and B = X [N, K] it is Y = X W^T of the DCU
- * decode page, section 6.1, on 8-bit data).  The element types are those
- * the survey's instruction table lists for this GEMM (FP8 E4M3 / E5M2 and
+ * decode page, section 6.1, on 8-bit data).  The element types are the
+ * 8-bit ones gfx950's matrix cores take for this GEMM (FP8 E4M3 / E5M2 and
  * INT8; OCP FP8 encodings, both operands in the same format): products and
  * sums in FP32 (FP8) or exact INT32 (INT8), then one FP32 multiply by
  * `scale` (the dequantisation factor, e.g. the product of per-tensor

@@ -17,8 +17,8 @@
  *    the linear layer Y = X W^T with X:[n,k], W:[m,k], Y:[n,m].
  *  - FlagGems "Hygon 优化" page, section "分组调度" (grouped scheduling): the
  *    GROUP_M map from a flat program id to an output tile.
- *  - the 8-bit GEMM (FP8 E4M3 / E5M2, INT8 inputs, the element types of the
- *    survey's instruction table) in the k-major layout of the DCU page's
+ *  - the 8-bit GEMM (FP8 E4M3 / E5M2, INT8 inputs: the 8-bit element types
+ *    of gfx950's matrix instructions) in the k-major layout of the DCU page's
  *    Y = X W^T, with one scale and a BF16 output (see oracle_gemm_tn_q).
  *  - "DCU decode" page, section 6.1 (attention shapes: per query head
  *    scores = Q K^T over the L cached tokens, prob = softmax(scores),
@@ -184,8 +184,8 @@ int64_t oracle_gemm_sampled(int fmt, const uint16_t *A, const uint16_t *B,
 }
 
 /* ---- 8-bit element types ------------------------------------------------
- * OCP 8-bit floating point (the survey's instruction table lists FP8 E4M3
- * and E5M2 for this GEMM): E4M3 has 1 sign, 4 exponent (bias 7) and 3
+ * OCP 8-bit floating point (gfx950's matrix instructions take FP8 E4M3
+ * and E5M2): E4M3 has 1 sign, 4 exponent (bias 7) and 3
  * mantissa bits, no infinities, S.1111.111 is NaN (largest finite 448);
  * E5M2 has 5 exponent bits (bias 15) and 2 mantissa bits with IEEE-style
  * infinities and NaNs (largest finite 57344).  Both have subnormals.
