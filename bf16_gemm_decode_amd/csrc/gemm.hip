@@ -11,7 +11,11 @@
 //    Each step's A tile (32 k-rows of BM m-contiguous elements) and B tile
 //    go straight from HBM into LDS with buffer loads that write LDS directly
 //    (no VGPR staging), issued S steps ahead of the step being computed, with
-//    explicit vmcnt waits and one barrier per step;
+//    explicit vmcnt waits and one barrier per step.  When every load of the
+//    launch lies inside A and B (tiles 10, 16 and 17, M and N multiples of
+//    the tile, K of 64, 16-byte rows) the same loads go through global
+//    addresses instead: they issue faster from L2, and nothing needs the
+//    buffer descriptors' range check;
 //  * A is m-contiguous, but an MFMA operand needs 8 consecutive k of one row
 //    per lane, so A is read out of LDS with the transposing ds_read_b64_tr_b16
 //    (lane i of each 16-lane group receives row i of a 16 x 4 block), from a
@@ -480,8 +484,11 @@ constexpr int pp_loads_after(int L, int t)
     return na < nb ? na : nb;
 }
 
+// GL: every load lies inside A and B (the caller checked M, N, K and the row
+// alignment against the tile), so the loads may use global addresses, which
+// issue faster from L2 than the range-checked buffer form.
 template <int DT, bool AK, int BM, int BN, int WGM, int WGN, int SA, int SB, int OCC, bool SPLIT,
-          bool PP = false, bool WIDE = false>
+          bool PP = false, bool WIDE = false, bool GL = false>
 __global__ void __launch_bounds__(WGM * WGN * 64)
 __attribute__((amdgpu_waves_per_eu(OCC, OCC)))
 gemm_fl_kernel(const uint16_t *__restrict__ A, const uint16_t *__restrict__ B,
@@ -610,14 +617,27 @@ gemm_fl_kernel(const uint16_t *__restrict__ A, const uint16_t *__restrict__ B,
     };
     // issue_a: m-major: load q of sub-step jj into A stage sa; k-major: load
     // q (of 2*LA) of A stage jj into stage sa
+    // (GL: the same bytes from the same offsets, relative to the pointer the
+    // descriptor would have been built on; every k then lies in [0, K))
+    static_assert(!GL || !SPLIT, "global-address loads: unsplit launches");
     auto issue_a = [&](const u32x4 &d, int jj, int sa, int q) {
-        uint32_t off = a_off[q];
-        if constexpr (AK) off = kmajor_off(jj, a_k[q], off);
-        dma_to_lds<16>(d, (uint32_t)uniform((int)(lds0 + sa * A_BYTES + (q * NW + wave) * 1024)), off);
+        const uint32_t lds = (uint32_t)uniform((int)(lds0 + sa * A_BYTES + (q * NW + wave) * 1024));
+        if constexpr (GL) {
+            const uint16_t *base = AK ? A + ((int64_t)m0 * ldk + kbase + jj * 2 * BK)
+                                      : A + (int64_t)(kbase + jj * BK) * M;
+            gdma16_to_lds((const void *)base, a_off[q], lds);
+        } else {
+            uint32_t off = a_off[q];
+            if constexpr (AK) off = kmajor_off(jj, a_k[q], off);
+            dma_to_lds<16>(d, lds, off);
+        }
     };
     auto issue_b = [&](const u32x4 &d, int pp, int sb, int q) {
-        dma_to_lds<16>(d, (uint32_t)uniform((int)(lds0 + B_BASE + sb * B_BYTES + (q * NW + wave) * 1024)),
-                       kmajor_off(pp, b_k0, b_offq(q)));
+        const uint32_t lds = (uint32_t)uniform((int)(lds0 + B_BASE + sb * B_BYTES + (q * NW + wave) * 1024));
+        if constexpr (GL)
+            gdma16_to_lds((const void *)(B + ((int64_t)n0 * ldk + kbase + pp * 2 * BK)), b_offq(q), lds);
+        else
+            dma_to_lds<16>(d, lds, kmajor_off(pp, b_k0, b_offq(q)));
     };
 
     // operand reads (stage-relative): m-major A through transposing reads;
@@ -1065,7 +1085,7 @@ constexpr bool kSplitTile = !dt_is_8bit(DT) && ((BM == 256 && BN == 128 && WGM *
                                                 (BM == 128 && BN == 128 && WGM * WGN == 4));
 
 template <int DT, bool AK, int BM, int BN, int WGM, int WGN, int SA, int SB, int OCC = 0, bool PP = false,
-          bool WIDE = false>
+          bool WIDE = false, bool GLOK = false>
 static hipError_t launch_fl(const GemmLaunch &L, hipStream_t stream)
 {
     constexpr int OC = OCC ? OCC : WGM * WGN / 4;
@@ -1079,6 +1099,15 @@ static hipError_t launch_fl(const GemmLaunch &L, hipStream_t stream)
             return hipGetLastError();
         }
         return hipErrorInvalidValue;
+    }
+    if constexpr (GLOK) {
+        if (L.in_range) {
+            hipLaunchKernelGGL((gemm_fl_kernel<DT, AK, BM, BN, WGM, WGN, SA, SB, OC, false, PP, WIDE, true>),
+                               dim3((unsigned)L.grid), block, 0, stream, L.A, L.B, L.C, L.M, L.N, L.K,
+                               L.num_pid_m, L.num_pid_n, L.group_m, L.num_xcd, L.c_vec, L.scale, L.K & ~7,
+                               (float *)L.clocks);
+            return hipGetLastError();
+        }
     }
     hipLaunchKernelGGL((gemm_fl_kernel<DT, AK, BM, BN, WGM, WGN, SA, SB, OC, false, PP, WIDE>),
                        dim3((unsigned)L.grid), block, 0, stream, L.A, L.B, L.C, L.M, L.N, L.K,
@@ -1123,11 +1152,11 @@ static hipError_t launch_dt(const GemmLaunch &L, hipStream_t s)
         return L.a_kmajor ? launch_fl<DT, true, 256, 128, 4, 1, 3, 4>(L, s)
                           : launch_fl<DT, false, 256, 128, 4, 1, 4, 4>(L, s);
     case TILE_256x256_FL8:
-        return L.a_kmajor ? launch_fl<DT, true, 256, 256, 4, 2, 2, 3>(L, s)
-                          : launch_fl<DT, false, 256, 256, 4, 2, 4, 3>(L, s);
+        return L.a_kmajor ? launch_fl<DT, true, 256, 256, 4, 2, 2, 3, 0, false, false, true>(L, s)
+                          : launch_fl<DT, false, 256, 256, 4, 2, 4, 3, 0, false, false, true>(L, s);
     case TILE_256x256_PP:
         return L.a_kmajor ? hipErrorInvalidValue
-                          : launch_fl<DT, false, 256, 256, 4, 2, 4, 3, 2, true>(L, s);
+                          : launch_fl<DT, false, 256, 256, 4, 2, 4, 3, 2, true, false, true>(L, s);
     case TILE_64x32_SK:
         return L.a_kmajor ? launch_fl<DT, true, 64, 32, 2, 1, 4, 2, 2>(L, s)
                           : launch_fl<DT, false, 64, 32, 2, 1, 4, 2, 2>(L, s);
@@ -1202,11 +1231,11 @@ static hipError_t launch_q(const GemmLaunch &L, hipStream_t s)
     if (!L.a_kmajor) return hipErrorInvalidValue;
     switch (L.tile) {
     case TILE_256x128_FL: return launch_fl<DT, true, 256, 128, 4, 1, 3, 4>(L, s);
-    case TILE_256x256_FL8: return launch_fl<DT, true, 256, 256, 4, 2, 2, 3>(L, s);
+    case TILE_256x256_FL8: return launch_fl<DT, true, 256, 256, 4, 2, 2, 3, 0, false, false, true>(L, s);
     case TILE_128x128_SK: return launch_fl<DT, true, 128, 128, 2, 2, 4, 3, 1>(L, s);
     case TILE_256x128_F8W:
         if constexpr (DT == DT_F8E4M3 || DT == DT_F8E5M2)
-            return launch_fl<DT, true, 256, 128, 4, 2, 3, 3, 2, false, true>(L, s);
+            return launch_fl<DT, true, 256, 128, 4, 2, 3, 3, 2, false, true, true>(L, s);
         break;
     }
     return hipErrorInvalidValue;

@@ -1,0 +1,74 @@
+"""The large full-line tiles (10, 16 and 17) load through global addresses
+when every load of the launch lies inside A and B (16-byte rows, M and N
+multiples of the tile, K a multiple of 64) and through range-checked buffer
+loads otherwise.  Both kinds of load must give the same bits: each product
+computed in range is compared with the same rows or columns of a product one
+ragged block larger (other loads; the extra rows and columns hold other
+data), and with the oracle."""
+import numpy as np
+import pytest
+
+import oracle
+import synth
+from helpers import assert_parity, gemm_gpu, gemm_tn_gpu, gemm_tn_q_gpu
+
+pytestmark = pytest.mark.gpu
+
+FMTS = ["f16", "bf16"]
+
+
+def _extra(rng, n, like):
+    return rng.integers(0, 1 << 14, size=n).astype(like.dtype)
+
+
+@pytest.mark.parametrize("tile", [16, 10])
+@pytest.mark.parametrize("fmt", FMTS)
+def test_column_major_in_range_equals_ragged(tile, fmt):
+    M, N, K = 512, 512, 1024
+    A, B = synth.gemm_operands(M, N, K, fmt, ("normal", 1.0, 1.0), 2100 + tile)
+    rng = np.random.default_rng(7)
+    print("case in-range", tile, fmt, flush=True)
+    c, guards, _ = gemm_gpu(A, B, M, N, K, fmt, tile=tile)
+    assert guards
+    assert_parity(c, oracle.gemm(A, B, M, N, K, fmt), fmt, "in range tile %d" % tile)
+    # 8 more rows of A (A(m,k) = A[m + k*M]): the first 512 rows of C agree
+    A2 = np.concatenate([A.reshape(K, M), _extra(rng, K * 8, A).reshape(K, 8)], axis=1).reshape(-1)
+    c2, _, _ = gemm_gpu(A2, B, M + 8, N, K, fmt, tile=tile)
+    assert np.array_equal(c2.reshape(N, M + 8)[:, :M], c.reshape(N, M)), "ragged M"
+    # 8 more columns of B: the first 512 columns of C agree
+    B2 = np.concatenate([B, _extra(rng, K * 8, B)])
+    c3, _, _ = gemm_gpu(A, B2, M, N + 8, K, fmt, tile=tile)
+    assert np.array_equal(c3[:M * N], c), "ragged N"
+
+
+@pytest.mark.parametrize("fmt", FMTS)
+def test_k_major_in_range_equals_ragged(fmt):
+    M, N, K = 512, 512, 1024
+    At, B = synth.gemm_operands(M, N, K, fmt, ("normal", 1.0, 1.0), 2200)
+    rng = np.random.default_rng(8)
+    print("case in-range tn", fmt, flush=True)
+    c, guards, _ = gemm_tn_gpu(At, B, M, N, K, fmt, tile=10)
+    assert guards
+    # 8 more rows of At (A(m,k) = At[k + m*K])
+    At2 = np.concatenate([At, _extra(rng, K * 8, At)])
+    c2, _, _ = gemm_tn_gpu(At2, B, M + 8, N, K, fmt, tile=10)
+    assert np.array_equal(c2.reshape(N, M + 8)[:, :M], c.reshape(N, M)), "ragged M"
+
+
+@pytest.mark.parametrize("fmt,tile", [("f8e4m3", 17), ("f8e5m2", 17), ("i8", 10)])
+def test_8bit_in_range_equals_ragged(fmt, tile):
+    M, N, K = 512, 256, 1024
+    At, B = synth.q8_operands(M, N, K, fmt, seed=2300)
+    print("case in-range q8", fmt, tile, flush=True)
+    c, guards, _ = gemm_tn_q_gpu(At, B, M, N, K, fmt, 0.5, tile)
+    assert guards
+    ref = oracle.gemm_tn_q(At, B, M, N, K, fmt, 0.5)
+    if fmt == "i8":
+        assert np.array_equal(c, ref.bits)
+    else:
+        ok, rep = oracle.check(c, ref, "bf16")
+        assert ok, rep
+    At2, _ = synth.q8_operands(M + 16, N, K, fmt, seed=2301)
+    At2 = np.concatenate([np.asarray(At).reshape(-1), np.asarray(At2).reshape(-1)[M * K:]])
+    c2, _, _ = gemm_tn_q_gpu(At2, B, M + 16, N, K, fmt, 0.5, tile)
+    assert np.array_equal(c2.reshape(N, M + 16)[:, :M], c.reshape(N, M)), "ragged M"
