@@ -619,12 +619,11 @@ gemm_fl_kernel(const uint16_t *__restrict__ A, const uint16_t *__restrict__ B,
     // q (of 2*LA) of A stage jj into stage sa
     // (GL: the same bytes from the same offsets, relative to the pointer the
     // descriptor would have been built on; every k then lies in [0, K))
-    static_assert(!GL || !SPLIT, "global-address loads: unsplit launches");
     auto issue_a = [&](const u32x4 &d, int jj, int sa, int q) {
         const uint32_t lds = (uint32_t)uniform((int)(lds0 + sa * A_BYTES + (q * NW + wave) * 1024));
         if constexpr (GL) {
-            const uint16_t *base = AK ? A + ((int64_t)m0 * ldk + kbase + jj * 2 * BK)
-                                      : A + (int64_t)(kbase + jj * BK) * M;
+            const uint16_t *base = AK ? A + ((int64_t)m0 * ldk + kb + kbase + jj * 2 * BK)
+                                      : A + (int64_t)(kb + kbase + jj * BK) * M;
             gdma16_to_lds((const void *)base, a_off[q], lds);
         } else {
             uint32_t off = a_off[q];
@@ -635,7 +634,7 @@ gemm_fl_kernel(const uint16_t *__restrict__ A, const uint16_t *__restrict__ B,
     auto issue_b = [&](const u32x4 &d, int pp, int sb, int q) {
         const uint32_t lds = (uint32_t)uniform((int)(lds0 + B_BASE + sb * B_BYTES + (q * NW + wave) * 1024));
         if constexpr (GL)
-            gdma16_to_lds((const void *)(B + ((int64_t)n0 * ldk + kbase + pp * 2 * BK)), b_offq(q), lds);
+            gdma16_to_lds((const void *)(B + ((int64_t)n0 * ldk + kb + kbase + pp * 2 * BK)), b_offq(q), lds);
         else
             dma_to_lds<16>(d, lds, kmajor_off(pp, b_k0, b_offq(q)));
     };
@@ -1091,6 +1090,15 @@ static hipError_t launch_fl(const GemmLaunch &L, hipStream_t stream)
     constexpr int OC = OCC ? OCC : WGM * WGN / 4;
     const dim3 block(WGM * WGN * 64);
     if (L.splits > 1) {
+        if constexpr (kSplitTile<DT, BM, BN, WGM, WGN> && !PP && !WIDE && GLOK) {
+            if (L.in_range) {
+                hipLaunchKernelGGL((gemm_fl_kernel<DT, AK, BM, BN, WGM, WGN, SA, SB, OC, true, false, false, true>),
+                                   dim3((unsigned)L.grid, (unsigned)L.splits), block, 0, stream, L.A, L.B,
+                                   L.C, L.M, L.N, L.K, L.num_pid_m, L.num_pid_n, L.group_m, L.num_xcd,
+                                   L.c_vec, L.scale, L.ks, L.part);
+                return hipGetLastError();
+            }
+        }
         if constexpr (kSplitTile<DT, BM, BN, WGM, WGN> && !PP && !WIDE) {
             hipLaunchKernelGGL((gemm_fl_kernel<DT, AK, BM, BN, WGM, WGN, SA, SB, OC, true>),
                                dim3((unsigned)L.grid, (unsigned)L.splits), block, 0, stream, L.A, L.B,

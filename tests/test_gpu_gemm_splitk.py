@@ -1,7 +1,8 @@
 """GPU parity of the split-K GEMM (gemm_splitk_ex) through the C ABI against
 the CPU oracle: both layouts of A, both 16-bit types, the three tiles that
 take slices, slice counts that divide K and ones that leave a short last
-slice (or fewer slices than asked), every output at small sizes and sampled
+slice (or fewer slices than asked), launches whose loads all lie in range
+and ragged ones, every output at small sizes and sampled
 outputs of a long-K product with the automatic slice count."""
 import numpy as np
 import pytest
@@ -37,6 +38,9 @@ CASES = [
     (304, 200, 4136, 0, 2, 9), (300, 200, 4136, 1, 3, 9), (520, 264, 2048, 0, 4, 10),
     (520, 264, 2048, 1, 4, 10), (136, 70, 8200, 0, 8, 13), (130, 70, 8200, 1, 5, 13),
     (256, 128, 192, 0, 3, 9), (64, 64, 4096, 1, 0, 0), (1000, 40, 3000, 0, 6, 0),
+    # every load in range (M, N multiples of 256, K of 64): tile 10's slices
+    # load through global addresses
+    (512, 256, 4096, 0, 4, 10), (512, 256, 4096, 1, 4, 10),
 ]
 
 
