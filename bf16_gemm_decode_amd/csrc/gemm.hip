@@ -12,8 +12,8 @@
 //    go straight from HBM into LDS with buffer loads that write LDS directly
 //    (no VGPR staging), issued S steps ahead of the step being computed, with
 //    explicit vmcnt waits and one barrier per step.  When every load of the
-//    launch lies inside A and B (tiles 10, 16 and 17, M and N multiples of
-//    the tile, K of 64, 16-byte rows) the same loads go through global
+//    launch lies inside A and B (the full-line tiles 9-13, 16 and 17, M and N
+//    multiples of the tile, K of 64, 16-byte rows) the same loads go through global
 //    addresses instead: they issue faster from L2, and nothing needs the
 //    buffer descriptors' range check;
 //  * A is m-contiguous, but an MFMA operand needs 8 consecutive k of one row
@@ -1157,8 +1157,8 @@ static hipError_t launch_dt(const GemmLaunch &L, hipStream_t s)
         return L.a_kmajor ? launch_fl<DT, true, 256, 256, 2, 2, 2, 3>(L, s)
                           : launch_fl<DT, false, 256, 256, 2, 2, 4, 3>(L, s);
     case TILE_256x128_FL:
-        return L.a_kmajor ? launch_fl<DT, true, 256, 128, 4, 1, 3, 4>(L, s)
-                          : launch_fl<DT, false, 256, 128, 4, 1, 4, 4>(L, s);
+        return L.a_kmajor ? launch_fl<DT, true, 256, 128, 4, 1, 3, 4, 0, false, false, true>(L, s)
+                          : launch_fl<DT, false, 256, 128, 4, 1, 4, 4, 0, false, false, true>(L, s);
     case TILE_256x256_FL8:
         return L.a_kmajor ? launch_fl<DT, true, 256, 256, 4, 2, 2, 3, 0, false, false, true>(L, s)
                           : launch_fl<DT, false, 256, 256, 4, 2, 4, 3, 0, false, false, true>(L, s);
@@ -1166,14 +1166,14 @@ static hipError_t launch_dt(const GemmLaunch &L, hipStream_t s)
         return L.a_kmajor ? hipErrorInvalidValue
                           : launch_fl<DT, false, 256, 256, 4, 2, 4, 3, 2, true, false, true>(L, s);
     case TILE_64x32_SK:
-        return L.a_kmajor ? launch_fl<DT, true, 64, 32, 2, 1, 4, 2, 2>(L, s)
-                          : launch_fl<DT, false, 64, 32, 2, 1, 4, 2, 2>(L, s);
+        return L.a_kmajor ? launch_fl<DT, true, 64, 32, 2, 1, 4, 2, 2, false, false, true>(L, s)
+                          : launch_fl<DT, false, 64, 32, 2, 1, 4, 2, 2, false, false, true>(L, s);
     case TILE_64x64_SK:
-        return L.a_kmajor ? launch_fl<DT, true, 64, 64, 2, 1, 4, 2, 2>(L, s)
-                          : launch_fl<DT, false, 64, 64, 2, 1, 4, 2, 2>(L, s);
+        return L.a_kmajor ? launch_fl<DT, true, 64, 64, 2, 1, 4, 2, 2, false, false, true>(L, s)
+                          : launch_fl<DT, false, 64, 64, 2, 1, 4, 2, 2, false, false, true>(L, s);
     case TILE_128x128_SK:
-        return L.a_kmajor ? launch_fl<DT, true, 128, 128, 2, 2, 4, 3, 1>(L, s)
-                          : launch_fl<DT, false, 128, 128, 2, 2, 4, 3, 1>(L, s);
+        return L.a_kmajor ? launch_fl<DT, true, 128, 128, 2, 2, 4, 3, 1, false, false, true>(L, s)
+                          : launch_fl<DT, false, 128, 128, 2, 2, 4, 3, 1, false, false, true>(L, s);
     case TILE_128x128:
 #define MIGEMM_V(va, vb) \
     if (L.vec_a == va && L.vec_b == vb) return launch_t<DT, 128, 128, 2, 2, 4, va, vb, 2>(L, s);
@@ -1238,9 +1238,9 @@ static hipError_t launch_q(const GemmLaunch &L, hipStream_t s)
 {
     if (!L.a_kmajor) return hipErrorInvalidValue;
     switch (L.tile) {
-    case TILE_256x128_FL: return launch_fl<DT, true, 256, 128, 4, 1, 3, 4>(L, s);
+    case TILE_256x128_FL: return launch_fl<DT, true, 256, 128, 4, 1, 3, 4, 0, false, false, true>(L, s);
     case TILE_256x256_FL8: return launch_fl<DT, true, 256, 256, 4, 2, 2, 3, 0, false, false, true>(L, s);
-    case TILE_128x128_SK: return launch_fl<DT, true, 128, 128, 2, 2, 4, 3, 1>(L, s);
+    case TILE_128x128_SK: return launch_fl<DT, true, 128, 128, 2, 2, 4, 3, 1, false, false, true>(L, s);
     case TILE_256x128_F8W:
         if constexpr (DT == DT_F8E4M3 || DT == DT_F8E5M2)
             return launch_fl<DT, true, 256, 128, 4, 2, 3, 3, 2, false, true, true>(L, s);

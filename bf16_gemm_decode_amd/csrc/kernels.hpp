@@ -113,8 +113,8 @@ struct GemmLaunch {
     uint64_t *clocks;             // measurement (full-line tiles, unsplit): per workgroup, shader
                                   // clocks and 10 ns real-time ticks it ran for; nullptr = off
     int in_range;                 // 1: every tile load lies inside A and B (16-byte rows, M and N
-                                  // multiples of the tile, K of 64): the full-line tiles 10, 16 and
-                                  // 17 may then load through global addresses (no range check)
+                                  // multiples of the tile, K of 64): the full-line tiles (9-13, 16,
+                                  // 17) then load through global addresses (no range check)
 };
 
 // Sum of split-K partials: C = round(sum_z part[z][n][m]) (gemm.hip).

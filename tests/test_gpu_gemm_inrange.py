@@ -1,4 +1,4 @@
-"""The large full-line tiles (10, 16 and 17) load through global addresses
+"""The full-line tiles (9-13, 16 and 17) load through global addresses
 when every load of the launch lies inside A and B (16-byte rows, M and N
 multiples of the tile, K a multiple of 64) and through range-checked buffer
 loads otherwise.  Both kinds of load must give the same bits: each product
@@ -10,7 +10,7 @@ import pytest
 
 import oracle
 import synth
-from helpers import assert_parity, gemm_gpu, gemm_tn_gpu, gemm_tn_q_gpu
+from helpers import assert_parity, gemm_gpu, gemm_tn_gpu, gemm_tn_q_gpu, kmajor_to_colmajor
 
 pytestmark = pytest.mark.gpu
 
@@ -21,7 +21,7 @@ def _extra(rng, n, like):
     return rng.integers(0, 1 << 14, size=n).astype(like.dtype)
 
 
-@pytest.mark.parametrize("tile", [16, 10])
+@pytest.mark.parametrize("tile", [16, 10, 9, 12, 11, 13])
 @pytest.mark.parametrize("fmt", FMTS)
 def test_column_major_in_range_equals_ragged(tile, fmt):
     M, N, K = 512, 512, 1024
@@ -41,21 +41,23 @@ def test_column_major_in_range_equals_ragged(tile, fmt):
     assert np.array_equal(c3[:M * N], c), "ragged N"
 
 
+@pytest.mark.parametrize("tile", [10, 9, 12, 13])
 @pytest.mark.parametrize("fmt", FMTS)
-def test_k_major_in_range_equals_ragged(fmt):
+def test_k_major_in_range_equals_ragged(tile, fmt):
     M, N, K = 512, 512, 1024
     At, B = synth.gemm_operands(M, N, K, fmt, ("normal", 1.0, 1.0), 2200)
     rng = np.random.default_rng(8)
     print("case in-range tn", fmt, flush=True)
-    c, guards, _ = gemm_tn_gpu(At, B, M, N, K, fmt, tile=10)
+    c, guards, _ = gemm_tn_gpu(At, B, M, N, K, fmt, tile=tile)
     assert guards
+    assert_parity(c, oracle.gemm(kmajor_to_colmajor(At, M, K), B, M, N, K, fmt), fmt, "in range tn tile %d" % tile)
     # 8 more rows of At (A(m,k) = At[k + m*K])
     At2 = np.concatenate([At, _extra(rng, K * 8, At)])
-    c2, _, _ = gemm_tn_gpu(At2, B, M + 8, N, K, fmt, tile=10)
+    c2, _, _ = gemm_tn_gpu(At2, B, M + 8, N, K, fmt, tile=tile)
     assert np.array_equal(c2.reshape(N, M + 8)[:, :M], c.reshape(N, M)), "ragged M"
 
 
-@pytest.mark.parametrize("fmt,tile", [("f8e4m3", 17), ("f8e5m2", 17), ("i8", 10)])
+@pytest.mark.parametrize("fmt,tile", [("f8e4m3", 17), ("f8e5m2", 17), ("i8", 10), ("i8", 9), ("f8e4m3", 13)])
 def test_8bit_in_range_equals_ragged(fmt, tile):
     M, N, K = 512, 256, 1024
     At, B = synth.q8_operands(M, N, K, fmt, seed=2300)
