@@ -33,8 +33,10 @@
 //  * out-of-range rows/columns are never stored; out-of-range k reads as
 //    zero through the buffer descriptors' range check, so ragged K needs no
 //    separate path;
-//  * the epilogue rounds each FP32 sum once to FP16/BF16 (nearest even) and
-//    stores it directly: no FP32 copy of C ever reaches memory.
+//  * the epilogue rounds each FP32 sum once to FP16/BF16 (nearest even); no
+//    FP32 copy of C ever reaches memory.  In range, the full-line tiles with
+//    64-row wave tiles pass the rounded tile through LDS and store whole
+//    128-byte lines of C; otherwise each lane stores its 4 rows directly.
 #include <type_traits>
 
 #include <algorithm>
@@ -1047,6 +1049,39 @@ gemm_fl_kernel(const uint16_t *__restrict__ A, const uint16_t *__restrict__ B,
         }
         return;
     }
+    // In range, with 64-row wave tiles: each wave converts its tile into its
+    // own LDS window (the rings are free once every wave has passed the
+    // barrier below: all operand reads done, no load in flight), one 128-byte
+    // column of 64 outputs every CS bytes, and writes C back in whole lines:
+    // lane l stores 16 bytes, rows 8(l%8).. of column l/8 of an 8-column
+    // group.  The direct stores below write each line in four 32-byte pieces.
+    constexpr int CS = TM * 2 + 16;
+    constexpr bool STAGE_C = GL && TM == 64 && NW * TN * CS <= LDS_BYTES;
+    if (STAGE_C && uniform((int)(((uintptr_t)C & 15) == 0))) {
+        __syncthreads();
+        // lane indices taken afresh (an opaque copy of the thread id), so
+        // that none is computed before the k loop and held through it
+        int t = (int)threadIdx.x;
+        asm volatile("" : "+v"(t));
+        const int eg = (t >> 4) & 3, eig = t & 15, el = t & 63;
+        MIGEMM_LDS unsigned char *win = (MIGEMM_LDS unsigned char *)smem + wave * (TN * CS);
+#pragma unroll
+        for (int i = 0; i < FM; ++i) {
+#pragma unroll
+            for (int j = 0; j < FN; ++j) {
+                const u16x4 v = {out16<DT>(acc[i][j][0], scale), out16<DT>(acc[i][j][1], scale),
+                                 out16<DT>(acc[i][j][2], scale), out16<DT>(acc[i][j][3], scale)};
+                *(MIGEMM_LDS u16x4 *)(win + (j * 16 + eig) * CS + (i * 16 + 4 * eg) * 2) = v;
+                __builtin_amdgcn_sched_barrier(0);   // convert and write block by block
+            }
+        }
+        uint16_t *cw = C + (size_t)(n0 + wn * TN) * M + m0 + wm * TM + (el & 7) * 8;
+#pragma unroll
+        for (int s = 0; s < TN / 8; ++s) {
+            const int c = s * 8 + (el >> 3);
+            *(u32x4 *)(cw + (size_t)c * M) = *(MIGEMM_LDS const u32x4 *)(win + c * CS + (el & 7) * 16);
+        }
+    } else {
 #pragma unroll
     for (int i = 0; i < FM; ++i) {
         const int m = m0 + wm * TM + i * 16 + 4 * g;
@@ -1065,6 +1100,7 @@ gemm_fl_kernel(const uint16_t *__restrict__ A, const uint16_t *__restrict__ B,
                     if (m + r < M) dst[r] = out16<DT>(acc[i][j][r], scale);
             }
         }
+    }
     }
     if (clocked && threadIdx.x == 0) {
         const uint64_t t1 = __builtin_amdgcn_s_memtime(), r1 = __builtin_amdgcn_s_memrealtime();
