@@ -1049,15 +1049,18 @@ gemm_fl_kernel(const uint16_t *__restrict__ A, const uint16_t *__restrict__ B,
         }
         return;
     }
-    // In range, with 64-row wave tiles: each wave converts its tile into its
-    // own LDS window (the rings are free once every wave has passed the
-    // barrier below: all operand reads done, no load in flight), one 128-byte
-    // column of 64 outputs every CS bytes, and writes C back in whole lines:
-    // lane l stores 16 bytes, rows 8(l%8).. of column l/8 of an 8-column
-    // group.  The direct stores below write each line in four 32-byte pieces.
+    // With 64-row wave tiles, C on a 16-byte boundary and M a multiple of 8:
+    // each wave converts its tile into its own LDS window (the rings are free
+    // once every wave has passed the barrier below: all operand reads done,
+    // no load in flight), one 128-byte column of 64 outputs every CS bytes,
+    // and writes C back in whole lines: lane l stores 16 bytes, rows
+    // 8(l%8).. of column l/8 of an 8-column group.  With M a multiple of 8
+    // each such piece lies wholly inside or wholly outside C, so a ragged
+    // edge only drops pieces.  The direct stores below write each line in
+    // four 32-byte pieces.
     constexpr int CS = TM * 2 + 16;
-    constexpr bool STAGE_C = GL && TM == 64 && NW * TN * CS <= LDS_BYTES;
-    if (STAGE_C && uniform((int)(((uintptr_t)C & 15) == 0))) {
+    constexpr bool STAGE_C = TM == 64 && NW * TN * CS <= LDS_BYTES;
+    if (STAGE_C && uniform((int)(((uintptr_t)C & 15) == 0 && (M & 7) == 0))) {
         __syncthreads();
         // lane indices taken afresh (an opaque copy of the thread id), so
         // that none is computed before the k loop and held through it
@@ -1075,11 +1078,13 @@ gemm_fl_kernel(const uint16_t *__restrict__ A, const uint16_t *__restrict__ B,
                 __builtin_amdgcn_sched_barrier(0);   // convert and write block by block
             }
         }
-        uint16_t *cw = C + (size_t)(n0 + wn * TN) * M + m0 + wm * TM + (el & 7) * 8;
+        const int gm = m0 + wm * TM + (el & 7) * 8, gn = n0 + wn * TN;
+        uint16_t *cw = C + (size_t)gn * M + gm;
 #pragma unroll
         for (int s = 0; s < TN / 8; ++s) {
             const int c = s * 8 + (el >> 3);
-            *(u32x4 *)(cw + (size_t)c * M) = *(MIGEMM_LDS const u32x4 *)(win + c * CS + (el & 7) * 16);
+            const u32x4 v = *(MIGEMM_LDS const u32x4 *)(win + c * CS + (el & 7) * 16);
+            if (GL || (gm < M && gn + c < N)) *(u32x4 *)(cw + (size_t)c * M) = v;
         }
     } else {
 #pragma unroll

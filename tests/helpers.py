@@ -37,14 +37,15 @@ class Guarded:
         return bool(np.all(h[:self.guard] == SENTINEL) and np.all(h[self.guard + self.count:] == SENTINEL))
 
 
-def gemm_gpu(A_bits, B_bits, M, N, K, fmt, tile=0, group_m=0, xcd_remap=1, stream=0):
+def gemm_gpu(A_bits, B_bits, M, N, K, fmt, tile=0, group_m=0, xcd_remap=1, stream=0, c_shift=0):
     """Run the library GEMM through the C ABI; returns (C bits, guards ok,
-    inputs unchanged)."""
+    inputs unchanged).  c_shift moves C by that many elements (4: C on an
+    8-byte but not a 16-byte boundary)."""
     import torch
     from bf16_gemm_decode_amd import binding
     dA, dB = dev(A_bits), dev(B_bits)
     cA, cB = dA.clone(), dB.clone()
-    C = Guarded(M * N)
+    C = Guarded(M * N, GUARD + c_shift)
     code = binding.gemm_ex_ptr(binding.F16 if fmt == "f16" else binding.BF16,
                                dA.data_ptr(), dB.data_ptr(), C.ptr, M, N, K,
                                tile, group_m, xcd_remap, stream)
@@ -54,14 +55,14 @@ def gemm_gpu(A_bits, B_bits, M, N, K, fmt, tile=0, group_m=0, xcd_remap=1, strea
     return C.out(), C.guards_intact(), unchanged
 
 
-def gemm_tn_gpu(At_bits, B_bits, M, N, K, fmt, tile=0, group_m=0, xcd_remap=1, stream=0):
+def gemm_tn_gpu(At_bits, B_bits, M, N, K, fmt, tile=0, group_m=0, xcd_remap=1, stream=0, c_shift=0):
     """gemm_tn_ex through the C ABI (A given k-major: A(m,k) = At[k + m*K]);
     returns (C bits, guards ok, inputs unchanged)."""
     import torch
     from bf16_gemm_decode_amd import binding
     dA, dB = dev(At_bits), dev(B_bits)
     cA, cB = dA.clone(), dB.clone()
-    C = Guarded(M * N)
+    C = Guarded(M * N, GUARD + c_shift)
     code = binding.gemm_tn_ex_ptr(binding.F16 if fmt == "f16" else binding.BF16,
                                   dA.data_ptr(), dB.data_ptr(), C.ptr, M, N, K,
                                   tile, group_m, xcd_remap, stream)
@@ -71,7 +72,7 @@ def gemm_tn_gpu(At_bits, B_bits, M, N, K, fmt, tile=0, group_m=0, xcd_remap=1, s
     return C.out(), C.guards_intact(), unchanged
 
 
-def gemm_tn_q_gpu(At, B, M, N, K, fmt, scale, tile=0, stream=0):
+def gemm_tn_q_gpu(At, B, M, N, K, fmt, scale, tile=0, stream=0, c_shift=0):
     """gemm_tn_q_ex (8-bit At, B; BF16 C) through the C ABI; returns (C bits,
     guards ok, inputs unchanged)."""
     import torch
@@ -80,7 +81,7 @@ def gemm_tn_q_gpu(At, B, M, N, K, fmt, scale, tile=0, stream=0):
     dA = torch.from_numpy(np.ascontiguousarray(At).view(np.uint8)).cuda()
     dB = torch.from_numpy(np.ascontiguousarray(B).view(np.uint8)).cuda()
     cA, cB = dA.clone(), dB.clone()
-    C = Guarded(M * N)
+    C = Guarded(M * N, GUARD + c_shift)
     code = binding.lib().gemm_tn_q_ex(q, dA.data_ptr(), dB.data_ptr(), C.ptr, M, N, K, scale,
                                       tile, 0, 1, stream)
     assert code == 0, "gemm_tn_q_ex returned %d" % code

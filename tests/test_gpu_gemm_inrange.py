@@ -4,7 +4,12 @@ multiples of the tile, K a multiple of 64) and through range-checked buffer
 loads otherwise.  Both kinds of load must give the same bits: each product
 computed in range is compared with the same rows or columns of a product one
 ragged block larger (other loads; the extra rows and columns hold other
-data), and with the oracle."""
+data), and with the oracle.
+
+The tiles with 64-row wave tiles also pass C through LDS and store whole
+128-byte lines when C lies on a 16-byte boundary and M is a multiple of 8
+(in range or ragged); with C moved by 8 bytes they store each output
+directly.  Both must give the same bits."""
 import numpy as np
 import pytest
 
@@ -74,3 +79,53 @@ def test_8bit_in_range_equals_ragged(fmt, tile):
     At2 = np.concatenate([np.asarray(At).reshape(-1), np.asarray(At2).reshape(-1)[M * K:]])
     c2, _, _ = gemm_tn_q_gpu(At2, B, M + 16, N, K, fmt, 0.5, tile)
     assert np.array_equal(c2.reshape(N, M + 16)[:, :M], c.reshape(N, M)), "ragged M"
+
+
+STAGED_SHAPES = [(512, 512, 1024), (520, 264, 1024), (1032, 136, 512), (516, 260, 256)]
+
+
+@pytest.mark.parametrize("tile", [16, 10, 9, 13])
+@pytest.mark.parametrize("shape", STAGED_SHAPES)
+def test_column_major_staged_c_equals_direct(tile, shape):
+    M, N, K = shape
+    fmt = "bf16" if tile % 2 else "f16"
+    A, B = synth.gemm_operands(M, N, K, fmt, ("normal", 1.0, 1.0), 2400 + tile)
+    print("case staged C", tile, shape, flush=True)
+    c, guards, _ = gemm_gpu(A, B, M, N, K, fmt, tile=tile)
+    c2, guards2, _ = gemm_gpu(A, B, M, N, K, fmt, tile=tile, c_shift=4)
+    assert guards and guards2
+    assert np.array_equal(c, c2), "staged and direct stores differ"
+    assert_parity(c, oracle.gemm(A, B, M, N, K, fmt), fmt, "staged C tile %d %s" % (tile, shape))
+
+
+@pytest.mark.parametrize("tile", [10, 9, 13])
+@pytest.mark.parametrize("shape", STAGED_SHAPES[:3])
+def test_k_major_staged_c_equals_direct(tile, shape):
+    M, N, K = shape
+    fmt = "bf16"
+    At, B = synth.gemm_operands(M, N, K, fmt, ("normal", 1.0, 1.0), 2500 + tile)
+    print("case staged C tn", tile, shape, flush=True)
+    c, guards, _ = gemm_tn_gpu(At, B, M, N, K, fmt, tile=tile)
+    c2, guards2, _ = gemm_tn_gpu(At, B, M, N, K, fmt, tile=tile, c_shift=4)
+    assert guards and guards2
+    assert np.array_equal(c, c2), "staged and direct stores differ"
+    assert_parity(c, oracle.gemm(kmajor_to_colmajor(At, M, K), B, M, N, K, fmt), fmt,
+                  "staged C tn tile %d %s" % (tile, shape))
+
+
+@pytest.mark.parametrize("fmt,tile", [("f8e4m3", 17), ("i8", 10), ("f8e5m2", 13)])
+@pytest.mark.parametrize("shape", [(512, 256, 1024), (520, 264, 1024)])
+def test_8bit_staged_c_equals_direct(fmt, tile, shape):
+    M, N, K = shape
+    At, B = synth.q8_operands(M, N, K, fmt, seed=2600)
+    print("case staged C q8", fmt, tile, shape, flush=True)
+    c, guards, _ = gemm_tn_q_gpu(At, B, M, N, K, fmt, 0.5, tile)
+    c2, guards2, _ = gemm_tn_q_gpu(At, B, M, N, K, fmt, 0.5, tile, c_shift=4)
+    assert guards and guards2
+    assert np.array_equal(c, c2), "staged and direct stores differ"
+    ref = oracle.gemm_tn_q(At, B, M, N, K, fmt, 0.5)
+    if fmt == "i8":
+        assert np.array_equal(c, ref.bits)
+    else:
+        ok, rep = oracle.check(c, ref, "bf16")
+        assert ok, rep
