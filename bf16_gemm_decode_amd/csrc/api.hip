@@ -48,10 +48,10 @@ struct ShapeConfig {
     int dtype, a_kmajor, M, N, K, tile, group_m;
 };
 constexpr ShapeConfig kShapeTable[] = {
-    {DT_F16, 0, 8192, 8192, 16384, TILE_256x256_PP, 8},      // 1.82-1.84 ms vs 1.92-2.04 on tile 10
-    {DT_BF16, 0, 4096, 34816, 5120, TILE_256x256_PP, 16},    // 1.22-1.27 ms vs 1.30 on tile 10
-    {DT_BF16, 1, 34816, 4096, 5120, TILE_256x256_FL8, 4},    // 1.316 ms vs 1.354 at 8
-    {DT_BF16, 0, 5000, 3000, 4100, TILE_256x256_PP, 16},     // 118-129 us vs 131-148 on tile 10
+    {DT_F16, 0, 8192, 8192, 16384, TILE_256x256_PP, 8},      // 1.54-1.64 ms vs 1.81-1.93 on tile 10
+    {DT_BF16, 0, 4096, 34816, 5120, TILE_256x256_PP, 8},     // 1.029 ms vs 1.034 at 4, 1.049 at 16; tile 10 1.10
+    {DT_BF16, 1, 34816, 4096, 5120, TILE_256x256_FL8, 4},    // 1.143 ms vs 1.166 at 8, 1.286 at 16
+    {DT_BF16, 0, 5000, 3000, 4100, TILE_256x256_PP, 16},     // 101-124 us vs 131-148 on tile 10
 };
 
 const ShapeConfig *find_shape(int dtype, bool a_kmajor, int M, int N, int K)

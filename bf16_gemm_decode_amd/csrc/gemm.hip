@@ -464,9 +464,20 @@ constexpr int fl_loads_after(int j, int need_a, int need_b)
 // like B (rows of A in place of columns of B).
 // Ping-pong tile: MFMAs of a sub-step issued in its load phase (the rest go
 // into its compute phase), and the spacing, in compute-phase MFMAs, of the B
-// fragment reads there.
+// fragment reads there.  PP_PRE applies when the loads go through global
+// addresses (every load in range), PP_PRE_BUF with the range-checked buffer
+// loads, whose slower issue leaves less room in the load phase.  Measured
+// (ms per launch, B read after every 2nd MFMA): in range, 8192^2 x 16384
+// FP16, 0 / 2 / 4 / 6 / 8 / 10 / 12 / 16 load-phase MFMAs 1.70 / 1.71 /
+// 1.65 / 1.64 / 1.61 / 1.62 / 1.69 / 1.68, and with a read after every MFMA
+// 8 / 16 / 24 take 1.62 / 1.72 / 1.85, every 3rd (2 or 4) 1.68; ragged,
+// 8000 x 8192 x 16384 FP16, 0 / 2 / 4 / 6 / 8: 1.61 / 1.59 / 1.61 / 1.65 /
+// 1.71, and 5000 x 3000 x 4100 BF16 0.115 / 0.113 / 0.114 / 0.118 / 0.120.
 #ifndef PP_PRE
-#define PP_PRE 2
+#define PP_PRE 8
+#endif
+#ifndef PP_PRE_BUF
+#define PP_PRE_BUF 2
 #endif
 #ifndef PP_BREAD_EVERY
 #define PP_BREAD_EVERY 2
@@ -951,7 +962,8 @@ gemm_fl_kernel(const uint16_t *__restrict__ A, const uint16_t *__restrict__ B,
             // phase before read; then the first PRE MFMAs of sub-step j, so
             // that for part of every phase both waves of a SIMD issue MFMAs.
             constexpr int NMF = FM * FN;
-            constexpr int PRE = PP_PRE < NMF ? PP_PRE : 0;
+            constexpr int PRE_ = GL ? PP_PRE : PP_PRE_BUF;
+            constexpr int PRE = PRE_ < NMF ? PRE_ : 0;
             auto load_phase = [&](int j, Frag &cur) {
                 phase_loads(j);
 #pragma unroll

@@ -216,12 +216,12 @@ def test_exact_shape_table():
     # measured exact-shape configurations apply when tile and GROUP_M are automatic
     plan = lambda dt, M, N, K, tile=0, gm=0, tn=False: binding.gemm_plan(
         dt, P, P + 2 ** 30, P + 2 ** 31, M, N, K, tile, gm, a_kmajor=tn)[1]
-    assert (plan(1, 4096, 34816, 5120)["tile"], plan(1, 4096, 34816, 5120)["group_m"]) == (16, 16)
+    assert (plan(1, 4096, 34816, 5120)["tile"], plan(1, 4096, 34816, 5120)["group_m"]) == (16, 8)
     assert (plan(1, 34816, 4096, 5120, tn=True)["tile"], plan(1, 34816, 4096, 5120, tn=True)["group_m"]) == (10, 4)
     assert (plan(0, 8192, 8192, 16384)["tile"], plan(0, 8192, 8192, 16384)["group_m"]) == (16, 8)
     assert (plan(1, 5000, 3000, 4100)["tile"], plan(1, 5000, 3000, 4100)["group_m"]) == (16, 16)
     # an explicit GROUP_M or tile, another dtype or shape: the heuristics
-    assert plan(1, 4096, 34816, 5120, gm=8)["group_m"] == 8
+    assert plan(1, 4096, 34816, 5120, gm=16)["group_m"] == 16
     assert plan(1, 4096, 34816, 5120, tile=9)["tile"] == 9
     assert plan(0, 4096, 34816, 5120)["group_m"] == 8
     assert plan(1, 4096, 34816, 5128)["group_m"] == 8
