@@ -37,6 +37,7 @@ def main(argv=None):
     A = torch.randn(M * K, generator=g, device="cuda").to(dt)
     B = (torch.randn(K * N, generator=g, device="cuda") * 0.02).to(dt)
     C = torch.empty(M * N, dtype=dt, device="cuda")
+    torch.cuda.synchronize()   # inputs are drawn on the default stream; the launches go to s
     s = torch.cuda.Stream()
     L = binding.lib()
     flop = roofline.gemm_flop(M, N, K)
