@@ -878,8 +878,8 @@ gemm_fl_kernel(const uint16_t *__restrict__ A, const uint16_t *__restrict__ B,
             for (int r = 0; r < NR; ++r) read_w(0, r, f0);
             // step p: stage p + 1 landed (it was issued two steps ago; only
             // stage p + 2's loads came after it), everyone has read stage p;
-            // then the MFMAs of stage p with the reads of stage p + 1 and the
-            // loads of stage p + S between them
+            // then the MFMAs of stage p with the loads of stage p + S and
+            // then the reads of stage p + 1 between them
             auto wstep = [&](int p, FragW &cur, FragW &nxt) {
                 __builtin_amdgcn_s_waitcnt((7 << 4) | 0xc00f);   // lgkmcnt(0)
                 if (p + 2 < P_) wait_vmcnt<NLS>();
@@ -894,12 +894,15 @@ gemm_fl_kernel(const uint16_t *__restrict__ A, const uint16_t *__restrict__ B,
                     for (int jj = 0; jj < FN; ++jj) {
                         mfma16x16x128_f8<DT>(acc[i][jj], cur.a[i], cur.b[jj]);
                         const int t = i * FN + jj;
-                        if (t < NR) read_w(ns, t, nxt);
-                        else if (t - NR < NLS) stage_load(pl, t - NR, da, db);
+                        // loads first (FP8 8192^2 x 16384, same box: E4M3
+                        // 0.906-0.915 ms against 0.928-0.936 reads first,
+                        // E5M2 0.889-0.892 against 0.910-0.913)
+                        if (t < NLS) stage_load(pl, t, da, db);
+                        else if (t - NLS < NR) read_w(ns, t - NLS, nxt);
                         __builtin_amdgcn_sched_barrier(0);
                     }
 #pragma unroll
-                for (int x = (FM * FN > NR ? FM * FN - NR : 0); x < NLS; ++x) stage_load(pl, x, da, db);
+                for (int x = (FM * FN > NLS ? FM * FN - NLS : 0); x < NR; ++x) read_w(ns, x, nxt);
             };
             for (int p = 0; p < P_; p += 2) {
                 wstep(p, f0, f1);
