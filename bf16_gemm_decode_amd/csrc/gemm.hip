@@ -470,7 +470,8 @@ constexpr int fl_loads_after(int j, int need_a, int need_b)
 // (ms per launch, B read after every 2nd MFMA): in range, 8192^2 x 16384
 // FP16, 0 / 2 / 4 / 6 / 8 / 10 / 12 / 16 load-phase MFMAs 1.70 / 1.71 /
 // 1.65 / 1.64 / 1.61 / 1.62 / 1.69 / 1.68, and with a read after every MFMA
-// 8 / 16 / 24 take 1.62 / 1.72 / 1.85, every 3rd (2 or 4) 1.68; ragged,
+// 8 / 16 / 24 take 1.62 / 1.72 / 1.85, every 3rd 1.68 (2 or 4 load-phase
+// MFMAs) and, in another run, 1.64 / 1.62 (8 / 6) against 1.56; ragged,
 // 8000 x 8192 x 16384 FP16, 0 / 2 / 4 / 6 / 8: 1.61 / 1.59 / 1.61 / 1.65 /
 // 1.71, and 5000 x 3000 x 4100 BF16 0.115 / 0.113 / 0.114 / 0.118 / 0.120.
 #ifndef PP_PRE
