@@ -500,9 +500,15 @@ constexpr int pp_loads_after(int L, int t)
 
 // GL: every load lies inside A and B (the caller checked M, N, K and the row
 // alignment against the tile), so the loads may use global addresses, which
-// issue faster from L2 than the range-checked buffer form.
+// issue faster from L2 than the range-checked buffer form.  GL with EDGE (the
+// ping-pong tile, m-major A): the k loop stays inside K and A's rows come in
+// whole 8-element pieces, but the tile may pass M or N; the lanes whose piece
+// of A lies past M or whose column of B lies past N load row 0 (column 0) of
+// the tile instead, so every address is inside A and B and every load is
+// issued (the exact vmcnt counts hold).  Those LDS rows and columns only feed
+// outputs past M or N, which are never stored.
 template <int DT, bool AK, int BM, int BN, int WGM, int WGN, int SA, int SB, int OCC, bool SPLIT,
-          bool PP = false, bool WIDE = false, bool GL = false>
+          bool PP = false, bool WIDE = false, bool GL = false, bool EDGE = false>
 __global__ void __launch_bounds__(WGM * WGN * 64)
 __attribute__((amdgpu_waves_per_eu(OCC, OCC)))
 gemm_fl_kernel(const uint16_t *__restrict__ A, const uint16_t *__restrict__ B,
@@ -520,6 +526,7 @@ gemm_fl_kernel(const uint16_t *__restrict__ A, const uint16_t *__restrict__ B,
     // MFMA per block adds the last K_total - ks (< 8) k, and the kernel
     // writes C.
     static_assert(!SPLIT || !dt_is_8bit(DT), "split-K: 16-bit types");
+    static_assert(!EDGE || (GL && PP && !AK && !SPLIT), "edge-clamped global loads: ping-pong tile only");
     const int kb = SPLIT ? (int)blockIdx.y * ks : 0;
     const int K = SPLIT ? min(ks, K_total - kb) : ks;
     const int ldk = K_total;
@@ -588,6 +595,8 @@ gemm_fl_kernel(const uint16_t *__restrict__ A, const uint16_t *__restrict__ B,
             const int kk = P / (BM * 2), b = P % (BM * 2);
             const int m = (((b >> 4) ^ swz_a<BM>(kk)) << 3);
             a_off[q] = (uint32_t)(((int64_t)kk * M + m0 + m) * 2);
+            if constexpr (EDGE)
+                if (m0 + m >= M) a_off[q] = (uint32_t)((int64_t)kk * M * 2);   // row 0 of the tile
         }
     }
     // every B load of a wave has the same chunk swizzle (it depends on the
@@ -647,8 +656,12 @@ gemm_fl_kernel(const uint16_t *__restrict__ A, const uint16_t *__restrict__ B,
     };
     auto issue_b = [&](const u32x4 &d, int pp, int sb, int q) {
         const uint32_t lds = (uint32_t)uniform((int)(lds0 + B_BASE + sb * B_BYTES + (q * NW + wave) * 1024));
-        if constexpr (GL)
-            gdma16_to_lds((const void *)(B + ((int64_t)n0 * ldk + kb + kbase + pp * 2 * BK)), b_offq(q), lds);
+        if constexpr (GL) {
+            uint32_t off = b_offq(q);
+            if constexpr (EDGE)   // column 8(q NW + wave) + l/8 past N: column 0, same k piece
+                if (n0 + 8 * (q * NW + wave) + (lane >> 3) >= N) off = (uint32_t)(b_k0 * 2);
+            gdma16_to_lds((const void *)(B + ((int64_t)n0 * ldk + kb + kbase + pp * 2 * BK)), off, lds);
+        }
         else
             dma_to_lds<16>(d, lds, kmajor_off(pp, b_k0, b_offq(q)));
     };
@@ -1111,7 +1124,7 @@ gemm_fl_kernel(const uint16_t *__restrict__ A, const uint16_t *__restrict__ B,
         for (int s = 0; s < TN / 8; ++s) {
             const int c = s * 8 + (el >> 3);
             const u32x4 v = *(MIGEMM_LDS const u32x4 *)(win + c * CS + (el & 7) * 16);
-            if (GL || (gm < M && gn + c < N)) *(u32x4 *)(cw + (size_t)c * M) = v;
+            if ((GL && !EDGE) || (gm < M && gn + c < N)) *(u32x4 *)(cw + (size_t)c * M) = v;
         }
     } else {
 #pragma unroll
@@ -1183,6 +1196,15 @@ static hipError_t launch_fl(const GemmLaunch &L, hipStream_t stream)
                                L.num_pid_m, L.num_pid_n, L.group_m, L.num_xcd, L.c_vec, L.scale, L.K & ~7,
                                (float *)L.clocks);
             return hipGetLastError();
+        }
+        if constexpr (PP && !AK) {
+            if (L.edge_gl) {
+                hipLaunchKernelGGL((gemm_fl_kernel<DT, AK, BM, BN, WGM, WGN, SA, SB, OC, false, PP, WIDE, true, true>),
+                                   dim3((unsigned)L.grid), block, 0, stream, L.A, L.B, L.C, L.M, L.N, L.K,
+                                   L.num_pid_m, L.num_pid_n, L.group_m, L.num_xcd, L.c_vec, L.scale, L.K & ~7,
+                                   (float *)L.clocks);
+                return hipGetLastError();
+            }
         }
     }
     hipLaunchKernelGGL((gemm_fl_kernel<DT, AK, BM, BN, WGM, WGN, SA, SB, OC, false, PP, WIDE>),

@@ -115,6 +115,10 @@ struct GemmLaunch {
     int in_range;                 // 1: every tile load lies inside A and B (16-byte rows, M and N
                                   // multiples of the tile, K of 64): the full-line tiles (9-13, 16,
                                   // 17) then load through global addresses (no range check)
+    int edge_gl;                  // 1: not in range, but 16-byte rows, an m-major A and (K & ~7) a
+                                  // multiple of 64: the ping-pong tile (16) loads through global
+                                  // addresses, lanes past M or N re-reading the tile's first row
+                                  // or column
 };
 
 // Sum of split-K partials: C = round(sum_z part[z][n][m]) (gemm.hip).

@@ -349,6 +349,24 @@ def test_pingpong_tile_bit_identical_random_shapes():
         assert np.array_equal(g16, g10), (M, N, K, fmt)
 
 
+def test_pingpong_edge_global_loads_bit_identical_to_tile_10():
+    # ragged M or N with 16-byte rows and K a multiple of 64: tile 16 loads
+    # through global addresses, the lanes past M or N re-reading the tile's
+    # first row or column (tile 10 takes the range-checked buffer loads);
+    # the results must agree bit for bit, and C's guard bands stay intact
+    for i, (M, N, K) in enumerate([(520, 264, 1024), (1032, 136, 512), (264, 600, 128), (8, 8, 64),
+                                   (776, 1000, 192), (2056, 520, 256), (256, 200, 1024)]):
+        fmt = FMTS[i % 2]
+        A, B = synth.gemm_operands(M, N, K, fmt, ("normal", 1.0, 1.0), seed=70 + i)
+        print("case pingpong edge", (M, N, K), fmt, flush=True)
+        g10, guards10, _ = gemm_gpu(A, B, M, N, K, fmt, tile=10)
+        g16, guards16, unchanged = gemm_gpu(A, B, M, N, K, fmt, tile=16)
+        assert guards10 and guards16 and unchanged
+        assert np.array_equal(g16, g10), (M, N, K, fmt)
+        if i == 0:
+            assert_parity(g16, oracle.gemm(A, B, M, N, K, fmt), fmt, "pingpong edge %s" % ((M, N, K),))
+
+
 def test_tensor_wrapper_and_stream():
     import torch
     from bf16_gemm_decode_amd import gemm
