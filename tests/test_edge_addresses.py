@@ -1,0 +1,63 @@
+"""Bounds of the ping-pong tile's global-address loads on ragged launches
+(gemm.hip, gemm_fl_kernel with EDGE): a model of the kernel's per-lane load
+offsets, with the lanes past M or N moved to the tile's row 0 or column 0,
+enumerated for every tile, wave, lane, and the first and last sub-step and
+stage (addresses grow with k, so those bound the rest).  Every 16-byte load
+must lie inside A (M*K*2 bytes) and B (N*K*2 bytes).  Host logic only: the
+tile constants below are tile 16's (256x256, 4x2 waves, rings of 4 A
+sub-steps of 32 k and 3 B stages of 64 k)."""
+import pytest
+
+BM, BN, WGM, WGN, BK = 256, 256, 4, 2, 32
+NW = WGM * WGN
+LA = BK * BM * 2 // (1024 * NW)          # A loads per wave per sub-step
+LB = BN * 128 // (1024 * NW)             # B loads per wave per 64-k stage
+
+
+def swz_a(kk):
+    return (((kk & 7) << 1) ^ (kk & 8)) & (BM // 8 - 1)
+
+
+def edge_loads(M, N, K):
+    ks = K & ~7
+    J = (((ks + BK - 1) // BK) + 1) & ~1
+    P_ = J // 2
+    for m0 in range(0, M, BM):
+        for n0 in range(0, N, BN):
+            for wave in range(NW):
+                for lane in range(64):
+                    for q in range(LA):
+                        P = (q * NW + wave) * 1024 + lane * 16
+                        kk, b = P // (BM * 2), P % (BM * 2)
+                        m = ((b >> 4) ^ swz_a(kk)) << 3
+                        off = (kk * M + m0 + m) * 2 if m0 + m < M else kk * M * 2
+                        for jj in {0, max(J - 1, 0)} if J else ():
+                            yield "A", jj * BK * M * 2 + off
+                    c0 = 8 * wave + (lane >> 3)
+                    x = (lane & 7) ^ ((c0 >> 1) & 7)
+                    for q in range(LB):
+                        col = n0 + c0 + 8 * q * NW
+                        off = (c0 * K + 8 * x) * 2 + 8 * q * NW * K * 2 if col < N else 8 * x * 2
+                        for pp in {0, max(P_ - 1, 0)} if P_ else ():
+                            yield "B", (n0 * K + pp * 2 * BK) * 2 + off
+
+
+@pytest.mark.parametrize("M,N,K", [(520, 264, 1024), (264, 136, 128), (8, 8, 64), (1032, 136, 512),
+                                   (776, 1000, 192), (2056, 520, 256), (256, 200, 1024), (5000, 3000, 64)])
+def test_edge_clamped_loads_stay_inside_operands(M, N, K):
+    assert (K & ~7) % 64 == 0 and M % 8 == 0          # the planner's condition for these launches
+    size = {"A": M * K * 2, "B": N * K * 2}
+    n = 0
+    for which, addr in edge_loads(M, N, K):
+        assert 0 <= addr and addr + 16 <= size[which], (which, addr, size[which])
+        n += 1
+    assert n > 0
+
+
+def test_unclamped_loads_would_leave_the_operands():
+    # the clamp matters: without it a ragged tile reads past the end of B
+    M, N, K = 520, 264, 1024
+    n0 = 256                                        # the last column tile
+    worst = max((n0 * K + (K - 2 * BK)) * 2 + (c0 * K + 8 * 7) * 2 + 8 * q * NW * K * 2
+                for c0 in range(64) for q in range(LB))
+    assert worst + 16 > N * K * 2
