@@ -501,12 +501,13 @@ constexpr int pp_loads_after(int L, int t)
 // GL: every load lies inside A and B (the caller checked M, N, K and the row
 // alignment against the tile), so the loads may use global addresses, which
 // issue faster from L2 than the range-checked buffer form.  GL with EDGE (the
-// ping-pong tile, m-major A): the k loop stays inside K and A's rows come in
-// whole 8-element pieces, but the tile may pass M or N; the lanes whose piece
-// of A lies past M or whose column of B lies past N load row 0 (column 0) of
-// the tile instead, so every address is inside A and B and every load is
-// issued (the exact vmcnt counts hold).  Those LDS rows and columns only feed
-// outputs past M or N, which are never stored.
+// 256x256 tiles 10 and 16, 16-bit types, unsplit): the k loop stays inside K
+// and the rows are 16-byte aligned (an m-major A's 8-element pieces never
+// straddle M), but the tile may pass M or N; the lanes whose piece or row of
+// A lies past M or whose column of B lies past N load row 0 (column 0) of
+// the tile at the same k instead, so every address is inside A and B and
+// every load is issued (the exact vmcnt counts hold).  Those LDS rows and
+// columns only feed outputs past M or N, which are never stored.
 template <int DT, bool AK, int BM, int BN, int WGM, int WGN, int SA, int SB, int OCC, bool SPLIT,
           bool PP = false, bool WIDE = false, bool GL = false, bool EDGE = false>
 __global__ void __launch_bounds__(WGM * WGN * 64)
@@ -526,7 +527,7 @@ gemm_fl_kernel(const uint16_t *__restrict__ A, const uint16_t *__restrict__ B,
     // MFMA per block adds the last K_total - ks (< 8) k, and the kernel
     // writes C.
     static_assert(!SPLIT || !dt_is_8bit(DT), "split-K: 16-bit types");
-    static_assert(!EDGE || (GL && PP && !AK && !SPLIT), "edge-clamped global loads: ping-pong tile only");
+    static_assert(!EDGE || (GL && !SPLIT && !WIDE && !dt_is_8bit(DT)), "edge-clamped global loads: 16-bit, unsplit");
     const int kb = SPLIT ? (int)blockIdx.y * ks : 0;
     const int K = SPLIT ? min(ks, K_total - kb) : ks;
     const int ldk = K_total;
@@ -588,6 +589,8 @@ gemm_fl_kernel(const uint16_t *__restrict__ A, const uint16_t *__restrict__ B,
     for (int q = 0; q < NAO; ++q) {
         if constexpr (AK) {
             kmajor_lane(q, ldk, a_off[q], a_k[q]);
+            if constexpr (EDGE)   // row 8(q NW + wave) + l/8 past M: row 0, same k piece
+                if (m0 + 8 * (q * NW + wave) + (lane >> 3) >= M) a_off[q] = (uint32_t)(a_k[q] * 2);
         } else {
             // m-major A: piece P = (q*NW + wave) KiB of the stage, row kk,
             // swizzled 16-byte chunks
@@ -1197,7 +1200,7 @@ static hipError_t launch_fl(const GemmLaunch &L, hipStream_t stream)
                                (float *)L.clocks);
             return hipGetLastError();
         }
-        if constexpr (PP && !AK) {
+        if constexpr (BM == 256 && BN == 256 && WGM * WGN == 8 && !WIDE && !dt_is_8bit(DT)) {
             if (L.edge_gl) {
                 hipLaunchKernelGGL((gemm_fl_kernel<DT, AK, BM, BN, WGM, WGN, SA, SB, OC, false, PP, WIDE, true, true>),
                                    dim3((unsigned)L.grid), block, 0, stream, L.A, L.B, L.C, L.M, L.N, L.K,

@@ -1,11 +1,11 @@
-"""Bounds of the ping-pong tile's global-address loads on ragged launches
-(gemm.hip, gemm_fl_kernel with EDGE): a model of the kernel's per-lane load
+"""Bounds of the 256x256 tiles' global-address loads on ragged launches
+(gemm.hip, gemm_fl_kernel with EDGE; tiles 10 and 16): a model of the kernel's per-lane load
 offsets, with the lanes past M or N moved to the tile's row 0 or column 0,
 enumerated for every tile, wave, lane, and the first and last sub-step and
 stage (addresses grow with k, so those bound the rest).  Every 16-byte load
 must lie inside A (M*K*2 bytes) and B (N*K*2 bytes).  Host logic only: the
-tile constants below are tile 16's (256x256, 4x2 waves, rings of 4 A
-sub-steps of 32 k and 3 B stages of 64 k)."""
+tile constants below are those of the 256x256 tiles (4x2 waves; an m-major A
+in sub-steps of 32 k rows, a k-major A and B in stages of 64 k)."""
 import pytest
 
 BM, BN, WGM, WGN, BK = 256, 256, 4, 2, 32
@@ -16,6 +16,23 @@ LB = BN * 128 // (1024 * NW)             # B loads per wave per 64-k stage
 
 def swz_a(kk):
     return (((kk & 7) << 1) ^ (kk & 8)) & (BM // 8 - 1)
+
+
+def kmajor_a_loads(M, K):
+    # k-major A (A(m,k) = A[k + m*K]): stage of 64 k, load q of 2*LA per
+    # stage fills rows 8(q NW + wave) + l/8 with 16-byte piece x
+    ks = K & ~7
+    P_ = ((((ks + BK - 1) // BK) + 1) & ~1) // 2
+    la = BM * 128 // (2048 * NW)
+    for m0 in range(0, M, BM):
+        for wave in range(NW):
+            for lane in range(64):
+                for q in range(2 * la):
+                    c = 8 * (q * NW + wave) + (lane >> 3)
+                    x = (lane & 7) ^ ((c >> 1) & 7)
+                    off = (c * K + 8 * x) * 2 if m0 + c < M else 8 * x * 2
+                    for pp in {0, max(P_ - 1, 0)} if P_ else ():
+                        yield "A", (m0 * K + pp * 2 * BK) * 2 + off
 
 
 def edge_loads(M, N, K):
@@ -50,6 +67,16 @@ def test_edge_clamped_loads_stay_inside_operands(M, N, K):
     n = 0
     for which, addr in edge_loads(M, N, K):
         assert 0 <= addr and addr + 16 <= size[which], (which, addr, size[which])
+        n += 1
+    assert n > 0
+
+
+@pytest.mark.parametrize("M,N,K", [(520, 264, 1024), (264, 136, 128), (8, 8, 64), (4000, 520, 512), (776, 1000, 192)])
+def test_edge_clamped_kmajor_a_loads_stay_inside_a(M, N, K):
+    size = M * K * 2
+    n = 0
+    for _, addr in kmajor_a_loads(M, K):
+        assert 0 <= addr and addr + 16 <= size, (addr, size)
         n += 1
     assert n > 0
 

@@ -129,3 +129,36 @@ def test_8bit_staged_c_equals_direct(fmt, tile, shape):
     else:
         ok, rep = oracle.check(c, ref, "bf16")
         assert ok, rep
+
+
+@pytest.mark.parametrize("tile", [10, 16])
+@pytest.mark.parametrize("kmajor", [False, True])
+@pytest.mark.parametrize("shape", [(520, 264, 1024), (264, 600, 128), (8, 8, 64), (4000, 520, 512)])
+def test_ragged_global_loads_equal_buffer_loads(tile, kmajor, shape):
+    # ragged M or N, 16-byte rows, K a multiple of 64: the 256x256 tiles load
+    # through global addresses (lanes past M or N re-reading the tile's first
+    # row or column); the same A placed 8 bytes later (rows no longer 16-byte
+    # aligned) takes the range-checked buffer loads.  Same bits.
+    import torch
+    from bf16_gemm_decode_amd import binding
+    from helpers import dev, Guarded
+    if tile == 16 and kmajor:
+        pytest.skip("the ping-pong tile takes an m-major A only")
+    M, N, K = shape
+    fmt = "bf16"
+    A, B = synth.gemm_operands(M, N, K, fmt, ("normal", 1.0, 1.0), 2700 + M + N)
+    print("case ragged global vs buffer", tile, kmajor, shape, flush=True)
+    fn = binding.gemm_tn_ex_ptr if kmajor else binding.gemm_ex_ptr
+    outs = []
+    for shift in (0, 4):
+        dA = dev(np.concatenate([np.zeros(shift, np.uint16), A]))
+        dB = dev(B)
+        C = Guarded(M * N)
+        code = fn(binding.BF16, dA.data_ptr() + 2 * shift, dB.data_ptr(), C.ptr, M, N, K, tile, 0, 1)
+        assert code == 0, code
+        torch.cuda.synchronize()
+        assert C.guards_intact()
+        outs.append(C.out())
+    assert np.array_equal(outs[0], outs[1]), "global and buffer loads differ"
+    ref_a = kmajor_to_colmajor(A, M, K) if kmajor else A
+    assert_parity(outs[0], oracle.gemm(ref_a, B, M, N, K, fmt), fmt, "ragged %s tile %d" % (shape, tile))
