@@ -225,7 +225,7 @@ int plan_gemm(int dtype, const uint16_t *A, const uint16_t *B, const uint16_t *C
     L.num_xcd = xcd_remap ? 8 : 1;
     L.grid = pm * pn;
     L.in_range = (L.vec_a == 8 && L.vec_b == 8 && M % bm == 0 && N % bn == 0 && K % 64 == 0) ? 1 : 0;
-    L.edge_gl = (!L.in_range && !q8 && L.vec_a == 8 && L.vec_b == 8 && (K & ~7) % 64 == 0) ? 1 : 0;
+    L.edge_gl = (!L.in_range && L.vec_a == 8 && L.vec_b == 8 && (K & ~7) % 64 == 0) ? 1 : 0;
     launch = (M > 0 && N > 0);
     return MIGEMM_OK;
 }

@@ -115,8 +115,8 @@ struct GemmLaunch {
     int in_range;                 // 1: every tile load lies inside A and B (16-byte rows, M and N
                                   // multiples of the tile, K of 64): the full-line tiles (9-13, 16,
                                   // 17) then load through global addresses (no range check)
-    int edge_gl;                  // 1: not in range, but 16-bit types, 16-byte rows and (K & ~7) a
-                                  // multiple of 64: the 256x256 tiles (10, 16) load through global
+    int edge_gl;                  // 1: not in range, but 16-byte rows and (K & ~7) a multiple of
+                                  // 64: the 8-wave 256-row tiles (10, 16, 17) load through global
                                   // addresses, lanes past M or N re-reading the tile's first row
                                   // or column
 };

@@ -35,12 +35,13 @@ def kmajor_a_loads(M, K):
                         yield "A", (m0 * K + pp * 2 * BK) * 2 + off
 
 
-def edge_loads(M, N, K):
+def edge_loads(M, N, K, bn=BN):
+    lb = bn * 128 // (1024 * NW)
     ks = K & ~7
     J = (((ks + BK - 1) // BK) + 1) & ~1
     P_ = J // 2
     for m0 in range(0, M, BM):
-        for n0 in range(0, N, BN):
+        for n0 in range(0, N, bn):
             for wave in range(NW):
                 for lane in range(64):
                     for q in range(LA):
@@ -52,20 +53,21 @@ def edge_loads(M, N, K):
                             yield "A", jj * BK * M * 2 + off
                     c0 = 8 * wave + (lane >> 3)
                     x = (lane & 7) ^ ((c0 >> 1) & 7)
-                    for q in range(LB):
+                    for q in range(lb):
                         col = n0 + c0 + 8 * q * NW
                         off = (c0 * K + 8 * x) * 2 + 8 * q * NW * K * 2 if col < N else 8 * x * 2
                         for pp in {0, max(P_ - 1, 0)} if P_ else ():
                             yield "B", (n0 * K + pp * 2 * BK) * 2 + off
 
 
+@pytest.mark.parametrize("bn", [256, 128])        # 256x256 tiles; the 256x128 FP8 tile (B side)
 @pytest.mark.parametrize("M,N,K", [(520, 264, 1024), (264, 136, 128), (8, 8, 64), (1032, 136, 512),
                                    (776, 1000, 192), (2056, 520, 256), (256, 200, 1024), (5000, 3000, 64)])
-def test_edge_clamped_loads_stay_inside_operands(M, N, K):
+def test_edge_clamped_loads_stay_inside_operands(M, N, K, bn):
     assert (K & ~7) % 64 == 0 and M % 8 == 0          # the planner's condition for these launches
     size = {"A": M * K * 2, "B": N * K * 2}
     n = 0
-    for which, addr in edge_loads(M, N, K):
+    for which, addr in edge_loads(M, N, K, bn):
         assert 0 <= addr and addr + 16 <= size[which], (which, addr, size[which])
         n += 1
     assert n > 0

@@ -162,3 +162,25 @@ def test_ragged_global_loads_equal_buffer_loads(tile, kmajor, shape):
     assert np.array_equal(outs[0], outs[1]), "global and buffer loads differ"
     ref_a = kmajor_to_colmajor(A, M, K) if kmajor else A
     assert_parity(outs[0], oracle.gemm(ref_a, B, M, N, K, fmt), fmt, "ragged %s tile %d" % (shape, tile))
+
+
+@pytest.mark.parametrize("fmt,tile", [("i8", 10), ("f8e4m3", 17), ("f8e5m2", 17)])
+@pytest.mark.parametrize("shape", [(520, 264, 1024), (4000, 136, 512), (8, 8, 128)])
+def test_8bit_ragged_global_loads_match_oracle(fmt, tile, shape):
+    # 8-bit operands always have 16-byte rows, so ragged M or N with K a
+    # multiple of 128 takes the global loads with the edge lanes re-reading
+    # the tile's first row or column: INT8 must equal the oracle bit for
+    # bit, FP8 within its bound; C's guard bands stay intact.  (The
+    # in-range-against-ragged test above compares such launches with
+    # in-range ones bit for bit.)
+    M, N, K = shape
+    At, B = synth.q8_operands(M, N, K, fmt, seed=2800 + M)
+    print("case 8-bit ragged global", fmt, tile, shape, flush=True)
+    c, guards, unchanged = gemm_tn_q_gpu(At, B, M, N, K, fmt, 0.5, tile)
+    assert guards and unchanged
+    ref = oracle.gemm_tn_q(At, B, M, N, K, fmt, 0.5)
+    if fmt == "i8":
+        assert np.array_equal(c, ref.bits)
+    else:
+        ok, rep = oracle.check(c, ref, "bf16")
+        assert ok, rep
