@@ -147,15 +147,18 @@ int plan_gemm(int dtype, const uint16_t *A, const uint16_t *B, const uint16_t *C
         auto take = [&](int t, int64_t c) {
             if (c < cost) { cost = c; best = t; }
         };
-        // With every load of the launch in range the full-line tiles load
-        // through global addresses and their smaller shapes overtake the
-        // other kernels (BF16, per round at K = 4096, measured: 256x128 74
-        // us, 128x128 46 with an m-major A, 42 k-major; 8192x1024x16384
-        // 0.295 ms on 256x128 against 0.34 on the plain 256x128 tile,
-        // 2048x2048x16384 0.18 on 128x128 against 0.22)
+        // With 16-byte rows and K a multiple of 64 the full-line tiles load
+        // through global addresses (in range, or with the lanes past M or N
+        // re-reading the tile's first row or column) and their smaller
+        // shapes overtake the other kernels (BF16, per round at K = 4096,
+        // measured: 256x128 74 us, 128x128 46 with an m-major A, 42
+        // k-major; 8192x1024x16384 0.295 ms on 256x128 against 0.34 on the
+        // plain 256x128 tile, 2048x2048x16384 0.18 on 128x128 against 0.22;
+        // ragged: 8000x1000x16384 0.256 on 256x128 against 0.29 on the
+        // plain one, 2000x2000x16384 0.163 on 128x128 against 0.204)
         const bool k64 = K % 64 == 0;
-        const bool in2 = wide && k64 && M % 256 == 0 && N % 128 == 0;
-        const bool in1 = wide && k64 && M % 128 == 0 && N % 128 == 0;
+        const bool in2 = wide && k64;
+        const bool in1 = wide && k64;
         if (fl) take(a_kmajor ? TILE_256x256_FL8 : TILE_256x256_PP, cdiv(t256, 256) * (a_kmajor ? 110 : 102));
         if (in2) take(TILE_256x128_FL, cdiv(t2, 256) * 74);
         else if (wide && !a_kmajor) take(TILE_256x128, cdiv(t2, 256) * 80);

@@ -501,7 +501,7 @@ constexpr int pp_loads_after(int L, int t)
 // GL: every load lies inside A and B (the caller checked M, N, K and the row
 // alignment against the tile), so the loads may use global addresses, which
 // issue faster from L2 than the range-checked buffer form.  GL with EDGE (the
-// 8-wave tiles with 256 rows, 10, 16 and 17, unsplit): the k loop stays inside K
+// full-line tiles, unsplit): the k loop stays inside K
 // and the rows are 16-byte aligned (an m-major A's 8-element pieces never
 // straddle M), but the tile may pass M or N; the lanes whose piece or row of
 // A lies past M or whose column of B lies past N load row 0 (column 0) of
@@ -527,7 +527,7 @@ gemm_fl_kernel(const uint16_t *__restrict__ A, const uint16_t *__restrict__ B,
     // MFMA per block adds the last K_total - ks (< 8) k, and the kernel
     // writes C.
     static_assert(!SPLIT || !dt_is_8bit(DT), "split-K: 16-bit types");
-    static_assert(!EDGE || (GL && !SPLIT && BM == 256 && WGM * WGN == 8), "edge-clamped global loads: 256-row 8-wave tiles, unsplit");
+    static_assert(!EDGE || (GL && !SPLIT), "edge-clamped global loads: unsplit launches");
     const int kb = SPLIT ? (int)blockIdx.y * ks : 0;
     const int K = SPLIT ? min(ks, K_total - kb) : ks;
     const int ldk = K_total;
@@ -1200,7 +1200,7 @@ static hipError_t launch_fl(const GemmLaunch &L, hipStream_t stream)
                                (float *)L.clocks);
             return hipGetLastError();
         }
-        if constexpr (BM == 256 && WGM * WGN == 8) {
+        {
             if (L.edge_gl) {
                 hipLaunchKernelGGL((gemm_fl_kernel<DT, AK, BM, BN, WGM, WGN, SA, SB, OC, false, PP, WIDE, true, true>),
                                    dim3((unsigned)L.grid), block, 0, stream, L.A, L.B, L.C, L.M, L.N, L.K,

@@ -116,7 +116,7 @@ struct GemmLaunch {
                                   // multiples of the tile, K of 64): the full-line tiles (9-13, 16,
                                   // 17) then load through global addresses (no range check)
     int edge_gl;                  // 1: not in range, but 16-byte rows and (K & ~7) a multiple of
-                                  // 64: the 8-wave 256-row tiles (10, 16, 17) load through global
+                                  // 64: the full-line tiles (9-13, 16, 17) load through global
                                   // addresses, lanes past M or N re-reading the tile's first row
                                   // or column
 };

@@ -117,15 +117,16 @@ def test_tn_plan_and_errors():
                                        ((1056, 768, 64), (12, 204)), ((1024, 1024, 1024), (12, 256)),
                                        ((1152, 1408, 256), (12, 396)),
                                        ((1536, 1536, 256), (13, 144)),
-                                       ((1544, 1536, 256), (13 if kmaj else 3, 156)),
+                                       ((1544, 1536, 256), (13, 156)),
                                        ((512, 512, 131072), (20, 256))):
             code, p = binding.gemm_plan(0, P, P + 2 ** 30, P + 2 ** 31, M, N, K, a_kmajor=kmaj)
             assert code == 0 and (p["tile"], p["grid"]) == (tile, grid), (M, N, K, kmaj, p)
-    # every load in range (16-byte rows, M and N multiples of the tile, K of
-    # 64): the full-line 256x128 and 128x128 tiles, which then load through
-    # global addresses; one ragged row block: the plain tiles
+    # 16-byte rows and K a multiple of 64: the full-line 256x128 and 128x128
+    # tiles, which then load through global addresses, in range or with the
+    # lanes past M or N re-reading the tile's first row or column
     for (M, N, K), tile in (((8192, 1024, 16384), 9), ((8200, 1024, 16384), 16), ((2048, 2048, 16384), 13),
-                            ((2056, 2048, 16384), 2), ((4096, 1024, 32768), 13), ((4096, 4096, 4096), 16)):
+                            ((2056, 2048, 16384), 9), ((4096, 1024, 32768), 13), ((4096, 4096, 4096), 16),
+                            ((8000, 1000, 16384), 9), ((2000, 2000, 16384), 13), ((3000, 3000, 4096), 16)):
         code, p = binding.gemm_plan(0, P, P + 2 ** 30, P + 2 ** 31, M, N, K)
         assert code == 0 and p["tile"] == tile, (M, N, K, p)
     # the small kernel's plan, and where it is not offered: B without 16-byte

@@ -131,11 +131,11 @@ def test_8bit_staged_c_equals_direct(fmt, tile, shape):
         assert ok, rep
 
 
-@pytest.mark.parametrize("tile", [10, 16])
+@pytest.mark.parametrize("tile", [10, 16, 9, 13, 12, 11])
 @pytest.mark.parametrize("kmajor", [False, True])
 @pytest.mark.parametrize("shape", [(520, 264, 1024), (264, 600, 128), (8, 8, 64), (4000, 520, 512)])
 def test_ragged_global_loads_equal_buffer_loads(tile, kmajor, shape):
-    # ragged M or N, 16-byte rows, K a multiple of 64: the 256x256 tiles load
+    # ragged M or N, 16-byte rows, K a multiple of 64: the full-line tiles load
     # through global addresses (lanes past M or N re-reading the tile's first
     # row or column); the same A placed 8 bytes later (rows no longer 16-byte
     # aligned) takes the range-checked buffer loads.  Same bits.
