@@ -90,3 +90,53 @@ def test_unclamped_loads_would_leave_the_operands():
     worst = max((n0 * K + (K - 2 * BK)) * 2 + (c0 * K + 8 * 7) * 2 + 8 * q * NW * K * 2
                 for c0 in range(64) for q in range(LB))
     assert worst + 16 > N * K * 2
+
+
+def generic_edge_loads(bm, bn, wgm, wgn, M, N, K, kmajor):
+    # the same model for any full-line tile: bm x bn, wgm x wgn waves
+    nw = wgm * wgn
+    ks = K & ~7
+    J = (((ks + BK - 1) // BK) + 1) & ~1
+    P_ = J // 2
+    la_m, la_k, lb = BK * bm * 2 // (1024 * nw), bm * 128 // (2048 * nw), bn * 128 // (1024 * nw)
+
+    def swz(kk):
+        return (((kk & 7) << 1) ^ (kk & 8)) & (bm // 8 - 1)
+    for m0 in range(0, M, bm):
+        for n0 in range(0, N, bn):
+            for wave in range(nw):
+                for lane in range(64):
+                    if not kmajor:
+                        for q in range(la_m):
+                            P = (q * nw + wave) * 1024 + lane * 16
+                            kk, b = P // (bm * 2), P % (bm * 2)
+                            m = ((b >> 4) ^ swz(kk)) << 3
+                            off = (kk * M + m0 + m) * 2 if m0 + m < M else kk * M * 2
+                            for jj in {0, max(J - 1, 0)} if J else ():
+                                yield "A", jj * BK * M * 2 + off
+                    else:
+                        for q in range(2 * la_k):
+                            c = 8 * (q * nw + wave) + (lane >> 3)
+                            x = (lane & 7) ^ ((c >> 1) & 7)
+                            off = (c * K + 8 * x) * 2 if m0 + c < M else 8 * x * 2
+                            for pp in {0, max(P_ - 1, 0)} if P_ else ():
+                                yield "A", (m0 * K + pp * 2 * BK) * 2 + off
+                    c0 = 8 * wave + (lane >> 3)
+                    x = (lane & 7) ^ ((c0 >> 1) & 7)
+                    for q in range(lb):
+                        col = n0 + c0 + 8 * q * nw
+                        off = (c0 * K + 8 * x) * 2 + 8 * q * nw * K * 2 if col < N else 8 * x * 2
+                        for pp in {0, max(P_ - 1, 0)} if P_ else ():
+                            yield "B", (n0 * K + pp * 2 * BK) * 2 + off
+
+
+@pytest.mark.parametrize("tile", [(256, 128, 4, 1), (128, 128, 2, 2), (64, 32, 2, 1), (64, 64, 2, 1)])
+@pytest.mark.parametrize("kmajor", [False, True])
+@pytest.mark.parametrize("M,N,K", [(520, 264, 1024), (8, 8, 64), (136, 40, 128), (1000, 1000, 256)])
+def test_edge_clamped_loads_four_wave_tiles(tile, kmajor, M, N, K):
+    size = {"A": M * K * 2, "B": N * K * 2}
+    n = 0
+    for which, addr in generic_edge_loads(*tile, M, N, K, kmajor):
+        assert 0 <= addr and addr + 16 <= size[which], (which, addr, size[which])
+        n += 1
+    assert n > 0
