@@ -140,8 +140,18 @@ int plan_gemm(int dtype, const uint16_t *A, const uint16_t *B, const uint16_t *C
         // 17.7, 512x512x2048 23.1 against 29.7).  Over a long K the
         // 128x128 tile's throughput per CU wins again (512x512x131072: 1586
         // us against 1831 on 64x32).
-        if (fl && t128 < 128 && K <= 8192)
+        // With 16-byte rows and K a multiple of 64 (global-address loads,
+        // ragged edges included; BF16, measured): 64x32 ahead of 64x64
+        // everywhere (1024^3 11.6 us against 12.1, 1408x1152x256 6.1
+        // against 6.7, 1024x1024x2048 20.0 against 20.9), and from K = 4096
+        // the 128x128 tile ahead of both (1000x1000x4096 42.9 against 45.0
+        // and 51.8, 1024x1024x8192 79.8 against 85.7 and 95.6): the cost
+        // model below then picks it.
+        if (fl && t128 < 128 && wide && K % 64 == 0) {
+            if (K <= 2048) return (int)TILE_64x32_SK;
+        } else if (fl && t128 < 128 && K <= 8192) {
             return cdiv(M, 64) * cdiv(N, 64) >= 128 ? (int)TILE_64x64_SK : (int)TILE_64x32_SK;
+        }
         int best = TILE_128x128;
         int64_t cost = INT64_MAX;
         auto take = [&](int t, int64_t c) {

@@ -108,14 +108,15 @@ def test_tn_plan_and_errors():
     assert code == 0 and (p["tile_m"], p["tile_n"]) == (256, 128) and p["grid"] == 242   # one round
     code, p = binding.gemm_plan(1, P, P + 2 ** 30, P + 2 ** 31, 2048, 2048, 4096, a_kmajor=True)
     assert code == 0 and (p["tile"], p["grid"]) == (13, 256)
-    # at most 512 tiles of 32x32 (16-byte rows of B, and of a k-major A):
-    # the small-problem kernel; fewer than 128 tiles of 128x128: the 64-row
-    # tiles (64x64 once they fill half the chip), both layouts
+    # at most 768 tiles of 32x32 (16-byte rows of B, and of a k-major A):
+    # the small-problem kernel; fewer than 128 tiles of 128x128 with 16-byte
+    # rows and K a multiple of 64: the 64x32 tile up to K = 2048, beyond it
+    # the 128x128 tile; both layouts
     for kmaj in (False, True):
         for (M, N, K), (tile, grid) in (((512, 512, 512), (20, 256)), ((1024, 512, 4096), (20, 512)),
                                        ((768, 768, 768), (20, 576)), ((1024, 768, 64), (20, 768)),
-                                       ((1056, 768, 64), (12, 204)), ((1024, 1024, 1024), (12, 256)),
-                                       ((1152, 1408, 256), (12, 396)),
+                                       ((1056, 768, 64), (11, 408)), ((1024, 1024, 1024), (11, 512)),
+                                       ((1152, 1408, 256), (11, 792)), ((1000, 1000, 4096), (13, 64)),
                                        ((1536, 1536, 256), (13, 144)),
                                        ((1544, 1536, 256), (13, 156)),
                                        ((512, 512, 131072), (20, 256))):
