@@ -231,10 +231,14 @@ size_t migemm_splitk_workspace_bytes(int M, int N, int splits);
  *   tile:    0 = automatic (with group_m 0: first an exact-shape table of
  *            measured configurations -- the headline FP16 GEMM, the prefill
  *            GEMM in both layouts, the ragged BF16 GEMM -- then tile 20 when
- *            its 32x32 tiles number at most 768 and B has 16-byte rows, then
- *            tile 12 or 11 below 128 tiles of 128x128 and K <= 8192, else the
- *            least estimated time over rounds of workgroups on the 256 CUs
- *            among tiles 16, 2 (9 without 16-byte rows) and 3); 1 = 256x256 (4 waves as 2x2, 4 LDS stages);
+ *            its 32x32 tiles number at most 768 and B has 16-byte rows, then,
+ *            below 128 tiles of 128x128, tile 11 when A and B have 16-byte
+ *            rows and K is a multiple of 64 up to 2048 (otherwise tile 12 or
+ *            11 for K <= 8192), else the least estimated time over rounds of
+ *            workgroups on the 256 CUs among tiles 16, 9 or 2, and 13 or 3,
+ *            the full-line 9 and 13 priced lower when A and B have 16-byte
+ *            rows and K is a multiple of 64, since they then load through
+ *            global addresses); 1 = 256x256 (4 waves as 2x2, 4 LDS stages);
  *            2 = 256x128 (5 stages); 3 = 128x128 (4 stages, two workgroups
  *            per CU); 4 = tile 1 with 5 stages; 5 = 256x256 with the 4 waves
  *            stacked along M; 6 = tile 1 with 3 stages; 7 = 256x256, waves
