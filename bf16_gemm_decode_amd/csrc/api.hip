@@ -131,7 +131,14 @@ int plan_gemm(int dtype, const uint16_t *A, const uint16_t *B, const uint16_t *C
     auto auto_tile = [&]() {
         const int64_t t256 = cdiv(M, 256) * cdiv(N, 256), t2 = cdiv(M, 256) * cdiv(N, 128),
                       t128 = cdiv(M, 128) * cdiv(N, 128);
-        if (small_ok && cdiv(M, 32) * cdiv(N, 32) <= kSmallMaxTiles) return (int)TILE_SMALL;
+        // The small-problem kernel up to 768 of its tiles; with 16-byte rows
+        // and K a multiple of 64 (the full-line tiles on global loads) only
+        // up to 512: above that 64x32 or 128x128 is ahead (BF16, measured:
+        // 768x768 at K = 1024 / 4096 / 8192 11.5 / 41.5 / 79.6 us against
+        // 12.5 / 44.2 / 86.6, 1024x768x512 7.1 against 8.4; at 512 tiles
+        // and below it stays well ahead, 512x1024x4096 32.7 against 41.5)
+        const int64_t small_max = wide && K % 64 == 0 ? 512 : kSmallMaxTiles;
+        if (small_ok && cdiv(M, 32) * cdiv(N, 32) <= small_max) return (int)TILE_SMALL;
         // Fewer than 128 tiles of 128x128 and a short K: the time per k
         // step (barrier and load latency, not the MFMAs) decides, so the
         // most workgroups win: 64x64 when they fill half the chip, else

@@ -231,7 +231,9 @@ size_t migemm_splitk_workspace_bytes(int M, int N, int splits);
  *   tile:    0 = automatic (with group_m 0: first an exact-shape table of
  *            measured configurations -- the headline FP16 GEMM, the prefill
  *            GEMM in both layouts, the ragged BF16 GEMM -- then tile 20 when
- *            its 32x32 tiles number at most 768 and B has 16-byte rows, then,
+ *            its 32x32 tiles number at most 768 (512 when A and B have
+ *            16-byte rows and K is a multiple of 64) and B has 16-byte rows,
+ *            then,
  *            below 128 tiles of 128x128, tile 11 when A and B have 16-byte
  *            rows and K is a multiple of 64 up to 2048 (otherwise tile 12 or
  *            11 for K <= 8192), else the least estimated time over rounds of

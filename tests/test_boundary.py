@@ -108,13 +108,13 @@ def test_tn_plan_and_errors():
     assert code == 0 and (p["tile_m"], p["tile_n"]) == (256, 128) and p["grid"] == 242   # one round
     code, p = binding.gemm_plan(1, P, P + 2 ** 30, P + 2 ** 31, 2048, 2048, 4096, a_kmajor=True)
     assert code == 0 and (p["tile"], p["grid"]) == (13, 256)
-    # at most 768 tiles of 32x32 (16-byte rows of B, and of a k-major A):
-    # the small-problem kernel; fewer than 128 tiles of 128x128 with 16-byte
+    # at most 512 tiles of 32x32 (16-byte rows, K a multiple of 64; 768
+    # otherwise): the small-problem kernel; fewer than 128 tiles of 128x128 with 16-byte
     # rows and K a multiple of 64: the 64x32 tile up to K = 2048, beyond it
     # the 128x128 tile; both layouts
     for kmaj in (False, True):
         for (M, N, K), (tile, grid) in (((512, 512, 512), (20, 256)), ((1024, 512, 4096), (20, 512)),
-                                       ((768, 768, 768), (20, 576)), ((1024, 768, 64), (20, 768)),
+                                       ((768, 768, 768), (11, 288)), ((768, 768, 4096), (13, 36)), ((1024, 768, 64), (11, 384)),
                                        ((1056, 768, 64), (11, 408)), ((1024, 1024, 1024), (11, 512)),
                                        ((1152, 1408, 256), (11, 792)), ((1000, 1000, 4096), (13, 64)),
                                        ((1536, 1536, 256), (13, 144)),
@@ -138,7 +138,7 @@ def test_tn_plan_and_errors():
         (20, 32, 32, 32, 4, 17 * 16, 16384)
     # 8 waves once there are at most 256 tiles and K >= 1024
     for (M, N, K), waves in (((512, 512, 1016), 4), ((512, 512, 1024), 8), ((544, 512, 1024), 4),
-                             ((256, 256, 32768), 8), ((768, 768, 4096), 4)):
+                             ((256, 256, 32768), 8), ((640, 640, 4096), 4)):
         code, p = binding.gemm_plan(1, P, P + 2 ** 30, P + 2 ** 31, M, N, K)
         assert code == 0 and (p["tile"], p["waves"], p["lds_bytes"]) == (20, waves, waves * 4096), (M, N, K, p)
     assert binding.gemm_plan(1, P, P + 2 ** 30, P + 2 ** 31, 512, 512, 516)[1]["tile"] != 20
